@@ -1,0 +1,153 @@
+/*
+ * moba.h — C ABI of libmoba.so, the MI355X (gfx950) MoBA prefill forward.
+ *
+ * MoBA (Mixture of Block Attention) cuts K into blocks of block_size
+ * tokens, mean-pools each block, lets every query score the eligible blocks
+ * by the inner product with the pooled key, always keeps the query's own
+ * block, keeps the top_k blocks in total, and runs softmax attention over
+ * the keys of the chosen blocks only (causal inside the own block).
+ * Sources, cited by page title and section:
+ *   [R] «MoBA 复现代码跑不通时先把本地仓库交给 Codex 读» (mhpq.cn)
+ *   [P] «月之暗面 MoBA 论文解读：用 TaoToken 统一 Key 跑通稀疏注意力配置骨架» (gsyq.cn)
+ *   [S] MOBA serving article, first heading «长上下文推理为什么卡在注意力这一步» (hncyxsy.com)
+ *
+ * Conventions for every entry point:
+ *   - Tensors q, k, v, o are [batch, heads, seq_len, head_dim], contiguous,
+ *     row-major, in device memory, of the problem's dtype (fp32 or bf16).
+ *   - block_idx is int32 [batch, heads, seq_len, top_k] in device memory.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     never allocates device memory and keeps no per-call state.
+ *   - stream is a hipStream_t (NULL = the null stream). Work is queued on
+ *     it and the call returns without synchronising; a device fault shows
+ *     at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched. On
+ *     error nothing is launched and no output is touched; the returned code
+ *     names the class of error and moba_last_error() (per calling thread)
+ *     names the parameter.
+ *   - Results are deterministic: the same inputs give bit-identical o and
+ *     block_idx on every call.
+ *   - Calls on different streams with distinct workspaces may run
+ *     concurrently.
+ */
+#ifndef MOBA_H
+#define MOBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOBA_ABI_VERSION 1
+
+typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype_t;
+
+typedef enum {
+  MOBA_OK = 0,
+  MOBA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOBA_ERR_SHAPE = 2,       /* non-positive size, or seq_len % block_size != 0 */
+  MOBA_ERR_ARG = 3,         /* top_k < 1, or another out-of-range scalar */
+  MOBA_ERR_DTYPE = 4,       /* dtype is neither MOBA_F32 nor MOBA_BF16 */
+  MOBA_ERR_UNSUPPORTED = 5, /* valid MoBA problem outside this build's kernel limits */
+  MOBA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moba_workspace_size */
+  MOBA_ERR_DEVICE = 7       /* a HIP call or kernel launch failed */
+} moba_status_t;
+
+/* One MoBA problem.
+ *   block_size — tokens per key block ([R] §3.1, [P] §3.1). seq_len must be
+ *                a multiple of it (the pages' code asserts the same, [R] §1.1).
+ *   top_k      — blocks each query attends, counting its own forced block
+ *                ([P] §3.1, [S] §3). top_k > seq_len / block_size is clamped,
+ *                so top_k >= the block count gives full attention.
+ *   causal     — nonzero: only blocks before the query's own block may be
+ *                chosen and the own block is causally masked ([P] §3.1
+ *                causal / mask_future, [S] §3). Zero: every other block is
+ *                eligible and no mask is applied inside blocks.
+ *   dtype      — moba_dtype_t of q, k, v and o. Arithmetic accumulates in
+ *                fp32; o is rounded to the dtype (nearest, ties to even).
+ * Kernel limits of this build (MOBA_ERR_UNSUPPORTED otherwise):
+ *   head_dim in {64, 128}; block_size a multiple of 64;
+ *   min(top_k, n_blocks) - 1 <= 16 unless top_k >= n_blocks;
+ *   seq_len < 2^27; batch * heads * n_blocks < 2^31. */
+typedef struct {
+  int64_t batch;
+  int64_t heads;
+  int64_t seq_len;
+  int64_t head_dim;
+  int64_t block_size;
+  int64_t top_k;
+  int32_t causal;
+  int32_t dtype;
+} moba_problem_t;
+
+/* MOBA_ABI_VERSION of the loaded library. */
+int moba_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* moba_status_str(int status);
+
+/* Detail of the last failing call on this thread, naming the bad
+ * parameter ("" after a successful call). Valid until the next call. */
+const char* moba_last_error(void);
+
+/* Bytes of device workspace moba_forward needs for *p (host only, no HIP
+ * call). Fails with the same codes as moba_forward's validation. */
+int moba_workspace_size(const moba_problem_t* p, size_t* bytes);
+
+/* MoBA prefill forward ([P] §3.1, [S] §3; steps listed at the top).
+ *   q, k, v  — inputs (see conventions); read only.
+ *   o        — output attention, same shape and dtype as q.
+ *   block_idx— output, per query the chosen block indices in ascending order
+ *              (own block included), padded with -1 up to top_k entries.
+ *              Among equal gate scores the lower block index is kept (the
+ *              pages' routing check sorts with a stable descending sort,
+ *              [P] §4.1).
+ *   workspace— device scratch of at least moba_workspace_size bytes,
+ *              256-byte aligned; its contents on entry do not matter and
+ *              are left undefined.
+ * Gate scores are selected exactly: a query whose fast (MFMA) scores leave
+ * the cut between kept and dropped blocks inside their rounding bound is
+ * re-scored in fp64. */
+int moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                 void* o, int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Full softmax attention on the same layout (causal if p->causal), used to
+ * measure MoBA's speedup over the method it approximates ([R] §1.2, [P] §1).
+ * block_size and top_k are ignored apart from validation of their sign;
+ * seq_len must be a multiple of 64. Needs no workspace. */
+int moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                       void* o, void* stream);
+
+/* Stage entry point: block mean-pooling only ([P] §3.1 mean_pool).
+ * kbar: device float64 [batch, heads, n_blocks, head_dim] — the pooled keys
+ * the gate uses. Uses the forward's workspace. */
+int moba_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Stage entry point: pooling, gate scores and top-k selection only; writes
+ * block_idx exactly as moba_forward does. Uses the forward's workspace. */
+int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* block_idx,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-kernel timing with HIP events on the launching stream.
+ * moba_timing_enable(1) creates an event pool (host call, not for use under
+ * graph capture) and starts recording a begin/end event pair around every
+ * kernel the library launches; moba_timing_enable(0) stops recording.
+ * moba_timing_read synchronises on the recorded events, writes up to
+ * max_entries {name, launches, total milliseconds} rows and clears the
+ * record; *n_entries receives the number of kernels seen. */
+typedef struct {
+  const char* name;
+  int64_t launches;
+  double total_ms;
+} moba_kernel_time_t;
+
+int moba_timing_enable(int enable);
+int moba_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOBA_H */

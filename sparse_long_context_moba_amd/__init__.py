@@ -1,0 +1,152 @@
+"""MoBA (Mixture of Block Attention) prefill forward for MI355X (gfx950).
+
+Python face of libmoba.so. PyTorch supplies device memory and the stream;
+every step of the computation runs in the library's HIP kernels.
+
+    o, idx = forward(q, k, v, block_size, top_k, causal=True)
+
+q, k, v: [batch, heads, seq_len, head_dim] contiguous CUDA tensors, float32
+or bfloat16. o has q's dtype; idx is int32 [batch, heads, seq_len, top_k]
+with each query's chosen blocks ascending (own block included), -1 padded.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (MOBA_BF16, MOBA_F32, moba_abi_version, moba_dense_forward, moba_forward,
+                   moba_last_error, moba_pool, moba_problem_t, moba_select, moba_status_str,
+                   moba_timing_enable, moba_timing_read, moba_workspace_size)
+
+__all__ = ["MobaError", "forward", "dense", "pool", "select", "problem", "workspace_bytes",
+           "timing", "moba_abi_version", "moba_forward", "moba_dense_forward", "moba_pool",
+           "moba_select", "moba_workspace_size", "moba_status_str", "moba_last_error",
+           "moba_timing_enable", "moba_timing_read", "moba_problem_t"]
+
+_DTYPES = {torch.float32: MOBA_F32, torch.bfloat16: MOBA_BF16}
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = _lib.STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{where}: {self.name} ({moba_status_str(status)}): {moba_last_error()}")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MobaError(status, where)
+
+
+def problem(q: torch.Tensor, block_size: int, top_k: int, causal: bool = True) -> moba_problem_t:
+    if q.dim() != 4:
+        raise ValueError(f"q must be [batch, heads, seq_len, head_dim], got shape {tuple(q.shape)}")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {q.dtype}")
+    B, H, S, D = q.shape
+    return moba_problem_t(B, H, S, D, int(block_size), int(top_k), 1 if causal else 0, _DTYPES[q.dtype])
+
+
+def _tensors(*ts):
+    q = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k and v must share shape, dtype and device")
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def workspace_bytes(p: moba_problem_t) -> int:
+    st, n = moba_workspace_size(p)
+    _check(st, "moba_workspace_size")
+    return n
+
+
+def _workspace(p, device):
+    n = workspace_bytes(p)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("workspace allocation is not 256-byte aligned")
+    return ws, n
+
+
+def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None, idx=None,
+            workspace=None):
+    """MoBA forward. Returns (o, block_idx)."""
+    _tensors(q, k, v)
+    p = problem(q, block_size, top_k, causal)
+    B, H, S, D = q.shape
+    o = torch.empty_like(q) if out is None else out
+    bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device) if idx is None else idx
+    if workspace is None:
+        ws, n = _workspace(p, q.device)
+    else:
+        ws, n = workspace, workspace.numel()
+    with torch.cuda.device(q.device):
+        _check(moba_forward(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), bi.data_ptr(),
+                            ws.data_ptr(), n, _stream(q.device)), "moba_forward")
+    return o, bi
+
+
+def dense(q, k, v, causal: bool = True, out=None):
+    """Full softmax attention (causal or not) with the library's dense kernel."""
+    _tensors(q, k, v)
+    p = problem(q, q.shape[2], 1, causal)
+    o = torch.empty_like(q) if out is None else out
+    with torch.cuda.device(q.device):
+        _check(moba_dense_forward(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  _stream(q.device)), "moba_dense_forward")
+    return o
+
+
+def pool(k, block_size: int):
+    """Block means of K as the gate uses them: float64 [B, H, n_blocks, D]."""
+    _tensors(k)
+    p = problem(k, block_size, 1, True)
+    B, H, S, D = k.shape
+    kbar = torch.empty((B, H, S // block_size if block_size > 0 else 0, D), dtype=torch.float64,
+                       device=k.device)
+    ws, n = _workspace(p, k.device)
+    with torch.cuda.device(k.device):
+        _check(moba_pool(p, k.data_ptr(), kbar.data_ptr(), ws.data_ptr(), n, _stream(k.device)),
+               "moba_pool")
+    return kbar
+
+
+def select(q, k, block_size: int, top_k: int, causal: bool = True):
+    """Routing only: int32 [B, H, S, top_k] exactly as forward() returns it."""
+    _tensors(q, k)
+    p = problem(q, block_size, top_k, causal)
+    B, H, S, D = q.shape
+    bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device)
+    ws, n = _workspace(p, q.device)
+    with torch.cuda.device(q.device):
+        _check(moba_select(p, q.data_ptr(), k.data_ptr(), bi.data_ptr(), ws.data_ptr(), n,
+                           _stream(q.device)), "moba_select")
+    return bi
+
+
+class timing:
+    """Context manager: per-kernel HIP-event timing of library launches.
+
+        with timing() as t: ...
+        t.rows -> [(kernel, launches, total_ms), ...]
+    """
+
+    def __enter__(self):
+        _check(moba_timing_enable(True), "moba_timing_enable")
+        moba_timing_read()  # drop anything recorded before
+        self.rows = []
+        return self
+
+    def __exit__(self, *exc):
+        _check(moba_timing_enable(False), "moba_timing_enable")
+        st, self.rows = moba_timing_read(64)
+        _check(st, "moba_timing_read")
+        return False

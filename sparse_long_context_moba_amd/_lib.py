@@ -1,0 +1,113 @@
+"""ctypes declarations of libmoba.so's C ABI (include/moba.h), same names.
+
+Argument marshalling only: every step of the MoBA forward runs in the HIP
+kernels behind these entry points. There is no fallback: if libmoba.so is
+missing or fails to load, importing the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoba.so")
+
+MOBA_F32, MOBA_BF16 = 0, 1
+STATUS_NAMES = {0: "MOBA_OK", 1: "MOBA_ERR_NULL", 2: "MOBA_ERR_SHAPE", 3: "MOBA_ERR_ARG",
+                4: "MOBA_ERR_DTYPE", 5: "MOBA_ERR_UNSUPPORTED", 6: "MOBA_ERR_WORKSPACE",
+                7: "MOBA_ERR_DEVICE"}
+EXPORTED = ["moba_abi_version", "moba_status_str", "moba_last_error", "moba_workspace_size",
+            "moba_forward", "moba_dense_forward", "moba_pool", "moba_select",
+            "moba_timing_enable", "moba_timing_read"]
+
+
+class moba_problem_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("block_size", ctypes.c_int64),
+                ("top_k", ctypes.c_int64), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class moba_kernel_time_t(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_long_context_moba_amd.build` "
+                          "(hipcc, gfx950). There is no non-HIP fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(moba_problem_t)
+    vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+    sig = {
+        "moba_abi_version": ([], ctypes.c_int),
+        "moba_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "moba_last_error": ([], ctypes.c_char_p),
+        "moba_workspace_size": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+        "moba_forward": ([P, vp, vp, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
+        "moba_dense_forward": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
+        "moba_pool": ([P, vp, vp, vp, sz, vp], ctypes.c_int),
+        "moba_select": ([P, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
+        "moba_timing_enable": ([ctypes.c_int], ctypes.c_int),
+        "moba_timing_read": ([ctypes.POINTER(moba_kernel_time_t), ctypes.c_int,
+                              ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+LIB = _load()
+
+
+def moba_abi_version() -> int:
+    return LIB.moba_abi_version()
+
+
+def moba_status_str(status: int) -> str:
+    return LIB.moba_status_str(status).decode()
+
+
+def moba_last_error() -> str:
+    return LIB.moba_last_error().decode()
+
+
+def moba_workspace_size(problem: moba_problem_t):
+    """-> (status, bytes)"""
+    n = ctypes.c_size_t(0)
+    st = LIB.moba_workspace_size(ctypes.byref(problem) if problem is not None else None, ctypes.byref(n))
+    return st, n.value
+
+
+def moba_forward(problem, q, k, v, o, block_idx, workspace, workspace_bytes, stream) -> int:
+    return LIB.moba_forward(ctypes.byref(problem) if problem is not None else None,
+                            q, k, v, o, block_idx, workspace, workspace_bytes, stream)
+
+
+def moba_dense_forward(problem, q, k, v, o, stream) -> int:
+    return LIB.moba_dense_forward(ctypes.byref(problem) if problem is not None else None, q, k, v, o, stream)
+
+
+def moba_pool(problem, k, kbar, workspace, workspace_bytes, stream) -> int:
+    return LIB.moba_pool(ctypes.byref(problem) if problem is not None else None, k, kbar, workspace,
+                         workspace_bytes, stream)
+
+
+def moba_select(problem, q, k, block_idx, workspace, workspace_bytes, stream) -> int:
+    return LIB.moba_select(ctypes.byref(problem) if problem is not None else None, q, k, block_idx,
+                           workspace, workspace_bytes, stream)
+
+
+def moba_timing_enable(enable: bool) -> int:
+    return LIB.moba_timing_enable(1 if enable else 0)
+
+
+def moba_timing_read(max_entries: int = 32):
+    """-> (status, [(name, launches, total_ms), ...])"""
+    buf = (moba_kernel_time_t * max_entries)()
+    n = ctypes.c_int(0)
+    st = LIB.moba_timing_read(buf, max_entries, ctypes.byref(n))
+    rows = [(buf[i].name.decode(), int(buf[i].launches), float(buf[i].total_ms))
+            for i in range(min(n.value, max_entries))]
+    return st, rows

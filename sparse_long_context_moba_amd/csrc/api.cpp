@@ -1,0 +1,422 @@
+// C ABI of libmoba.so: validation, workspace layout and the launch sequence
+// of the MoBA prefill forward (pool -> gate/top-k -> varlen pack -> past-block
+// gather attention -> own-block attention + merge).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moba.h"
+#include "launch.h"
+
+namespace moba {
+
+// ------------------------------------------------------------ errors
+static thread_local std::string g_err;
+
+static int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+// ------------------------------------------------------------ timing
+namespace {
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t begin, end;
+};
+std::atomic<bool> g_timing{false};
+std::mutex g_tmu;
+std::vector<hipEvent_t> g_events;
+std::vector<TimedLaunch> g_launches;
+size_t g_next_event = 0;
+constexpr size_t kEventPool = 2 * 16384;
+}  // namespace
+
+KernelTimer::KernelTimer(hipStream_t s, const char* name) : stream(s), slot(-1) {
+  if (!g_timing.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_next_event + 2 > g_events.size()) return;
+  TimedLaunch tl{name, g_events[g_next_event], g_events[g_next_event + 1]};
+  g_next_event += 2;
+  if (hipEventRecord(tl.begin, s) != hipSuccess) return;
+  g_launches.push_back(tl);
+  slot = (int)g_launches.size() - 1;
+}
+
+KernelTimer::~KernelTimer() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  (void)hipEventRecord(g_launches[slot].end, stream);
+}
+
+// ------------------------------------------------------------ planning
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct Plan {
+  int64_t B, H, S, D, Bs, top_k, bh, nb, k_eff, slots;
+  bool causal, bf16_in;
+  int64_t pairs;       // (query, kept past block) pairs over all heads
+  int64_t max_tiles;   // upper bound on gather tiles
+  int rows_per_run;
+  // workspace offsets (bytes)
+  size_t psum, kbar64, kbar32, kbar_hi, kbar_lo, norm, normmax, count, rank, offset, tile_start, qlist,
+      part_o, part_lse, total;
+};
+
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
+  if (!p) return fail(MOBA_ERR_NULL, "problem pointer is NULL");
+  const char* names[] = {"batch", "heads", "seq_len", "head_dim", "block_size"};
+  const int64_t vals[] = {p->batch, p->heads, p->seq_len, p->head_dim, p->block_size};
+  for (int i = 0; i < 5; ++i)
+    if (vals[i] < 1) return fail(MOBA_ERR_SHAPE, std::string(names[i]) + " must be >= 1, got " + std::to_string(vals[i]));
+  if (p->seq_len % p->block_size != 0)
+    return fail(MOBA_ERR_SHAPE, "seq_len " + std::to_string(p->seq_len) + " is not a multiple of block_size " +
+                                    std::to_string(p->block_size));
+  if (p->top_k < 1) return fail(MOBA_ERR_ARG, "top_k must be >= 1, got " + std::to_string(p->top_k));
+  if (p->dtype != MOBA_F32 && p->dtype != MOBA_BF16)
+    return fail(MOBA_ERR_DTYPE, "dtype must be MOBA_F32 (0) or MOBA_BF16 (1), got " + std::to_string(p->dtype));
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(MOBA_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " + std::to_string(p->head_dim));
+  if (p->block_size % 64 != 0)
+    return fail(MOBA_ERR_UNSUPPORTED, "block_size must be a multiple of 64, got " + std::to_string(p->block_size));
+  if (p->seq_len >= (int64_t(1) << 27))
+    return fail(MOBA_ERR_UNSUPPORTED, "seq_len must be below 2^27, got " + std::to_string(p->seq_len));
+  Plan& P = *pl;
+  P.B = p->batch;
+  P.H = p->heads;
+  P.S = p->seq_len;
+  P.D = p->head_dim;
+  P.Bs = p->block_size;
+  P.top_k = p->top_k;
+  P.bh = P.B * P.H;
+  P.nb = P.S / P.Bs;
+  P.k_eff = std::min(P.top_k, P.nb);
+  P.slots = P.k_eff - 1;
+  P.causal = p->causal != 0;
+  P.bf16_in = p->dtype == MOBA_BF16;
+  if (P.bh * P.nb >= (int64_t(1) << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "batch * heads * n_blocks must be below 2^31");
+  if (P.slots > kMaxSlotsHost && P.k_eff < P.nb)
+    return fail(MOBA_ERR_UNSUPPORTED, "top_k " + std::to_string(P.top_k) + " keeps more than " +
+                                          std::to_string(kMaxSlotsHost) + " past blocks per query; use top_k <= " +
+                                          std::to_string(kMaxSlotsHost + 1) + " or top_k >= n_blocks (" +
+                                          std::to_string(P.nb) + ")");
+  if (P.S * std::max<int64_t>(P.slots, 1) >= (int64_t(1) << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "seq_len * (min(top_k, n_blocks) - 1) must be below 2^31");
+  // Exact pair count: every query in block c keeps min(k_eff - 1, eligible) past blocks.
+  int64_t per_head = 0;
+  for (int64_t c = 0; c < P.nb; ++c) {
+    const int64_t elig = P.causal ? c : P.nb - 1;
+    per_head += P.Bs * std::min(P.slots, elig);
+  }
+  P.pairs = per_head * P.bh;
+  if (P.pairs >= (int64_t(1) << 31)) return fail(MOBA_ERR_UNSUPPORTED, "too many (query, block) pairs for int32 lists");
+  P.max_tiles = P.pairs / kGatherTileM + P.bh * P.nb + 1;
+  P.rows_per_run = 64;
+  for (int r : {256, 192, 128}) {
+    if (P.Bs % r == 0) {
+      P.rows_per_run = r;
+      break;
+    }
+  }
+  const size_t esz = P.bf16_in ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up(bytes);
+    return at;
+  };
+  const size_t nbd = (size_t)(P.bh * P.nb * P.D);
+  P.psum = take((size_t)(P.bh * (P.S / P.rows_per_run) * P.D) * 8);
+  P.kbar64 = take(nbd * 8);
+  P.kbar32 = take(nbd * 4);
+  P.kbar_hi = take(nbd * 2);
+  P.kbar_lo = take(nbd * 2);
+  P.norm = take((size_t)(P.bh * P.nb) * 4);
+  P.normmax = take((size_t)P.bh * 4);
+  P.count = take((size_t)(P.bh * P.nb) * 4);
+  P.rank = take((size_t)(P.bh * P.S * P.slots) * 4);
+  if (need_select) {
+    P.offset = take((size_t)(P.bh * P.nb + 1) * 4);
+    P.tile_start = take((size_t)(P.bh * P.nb + 1) * 4);
+    P.qlist = take((size_t)P.pairs * 4);
+    P.part_o = take((size_t)(P.bh * P.S * P.slots * P.D) * esz);
+    P.part_lse = take((size_t)(P.bh * P.S * P.slots) * 4);
+  }
+  P.total = off;
+  return MOBA_OK;
+}
+
+int check_ws(const Plan& P, void* ws, size_t bytes) {
+  if (bytes < P.total)
+    return fail(MOBA_ERR_WORKSPACE, "workspace_bytes " + std::to_string(bytes) + " < required " + std::to_string(P.total));
+  if (P.total > 0 && !ws) return fail(MOBA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return fail(MOBA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return MOBA_OK;
+}
+
+int dev_fail(hipError_t e, const char* what) {
+  return fail(MOBA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define MOBA_TRY(expr, what)                     \
+  do {                                           \
+    hipError_t _e = (expr);                      \
+    if (_e != hipSuccess) return dev_fail(_e, what); \
+  } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// pool + gate: writes block_idx, counts and ranks.
+int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, void* ws, hipStream_t s,
+               double* kbar64_out) {
+  MOBA_TRY(launch_zero(at<char>(ws, P.normmax), P.bh, s), "clear normmax");
+  MOBA_TRY(launch_zero(at<char>(ws, P.count), P.bh * P.nb, s), "clear counts");
+  PoolArgs pa{};
+  pa.k = k;
+  pa.bh = P.bh;
+  pa.seq_len = P.S;
+  pa.block_size = P.Bs;
+  pa.head_dim = (int)P.D;
+  pa.bf16_in = P.bf16_in;
+  pa.rows_per_run = P.rows_per_run;
+  pa.psum = at<double>(ws, P.psum);
+  pa.kbar64 = kbar64_out ? kbar64_out : at<double>(ws, P.kbar64);
+  pa.kbar32 = at<float>(ws, P.kbar32);
+  pa.kbar_hi = at<bf16>(ws, P.kbar_hi);
+  pa.kbar_lo = at<bf16>(ws, P.kbar_lo);
+  pa.norm = at<float>(ws, P.norm);
+  pa.normmax = at<unsigned>(ws, P.normmax);
+  MOBA_TRY(launch_pool(pa, s), "pool launch");
+  if (!block_idx) return MOBA_OK;
+  GateArgs ga{};
+  ga.q = q;
+  ga.kbar64 = pa.kbar64;
+  ga.kbar32 = pa.kbar32;
+  ga.kbar_hi = pa.kbar_hi;
+  ga.kbar_lo = pa.kbar_lo;
+  ga.norm = reinterpret_cast<const float*>(pa.normmax);
+  ga.bh = P.bh;
+  ga.seq_len = P.S;
+  ga.block_size = P.Bs;
+  ga.n_blocks = P.nb;
+  ga.head_dim = (int)P.D;
+  ga.bf16_in = P.bf16_in;
+  ga.causal = P.causal;
+  ga.top_k = (int)P.top_k;
+  ga.k_eff = (int)P.k_eff;
+  ga.block_idx = block_idx;
+  ga.count = at<int32_t>(ws, P.count);
+  ga.rank = at<int32_t>(ws, P.rank);
+  MOBA_TRY(launch_gate(ga, s), "gate launch");
+  return MOBA_OK;
+}
+
+AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, void* o) {
+  AttnArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.o = o;
+  aa.bh = P.bh;
+  aa.seq_len = P.S;
+  aa.block_size = P.Bs;
+  aa.n_blocks = P.nb;
+  aa.head_dim = (int)P.D;
+  aa.bf16_in = P.bf16_in;
+  aa.causal = P.causal;
+  aa.k_eff = (int)P.k_eff;
+  return aa;
+}
+
+}  // namespace
+}  // namespace moba
+
+using namespace moba;
+
+extern "C" {
+
+int moba_abi_version(void) { return MOBA_ABI_VERSION; }
+
+const char* moba_status_str(int status) {
+  switch (status) {
+    case MOBA_OK: return "ok";
+    case MOBA_ERR_NULL: return "null pointer";
+    case MOBA_ERR_SHAPE: return "invalid shape";
+    case MOBA_ERR_ARG: return "invalid argument";
+    case MOBA_ERR_DTYPE: return "invalid dtype";
+    case MOBA_ERR_UNSUPPORTED: return "outside kernel limits";
+    case MOBA_ERR_WORKSPACE: return "workspace too small";
+    case MOBA_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* moba_last_error(void) { return g_err.c_str(); }
+
+int moba_workspace_size(const moba_problem_t* p, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
+  Plan P;
+  const int st = plan_problem(p, &P, true);
+  if (st != MOBA_OK) return st;
+  *bytes = P.total;
+  return MOBA_OK;
+}
+
+int moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                 int32_t* block_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan P;
+  int st = plan_problem(p, &P, true);
+  if (st != MOBA_OK) return st;
+  if (!q) return fail(MOBA_ERR_NULL, "q is NULL");
+  if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
+  if (!v) return fail(MOBA_ERR_NULL, "v is NULL");
+  if (!o) return fail(MOBA_ERR_NULL, "o is NULL");
+  if (!block_idx) return fail(MOBA_ERR_NULL, "block_idx is NULL");
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != MOBA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_select(P, q, k, block_idx, workspace, s, nullptr);
+  if (st != MOBA_OK) return st;
+  AttnArgs aa = attn_args(P, q, k, v, o);
+  aa.part_o = at<void>(workspace, P.part_o);
+  aa.part_lse = at<float>(workspace, P.part_lse);
+  if (P.pairs > 0) {
+    PackArgs pk{};
+    pk.bh = P.bh;
+    pk.seq_len = P.S;
+    pk.block_size = P.Bs;
+    pk.n_blocks = P.nb;
+    pk.causal = P.causal;
+    pk.top_k = (int)P.top_k;
+    pk.k_eff = (int)P.k_eff;
+    pk.tile_m = kGatherTileM;
+    pk.block_idx = block_idx;
+    pk.count = at<int32_t>(workspace, P.count);
+    pk.rank = at<int32_t>(workspace, P.rank);
+    pk.offset = at<int32_t>(workspace, P.offset);
+    pk.tile_start = at<int32_t>(workspace, P.tile_start);
+    pk.qlist = at<int32_t>(workspace, P.qlist);
+    MOBA_TRY(launch_pack(pk, s), "pack launch");
+    aa.offset = pk.offset;
+    aa.tile_start = pk.tile_start;
+    aa.qlist = pk.qlist;
+    aa.max_tiles = P.max_tiles;
+    MOBA_TRY(launch_gather(aa, s), "gather launch");
+  }
+  MOBA_TRY(launch_diag_merge(aa, s), "diag launch");
+  return MOBA_OK;
+}
+
+int moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                       void* stream) {
+  g_err.clear();
+  if (!p) return fail(MOBA_ERR_NULL, "problem pointer is NULL");
+  // Dense attention ignores the block structure: validate it as a problem
+  // whose only block is the whole sequence.
+  moba_problem_t d = *p;
+  if (d.seq_len >= 1) d.block_size = d.seq_len % 64 == 0 ? 64 : d.seq_len;
+  if (d.top_k < 1) return fail(MOBA_ERR_ARG, "top_k must be >= 1, got " + std::to_string(p->top_k));
+  d.top_k = 1;
+  Plan P;
+  const int st = plan_problem(&d, &P, false);
+  if (st != MOBA_OK) {
+    if (st == MOBA_ERR_UNSUPPORTED && p->seq_len % 64 != 0)
+      return fail(MOBA_ERR_UNSUPPORTED, "seq_len must be a multiple of 64 for dense attention");
+    return st;
+  }
+  if (!q) return fail(MOBA_ERR_NULL, "q is NULL");
+  if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
+  if (!v) return fail(MOBA_ERR_NULL, "v is NULL");
+  if (!o) return fail(MOBA_ERR_NULL, "o is NULL");
+  AttnArgs aa = attn_args(P, q, k, v, o);
+  MOBA_TRY(launch_dense(aa, static_cast<hipStream_t>(stream)), "dense launch");
+  return MOBA_OK;
+}
+
+int moba_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  g_err.clear();
+  Plan P;
+  int st = plan_problem(p, &P, true);
+  if (st != MOBA_OK) return st;
+  if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
+  if (!kbar) return fail(MOBA_ERR_NULL, "kbar is NULL");
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != MOBA_OK) return st;
+  return run_select(P, nullptr, k, nullptr, workspace, static_cast<hipStream_t>(stream), kbar);
+}
+
+int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* block_idx, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan P;
+  int st = plan_problem(p, &P, true);
+  if (st != MOBA_OK) return st;
+  if (!q) return fail(MOBA_ERR_NULL, "q is NULL");
+  if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
+  if (!block_idx) return fail(MOBA_ERR_NULL, "block_idx is NULL");
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != MOBA_OK) return st;
+  return run_select(P, q, k, block_idx, workspace, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int moba_timing_enable(int enable) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (enable && g_events.empty()) {
+    g_events.resize(kEventPool);
+    for (auto& e : g_events) {
+      const hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) {
+        g_events.clear();
+        return dev_fail(r, "hipEventCreate");
+      }
+    }
+  }
+  g_timing.store(enable != 0);
+  return MOBA_OK;
+}
+
+int moba_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries) {
+  g_err.clear();
+  if (!n_entries) return fail(MOBA_ERR_NULL, "n_entries is NULL");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  std::vector<moba_kernel_time_t> agg;
+  for (const auto& tl : g_launches) {
+    hipError_t r = hipEventSynchronize(tl.end);
+    if (r != hipSuccess) return dev_fail(r, "hipEventSynchronize");
+    float ms = 0.f;
+    r = hipEventElapsedTime(&ms, tl.begin, tl.end);
+    if (r != hipSuccess) return dev_fail(r, "hipEventElapsedTime");
+    auto it = std::find_if(agg.begin(), agg.end(),
+                           [&](const moba_kernel_time_t& x) { return std::strcmp(x.name, tl.name) == 0; });
+    if (it == agg.end()) agg.push_back({tl.name, 1, (double)ms});
+    else {
+      it->launches += 1;
+      it->total_ms += ms;
+    }
+  }
+  g_launches.clear();
+  g_next_event = 0;
+  *n_entries = (int)agg.size();
+  for (int i = 0; i < (int)agg.size() && i < max_entries; ++i) out[i] = agg[i];
+  return MOBA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Shared device types and helpers for the gfx950 MoBA kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moba {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kMaxSlots = 16;  // max past blocks per query outside "keep all" mode
+
+// ----------------------------------------------------------------- MFMA
+// Lane layouts (checked on gfx950 with integer-valued operands):
+//  32x32x16 bf16: A[i = l%32][k = 8*(l/32) + e], B[k = 8*(l/32) + e][j = l%32],
+//                 C[i = 8*(r/4) + 4*(l/32) + r%4][j = l%32], e < 8, r < 16.
+//  32x32x2 f32:   A[i = l%32][k = l/32], B[k = l/32][j = l%32], C as above.
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row index inside a 32x32 C tile held in accumulator element r of lane half h.
+__device__ __forceinline__ constexpr int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ int shfl_xor32(int x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ double shfl_xor32(double x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short u) {
+  return __uint_as_float(((unsigned)u) << 16);
+}
+
+// Round to nearest even fp32 -> bf16 (inputs here are finite).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+template <typename T>
+struct io;
+template <>
+struct io<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+};
+
+}  // namespace moba

@@ -1,0 +1,96 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moba {
+
+typedef __bf16 bf16;
+
+// Past blocks one query may keep when top_k < n_blocks (register top-k limit).
+constexpr int kMaxSlotsHost = 16;
+
+// Optional per-kernel event timing (enabled through moba_timing_enable).
+// Records a begin event at construction and an end event at destruction on
+// the launching stream; does nothing while timing is off.
+struct KernelTimer {
+  KernelTimer(hipStream_t s, const char* name);
+  ~KernelTimer();
+  hipStream_t stream;
+  int slot;
+};
+
+struct PoolArgs {
+  const void* k;
+  int64_t bh, seq_len, block_size;
+  int head_dim;
+  bool bf16_in;
+  int rows_per_run;
+  double* psum;      // [bh * seq_len / rows_per_run, D]
+  double* kbar64;    // [bh * nb, D]
+  float* kbar32;     // [bh * nb, D]
+  bf16* kbar_hi;     // [bh * nb, D]
+  bf16* kbar_lo;     // [bh * nb, D]
+  float* norm;       // [bh * nb]
+  unsigned* normmax; // [bh], float bits of the largest block norm; zeroed before the launch
+};
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+
+struct GateArgs {
+  const void* q;
+  const double* kbar64;
+  const float* kbar32;
+  const bf16* kbar_hi;
+  const bf16* kbar_lo;
+  const float* norm;  // [bh] largest block-mean L2 norm of the head
+  int64_t bh, seq_len, block_size, n_blocks;
+  int head_dim;
+  bool bf16_in;
+  bool causal;
+  int top_k;        // columns of block_idx
+  int k_eff;        // min(top_k, n_blocks)
+  int32_t* block_idx;  // [bh, S, top_k]
+  int32_t* count;      // [bh * nb], zeroed before the launch
+  int32_t* rank;       // [bh, S, k_eff - 1]: position of (t, slot) in its block's list
+};
+hipError_t launch_gate(const GateArgs& a, hipStream_t s);
+
+struct PackArgs {
+  int64_t bh, seq_len, block_size, n_blocks;
+  bool causal;
+  int top_k, k_eff;
+  int tile_m;                 // queries per gather tile
+  const int32_t* block_idx;   // [bh, S, top_k]
+  const int32_t* count;       // [bh * nb]
+  const int32_t* rank;        // [bh, S, k_eff - 1]
+  int32_t* offset;            // [bh * nb + 1] exclusive scan of count
+  int32_t* tile_start;        // [bh * nb + 1] exclusive scan of ceil(count / tile_m)
+  int32_t* qlist;             // [pairs]: t * (k_eff - 1) + slot
+};
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_zero(void* p, int64_t n_words, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t bh, seq_len, block_size, n_blocks;
+  int head_dim;
+  bool bf16_in;
+  bool causal;
+  int k_eff;
+  // gather (past blocks)
+  const int32_t* offset;
+  const int32_t* tile_start;
+  const int32_t* qlist;
+  int64_t max_tiles;          // grid bound for the gather launch
+  void* part_o;               // [bh, S, k_eff - 1, D] in the input dtype, lane-native order
+  float* part_lse;            // [bh, S, k_eff - 1], log2 domain
+};
+constexpr int kGatherTileM = 128;
+hipError_t launch_gather(const AttnArgs& a, hipStream_t s);
+hipError_t launch_diag_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_dense(const AttnArgs& a, hipStream_t s);
+
+}  // namespace moba

@@ -1,0 +1,109 @@
+// Varlen packing of the routed (query, past block) pairs.
+//
+// After routing, each past block is attended by its own batch of queries,
+// the varlen layout the MoBA pages describe for handing the chosen blocks to
+// the attention kernel without concatenating them into one long sequence
+// («MoBA 复现代码跑不通…» §3.3; the hncyxsy.com MOBA article §3).
+//
+//  pack_scan    — one workgroup: exclusive scans of the per-block query
+//                 counts (list offsets) and of ceil(count / tile_m) (gather
+//                 tile starts) over all heads and blocks.
+//  pack_scatter — one thread per query: places each of its kept past blocks
+//                 into that block's list at offset + rank, where rank came
+//                 from the gate's atomic count. Entries are t*(k_eff-1)+slot.
+#include "common.h"
+#include "launch.h"
+
+namespace moba {
+
+__global__ __launch_bounds__(1024) void pack_scan_kernel(const int32_t* __restrict__ count, int64_t n,
+                                                         int tile_m, int32_t* __restrict__ offset,
+                                                         int32_t* __restrict__ tile_start) {
+  __shared__ int64_t sc[1024];
+  __shared__ int64_t st[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t lo = min<int64_t>(n, tid * per), hi = min<int64_t>(n, lo + per);
+  int64_t c_sum = 0, t_sum = 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int32_t c = count[i];
+    c_sum += c;
+    t_sum += (c + tile_m - 1) / tile_m;
+  }
+  sc[tid] = c_sum;
+  st[tid] = t_sum;
+  __syncthreads();
+  // Inclusive Hillis-Steele scan over the 1024 per-thread totals.
+  for (int w = 1; w < 1024; w <<= 1) {
+    const int64_t a = tid >= w ? sc[tid - w] : 0;
+    const int64_t b = tid >= w ? st[tid - w] : 0;
+    __syncthreads();
+    sc[tid] += a;
+    st[tid] += b;
+    __syncthreads();
+  }
+  int64_t c_run = tid ? sc[tid - 1] : 0, t_run = tid ? st[tid - 1] : 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    offset[i] = (int32_t)c_run;
+    tile_start[i] = (int32_t)t_run;
+    const int32_t c = count[i];
+    c_run += c;
+    t_run += (c + tile_m - 1) / tile_m;
+  }
+  if (tid == 1023) {
+    offset[n] = (int32_t)sc[1023];
+    tile_start[n] = (int32_t)st[1023];
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= a.bh * a.seq_len) return;
+  const int64_t bh = q / a.seq_len, t = q % a.seq_len;
+  const int c = (int)(t / a.block_size);
+  const int slots = a.k_eff - 1;
+  const int32_t* row = a.block_idx + q * a.top_k;
+  const int32_t* rk = a.rank + q * slots;
+  int s = 0;
+  for (int i = 0; i < a.top_k; ++i) {
+    const int j = row[i];
+    if (j < 0) break;
+    if (j == c) continue;
+    const int64_t blk = bh * a.n_blocks + j;
+    a.qlist[a.offset[blk] + rk[s]] = (int32_t)(t * slots + s);
+    ++s;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Clears n 32-bit words with a kernel (not a memset node, so the sequence
+// stays safe to capture in a HIP graph).
+hipError_t launch_zero(void* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  KernelTimer t(s, "zero_fill");
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
+  const int64_t n = a.bh * a.n_blocks;
+  {
+    KernelTimer t(s, "pack_scan");
+    hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(1024), 0, s, a.count, n, a.tile_m, a.offset,
+                       a.tile_start);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nq = a.bh * a.seq_len;
+  {
+    KernelTimer t(s, "pack_scatter");
+    hipLaunchKernelGGL(pack_scatter_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moba

@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moba.h declares, and rejects bad arguments on the host (validation
+happens before any HIP call, so these run anywhere)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sparse_long_context_moba_amd", "libmoba.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoba.so not built")
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "moba.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moba_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    from sparse_long_context_moba_amd import _lib
+    names = _header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(_lib.LIB, n), n
+    assert sorted(_lib.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings():
+    from sparse_long_context_moba_amd import _lib
+    assert _lib.moba_abi_version() == 1
+    for code in range(8):
+        assert _lib.moba_status_str(code)
+    assert _lib.moba_status_str(99) == "unknown status"
+
+
+def _p(**kw):
+    from sparse_long_context_moba_amd._lib import moba_problem_t
+    base = dict(batch=1, heads=2, seq_len=1024, head_dim=128, block_size=256, top_k=3, causal=1, dtype=1)
+    base.update(kw)
+    return moba_problem_t(**base)
+
+
+FAKE = 0x1000  # never dereferenced: validation fails or stops before any launch
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(batch=0), 2, "batch"),
+    (dict(heads=-1), 2, "heads"),
+    (dict(seq_len=0), 2, "seq_len"),
+    (dict(head_dim=0), 2, "head_dim"),
+    (dict(block_size=0), 2, "block_size"),
+    (dict(seq_len=1000), 2, "multiple"),
+    (dict(top_k=0), 3, "top_k"),
+    (dict(dtype=7), 4, "dtype"),
+    (dict(head_dim=96), 5, "head_dim"),
+    (dict(block_size=32, seq_len=1024), 5, "block_size"),
+    (dict(top_k=18, block_size=64, seq_len=4096), 5, "top_k"),
+    (dict(seq_len=1 << 27, block_size=1 << 20), 5, "seq_len"),
+])
+def test_forward_validation(kw, code, word):
+    from sparse_long_context_moba_amd import _lib
+    st = _lib.moba_forward(_p(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == code
+    assert word in _lib.moba_last_error()
+    st2, _ = _lib.moba_workspace_size(_p(**kw))
+    assert st2 == code
+
+
+def test_null_pointers_and_workspace():
+    from sparse_long_context_moba_amd import _lib
+    assert _lib.moba_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == 1
+    for i, name in enumerate(["q", "k", "v", "o", "block_idx"]):
+        args = [FAKE] * 5
+        args[i] = None
+        st = _lib.moba_forward(_p(), *args, FAKE, 1 << 40, None)
+        assert st == 1 and name in _lib.moba_last_error()
+    st, need = _lib.moba_workspace_size(_p())
+    assert st == 0 and need > 0
+    assert _lib.moba_forward(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 6
+    assert _lib.moba_forward(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == 6
+    assert _lib.moba_forward(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, need, None) == 6
+    assert _lib.moba_dense_forward(_p(seq_len=1000, block_size=1000), FAKE, FAKE, FAKE, FAKE, None) == 5
+    assert _lib.moba_dense_forward(_p(), None, FAKE, FAKE, FAKE, None) == 1
+    assert _lib.moba_pool(_p(), FAKE, None, FAKE, need, None) == 1
+    assert _lib.moba_select(_p(), FAKE, FAKE, None, FAKE, need, None) == 1
+
+
+def test_topk_beyond_blocks_is_clamped_not_an_error():
+    from sparse_long_context_moba_amd import _lib
+    st, a = _lib.moba_workspace_size(_p(top_k=4, seq_len=1024, block_size=256))
+    st2, b = _lib.moba_workspace_size(_p(top_k=400, seq_len=1024, block_size=256))
+    assert st == 0 and st2 == 0 and a == b
+
+
+def test_workspace_of_named_workloads_fits_hbm():
+    import synth
+    from sparse_long_context_moba_amd import _lib
+    for name in synth.WORKLOAD_ORDER:
+        w = synth.WORKLOADS[name]
+        p = _p(batch=w.batch, heads=w.heads, seq_len=w.seq_len, head_dim=w.head_dim,
+               block_size=w.block_size, top_k=w.top_k, causal=int(w.causal),
+               dtype=1 if w.dtype == "bf16" else 0)
+        st, n = _lib.moba_workspace_size(p)
+        assert st == 0, _lib.moba_last_error()
+        assert 0 < n < 64 << 30, (name, n)

@@ -1,0 +1,100 @@
+"""GPU parity at the named workloads' full sizes, in the launch
+configuration bench.py times: the whole forward runs on the GPU, and 4096
+seeded sampled query rows (plus edge rows) are checked against the fp64
+oracle on the same seeded inputs."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moba as orc
+from tests.parity import check_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload(w):
+    """Generate the workload's inputs per head on the host (worker processes)
+    and copy them into device tensors; keep the host copies for the oracle."""
+    shape = (w.batch, w.heads, w.seq_len, w.head_dim)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = [torch.empty(shape, dtype=tdt, device="cuda") for _ in range(3)]
+    host = {}
+    for b, h, q, k, v in synth.iter_heads_parallel(w):
+        for i, x in enumerate((q, k, v)):
+            t = torch.from_numpy(x)
+            dev[i][b, h].copy_(t.view(torch.bfloat16) if w.dtype == "bf16" else t)
+        host[(b, h)] = (q, k, v)
+    return dev, host
+
+
+def _as_f32(x, dtype):
+    if dtype == "bf16":
+        return (x.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return x
+
+
+def _oracle_head(args):
+    qb, kb, vb, rows, w = args
+    q, k, v = (_as_f32(x, w.dtype) for x in (qb, kb, vb))
+    res = orc.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=rows)
+    return res, q, k, v
+
+
+def _run(name, n_rows=4096):
+    import sparse_long_context_moba_amd as moba
+    w = synth.WORKLOADS[name]
+    t0 = time.time()
+    say(f"[gpu] {name}: generating and uploading inputs")
+    (qd, kd, vd), host = _upload(w)
+    say(f"[gpu] {name}: inputs ready in {time.time() - t0:.1f}s; running moba.forward")
+    o, idx = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, n_rows)
+    sel = torch.from_numpy(rows).cuda()
+    o_rows = o[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
+    idx_rows = idx[sel[:, 0], sel[:, 1], sel[:, 2]].cpu().numpy()
+    del o, idx, qd, kd, vd
+    torch.cuda.empty_cache()
+    say(f"[gpu] {name}: forward done; oracle on {len(rows)} rows")
+    groups = {}
+    for i, (b, h, t) in enumerate(rows):
+        groups.setdefault((int(b), int(h)), []).append(i)
+    stats = {"rows": 0, "max_err": 0.0, "flagged": 0, "tie_diff": 0}
+    import multiprocessing as mp
+    keys = sorted(groups)
+    jobs = [(*host[bh], rows[groups[bh], 2], w) for bh in keys]
+    with mp.get_context("fork").Pool(min(16, len(jobs))) as pool:
+        for bh, (res, q, k, v) in zip(keys, pool.imap(_oracle_head, jobs)):
+            ii = groups[bh]
+            st = check_rows(o_rows[ii], idx_rows[ii], res, rows[ii, 2], q, k, v, w.block_size,
+                            w.top_k, w.causal, w.dtype, label=f"{name} b={bh[0]} h={bh[1]}")
+            stats["rows"] += st["rows"]
+            stats["max_err"] = max(stats["max_err"], st["max_err"])
+            stats["flagged"] += st["flagged"]
+            stats["tie_diff"] += st["tie_diff"]
+    say(f"[gpu] {name}: ok {stats} in {time.time() - t0:.1f}s")
+    assert stats["rows"] == len(rows)
+
+
+def test_tiny_all_rows():
+    _run("tiny", n_rows=4096)
+
+
+def test_headline_32k_sampled():
+    _run("headline_32k")
+
+
+def test_coarse_32k_sampled():
+    _run("coarse_32k")
+
+
+def test_long_128k_sampled():
+    _run("long_128k")
+
+
+@pytest.mark.slow
+def test_long_1m_sampled():
+    _run("long_1m")
