@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""MoBA prefill forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole MoBA forward (pool -> gate/top-k -> varlen pack ->
+past-block attention -> own-block attention and merge) over one batch of
+seeded synthetic Q/K/V already resident in HBM. Prints one JSON line:
+throughput in tokens/s, effective TFLOP/s of the algorithmic work, the
+roofline of the dominant kernel (HIP-event durations of its launches inside
+the timed region), the speedup over the library's dense causal kernel, and
+the CPU fp64 oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (MFMA and vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoBA fwd tokens/sec + effective TFLOP/s (% bf16 MFMA peak) at 32K/128K/1M"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def work_model(w):
+    """Algorithmic work of one forward, counted from MoBA's definition:
+    gate 2*D flops per (query, eligible past block); attention 4*D flops per
+    (query, attended key), split into past blocks and the own block."""
+    S, D, Bs, nb, bh = w.seq_len, w.head_dim, w.block_size, w.n_blocks, w.batch * w.heads
+    k_eff = min(w.top_k, nb)
+    gate_pairs = past_pairs = own_keys = 0
+    for c in range(nb):
+        elig = c if w.causal else nb - 1
+        gate_pairs += Bs * elig
+        past_pairs += Bs * min(k_eff - 1, elig)
+        own_keys += Bs * (Bs + 1) // 2 if w.causal else Bs * Bs
+    dense_keys = S * (S + 1) // 2 if w.causal else S * S
+    esz = 2 if w.dtype == "bf16" else 4
+    return {
+        "gate_flops": bh * 2 * D * gate_pairs,
+        "past_flops": bh * 4 * D * past_pairs * Bs,
+        "own_flops": bh * 4 * D * own_keys,
+        "dense_flops": bh * 4 * D * dense_keys,
+        "past_pairs": bh * past_pairs,
+        "attended_keys": bh * (past_pairs * Bs + own_keys),
+        "dense_keys": bh * dense_keys,
+        "k_bytes": bh * S * D * esz,
+        "qkvo_bytes": 4 * bh * S * D * esz,
+    }
+
+
+def kernel_units(w, wm):
+    """(bound, algorithmic work per launch, unit) for each library kernel."""
+    D, bh, nb = w.head_dim, w.batch * w.heads, w.n_blocks
+    rows_per_run = next((r for r in (256, 192, 128) if w.block_size % r == 0), 64)
+    return {
+        "gather_attn": ("mfma", wm["past_flops"], "flop"),
+        "diag_merge": ("mfma", wm["own_flops"], "flop"),
+        "gate_topk": ("mfma", wm["gate_flops"], "flop"),
+        "pool_partial": ("hbm", wm["k_bytes"] + bh * (w.seq_len // rows_per_run) * D * 8, "byte"),
+        "dense_attn": ("mfma", wm["dense_flops"], "flop"),
+    }
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gather_attn": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/common.h"],
+    "diag_merge": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/common.h"],
+    "gate_topk": ["sparse_long_context_moba_amd/csrc/gate.hip", "sparse_long_context_moba_amd/csrc/common.h"],
+    "pool_partial": ["sparse_long_context_moba_amd/csrc/pool.hip", "sparse_long_context_moba_amd/csrc/common.h"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    text = open(path).read()
+    m = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    d = re.search(r"source_digest:\s*([0-9a-f]+)", text)
+    if not m or not d or d.group(1) != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m.group(1))
+
+
+def upload(w, torch):
+    shape = (w.batch, w.heads, w.seq_len, w.head_dim)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = [torch.empty(shape, dtype=tdt, device="cuda") for _ in range(3)]
+    for b, h, q, k, v in synth.iter_heads_parallel(w):
+        for i, x in enumerate((q, k, v)):
+            t = torch.from_numpy(x)
+            dev[i][b, h].copy_(t.view(torch.bfloat16) if w.dtype == "bf16" else t)
+    torch.cuda.synchronize()
+    return dev
+
+
+def cpu_baseline(w, n_rows):
+    """The fp64 oracle on a bounded seeded sample of the workload, on this
+    host's cores; extrapolated to a full forward (pool every head + every
+    row) and reported as tokens/s."""
+    from oracle import sampled
+    rows = synth.sample_rows(w, n_rows)
+    out = sampled.oracle_rows(w, rows)
+    heads = out["heads"]
+    pool_per_head = out["pool_s"] / heads
+    row_s = (out["oracle_s"] - out["pool_s"]) / len(rows)
+    bh = w.batch * w.heads
+    cpu_seconds = pool_per_head * bh + row_s * bh * w.seq_len
+    full_wall = cpu_seconds / out["workers"]
+    return {
+        "value": w.batch * w.seq_len / full_wall,
+        "unit": "tokens/s",
+        "cores": out["workers"],
+        "kind": "oracle",
+        "sample": (f"{len(rows)} seeded query rows over {heads} heads of {w.name} (fp64 NumPy, "
+                   f"{out['workers']} processes, 1 BLAS thread each); measured {out['oracle_s']:.1f} CPU-s "
+                   f"(pool {out['pool_s']:.1f} s + rows); value extrapolated to a full forward "
+                   f"({bh} heads x {w.seq_len} rows) = {full_wall:.1f} s wall"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--dense-steps", type=int, default=2, help="timed dense causal forwards (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=16384, help="oracle sample size (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(MoBA shards over heads with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_long_context_moba_amd as moba
+
+    w = synth.WORKLOADS[args.workload]
+    wm = work_model(w)
+    log(f"workload {w.name}: B={w.batch} H={w.heads} S={w.seq_len} D={w.head_dim} "
+        f"block={w.block_size} top_k={w.top_k} {w.dtype}; generating inputs")
+    t0 = time.time()
+    q, k, v = upload(w, torch)
+    log(f"inputs resident in HBM after {time.time() - t0:.1f}s")
+    p = moba.problem(q, w.block_size, w.top_k, w.causal)
+    ws = torch.empty(moba.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    idx = torch.empty((w.batch, w.heads, w.seq_len, w.top_k), dtype=torch.int32, device="cuda")
+
+    def step():
+        moba.forward(q, k, v, w.block_size, w.top_k, w.causal, out=o, idx=idx, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    with moba.timing() as tm:
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    ms_per_step = 1e3 * elapsed / args.steps
+    kern = {name: {"launches": n, "avg_ms": tot / n, "total_ms": tot} for name, n, tot in tm.rows}
+    log("kernels: " + ", ".join(f"{n} {v['avg_ms']:.3f}ms" for n, v in kern.items()))
+
+    algo_flops = wm["gate_flops"] + wm["past_flops"] + wm["own_flops"]
+    eff_tflops = algo_flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    units = kernel_units(w, wm)
+    dom = max((n for n in kern if n in units), key=lambda n: kern[n]["total_ms"])
+    bound, work, unit = units[dom]
+    avg_s = kern[dom]["avg_ms"] * 1e-3
+    if bound == "hbm":
+        achieved, rpeak, runit = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, rpeak, runit = work / avg_s / 1e12, peak, "TFLOP/s"
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": rpeak, "unit": runit,
+                "frac": round(achieved / rpeak, 4), "traffic": measured_traffic(dom, w.name),
+                "work_per_launch": work, "work_unit": unit, "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
+    attn_gate_ms = sum(kern[n]["avg_ms"] for n in ("gate_topk", "gather_attn", "diag_merge") if n in kern)
+    attn_gate_frac = (wm["gate_flops"] + wm["past_flops"] + wm["own_flops"]) / (attn_gate_ms * 1e-3) / 1e12 / peak
+
+    dense = None
+    if args.dense_steps > 0:
+        od = torch.empty_like(q)
+        moba.dense(q, k, v, w.causal, out=od)
+        torch.cuda.synchronize()
+        td = time.perf_counter()
+        for _ in range(args.dense_steps):
+            moba.dense(q, k, v, w.causal, out=od)
+        torch.cuda.synchronize()
+        dense_ms = 1e3 * (time.perf_counter() - td) / args.dense_steps
+        dense = {"ms": round(dense_ms, 3), "speedup": round(dense_ms / ms_per_step, 2),
+                 "tflops": round(wm["dense_flops"] / (dense_ms * 1e-3) / 1e12, 1)}
+        log(f"dense causal: {dense_ms:.3f} ms, speedup {dense['speedup']}x")
+        del od
+
+    cpu = None
+    if args.cpu_rows > 0:
+        log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
+        cpu = cpu_baseline(w, args.cpu_rows)
+        log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
+
+    tokens = w.batch * w.seq_len
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded q, v ~ N(0,1); k ~ N(0,1) + per-block N(0, 0.5^2) bias)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "top_k": w.top_k,
+                   "causal": w.causal, "parallelism": "single GPU"},
+        "effective_tflops": round(eff_tflops, 2),
+        "pct_peak": round(100 * eff_tflops / peak, 2),
+        "attn_gate_kernels_pct_peak": round(100 * attn_gate_frac, 2),
+        "sparsity": {"realized": round(1 - wm["attended_keys"] / wm["dense_keys"], 4),
+                     "theoretical_1_minus_k_over_nb": round(1 - w.top_k / w.n_blocks, 4)},
+        "kernels_ms": {n: round(v["avg_ms"], 4) for n, v in kern.items()},
+        "dense_causal": dense,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,16 +22,19 @@ def _head_rows(args):
     t0 = time.perf_counter()
     q, k, v = synth.make_head(w.seed, b, h, w.seq_len, w.head_dim, w.block_size, w.dtype)
     t1 = time.perf_counter()
-    res = moba.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=ts)
+    moba.pool_keys(k, w.block_size)
     t2 = time.perf_counter()
-    return b, h, ts, res, t1 - t0, t2 - t1
+    res = moba.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=ts)
+    t3 = time.perf_counter()
+    return b, h, ts, res, t1 - t0, t2 - t1, t3 - t2
 
 
 def oracle_rows(w: "synth.Workload", rows: np.ndarray, workers: int | None = None):
     """rows: int64 [n, 3] of (b, h, t). Returns dict keyed like forward_head
     (o, idx, flag, a, b) in the order of `rows`, plus timing fields:
-    gen_s (input regeneration) and oracle_s (pooling + rows), summed over
-    workers, and wall_s, workers."""
+    gen_s (input regeneration), pool_s (one pooling pass per head) and
+    oracle_s (pooling + the rows), summed over workers, plus heads, wall_s
+    and workers."""
     rows = np.asarray(rows, dtype=np.int64)
     groups = {}
     for i, (b, h, t) in enumerate(rows):
@@ -43,7 +46,7 @@ def oracle_rows(w: "synth.Workload", rows: np.ndarray, workers: int | None = Non
     n = len(rows)
     out = {"o": np.zeros((n, w.head_dim)), "idx": np.zeros((n, w.top_k), np.int64),
            "flag": np.zeros(n, bool), "a": np.zeros(n), "b": np.zeros(n)}
-    gen_s = orc_s = 0.0
+    gen_s = orc_s = pool_s = 0.0
     t0 = time.perf_counter()
     if workers == 1:
         results = map(_head_rows, jobs)
@@ -53,8 +56,9 @@ def oracle_rows(w: "synth.Workload", rows: np.ndarray, workers: int | None = Non
         pool = mp.get_context("fork").Pool(workers)
         results = pool.imap_unordered(_head_rows, jobs)
     try:
-        for b, h, ts, res, g, o in results:
+        for b, h, ts, res, g, p, o in results:
             gen_s += g
+            pool_s += p
             orc_s += o
             for r, (i, _) in enumerate(groups[(b, h)]):
                 for key in out:
@@ -65,6 +69,8 @@ def oracle_rows(w: "synth.Workload", rows: np.ndarray, workers: int | None = Non
             pool.join()
     out["gen_s"] = gen_s
     out["oracle_s"] = orc_s
+    out["pool_s"] = pool_s
+    out["heads"] = len(jobs)
     out["wall_s"] = time.perf_counter() - t0
     out["workers"] = workers
     return out

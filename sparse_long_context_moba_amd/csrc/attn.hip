@@ -33,38 +33,58 @@ namespace {
 constexpr int kSub = 64;  // keys per LDS subtile
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Online-softmax update shared by both engines: scales and masks the raw
-// scores in place (log2 domain), returns the rescale factor of the old state.
-template <bool MASK>
-__device__ __forceinline__ float softmax_rows(f32x16 (&s)[2], float& m, float& l, int h, int key0,
-                                              int qpos, float sl2) {
+// Max / sum of a value over the two lanes (l, l^32) that hold one query.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Online-softmax update shared by both engines. s holds raw scores of 64
+// keys for this lane's query; on return it holds the weights
+// exp2(s*sl2 - m). m is the running reference (log2 domain); it is raised
+// only when a row's maximum exceeds it by more than 8, so weights stay
+// below 2^8 and the output accumulators are rescaled rarely.
+template <bool MASK, int DT>
+__device__ __forceinline__ void online_softmax(f32x16 (&s)[2], float& m, float& l, f32x16 (&o)[DT], int h,
+                                               int key0, int qpos, float sl2) {
+  if (MASK) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key0 + 32 * nt + crow(r, h) > qpos) s[nt][r] = kNegInf;
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[nt][r] * sl2;
-      if (MASK) {
-        if (key0 + 32 * nt + crow(r, h) > qpos) x = kNegInf;
-      }
-      s[nt][r] = x;
-      mx = fmaxf(mx, x);
-    }
-  mx = fmaxf(mx, shfl_xor32(mx));
-  const float mn = fmaxf(m, mx);
-  const float alpha = fast_exp2(m - mn);
-  m = mn;
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[nt][r], s[nt][r + 1]));
+  mx = pair_max(mx) * sl2;
+  if (__builtin_amdgcn_ballot_w64(mx > m + 8.f)) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    m = mn;
+  }
+  const float nm = -m;
   float rs = 0.f;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(s[nt][r] - mn);
+      const float e = fast_exp2(__builtin_fmaf(s[nt][r], sl2, nm));
       s[nt][r] = e;
       rs += e;
     }
-  l = l * alpha + rs;
-  return alpha;
+  l += rs;
 }
 
 // ------------------------------------------------------------ bf16 engine
@@ -85,29 +105,29 @@ struct EngBF16 {
 
   template <int NT>
   struct Stage {
-    uint4 k[(KCH + NT - 1) / NT];
-    uint4 v[(VPT + NT - 1) / NT][4];
+    u32x4 k[(KCH + NT - 1) / NT];
+    u32x4 v[4 * ((VPT + NT - 1) / NT)];  // four key rows per patch
   };
 
-  __device__ void init() {
+  __device__ __forceinline__ void init() {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
     m = kNegInf;
     l = 0.f;
   }
-  __device__ void load_q(const bf16* qrow, int h) {
+  __device__ __forceinline__ void load_q(const bf16* qrow, int h) {
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * h);
   }
 
   template <int NT>
-  static __device__ void fetch(Stage<NT>& st, const bf16* kp, const bf16* vp, int tid) {
+  static __device__ __forceinline__ void fetch(Stage<NT>& st, const bf16* kp, const bf16* vp, int tid) {
 #pragma unroll
     for (int i = 0; i < (KCH + NT - 1) / NT; ++i) {
       const int id = tid + NT * i;
       if (KCH % NT == 0 || id < KCH) {
         const int row = id / (D / 8), cc = id % (D / 8);
-        st.k[i] = *reinterpret_cast<const uint4*>(kp + (int64_t)row * D + 8 * cc);
+        st.k[i] = *reinterpret_cast<const u32x4*>(kp + (int64_t)row * D + 8 * cc);
       }
     }
 #pragma unroll
@@ -117,19 +137,19 @@ struct EngBF16 {
         const int kg = id / (D / 8), dg = id % (D / 8);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          st.v[i][r] = *reinterpret_cast<const uint4*>(vp + (int64_t)(4 * kg + r) * D + 8 * dg);
+          st.v[4 * i + r] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(4 * kg + r) * D + 8 * dg);
       }
     }
   }
 
   template <int NT>
-  static __device__ void store(const Stage<NT>& st, bf16* Ks, bf16* Vs, int tid) {
+  static __device__ __forceinline__ void store(const Stage<NT>& st, bf16* Ks, bf16* Vs, int tid) {
 #pragma unroll
     for (int i = 0; i < (KCH + NT - 1) / NT; ++i) {
       const int id = tid + NT * i;
       if (KCH % NT == 0 || id < KCH) {
         const int row = id / (D / 8), cc = id % (D / 8);
-        *reinterpret_cast<uint4*>(Ks + row * KS + 8 * cc) = st.k[i];
+        *reinterpret_cast<u32x4*>(Ks + row * KS + 8 * cc) = st.k[i];
       }
     }
 #pragma unroll
@@ -137,13 +157,13 @@ struct EngBF16 {
       const int id = tid + NT * i;
       if (VPT % NT == 0 || id < VPT) {
         const int kg = id / (D / 8), dg = id % (D / 8);
-        const uint4 r0 = st.v[i][0], r1 = st.v[i][1], r2 = st.v[i][2], r3 = st.v[i][3];
+        const u32x4 r0 = st.v[4 * i], r1 = st.v[4 * i + 1], r2 = st.v[4 * i + 2], r3 = st.v[4 * i + 3];
         bf16* vd = Vs + (8 * dg) * VS + 4 * kg;
         // Element e of the four key rows -> V^T row (8*dg + e), keys 4*kg..4*kg+3.
 #define MOBA_VT_PUT(e, W)                                                                    \
-  *reinterpret_cast<uint2*>(vd + (e) * VS) =                                               \
-      ((e) & 1) ? make_uint2((r0.W >> 16) | (r1.W & 0xffff0000u), (r2.W >> 16) | (r3.W & 0xffff0000u)) \
-                : make_uint2((r0.W & 0xffffu) | (r1.W << 16), (r2.W & 0xffffu) | (r3.W << 16));
+  *reinterpret_cast<u32x2*>(vd + (e) * VS) =                                               \
+      ((e) & 1) ? u32x2{(r0.W >> 16) | (r1.W & 0xffff0000u), (r2.W >> 16) | (r3.W & 0xffff0000u)} \
+                : u32x2{(r0.W & 0xffffu) | (r1.W << 16), (r2.W & 0xffffu) | (r3.W << 16)};
         MOBA_VT_PUT(0, x)
         MOBA_VT_PUT(1, x)
         MOBA_VT_PUT(2, y)
@@ -158,7 +178,7 @@ struct EngBF16 {
   }
 
   template <bool MASK>
-  __device__ void step(const bf16* Ks, const bf16* Vs, int col, int h, int key0, int qpos, float sl2) {
+  __device__ __forceinline__ void step(const bf16* Ks, const bf16* Vs, int col, int h, int key0, int qpos, float sl2) {
     f32x16 s[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -169,7 +189,7 @@ struct EngBF16 {
         s[nt] = mfma_bf16(a, qf[kk], s[nt]);
       }
     }
-    const float alpha = softmax_rows<MASK>(s, m, l, h, key0, qpos, sl2);
+    online_softmax<MASK>(s, m, l, o, h, key0, qpos, sl2);
     bf16x8 pb[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -177,8 +197,6 @@ struct EngBF16 {
       for (int r = 0; r < 16; ++r) pb[nt][r >> 3][r & 7] = to_bf16(s[nt][r]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -193,7 +211,7 @@ struct EngBF16 {
   }
 
   // 16 output values of d-tile dt, lane-native order, to memory.
-  static __device__ void put16(bf16* dst, const f32x16& x, float scale) {
+  static __device__ __forceinline__ void put16(bf16* dst, const f32x16& x, float scale) {
     bf16x8 a, b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -203,7 +221,7 @@ struct EngBF16 {
     *reinterpret_cast<bf16x8*>(dst) = a;
     *reinterpret_cast<bf16x8*>(dst + 8) = b;
   }
-  static __device__ void get16(const bf16* src, float (&x)[16]) {
+  static __device__ __forceinline__ void get16(const bf16* src, float (&x)[16]) {
     const bf16x8 a = *reinterpret_cast<const bf16x8*>(src);
     const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + 8);
 #pragma unroll
@@ -213,7 +231,7 @@ struct EngBF16 {
     }
   }
   // Four consecutive output coordinates (one r-group) to o.
-  static __device__ void put4(bf16* dst, float a0, float a1, float a2, float a3) {
+  static __device__ __forceinline__ void put4(bf16* dst, float a0, float a1, float a2, float a3) {
     bf16x4 v;
     v[0] = to_bf16(a0);
     v[1] = to_bf16(a1);
@@ -240,48 +258,48 @@ struct EngF32 {
 
   template <int NT>
   struct Stage {
-    uint4 k[(CH + NT - 1) / NT];
-    uint4 v[(CH + NT - 1) / NT];
+    u32x4 k[(CH + NT - 1) / NT];
+    u32x4 v[(CH + NT - 1) / NT];
   };
 
-  __device__ void init() {
+  __device__ __forceinline__ void init() {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
     m = kNegInf;
     l = 0.f;
   }
-  __device__ void load_q(const float* qrow, int h) {
+  __device__ __forceinline__ void load_q(const float* qrow, int h) {
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) qf[kk] = qrow[2 * kk + h];
   }
   template <int NT>
-  static __device__ void fetch(Stage<NT>& st, const float* kp, const float* vp, int tid) {
+  static __device__ __forceinline__ void fetch(Stage<NT>& st, const float* kp, const float* vp, int tid) {
 #pragma unroll
     for (int i = 0; i < (CH + NT - 1) / NT; ++i) {
       const int id = tid + NT * i;
       if (CH % NT == 0 || id < CH) {
         const int row = id / (D / 4), cc = id % (D / 4);
-        st.k[i] = *reinterpret_cast<const uint4*>(kp + (int64_t)row * D + 4 * cc);
-        st.v[i] = *reinterpret_cast<const uint4*>(vp + (int64_t)row * D + 4 * cc);
+        st.k[i] = *reinterpret_cast<const u32x4*>(kp + (int64_t)row * D + 4 * cc);
+        st.v[i] = *reinterpret_cast<const u32x4*>(vp + (int64_t)row * D + 4 * cc);
       }
     }
   }
   template <int NT>
-  static __device__ void store(const Stage<NT>& st, float* Ks, float* Vs, int tid) {
+  static __device__ __forceinline__ void store(const Stage<NT>& st, float* Ks, float* Vs, int tid) {
 #pragma unroll
     for (int i = 0; i < (CH + NT - 1) / NT; ++i) {
       const int id = tid + NT * i;
       if (CH % NT == 0 || id < CH) {
         const int row = id / (D / 4), cc = id % (D / 4);
         float* kd = Ks + row * KS + 4 * cc;
-        *reinterpret_cast<uint2*>(kd) = make_uint2(st.k[i].x, st.k[i].y);
-        *reinterpret_cast<uint2*>(kd + 2) = make_uint2(st.k[i].z, st.k[i].w);
-        *reinterpret_cast<uint4*>(Vs + row * VS + 4 * cc) = st.v[i];
+        *reinterpret_cast<u32x2*>(kd) = u32x2{st.k[i].x, st.k[i].y};
+        *reinterpret_cast<u32x2*>(kd + 2) = u32x2{st.k[i].z, st.k[i].w};
+        *reinterpret_cast<u32x4*>(Vs + row * VS + 4 * cc) = st.v[i];
       }
     }
   }
   template <bool MASK>
-  __device__ void step(const float* Ks, const float* Vs, int col, int h, int key0, int qpos, float sl2) {
+  __device__ __forceinline__ void step(const float* Ks, const float* Vs, int col, int h, int key0, int qpos, float sl2) {
     f32x16 s[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -289,11 +307,9 @@ struct EngF32 {
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) s[nt] = mfma_f32(Ks[(32 * nt + col) * KS + 2 * kk + h], qf[kk], s[nt]);
     }
-    const float alpha = softmax_rows<MASK>(s, m, l, h, key0, qpos, sl2);
+    online_softmax<MASK>(s, m, l, o, h, key0, qpos, sl2);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -301,7 +317,7 @@ struct EngF32 {
           o[dt] = mfma_f32(Vs[(32 * nt + crow(r, h)) * VS + 32 * dt + col], s[nt][r], o[dt]);
     }
   }
-  static __device__ void put16(float* dst, const f32x16& x, float scale) {
+  static __device__ __forceinline__ void put16(float* dst, const f32x16& x, float scale) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       f32x4 v;
@@ -310,7 +326,7 @@ struct EngF32 {
       *reinterpret_cast<f32x4*>(dst + 4 * q4) = v;
     }
   }
-  static __device__ void get16(const float* src, float (&x)[16]) {
+  static __device__ __forceinline__ void get16(const float* src, float (&x)[16]) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q4);
@@ -318,7 +334,7 @@ struct EngF32 {
       for (int e = 0; e < 4; ++e) x[4 * q4 + e] = v[e];
     }
   }
-  static __device__ void put4(float* dst, float a0, float a1, float a2, float a3) {
+  static __device__ __forceinline__ void put4(float* dst, float a0, float a1, float a2, float a3) {
     f32x4 v;
     v[0] = a0;
     v[1] = a1;
@@ -343,7 +359,7 @@ struct EngOf<float, D> {
 
 // ------------------------------------------------------- past-block gather
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void gather_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gather_attn_kernel(AttnArgs a) {
   using E = typename EngOf<T, D>::type;
   constexpr int NT = 64 * NW, M = 32 * NW;
   extern __shared__ __align__(16) char smem[];
@@ -396,7 +412,7 @@ __global__ __launch_bounds__(64 * NW) void gather_attn_kernel(AttnArgs a) {
     if (wave_on) eng.template step<false>(Ks, Vs, col, h, 0, 0, sl2);
   }
   if (!wave_on) return;
-  const float lt = eng.l + shfl_xor32(eng.l);
+  const float lt = pair_sum(eng.l);
   if (valid) {
     const int64_t rec = bh * a.seq_len * slots + ev;
     T* dst = reinterpret_cast<T*>(a.part_o) + rec * D + h * (D / 2);
@@ -409,7 +425,7 @@ __global__ __launch_bounds__(64 * NW) void gather_attn_kernel(AttnArgs a) {
 
 // --------------------------------------------- own block + merge (and dense)
 template <typename T, int D, int NW, bool DENSE>
-__global__ __launch_bounds__(64 * NW) void diag_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void diag_attn_kernel(AttnArgs a) {
   using E = typename EngOf<T, D>::type;
   constexpr int NT = 64 * NW, M = 32 * NW;
   extern __shared__ __align__(16) char smem[];
@@ -437,29 +453,34 @@ __global__ __launch_bounds__(64 * NW) void diag_attn_kernel(AttnArgs a) {
   const int nsub = (kend - kb) / kSub;
   typename E::template Stage<NT> st;
   E::template fetch<NT>(st, kp, vp, tid);
-  for (int sub = 0; sub < nsub; ++sub) {
+  // Subtiles entirely before the workgroup's first query need no mask; with
+  // causal attention the last M/64 subtiles hold the diagonal.
+  const int nfree = a.causal ? (q0 - kb) / kSub : nsub;
+  int sub = 0;
+  for (; sub < nfree; ++sub) {
+    __syncthreads();
+    E::template store<NT>(st, Ks, Vs, tid);
+    __syncthreads();
+    if (sub + 1 < nsub) E::template fetch<NT>(st, kp + (int64_t)(sub + 1) * kSub * D, vp + (int64_t)(sub + 1) * kSub * D, tid);
+    eng.template step<false>(Ks, Vs, col, h, 0, 0, sl2);
+  }
+  for (; sub < nsub; ++sub) {
     __syncthreads();
     E::template store<NT>(st, Ks, Vs, tid);
     __syncthreads();
     if (sub + 1 < nsub) E::template fetch<NT>(st, kp + (int64_t)(sub + 1) * kSub * D, vp + (int64_t)(sub + 1) * kSub * D, tid);
     const int key0 = kb + sub * kSub;
-    if (a.causal) {
-      if (key0 > qw0 + 31) continue;  // every key after every query of this wave
-      if (key0 + kSub - 1 > qw0) eng.template step<true>(Ks, Vs, col, h, key0, t, sl2);
-      else eng.template step<false>(Ks, Vs, col, h, key0, t, sl2);
-    } else {
-      eng.template step<false>(Ks, Vs, col, h, key0, t, sl2);
-    }
+    // Skip a subtile whose keys all come after every query of this wave.
+    if (key0 <= qw0 + 31) eng.template step<true>(Ks, Vs, col, h, key0, t, sl2);
   }
 
-  const float lt = eng.l + shfl_xor32(eng.l);
-  float out[E::DT][16];
+  const float lt = pair_sum(eng.l);
   if (DENSE) {
     const float inv = 1.f / lt;
 #pragma unroll
     for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) out[dt][r] = eng.o[dt][r] * inv;
+      for (int r = 0; r < 16; ++r) eng.o[dt][r] *= inv;
   } else {
     // Merge with the past-block partials: one softmax over all chosen keys.
     const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
@@ -475,7 +496,7 @@ __global__ __launch_bounds__(64 * NW) void diag_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) out[dt][r] = eng.o[dt][r] * sd;
+      for (int r = 0; r < 16; ++r) eng.o[dt][r] *= sd;
     const T* po = reinterpret_cast<const T*>(a.part_o);
     for (int s = 0; s < n; ++s) {
       const float ws = fast_exp2(a.part_lse[rec0 + s] - mx);
@@ -486,22 +507,22 @@ __global__ __launch_bounds__(64 * NW) void diag_attn_kernel(AttnArgs a) {
         float x[16];
         E::get16(src + 16 * dt, x);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) out[dt][r] = __builtin_fmaf(ws, x[r], out[dt][r]);
+        for (int r = 0; r < 16; ++r) eng.o[dt][r] = __builtin_fmaf(ws, x[r], eng.o[dt][r]);
       }
     }
     const float inv = 1.f / wsum;
 #pragma unroll
     for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) out[dt][r] *= inv;
+      for (int r = 0; r < 16; ++r) eng.o[dt][r] *= inv;
   }
   T* orow = reinterpret_cast<T*>(a.o) + (bh * a.seq_len + t) * D;
 #pragma unroll
   for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
-      E::put4(orow + 32 * dt + 8 * rg + 4 * h, out[dt][4 * rg], out[dt][4 * rg + 1], out[dt][4 * rg + 2],
-              out[dt][4 * rg + 3]);
+      E::put4(orow + 32 * dt + 8 * rg + 4 * h, eng.o[dt][4 * rg], eng.o[dt][4 * rg + 1], eng.o[dt][4 * rg + 2],
+              eng.o[dt][4 * rg + 3]);
 }
 
 namespace {

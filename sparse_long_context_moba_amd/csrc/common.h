@@ -12,6 +12,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+// Native vector types for raw 16/8-byte moves (HIP's uint4 is a struct
+// whose copies can defeat register promotion).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr float kNegInf = -__builtin_huge_valf();

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void pool_partial_kernel(const T* __restrict__
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
   for (int r = rg; r < rows_per_run; r += RG) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(base + (int64_t)r * D);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(base + (int64_t)r * D);
     if constexpr (sizeof(T) == 2) {
       const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
