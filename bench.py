@@ -107,11 +107,11 @@ def measured_traffic(kernel, workload):
     return float(m.group(1))
 
 
-def upload(w, torch):
+def upload(w, torch, workers=None):
     shape = (w.batch, w.heads, w.seq_len, w.head_dim)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = [torch.empty(shape, dtype=tdt, device="cuda") for _ in range(3)]
-    for b, h, q, k, v in synth.iter_heads_parallel(w):
+    for b, h, q, k, v in synth.iter_heads_parallel(w, workers):
         for i, x in enumerate((q, k, v)):
             t = torch.from_numpy(x)
             dev[i][b, h].copy_(t.view(torch.bfloat16) if w.dtype == "bf16" else t)
@@ -151,7 +151,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER)
     ap.add_argument("--dense-steps", type=int, default=2, help="timed dense causal forwards (0 = skip)")
-    ap.add_argument("--cpu-rows", type=int, default=16384, help="oracle sample size (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=65536, help="oracle sample size (0 = skip)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a plain device copy whose "
+                         "HBM counters calibrate FETCH_SIZE/WRITE_SIZE readings)")
+    ap.add_argument("--gen-workers", type=int, default=None,
+                    help="processes generating the inputs (default: one per core, up to 16; use 1 under a profiler)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -167,7 +172,7 @@ def main():
     log(f"workload {w.name}: B={w.batch} H={w.heads} S={w.seq_len} D={w.head_dim} "
         f"block={w.block_size} top_k={w.top_k} {w.dtype}; generating inputs")
     t0 = time.time()
-    q, k, v = upload(w, torch)
+    q, k, v = upload(w, torch, args.gen_workers)
     log(f"inputs resident in HBM after {time.time() - t0:.1f}s")
     p = moba.problem(q, w.block_size, w.top_k, w.causal)
     ws = torch.empty(moba.workspace_bytes(p), dtype=torch.uint8, device="cuda")
@@ -177,6 +182,15 @@ def main():
     def step():
         moba.forward(q, k, v, w.block_size, w.top_k, w.causal, out=o, idx=idx, workspace=ws)
 
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -2,7 +2,9 @@
 
 Argument marshalling only: every step of the MoBA forward runs in the HIP
 kernels behind these entry points. There is no fallback: if libmoba.so is
-missing or fails to load, importing the binding raises.
+missing or fails to load, the first call (or lib()) raises ImportError. The
+library is opened on first use so that the build module can be imported
+before anything is built.
 """
 from __future__ import annotations
 
@@ -58,56 +60,64 @@ def _load():
     return lib
 
 
-LIB = _load()
+_LIB = None
+
+
+def lib():
+    """The loaded libmoba.so (opened on first use; raises if not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
 
 
 def moba_abi_version() -> int:
-    return LIB.moba_abi_version()
+    return lib().moba_abi_version()
 
 
 def moba_status_str(status: int) -> str:
-    return LIB.moba_status_str(status).decode()
+    return lib().moba_status_str(status).decode()
 
 
 def moba_last_error() -> str:
-    return LIB.moba_last_error().decode()
+    return lib().moba_last_error().decode()
 
 
 def moba_workspace_size(problem: moba_problem_t):
     """-> (status, bytes)"""
     n = ctypes.c_size_t(0)
-    st = LIB.moba_workspace_size(ctypes.byref(problem) if problem is not None else None, ctypes.byref(n))
+    st = lib().moba_workspace_size(ctypes.byref(problem) if problem is not None else None, ctypes.byref(n))
     return st, n.value
 
 
 def moba_forward(problem, q, k, v, o, block_idx, workspace, workspace_bytes, stream) -> int:
-    return LIB.moba_forward(ctypes.byref(problem) if problem is not None else None,
+    return lib().moba_forward(ctypes.byref(problem) if problem is not None else None,
                             q, k, v, o, block_idx, workspace, workspace_bytes, stream)
 
 
 def moba_dense_forward(problem, q, k, v, o, stream) -> int:
-    return LIB.moba_dense_forward(ctypes.byref(problem) if problem is not None else None, q, k, v, o, stream)
+    return lib().moba_dense_forward(ctypes.byref(problem) if problem is not None else None, q, k, v, o, stream)
 
 
 def moba_pool(problem, k, kbar, workspace, workspace_bytes, stream) -> int:
-    return LIB.moba_pool(ctypes.byref(problem) if problem is not None else None, k, kbar, workspace,
+    return lib().moba_pool(ctypes.byref(problem) if problem is not None else None, k, kbar, workspace,
                          workspace_bytes, stream)
 
 
 def moba_select(problem, q, k, block_idx, workspace, workspace_bytes, stream) -> int:
-    return LIB.moba_select(ctypes.byref(problem) if problem is not None else None, q, k, block_idx,
+    return lib().moba_select(ctypes.byref(problem) if problem is not None else None, q, k, block_idx,
                            workspace, workspace_bytes, stream)
 
 
 def moba_timing_enable(enable: bool) -> int:
-    return LIB.moba_timing_enable(1 if enable else 0)
+    return lib().moba_timing_enable(1 if enable else 0)
 
 
 def moba_timing_read(max_entries: int = 32):
     """-> (status, [(name, launches, total_ms), ...])"""
     buf = (moba_kernel_time_t * max_entries)()
     n = ctypes.c_int(0)
-    st = LIB.moba_timing_read(buf, max_entries, ctypes.byref(n))
+    st = lib().moba_timing_read(buf, max_entries, ctypes.byref(n))
     rows = [(buf[i].name.decode(), int(buf[i].launches), float(buf[i].total_ms))
             for i in range(min(n.value, max_entries))]
     return st, rows

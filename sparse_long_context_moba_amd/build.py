@@ -17,6 +17,10 @@ SOURCES = ["api.cpp", "pool.hip", "gate.hip", "pack.hip", "attn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
+    # NaN inputs are outside the contract; without this every fmaxf on an
+    # MFMA result gets an extra canonicalising max. Infinities stay honoured
+    # (masked scores are -inf).
+    "-fno-honor-nans",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

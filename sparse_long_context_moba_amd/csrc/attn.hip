@@ -21,9 +21,16 @@
 // LDS as the A operand, Q held in registers as the B operand), so lane l
 // holds 32 scores of query l%32 per 64 keys and the row statistics need a
 // single exchange with lane l^32. P stays in registers and feeds
-// O^T = V^T P^T directly as the B operand; the A operand reads V^T from an
-// LDS copy that is transposed while it is staged. fp32 inputs use
-// MFMA 32x32x2 f32 with the same register layout and untransposed V.
+// O^T = V^T P^T directly as the B operand.
+// bf16 K/V subtiles move HBM -> LDS by direct loads (global_load_lds, 16 B
+// per lane, double-buffered, no register staging) into a row-major layout
+// whose 16-byte chunks are XOR-swizzled per row. The A operand of P.V is
+// read with the LDS transpose load ds_read_b64_tr_b16: 16 lanes naming a
+// 4-key x 16-dim patch of V receive V^T fragments directly. Separate
+// swizzles for K and V keep the K reads (16 rows at one chunk) and the
+// transpose reads (4 rows x 4 chunks per 32 lanes) free of bank conflicts.
+// fp32 inputs use MFMA 32x32x2 f32 with the same register layout and
+// register-staged LDS tiles.
 #include "common.h"
 #include "launch.h"
 
@@ -88,26 +95,55 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[2], float& m, float& 
 }
 
 // ------------------------------------------------------------ bf16 engine
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16*l, lds_base being wave-uniform.
+// Issued from inline assembly so that the compiler does not make unrelated
+// LDS reads wait for it; the caller waits explicitly (lds_dma_wait) before
+// the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 template <int D>
 struct EngBF16 {
   using T = bf16;
+  static constexpr bool kDMA = true;
   static constexpr int KC = D / 16, DT = D / 32;
-  static constexpr int KS = D + 8;     // K row stride in LDS (elements)
-  static constexpr int VS = kSub + 4;  // V^T row stride in LDS (elements)
-  static constexpr int KELEMS = kSub * KS;
-  static constexpr int LDS_BYTES = (kSub * KS + D * VS) * 2;
-  static constexpr int KCH = kSub * D / 8;  // 16-byte chunks of a K subtile
-  static constexpr int VPT = 16 * (D / 8);  // 4-key x 8-dim patches of a V subtile
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;       // bytes per K/V row in LDS
+  static constexpr int TB = kSub * ROWB;   // bytes of one K (or V) subtile
+  static constexpr int BUF_BYTES = 2 * TB; // K subtile, then V subtile
+  static constexpr int SLOTS = kSub * CPR; // 16-byte slots per subtile
 
   bf16x8 qf[KC];
   f32x16 o[DT];
   float m, l;
 
   template <int NT>
-  struct Stage {
-    u32x4 k[(KCH + NT - 1) / NT];
-    u32x4 v[4 * ((VPT + NT - 1) / NT)];  // four key rows per patch
-  };
+  struct Stage {};
+
+  // Physical chunk of logical chunk x in row r is x ^ swz(r) for K and
+  // x ^ swzv(r) for V. LDS serves 256 bytes (64 banks) per cycle: 16 lanes
+  // of a 16-byte read or 32 lanes of an 8-byte read.
+  //  - K reads: 16 consecutive rows at one logical chunk. swz is a bijection
+  //    of r % 16 (D = 128, a row spans the 64 banks) or of (r / 2) % 8 within
+  //    each parity (D = 64, two rows span them).
+  //  - V transpose reads: 4 aligned rows x logical chunks x0 .. x0+3 (x0 a
+  //    multiple of 4) per 32 lanes. swzv only moves whole 64-byte segments:
+  //    bits 2-3 differ across the 4 rows (D = 128), or bit 2 differs between
+  //    rows of equal parity (D = 64).
+  static __device__ __forceinline__ int swz(int r) {
+    return CPR == 16 ? ((2 * (r & 7)) | ((r >> 3) & 1)) : ((2 * (r & 3)) | ((r >> 2) & 1));
+  }
+  static __device__ __forceinline__ int swzv(int r) {
+    return CPR == 16 ? (4 * (r & 3)) : (((r >> 1) & 1) << 2);
+  }
 
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -120,75 +156,66 @@ struct EngBF16 {
     for (int kk = 0; kk < KC; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * h);
   }
 
+  // Queue the direct HBM -> LDS loads of one K and one V subtile (64 rows
+  // each) into buf. Each wave instruction fills 64 consecutive 16-byte slots;
+  // the lane picks the source chunk that belongs in its slot.
   template <int NT>
-  static __device__ __forceinline__ void fetch(Stage<NT>& st, const bf16* kp, const bf16* vp, int tid) {
+  static __device__ __forceinline__ void begin(Stage<NT>&, const bf16* kp, const bf16* vp, char* buf, int tid) {
+    constexpr int NW = NT / 64, INSTS = SLOTS / 64;
+    static_assert(INSTS % NW == 0, "subtile slots must split evenly over the waves");
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
 #pragma unroll
-    for (int i = 0; i < (KCH + NT - 1) / NT; ++i) {
-      const int id = tid + NT * i;
-      if (KCH % NT == 0 || id < KCH) {
-        const int row = id / (D / 8), cc = id % (D / 8);
-        st.k[i] = *reinterpret_cast<const u32x4*>(kp + (int64_t)row * D + 8 * cc);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < (VPT + NT - 1) / NT; ++i) {
-      const int id = tid + NT * i;
-      if (VPT % NT == 0 || id < VPT) {
-        const int kg = id / (D / 8), dg = id % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          st.v[4 * i + r] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(4 * kg + r) * D + 8 * dg);
-      }
+    for (int ii = 0; ii < INSTS / NW; ++ii) {
+      const int i = ii * NW + w;
+      const int sl = i * 64 + lane;
+      const int row = sl / CPR, x = (sl % CPR) ^ swz(sl / CPR);
+      lds_dma16(kp + row * D + 8 * x, base + i * 1024);
+      lds_dma16(vp + row * D + 8 * ((sl % CPR) ^ swzv(row)), base + TB + i * 1024);
     }
   }
-
+  // Wait for this wave's queued loads (the caller's barrier covers the rest).
   template <int NT>
-  static __device__ __forceinline__ void store(const Stage<NT>& st, bf16* Ks, bf16* Vs, int tid) {
-#pragma unroll
-    for (int i = 0; i < (KCH + NT - 1) / NT; ++i) {
-      const int id = tid + NT * i;
-      if (KCH % NT == 0 || id < KCH) {
-        const int row = id / (D / 8), cc = id % (D / 8);
-        *reinterpret_cast<u32x4*>(Ks + row * KS + 8 * cc) = st.k[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < (VPT + NT - 1) / NT; ++i) {
-      const int id = tid + NT * i;
-      if (VPT % NT == 0 || id < VPT) {
-        const int kg = id / (D / 8), dg = id % (D / 8);
-        const u32x4 r0 = st.v[4 * i], r1 = st.v[4 * i + 1], r2 = st.v[4 * i + 2], r3 = st.v[4 * i + 3];
-        bf16* vd = Vs + (8 * dg) * VS + 4 * kg;
-        // Element e of the four key rows -> V^T row (8*dg + e), keys 4*kg..4*kg+3.
-#define MOBA_VT_PUT(e, W)                                                                    \
-  *reinterpret_cast<u32x2*>(vd + (e) * VS) =                                               \
-      ((e) & 1) ? u32x2{(r0.W >> 16) | (r1.W & 0xffff0000u), (r2.W >> 16) | (r3.W & 0xffff0000u)} \
-                : u32x2{(r0.W & 0xffffu) | (r1.W << 16), (r2.W & 0xffffu) | (r3.W << 16)};
-        MOBA_VT_PUT(0, x)
-        MOBA_VT_PUT(1, x)
-        MOBA_VT_PUT(2, y)
-        MOBA_VT_PUT(3, y)
-        MOBA_VT_PUT(4, z)
-        MOBA_VT_PUT(5, z)
-        MOBA_VT_PUT(6, w)
-        MOBA_VT_PUT(7, w)
-#undef MOBA_VT_PUT
-      }
-    }
+  static __device__ __forceinline__ void land(Stage<NT>&, char*, int) {
+    lds_dma_wait();
   }
 
   template <bool MASK>
-  __device__ __forceinline__ void step(const bf16* Ks, const bf16* Vs, int col, int h, int key0, int qpos, float sl2) {
-    f32x16 s[2];
+  __device__ __forceinline__ void step(const char* buf, int lane, int key0, int qpos, float sl2) {
+    const int h = lane >> 5, col = lane & 31;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      // Rows col and 32 + col share swz (it depends on row % 16 only), so
+      // one offset pattern serves both key halves.
+      const int sw = swz(col);
+      const char* r0 = buf + col * ROWB;
+      const char* r1 = r0 + 32 * ROWB;
+      bf16x8 a[KC];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      s[nt] = f32x16{};
+      for (int kk = 0; kk < KC; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(r0 + 16 * ((2 * kk + h) ^ sw));
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * nt + col) * KS + 16 * kk + 8 * h);
-        s[nt] = mfma_bf16(a, qf[kk], s[nt]);
+        s[0] = mfma_bf16(a[kk], qf[kk], s[0]);
+        a[kk] = *reinterpret_cast<const bf16x8*>(r1 + 16 * ((2 * kk + h) ^ sw));
       }
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) s[1] = mfma_bf16(a[kk], qf[kk], s[1]);
     }
+    // P.V operands: lane j of each 16-lane group names row K0 + j/4, dims
+    // D0 + 4*(j%4) .. +3 and receives V[K0 + e][D0 + j], e < 4, i.e. a V^T
+    // fragment.
+    const int j = lane & 15, half = (lane >> 4) & 1;
+    const char* vb = buf + TB;
+    auto vfrag = [&](int dt, int nt, int g) {
+      const int d = 32 * dt + 16 * half + 4 * (j & 3);
+      const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
+      const char* a0 = vb + r0 * ROWB + 16 * ((d >> 3) ^ swzv(r0)) + 2 * (d & 7);
+      const char* a1 = vb + r1 * ROWB + 16 * ((d >> 3) ^ swzv(r1)) + 2 * (d & 7);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     online_softmax<MASK>(s, m, l, o, h, key0, qpos, sl2);
     bf16x8 pb[2][2];
 #pragma unroll
@@ -196,18 +223,9 @@ struct EngBF16 {
 #pragma unroll
       for (int r = 0; r < 16; ++r) pb[nt][r >> 3][r & 7] = to_bf16(s[nt][r]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const bf16* vp = Vs + (32 * dt + col) * VS + 32 * nt + 16 * g + 4 * h;
-          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vp);
-          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vp + 8);
-          const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dt] = mfma_bf16(av, pb[nt][g], o[dt]);
-        }
-    }
+      for (int i = 0; i < 4; ++i) o[dt] = mfma_bf16(vfrag(dt, i >> 1, i & 1), pb[i >> 1][i & 1], o[dt]);
   }
 
   // 16 output values of d-tile dt, lane-native order, to memory.
@@ -245,11 +263,11 @@ struct EngBF16 {
 template <int D>
 struct EngF32 {
   using T = float;
+  static constexpr bool kDMA = false;
   static constexpr int KC = D / 2, DT = D / 32;
   static constexpr int KS = D + 2;  // K row stride (floats): conflict-free column reads
   static constexpr int VS = D + 8;  // V row stride (floats): the two lane halves hit disjoint banks
-  static constexpr int KELEMS = kSub * KS;
-  static constexpr int LDS_BYTES = (kSub * KS + kSub * VS) * 4;
+  static constexpr int BUF_BYTES = (kSub * KS + kSub * VS) * 4;
   static constexpr int CH = kSub * D / 4;  // 16-byte chunks per subtile
 
   float qf[KC];
@@ -272,8 +290,9 @@ struct EngF32 {
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) qf[kk] = qrow[2 * kk + h];
   }
+  // Load one K and one V subtile into registers.
   template <int NT>
-  static __device__ __forceinline__ void fetch(Stage<NT>& st, const float* kp, const float* vp, int tid) {
+  static __device__ __forceinline__ void begin(Stage<NT>& st, const float* kp, const float* vp, char*, int tid) {
 #pragma unroll
     for (int i = 0; i < (CH + NT - 1) / NT; ++i) {
       const int id = tid + NT * i;
@@ -284,8 +303,11 @@ struct EngF32 {
       }
     }
   }
+  // Write the staged registers to the LDS buffer.
   template <int NT>
-  static __device__ __forceinline__ void store(const Stage<NT>& st, float* Ks, float* Vs, int tid) {
+  static __device__ __forceinline__ void land(const Stage<NT>& st, char* buf, int tid) {
+    float* Ks = reinterpret_cast<float*>(buf);
+    float* Vs = Ks + kSub * KS;
 #pragma unroll
     for (int i = 0; i < (CH + NT - 1) / NT; ++i) {
       const int id = tid + NT * i;
@@ -299,7 +321,10 @@ struct EngF32 {
     }
   }
   template <bool MASK>
-  __device__ __forceinline__ void step(const float* Ks, const float* Vs, int col, int h, int key0, int qpos, float sl2) {
+  __device__ __forceinline__ void step(const char* buf, int lane, int key0, int qpos, float sl2) {
+    const int h = lane >> 5, col = lane & 31;
+    const float* Ks = reinterpret_cast<const float*>(buf);
+    const float* Vs = Ks + kSub * KS;
     f32x16 s[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -355,6 +380,66 @@ struct EngOf<float, D> {
   using type = EngF32<D>;
 };
 
+// Streams nsub consecutive 64-key subtiles of K and V through LDS and calls
+// compute(buf, sub) on each. Direct-load engines double-buffer (loads of
+// subtile sub+1 run under the compute of subtile sub; the two buffers are
+// distinct objects so the compiler need not order the loads against the
+// reads of the other buffer); register-staged engines prefetch into
+// registers and use one buffer.
+template <class E, int NT, class F>
+__device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const typename E::T* kp,
+                                                const typename E::T* vp, int nsub, int D, int tid, F&& compute) {
+  typename E::template Stage<NT> st;
+  E::template begin<NT>(st, kp, vp, bufA, tid);
+  E::template land<NT>(st, bufA, tid);
+  // Also tell the compiler that every vector-memory load issued so far (the
+  // query fragments) has completed, so that it emits no vmcnt waits inside
+  // the loop, where the only outstanding loads are the next subtile's.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  const int64_t step_elems = (int64_t)kSub * D;
+  if constexpr (E::kDMA) {
+    for (int sub = 0; sub < nsub; sub += 2) {
+      const bool m1 = sub + 1 < nsub;
+      if (m1) E::template begin<NT>(st, kp + (sub + 1) * step_elems, vp + (sub + 1) * step_elems, bufB, tid);
+      compute(bufA, sub);
+      if (m1) E::template land<NT>(st, bufB, tid);
+      __syncthreads();
+      if (!m1) break;
+      const bool m2 = sub + 2 < nsub;
+      if (m2) E::template begin<NT>(st, kp + (sub + 2) * step_elems, vp + (sub + 2) * step_elems, bufA, tid);
+      compute(bufB, sub + 1);
+      if (m2) E::template land<NT>(st, bufA, tid);
+      __syncthreads();
+    }
+  } else {
+    for (int sub = 0; sub < nsub; ++sub) {
+      const bool more = sub + 1 < nsub;
+      if (more) E::template begin<NT>(st, kp + (sub + 1) * step_elems, vp + (sub + 1) * step_elems, bufA, tid);
+      compute(bufA, sub);
+      if (more) {
+        __syncthreads();
+        E::template land<NT>(st, bufA, tid);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// LDS for one kernel: two static subtile buffers for direct-load engines,
+// the dynamic allocation (one buffer) otherwise.
+#define MOBA_KERNEL_LDS(E)                                                   \
+  extern __shared__ __align__(16) char dyn_smem[];                           \
+  __shared__ __align__(16) char lds_a[E::kDMA ? E::BUF_BYTES : 16];          \
+  __shared__ __align__(16) char lds_b[E::kDMA ? E::BUF_BYTES : 16];          \
+  char* bufA = E::kDMA ? lds_a : dyn_smem;                                   \
+  char* bufB = E::kDMA ? lds_b : dyn_smem;
+
+template <class E>
+constexpr int dyn_lds_bytes() {
+  return E::kDMA ? 0 : E::BUF_BYTES;
+}
+
 }  // namespace
 
 // ------------------------------------------------------- past-block gather
@@ -362,9 +447,7 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gather_attn_kernel(AttnArgs a) {
   using E = typename EngOf<T, D>::type;
   constexpr int NT = 64 * NW, M = 32 * NW;
-  extern __shared__ __align__(16) char smem[];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = Ks + E::KELEMS;
+  MOBA_KERNEL_LDS(E)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
 
   // Tiles are numbered per (head, block) in order; consecutive tiles share a
@@ -402,15 +485,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + j * a.block_size) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
   const int nsub = (int)(a.block_size / kSub);
-  typename E::template Stage<NT> st;
-  E::template fetch<NT>(st, kp, vp, tid);
-  for (int sub = 0; sub < nsub; ++sub) {
-    __syncthreads();
-    E::template store<NT>(st, Ks, Vs, tid);
-    __syncthreads();
-    if (sub + 1 < nsub) E::template fetch<NT>(st, kp + (int64_t)(sub + 1) * kSub * D, vp + (int64_t)(sub + 1) * kSub * D, tid);
-    if (wave_on) eng.template step<false>(Ks, Vs, col, h, 0, 0, sl2);
-  }
+  stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, [&](const char* buf, int) {
+    if (wave_on) eng.template step<false>(buf, lane, 0, 0, sl2);
+  });
   if (!wave_on) return;
   const float lt = pair_sum(eng.l);
   if (valid) {
@@ -428,9 +505,7 @@ template <typename T, int D, int NW, bool DENSE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void diag_attn_kernel(AttnArgs a) {
   using E = typename EngOf<T, D>::type;
   constexpr int NT = 64 * NW, M = 32 * NW;
-  extern __shared__ __align__(16) char smem[];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = Ks + E::KELEMS;
+  MOBA_KERNEL_LDS(E)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   // Heavier tiles (later in the sequence) first, heads interleaved.
   const int64_t ntile = a.seq_len / M;
@@ -451,28 +526,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + kb) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
   const int nsub = (kend - kb) / kSub;
-  typename E::template Stage<NT> st;
-  E::template fetch<NT>(st, kp, vp, tid);
   // Subtiles entirely before the workgroup's first query need no mask; with
   // causal attention the last M/64 subtiles hold the diagonal.
   const int nfree = a.causal ? (q0 - kb) / kSub : nsub;
-  int sub = 0;
-  for (; sub < nfree; ++sub) {
-    __syncthreads();
-    E::template store<NT>(st, Ks, Vs, tid);
-    __syncthreads();
-    if (sub + 1 < nsub) E::template fetch<NT>(st, kp + (int64_t)(sub + 1) * kSub * D, vp + (int64_t)(sub + 1) * kSub * D, tid);
-    eng.template step<false>(Ks, Vs, col, h, 0, 0, sl2);
-  }
-  for (; sub < nsub; ++sub) {
-    __syncthreads();
-    E::template store<NT>(st, Ks, Vs, tid);
-    __syncthreads();
-    if (sub + 1 < nsub) E::template fetch<NT>(st, kp + (int64_t)(sub + 1) * kSub * D, vp + (int64_t)(sub + 1) * kSub * D, tid);
-    const int key0 = kb + sub * kSub;
-    // Skip a subtile whose keys all come after every query of this wave.
-    if (key0 <= qw0 + 31) eng.template step<true>(Ks, Vs, col, h, key0, t, sl2);
-  }
+  stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, [&](const char* buf, int sub) {
+    if (sub < nfree) {
+      eng.template step<false>(buf, lane, 0, 0, sl2);
+    } else {
+      const int key0 = kb + sub * kSub;
+      // Skip a subtile whose keys all come after every query of this wave.
+      if (key0 <= qw0 + 31) eng.template step<true>(buf, lane, key0, t, sl2);
+    }
+  });
 
   const float lt = pair_sum(eng.l);
   if (DENSE) {
@@ -538,11 +603,12 @@ hipError_t gather_t(const AttnArgs& a, hipStream_t s) {
   using E = typename EngOf<T, D>::type;
   constexpr int NW = 4;
   auto kern = gather_attn_kernel<T, D, NW>;
-  hipError_t e = prep_lds(kern, E::LDS_BYTES);
+  constexpr int lds = dyn_lds_bytes<E>();
+  hipError_t e = prep_lds(kern, lds);
   if (e != hipSuccess) return e;
   const int64_t grid = (a.max_tiles + 7) / 8 * 8;
   KernelTimer timer(s, "gather_attn");
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), E::LDS_BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), lds, s, a);
   return hipGetLastError();
 }
 
@@ -552,18 +618,19 @@ hipError_t diag_t(const AttnArgs& a, hipStream_t s) {
   // 128-query tiles when they stay inside one block (and one sequence), else 64.
   const bool four = DENSE ? (a.seq_len % 128 == 0) : (a.block_size % 128 == 0);
   const char* name = DENSE ? "dense_attn" : "diag_merge";
+  constexpr int lds = dyn_lds_bytes<E>();
   if (four) {
     auto kern = diag_attn_kernel<T, D, 4, DENSE>;
-    hipError_t e = prep_lds(kern, E::LDS_BYTES);
+    hipError_t e = prep_lds(kern, lds);
     if (e != hipSuccess) return e;
     KernelTimer timer(s, name);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.bh * (a.seq_len / 128))), dim3(256), E::LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.bh * (a.seq_len / 128))), dim3(256), lds, s, a);
   } else {
     auto kern = diag_attn_kernel<T, D, 2, DENSE>;
-    hipError_t e = prep_lds(kern, E::LDS_BYTES);
+    hipError_t e = prep_lds(kern, lds);
     if (e != hipSuccess) return e;
     KernelTimer timer(s, name);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), E::LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), lds, s, a);
   }
   return hipGetLastError();
 }

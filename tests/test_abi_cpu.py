@@ -24,7 +24,7 @@ def test_exports_every_declared_function():
     names = _header_functions()
     assert len(names) >= 10
     for n in names:
-        assert hasattr(_lib.LIB, n), n
+        assert hasattr(_lib.lib(), n), n
     assert sorted(_lib.EXPORTED) == names
 
 
