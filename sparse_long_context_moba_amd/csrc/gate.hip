@@ -12,17 +12,25 @@
 //
 // Mapping on gfx950: a workgroup owns 128 consecutive queries of one head,
 // a wave 32 of them (they share c because block_size is a multiple of 64).
-// Tiles of 32 pooled keys are staged in LDS once per workgroup. Scores come
-// from bf16 MFMA 32x32x16 with the pooled keys as the A operand (rows =
-// blocks) and the queries as the B operand (columns = queries), so lane l
-// holds 16 block scores of query l%32 and the per-query top-k runs in
-// registers; the two lane halves merge their lists with one exchange. The
-// pooled keys enter as a bf16 hi/lo pair (two MFMA passes, fp32 accumulate);
-// fp32 inputs use fp32 MFMA on the fp32 means.
+// Tiles of 32 pooled keys are staged in LDS once per workgroup, double
+// buffered, one barrier per tile. Scores come from bf16 MFMA 32x32x16 with
+// the pooled keys as the A operand (rows = blocks) and the queries as the
+// B operand (columns = queries), so lane l holds 16 block scores of query
+// l%32. The pooled keys enter as a bf16 hi/lo pair (two MFMA passes, fp32
+// accumulate); fp32 inputs use fp32 MFMA on the fp32 means. The MFMAs of
+// tile i+1 are interleaved in the instruction stream with the selection
+// work of tile i (waves issue in order).
+//
+// Selection: each lane keeps the top-TT of its own scores as sortable keys:
+// within a segment of 8 tiles as fp32 keys carrying their position in the
+// low mantissa bits (insertion = one max and TT-1 med3, independent of each
+// other), merged at the segment end into fp64 keys carrying the block index
+// (exact, see score_key). The two lane halves merge their lists at the end.
 //
 // Exactness: every fast score carries a rounding bound
 //   eps = gamma * ||q_t||_2 * max_j ||kbar_j||_2   (Cauchy-Schwarz),
-// gamma covering the hi/lo residual and the fp32 accumulation. If the gap
+// gamma covering the hi/lo residual, the fp32 accumulation and the segment
+// key truncation. If the gap
 // between the last kept and the first dropped fast score is not above
 // 2*eps, the query's tracked candidates (or, if the bound reaches beyond the
 // tracked list, all its eligible blocks) are re-scored in fp64 from the fp64
@@ -43,32 +51,16 @@ namespace moba {
 namespace {
 
 constexpr int kNoBlock = 0x7fffffff;
-constexpr int kGateQ = 128;         // queries per workgroup
 constexpr int kTileB = 32;          // pooled keys per LDS tile
 constexpr int kLdsBinsMax = 8192;   // per-workgroup histogram bins kept in LDS
 constexpr int kRankQ = 1024;        // queries per rank workgroup
 
 // Strict order: higher score first, then lower block index.
-__device__ __forceinline__ bool better(float s1, int j1, float s2, int j2) {
-  return s1 > s2 || (s1 == s2 && j1 < j2);
-}
 __device__ __forceinline__ bool better64(double s1, int j1, double s2, int j2) {
   return s1 > s2 || (s1 == s2 && j1 < j2);
 }
 
-// Insert (s, j) into a list sorted by `better`, keeping its length.
-template <int N>
-__device__ __forceinline__ void insert_full(float (&ls)[N], int (&lj)[N], float s, int j) {
-#pragma unroll
-  for (int i = N - 1; i >= 0; --i) {
-    const bool here = better(s, j, ls[i], lj[i]);
-    const bool above = (i > 0) ? better(s, j, ls[i - 1], lj[i - 1]) : false;
-    const float ns = above ? ls[i - 1] : (here ? s : ls[i]);
-    const int nj = above ? lj[i - 1] : (here ? j : lj[i]);
-    ls[i] = ns;
-    lj[i] = nj;
-  }
-}
+// Insert (s, j) into a list sorted by `better64`, keeping its length.
 template <int N>
 __device__ __forceinline__ void insert_full64(double (&ls)[N], int (&lj)[N], double s, int j) {
 #pragma unroll
@@ -80,6 +72,105 @@ __device__ __forceinline__ void insert_full64(double (&ls)[N], int (&lj)[N], dou
     ls[i] = ns;
     lj[i] = nj;
   }
+}
+
+// Sortable keys for the fast top-k. A fast score s (fp32) converts exactly
+// to fp64, which leaves the low 29 mantissa bits zero; the block index goes
+// there. Keys of distinct scores keep the scores' order (the index is below
+// one fp32 ulp), keys of equal scores differ, and both parts come back
+// exactly, so a descending list of keys is kept with fp64 max/min alone:
+// inserting key x walks the list with L[i], x = max(L[i], x), min(L[i], x).
+// (s = +-0 gives subnormal keys, which fp64 compares keep.) Equal fast
+// scores are ordered by index here in either direction; a tie in the fast
+// scores is always inside the rounding band, so it is settled by the fp64
+// re-scoring below, with the lower index first.
+constexpr unsigned kKeyIdxMask = 0x1fffffffu;
+// Below every score key (about -2^1023; its index part marks "no block").
+constexpr double kKeyNone = __builtin_bit_cast(double, 0xffe000001fffffffull);
+
+__device__ __forceinline__ double score_key(float s, int j) {
+  u32x2 b = __builtin_bit_cast(u32x2, (double)s);
+  b.x += (unsigned)j;
+  return __builtin_bit_cast(double, b);
+}
+__device__ __forceinline__ float key_score(double k) {
+  u32x2 b = __builtin_bit_cast(u32x2, k);
+  b.x &= ~kKeyIdxMask;
+  return (float)__builtin_bit_cast(double, b);
+}
+__device__ __forceinline__ int key_block(double k) {
+  const unsigned j = __builtin_bit_cast(u32x2, k).x & kKeyIdxMask;
+  return j == kKeyIdxMask ? kNoBlock : (int)j;
+}
+template <int N>
+__device__ __forceinline__ void insert_key(double (&L)[N], double x) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const double hi = __builtin_fmax(L[i], x);
+    x = __builtin_fmin(L[i], x);
+    L[i] = hi;
+  }
+}
+
+// Segment keys. The scan runs in segments of kSegTiles tiles; within one, a
+// lane's scores become fp32 keys whose low kSegBits mantissa bits hold the
+// score's position in the segment (tile in segment, accumulator element r;
+// the lane half is implicit). Positions are distinct, so keys are distinct
+// and order like the truncated scores (truncation moves a score by less
+// than 2^-16 of itself, which the rounding bound covers). Inserting x into
+// a descending list S is then S'[0] = max(S[0], x), S'[i] = med3(S[i-1],
+// S[i], x): one independent operation per slot. At the end of a segment the
+// lane's surviving keys are decoded and merged into its fp64 key list.
+constexpr int kSegTiles = 8;
+constexpr int kSegBits = 7;  // 3 bits of tile, 4 of accumulator element
+constexpr unsigned kSegMask = (1u << kSegBits) - 1;
+static_assert((kSegTiles << 4) == (1 << kSegBits), "segment position bits");
+
+template <int QG, int TT, bool MASK>
+__device__ __forceinline__ void absorb(float (&S)[QG][TT], const f32x16 (&acc)[QG], int tis, int jb, int jend,
+                                       int c) {
+  const unsigned pos0 = (unsigned)tis << 4;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const unsigned pos = pos0 + r;
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      // The element is read as a scalar first: this compiler turns
+      // __builtin_bit_cast of a vector element into a cast of element 0.
+      const float sv = acc[g][r];
+      float x = __uint_as_float((__float_as_uint(sv) & ~kSegMask) | pos);
+      if (MASK) {
+        const int j = jb + 8 * (r >> 2) + (r & 3);
+        x = (j < jend && j != c) ? x : kNegInf;
+      }
+      float n[TT];
+      n[0] = __builtin_fmaxf(S[g][0], x);
+#pragma unroll
+      for (int i = 1; i < TT; ++i) n[i] = __builtin_amdgcn_fmed3f(S[g][i - 1], S[g][i], x);
+#pragma unroll
+      for (int i = 0; i < TT; ++i) S[g][i] = n[i];
+    }
+  }
+}
+
+// Moves a segment's keys (segment starting at block seg0) into the fp64 key
+// lists and clears the segment lists. h is the lane half.
+template <int QG, int TT>
+__device__ __forceinline__ void flush_segment(float (&S)[QG][TT], double (&L)[QG][TT], int seg0, int h) {
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      const unsigned kb = __builtin_bit_cast(unsigned, S[g][i]);
+      const unsigned p = kb & kSegMask, r = p & 15;
+      const int j = seg0 + 32 * (int)(p >> 4) + 8 * (int)(r >> 2) + 4 * h + (int)(r & 3);
+      const bool empty = S[g][i] == kNegInf;
+      // (An empty slot decodes to garbage; it is replaced, not inserted.)
+      const float sv = empty ? 0.f : __builtin_bit_cast(float, kb & ~kSegMask);
+      const double x = score_key(sv, j);
+      insert_key(L[g], empty ? kKeyNone : x);
+      S[g][i] = kNegInf;
+    }
 }
 
 // Per-dtype query fragment (the lane's half of q_t's coordinates), pooled
@@ -108,34 +199,88 @@ struct GateOps<bf16, D> {
       }
     return s;
   }
-  // Stage rows j0 .. j0+31 (clamped to the last block) of hi and lo.
-  static __device__ void stage(char* lds, const GateArgs& a, int64_t bh, int j0, int tid) {
-    bf16* hi = reinterpret_cast<bf16*>(lds);
-    bf16* lo = hi + kTileB * KR;
-    constexpr int CH = kTileB * D / 8;  // 16-byte chunks per tile (per hi or lo)
+  // Staging of one tile, rows j0 .. j0+31 of hi then lo (rows past the last
+  // block repeat it): NLD 16-byte chunks per thread, fetched into registers
+  // one tile ahead and stored to LDS after the current tile is scored.
+  using Chunk = u32x4;
+  static constexpr int CPR = D / 8;             // chunks per row
+  static constexpr int CH = kTileB * CPR;       // chunks per tile of hi (or lo)
+  static constexpr int NLD = 2 * CH / 256;
+  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t bh, int j0, int tid) {
+    const int64_t head = bh * a.n_blocks * D;
+    if (j0 + kTileB <= a.n_blocks) {
+      // Whole tile: a uniform base and a fixed per-thread offset.
+      const bf16* hi = a.kbar_hi + head + (int64_t)j0 * D;
+      const bf16* lo = a.kbar_lo + head + (int64_t)j0 * D;
 #pragma unroll
-    for (int i = tid; i < 2 * CH; i += 256) {
-      const int which = i / CH, id = i % CH;
-      const int row = id / (D / 8), cc = id % (D / 8);
-      const int j = min(j0 + row, (int)a.n_blocks - 1);
-      const bf16* src = (which ? a.kbar_lo : a.kbar_hi) + (bh * a.n_blocks + j) * D + 8 * cc;
-      *reinterpret_cast<u32x4*>((which ? lo : hi) + row * KR + 8 * cc) = *reinterpret_cast<const u32x4*>(src);
+      for (int n = 0; n < NLD; ++n) {
+        const int i = tid + 256 * n, id = i % CH;
+        r[n] = *reinterpret_cast<const Chunk*>((i < CH ? hi : lo) + (id / CPR) * D + 8 * (id % CPR));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NLD; ++n) {
+        const int i = tid + 256 * n, id = i % CH;
+        const int j = min(j0 + id / CPR, (int)a.n_blocks - 1);
+        r[n] = *reinterpret_cast<const Chunk*>((i < CH ? a.kbar_hi : a.kbar_lo) + head + (int64_t)j * D + 8 * (id % CPR));
+      }
     }
   }
-  __device__ f32x16 scores(const char* lds, int col, int h) const {
+  static __device__ void put(char* lds, const Chunk (&r)[NLD], int tid) {
+    bf16* hi = reinterpret_cast<bf16*>(lds);
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int i = tid + 256 * n, which = i / CH, id = i % CH;
+      *reinterpret_cast<Chunk*>(hi + which * kTileB * KR + (id / CPR) * KR + 8 * (id % CPR)) = r[n];
+    }
+  }
+  static constexpr int QG_MAX = 2;  // 32-query groups per wave
+  // Scores of every group against the tile: each pooled-key fragment is read
+  // from LDS once and feeds one MFMA per group (independent chains).
+  template <int QG>
+  static __device__ void scores(const char* lds, int col, int h, const GateOps (&qf)[QG], f32x16 (&acc)[QG]) {
     const bf16* hi = reinterpret_cast<const bf16*>(lds) + col * KR + 8 * h;
     const bf16* lo = hi + kTileB * KR;
-    f32x16 acc = {};
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(hi + 16 * kk), f[kk], acc);
+    for (int g = 0; g < QG; ++g) acc[g] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(lo + 16 * kk), f[kk], acc);
-    return acc;
+    for (int kk = 0; kk < KC; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(hi + 16 * kk);
+#pragma unroll
+      for (int g = 0; g < QG; ++g) acc[g] = mfma_bf16(af, qf[g].f[kk], acc[g]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(lo + 16 * kk);
+#pragma unroll
+      for (int g = 0; g < QG; ++g) acc[g] = mfma_bf16(af, qf[g].f[kk], acc[g]);
+    }
+  }
+  // Issue order for the steady state (waves issue in order, so the MFMA
+  // chains only overlap the selection work if the two are interleaved in
+  // the instruction stream): a few fragment reads ahead, then per fragment
+  // its QG MFMAs and an even share of the selection's VALU work.
+  template <int QG, int TT>
+  static __device__ __forceinline__ void interleave() {
+    constexpr int NF = 2 * KC;                     // fragments (hi and lo)
+    constexpr int VALU = 16 * QG * (TT + 1) + 16;  // selection work per tile
+    constexpr int PER = (VALU + NF - 1) / NF;
+    constexpr int AHEAD = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+      if (f + AHEAD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   }
   // Relative rounding bound of a fast score: hi/lo residual (<= 2^-16 of
-  // each mean coordinate, taken as 2^-15) plus 2D+16 fp32 accumulation
-  // steps at 2^-22 each (a 4x margin over rounding to nearest).
-  static __device__ constexpr float gamma() { return 3.0517578e-05f + (2 * D + 16) * 2.3841858e-07f; }
+  // each mean coordinate, taken as 2^-15), 2D+16 fp32 accumulation steps at
+  // 2^-22 each (a 4x margin over rounding to nearest) and the segment key
+  // truncation (2^-16).
+  static __device__ constexpr float gamma() {
+    return 3.0517578e-05f + (2 * D + 16) * 2.3841858e-07f + 1.5258789e-05f;
+  }
 };
 
 template <int D>
@@ -154,197 +299,160 @@ struct GateOps<float, D> {
     for (int kk = 0; kk < KC; ++kk) s = __builtin_fmaf(f[kk], f[kk], s);
     return s;
   }
-  static __device__ void stage(char* lds, const GateArgs& a, int64_t bh, int j0, int tid) {
-    float* kt = reinterpret_cast<float*>(lds);
-    constexpr int CH = kTileB * D / 2;  // 8-byte chunks per tile
-    for (int id = tid; id < CH; id += 256) {
-      const int row = id / (D / 2), cc = id % (D / 2);
-      const int j = min(j0 + row, (int)a.n_blocks - 1);
-      *reinterpret_cast<float2*>(kt + row * KR + 2 * cc) =
-          *reinterpret_cast<const float2*>(a.kbar32 + (bh * a.n_blocks + j) * D + 2 * cc);
+  // 8-byte chunks: the padded row stride (D + 2 floats) keeps the column
+  // reads conflict-free but leaves odd rows 8-byte aligned.
+  using Chunk = u32x2;
+  static constexpr int CPR = D / 2;
+  static constexpr int CH = kTileB * CPR;
+  static constexpr int NLD = CH / 256;
+  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t bh, int j0, int tid) {
+    const float* head = a.kbar32 + bh * a.n_blocks * D;
+    if (j0 + kTileB <= a.n_blocks) {
+      const float* base = head + (int64_t)j0 * D;
+#pragma unroll
+      for (int n = 0; n < NLD; ++n) {
+        const int id = tid + 256 * n;
+        r[n] = *reinterpret_cast<const Chunk*>(base + (id / CPR) * D + 2 * (id % CPR));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NLD; ++n) {
+        const int id = tid + 256 * n;
+        const int j = min(j0 + id / CPR, (int)a.n_blocks - 1);
+        r[n] = *reinterpret_cast<const Chunk*>(head + (int64_t)j * D + 2 * (id % CPR));
+      }
     }
   }
-  __device__ f32x16 scores(const char* lds, int col, int h) const {
-    const float* kt = reinterpret_cast<const float*>(lds) + col * KR + h;
-    f32x16 acc = {};
+  static __device__ void put(char* lds, const Chunk (&r)[NLD], int tid) {
+    float* kt = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) acc = mfma_f32(kt[2 * kk], f[kk], acc);
-    return acc;
+    for (int n = 0; n < NLD; ++n) {
+      const int id = tid + 256 * n;
+      *reinterpret_cast<Chunk*>(kt + (id / CPR) * KR + 2 * (id % CPR)) = r[n];
+    }
   }
-  // fp32 products and 2D+16 accumulation steps at 2^-22 each.
-  static __device__ constexpr float gamma() { return (2 * D + 16) * 2.3841858e-07f; }
+  static constexpr int QG_MAX = 1;  // the fp32 query fragment alone takes D/2 registers
+  template <int QG>
+  static __device__ void scores(const char* lds, int col, int h, const GateOps (&qf)[QG], f32x16 (&acc)[QG]) {
+    static_assert(QG == 1, "one query group");
+    const float* kt = reinterpret_cast<const float*>(lds) + col * KR + h;
+    acc[0] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) acc[0] = mfma_f32(kt[2 * kk], qf[0].f[kk], acc[0]);
+  }
+  template <int QG, int TT>
+  static __device__ __forceinline__ void interleave() {
+    constexpr int VALU = 16 * QG * (TT + 1) + 16;
+    constexpr int PER = (VALU + KC - 1) / KC;
+#pragma unroll
+    for (int f = 0; f < KC; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+    }
+  }
+  // fp32 products and 2D+16 accumulation steps at 2^-22 each, and the
+  // segment key truncation (2^-16).
+  static __device__ constexpr float gamma() { return (2 * D + 16) * 2.3841858e-07f + 1.5258789e-05f; }
 };
 
-}  // namespace
-
+// 32-query groups per wave. A second group would give independent MFMA and
+// selection chains and halve the LDS fragment reads, but with the pipelined
+// accumulators it does not fit the register file without spills; one group
+// at three waves per SIMD does.
 template <typename T, int D, int TT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT <= 4 ? 3 : 2))) void gate_topk_kernel(
-    GateArgs a) {
-  using Ops = GateOps<T, D>;
-  extern __shared__ __align__(16) char smem[];
-  char* tile = smem;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int64_t wg_per_head = (a.seq_len + kGateQ - 1) / kGateQ;
-  const int64_t bh = blockIdx.x / wg_per_head;
-  const int64_t qb = (blockIdx.x % wg_per_head) * kGateQ;
-  const int64_t t0 = qb + 32 * w;
-  const bool wave_on = t0 < a.seq_len;  // workgroup-uniform control flow below
-  const int64_t t = wave_on ? t0 + col : qb;
-  const int NB = (int)a.n_blocks;
-  const int c = (int)(t / a.block_size);
-  const int n_elig = a.causal ? c : NB - 1;
-  const int m = min(a.k_eff - 1, n_elig);
-  const bool scoring = wave_on && m > 0 && m < n_elig;  // wave-uniform
-  int32_t* idx_row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
+__host__ __device__ constexpr int gate_groups() {
+  return 1;
+}
+// Waves per SIMD the register budget is set for.
+template <typename T, int D, int TT>
+constexpr int gate_waves() {
+  return (sizeof(T) == 2 && TT <= 6) ? 3 : 2;
+}
 
-  // ---- fast scores over the eligible blocks, top-TT per lane half
-  Ops qf;
-  const T* qrow = reinterpret_cast<const T*>(a.q) + (bh * a.seq_len + t) * D;
-  float qnorm = 0.f;
-  if (scoring) {
-    qf.load(qrow, h);
-    float qss = qf.sumsq();
-    qss += shfl_xor32(qss);
-    qnorm = __builtin_sqrtf(qss) * 1.0001f;
-  }
-  float ls[TT];
-  int lj[TT];
+// fp64 re-scoring of the wave's ambiguous queries (lanes with `amb` set,
+// lane half 0), one query at a time by the whole wave. The queries share c
+// and the eligible set. Candidates are the query's tracked list, or every
+// eligible block when its rounding band reaches past the list (`tracked`
+// false). 64 lanes split each candidate's dot product into D/8 slices of 8
+// coordinates and sum the slices in a fixed order (deterministic). The
+// query in lane column L gets the exact top-TT in sel.
+template <typename T, int D, int TT>
+__device__ void rescore_ambiguous(const GateArgs& a, int64_t bh, int64_t tg, int c, int jend, bool amb,
+                                  bool tracked, const int (&lj)[TT], int (&sel)[TT], int lane, int col) {
+  uint64_t pend = __builtin_amdgcn_ballot_w64(amb);
+  const double* kb64 = a.kbar64 + bh * a.n_blocks * (int64_t)D;
+  constexpr int SL = D / 8;    // 8-coordinate slices per candidate
+  constexpr int G = 64 / SL;   // candidates per pass
+  const int gi = lane / SL, sl = lane % SL;
+  while (pend) {
+    const int ln = __builtin_ctzll(pend);
+    pend &= pend - 1;
+    const bool trk = __builtin_amdgcn_readlane((int)tracked, ln);
+    // This lane's slice of the ambiguous query's coordinates, in fp64.
+    const T* qL = reinterpret_cast<const T*>(a.q) + (bh * a.seq_len + tg + ln) * D + 8 * sl;
+    double qd[8];
 #pragma unroll
-  for (int i = 0; i < TT; ++i) {
-    ls[i] = kNegInf;
-    lj[i] = kNoBlock;
-  }
-  const int jend = a.causal ? c : NB;  // this wave's scan bound
-  // Scan bound of the whole workgroup (its last valid query has the largest c).
-  const int64_t t_last = min<int64_t>(qb + kGateQ, a.seq_len) - 1;
-  const int wg_jend = a.causal ? (int)(t_last / a.block_size) : NB;
-  for (int jt = 0; jt < wg_jend; jt += kTileB) {
-    __syncthreads();
-    Ops::stage(tile, a, bh, jt, tid);
-    __syncthreads();
-    if (!scoring || jt >= jend) continue;
-    const f32x16 acc = qf.scores(tile, col, h);
+    for (int e = 0; e < 8; ++e) qd[e] = (double)(float)qL[e];
+    int cj[TT];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = jt + crow(r, h);
-      const bool ok = j < jend && j != c;
-      const float s = ok ? acc[r] : kNegInf;
-      // Blocks reach a lane in increasing j, so a strict test keeps the
-      // lower index first among equal scores.
-      if (s > ls[TT - 1]) {
-#pragma unroll
-        for (int i = TT - 1; i >= 0; --i) {
-          const bool here = s > ls[i];
-          const bool above = (i > 0) ? (s > ls[i - 1]) : false;
-          const float ns = above ? ls[i - 1] : (here ? s : ls[i]);
-          const int nj = above ? lj[i - 1] : (here ? j : lj[i]);
-          ls[i] = ns;
-          lj[i] = nj;
-        }
-      }
-    }
-  }
-
-  int sel[TT];
-#pragma unroll
-  for (int i = 0; i < TT; ++i) sel[i] = lj[i];
-  if (scoring) {
-    // Merge the two lane halves (each lane merges the other's list into its
-    // own; the order is strict, so both halves end with the same list).
-    float ps[TT];
-    int pj[TT];
+    for (int i = 0; i < TT; ++i) cj[i] = __builtin_amdgcn_readlane(lj[i], ln);
+    double es[TT];
+    int ej[TT];
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-      ps[i] = shfl_xor32(ls[i]);
-      pj[i] = shfl_xor32(lj[i]);
+      es[i] = -__builtin_huge_val();
+      ej[i] = kNoBlock;
     }
+    const int ncand = trk ? TT : jend;
+    for (int base = 0; base < ncand; base += G) {
+      const int ci = base + gi;
+      int j = kNoBlock;
+      if (trk) {
 #pragma unroll
-    for (int i = 0; i < TT; ++i) insert_full(ls, lj, ps[i], pj[i]);
-#pragma unroll
-    for (int i = 0; i < TT; ++i) sel[i] = lj[i];
-
-    // ---- exactness check: is the cut between kept and dropped blocks
-    // farther apart than twice the fast scores' rounding bound?
-    const float eps = Ops::gamma() * qnorm * a.norm[bh] + 1e-30f;
-    const bool amb = !(ls[m - 1] - ls[m] > 2.f * eps);
-    const bool tracked = n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps;
-    // ---- fp64 re-scoring, one ambiguous query at a time, by the whole wave
-    // (c, m and the eligible set are the same for every query of the wave).
-    uint64_t pend = __builtin_amdgcn_ballot_w64(amb && h == 0);
-    const double* kb64 = a.kbar64 + bh * NB * (int64_t)D;
-    constexpr int SL = D / 8;    // 8-coordinate slices per candidate
-    constexpr int G = 64 / SL;   // candidates per pass
-    const int gi = lane / SL, sl = lane % SL;
-    while (pend) {
-      const int L = __builtin_ctzll(pend);
-      pend &= pend - 1;
-      const bool trk = __builtin_amdgcn_readlane((int)tracked, L);
-      // This lane's slice of the ambiguous query's coordinates, in fp64.
-      const T* qL = reinterpret_cast<const T*>(a.q) + (bh * a.seq_len + t0 + L) * D + 8 * sl;
-      double qd[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qd[e] = (double)(float)qL[e];
-      int cj[TT];
-#pragma unroll
-      for (int i = 0; i < TT; ++i) cj[i] = __builtin_amdgcn_readlane(lj[i], L);
-      double es[TT];
-      int ej[TT];
-#pragma unroll
-      for (int i = 0; i < TT; ++i) {
-        es[i] = -__builtin_huge_val();
-        ej[i] = kNoBlock;
+        for (int i = 0; i < TT; ++i)
+          if (ci == i) j = cj[i];
+      } else if (ci < jend && ci != c) {
+        j = ci;
       }
-      // Candidates: the tracked list, or every eligible block when the
-      // rounding band reaches past the list.
-      const int ncand = trk ? TT : jend;
-      for (int base = 0; base < ncand; base += G) {
-        const int ci = base + gi;
-        int j = kNoBlock;
-        if (trk) {
+      double p = 0.0;
+      if (j != kNoBlock) {
+        const double* kr = kb64 + (int64_t)j * D + 8 * sl;
 #pragma unroll
-          for (int i = 0; i < TT; ++i)
-            if (ci == i) j = cj[i];
-        } else if (ci < jend && ci != c) {
-          j = ci;
-        }
-        double p = 0.0;
-        if (j != kNoBlock) {
-          const double* kr = kb64 + (int64_t)j * D + 8 * sl;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p = __builtin_fma(qd[e], kr[e], p);
-        }
-        // Sum the SL slices of each candidate (fixed order: deterministic).
-#pragma unroll
-        for (int w = SL / 2; w > 0; w >>= 1) p += __shfl_xor(p, w);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const int jg = __builtin_amdgcn_readlane(j, g * SL);
-          if (jg == kNoBlock) continue;
-          const int lo_bits = __builtin_amdgcn_readlane((int)(__double_as_longlong(p) & 0xffffffff), g * SL);
-          const int hi_bits = __builtin_amdgcn_readlane((int)(__double_as_longlong(p) >> 32), g * SL);
-          const double pg = __longlong_as_double(((long long)hi_bits << 32) | (unsigned)lo_bits);
-          if (better64(pg, jg, es[TT - 1], ej[TT - 1])) insert_full64(es, ej, pg, jg);
-        }
+        for (int e = 0; e < 8; ++e) p = __builtin_fma(qd[e], kr[e], p);
       }
-      if (col == L) {
 #pragma unroll
-        for (int i = 0; i < TT; ++i) sel[i] = ej[i];
+      for (int w = SL / 2; w > 0; w >>= 1) p += __shfl_xor(p, w);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int jg = __builtin_amdgcn_readlane(j, g * SL);
+        if (jg == kNoBlock) continue;
+        const int lo_bits = __builtin_amdgcn_readlane((int)(__double_as_longlong(p) & 0xffffffff), g * SL);
+        const int hi_bits = __builtin_amdgcn_readlane((int)(__double_as_longlong(p) >> 32), g * SL);
+        const double pg = __longlong_as_double(((long long)hi_bits << 32) | (unsigned)lo_bits);
+        if (better64(pg, jg, es[TT - 1], ej[TT - 1])) insert_full64(es, ej, pg, jg);
       }
+    }
+    if (col == ln) {
+#pragma unroll
+      for (int i = 0; i < TT; ++i) sel[i] = ej[i];
     }
   }
+}
 
-  // ---- write the row: kept past blocks ascending, with the own block
-  if (!wave_on || h != 0) return;
+// Writes one block_idx row: the m kept past blocks and the own block c,
+// ascending, padded with -1. Without scoring, either only c (m = 0) or every
+// block below jstop (all eligible blocks are kept).
+template <int TT>
+__device__ void write_row(int32_t* row, const int (&sel)[TT], bool scoring, int m, int c, int jstop, int top_k) {
+  int col_out = 0;
   if (!scoring) {
-    // Only the own block (m = 0), or every eligible block is kept.
-    int col_out = 0;
     if (m == 0) {
-      idx_row[col_out++] = c;
+      row[col_out++] = c;
     } else {
-      const int jstop = a.causal ? c + 1 : NB;
-      for (int j = 0; j < jstop; ++j) idx_row[col_out++] = j;
+      for (int j = 0; j < jstop; ++j) row[col_out++] = j;
     }
-    for (; col_out < a.top_k; ++col_out) idx_row[col_out] = -1;
+    for (; col_out < top_k; ++col_out) row[col_out] = -1;
     return;
   }
   int srt[TT];
@@ -358,21 +466,152 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT <= 4 ? 3
       srt[k - 1] = min(x, y);
       srt[k] = max(x, y);
     }
-  int col_out = 0;
   bool own_done = false;
 #pragma unroll
   for (int i = 0; i < TT; ++i) {
     if (i < m) {
       const int j = srt[i];
       if (!own_done && c < j) {
-        idx_row[col_out++] = c;
+        row[col_out++] = c;
         own_done = true;
       }
-      idx_row[col_out++] = j;
+      row[col_out++] = j;
     }
   }
-  if (!own_done) idx_row[col_out++] = c;
-  for (; col_out < a.top_k; ++col_out) idx_row[col_out] = -1;
+  if (!own_done) row[col_out++] = c;
+  for (; col_out < top_k; ++col_out) row[col_out] = -1;
+}
+
+}  // namespace
+
+template <typename T, int D, int TT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT>()))) void gate_topk_kernel(
+    GateArgs a) {
+  using Ops = GateOps<T, D>;
+  constexpr int QG = gate_groups<T, D, TT>();
+  constexpr int WQ = 32 * QG;       // queries per wave
+  constexpr int WGQ = 4 * WQ;       // queries per workgroup
+  extern __shared__ __align__(16) char smem[];
+  char* tile = smem;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int64_t wg_per_head = (a.seq_len + WGQ - 1) / WGQ;
+  // Within a head, workgroups run latest queries first: they scan the most
+  // blocks (causal), so the short ones fill the tail of the launch.
+  const int64_t bh = blockIdx.x / wg_per_head;
+  const int64_t qb = (wg_per_head - 1 - blockIdx.x % wg_per_head) * WGQ;
+  // The wave's queries t0 .. t0 + WQ - 1 (group g, lane column col: query
+  // t0 + 32 g + col) lie in one block, as block_size is a multiple of 64 and
+  // seq_len a multiple of block_size.
+  const int64_t t0 = qb + WQ * w;
+  const bool wave_on = t0 < a.seq_len;  // workgroup-uniform control flow below
+  const int64_t tw = wave_on ? t0 : qb;
+  const int NB = (int)a.n_blocks;
+  const int c = (int)(tw / a.block_size);
+  const int n_elig = a.causal ? c : NB - 1;
+  const int m = min(a.k_eff - 1, n_elig);
+  const bool scoring = wave_on && m > 0 && m < n_elig;  // wave-uniform
+
+  // ---- fast scores over the eligible blocks, top-TT per lane half
+  Ops qf[QG];
+  float qnorm[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    qnorm[g] = 0.f;
+    if (scoring) {
+      qf[g].load(reinterpret_cast<const T*>(a.q) + (bh * a.seq_len + tw + 32 * g + col) * D, h);
+      float qss = qf[g].sumsq();
+      qss += shfl_xor32(qss);
+      qnorm[g] = __builtin_sqrtf(qss) * 1.0001f;
+    }
+  }
+  double L[QG][TT];
+  float S[QG][TT];
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      L[g][i] = kKeyNone;
+      S[g][i] = kNegInf;
+    }
+  const int jend = a.causal ? c : NB;  // this wave's scan bound
+  // Scan bound of the whole workgroup (its last valid query has the largest c).
+  const int64_t t_last = min<int64_t>(qb + WGQ, a.seq_len) - 1;
+  const int wg_jend = a.causal ? (int)(t_last / a.block_size) : NB;
+  // Tile pipeline. Tile i sits in LDS buffer i & 1. Step i stores tile i+1
+  // (fetched into registers one step earlier) to the other buffer, passes
+  // the workgroup barrier, fetches tile i+2, issues the MFMAs of tile i+1
+  // and, while they run, folds the scores of tile i (issued one step
+  // earlier) into the key lists. Only the ordering of independent work
+  // changes; every tile is scored and folded exactly once.
+  const int ntiles = (wg_jend + kTileB - 1) / kTileB;  // workgroup-uniform
+  const int my_tiles = scoring ? (jend + kTileB - 1) / kTileB : 0;
+  typename Ops::Chunk stg[Ops::NLD];
+  f32x16 acc_a[QG], acc_b[QG];
+  if (ntiles > 0) {
+    Ops::fetch(stg, a, bh, 0, tid);
+    Ops::put(tile, stg, tid);
+  }
+  __syncthreads();
+  if (ntiles > 1) Ops::fetch(stg, a, bh, kTileB, tid);
+  if (my_tiles > 0) Ops::template scores<QG>(tile, col, h, qf, acc_a);
+  auto step = [&](int i, f32x16(&cur)[QG], f32x16(&nxt)[QG]) {
+    char* next_buf = tile + ((i + 1) & 1) * Ops::TILE_BYTES;
+    if (i + 1 < ntiles) Ops::put(next_buf, stg, tid);
+    __syncthreads();
+    if (i + 2 < ntiles) Ops::fetch(stg, a, bh, (i + 2) * kTileB, tid);
+    const bool do_next = i + 1 < my_tiles, do_cur = i < my_tiles;
+    const int jt = i * kTileB, tis = i % kSegTiles;
+    const int jb = jt + 4 * h;
+    const bool full = jt + kTileB <= jend && (a.causal || c < jt || c >= jt + kTileB);
+    if (do_cur && do_next && full) {  // the steady state: one basic block
+      Ops::template scores<QG>(next_buf, col, h, qf, nxt);
+      absorb<QG, TT, false>(S, cur, tis, jb, jend, c);
+      Ops::template interleave<QG, TT>();
+    } else if (do_cur && full) {
+      absorb<QG, TT, false>(S, cur, tis, jb, jend, c);
+    } else {
+      if (do_next) Ops::template scores<QG>(next_buf, col, h, qf, nxt);
+      if (do_cur) absorb<QG, TT, true>(S, cur, tis, jb, jend, c);
+    }
+    if (do_cur && (tis == kSegTiles - 1 || i + 1 == my_tiles))
+      flush_segment<QG, TT>(S, L, (i - tis) * kTileB, h);
+  };
+  for (int i = 0; i < ntiles; i += 2) {
+    step(i, acc_a, acc_b);
+    if (i + 1 < ntiles) step(i + 1, acc_b, acc_a);
+  }
+  if (!wave_on) return;
+
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const int64_t t = tw + 32 * g + col;
+    int32_t* idx_row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
+    int sel[TT];
+    if (scoring) {
+      // Merge the two lane halves (keys are distinct, so both halves end
+      // with the same list), then decode scores and block indices.
+      double P[TT];
+#pragma unroll
+      for (int i = 0; i < TT; ++i) P[i] = shfl_xor32(L[g][i]);
+#pragma unroll
+      for (int i = 0; i < TT; ++i) insert_key(L[g], P[i]);
+      float ls[TT];
+      int lj[TT];
+#pragma unroll
+      for (int i = 0; i < TT; ++i) {
+        ls[i] = key_score(L[g][i]);
+        lj[i] = key_block(L[g][i]);
+        sel[i] = lj[i];
+      }
+      // ---- exactness check: is the cut between kept and dropped blocks
+      // farther apart than twice the fast scores' rounding bound?
+      const float eps = Ops::gamma() * qnorm[g] * a.norm[bh] + 1e-30f;
+      const bool amb = !(ls[m - 1] - ls[m] > 2.f * eps);
+      const bool tracked = n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps;
+      rescore_ambiguous<T, D, TT>(a, bh, tw + 32 * g, c, jend, amb && h == 0, tracked, lj, sel, lane, col);
+    }
+    if (h == 0) write_row<TT>(idx_row, sel, scoring, m, c, a.causal ? c + 1 : NB, a.top_k);
+  }
 }
 
 // Numbers every (query, kept past block) pair inside that block's query
@@ -431,21 +670,25 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
 }
 
 template <typename T, int D, int TT>
-static void gate_go(const GateArgs& a, hipStream_t s, dim3 grid, int lds) {
+static void gate_go(const GateArgs& a, hipStream_t s) {
+  constexpr int WGQ = 4 * 32 * gate_groups<T, D, TT>();  // queries per workgroup
+  const int64_t wg_per_head = (a.seq_len + WGQ - 1) / WGQ;
+  const dim3 grid((unsigned)(a.bh * wg_per_head));
+  const int lds = 2 * GateOps<T, D>::TILE_BYTES;
   hipLaunchKernelGGL((gate_topk_kernel<T, D, TT>), grid, dim3(256), lds, s, a);
 }
 
 template <typename T, int D>
 static hipError_t gate_launch_t(const GateArgs& a, hipStream_t s) {
-  const int64_t wg_per_head = (a.seq_len + kGateQ - 1) / kGateQ;
-  const dim3 grid((unsigned)(a.bh * wg_per_head));
   const int m = a.k_eff - 1;
-  const int lds = GateOps<T, D>::TILE_BYTES;
   {
+    // The list tracks m + 2 or more blocks so that a rounding band at the
+    // cut usually ends inside it.
     KernelTimer timer(s, "gate_topk");
-    if (m <= 2) gate_go<T, D, 4>(a, s, grid, lds);
-    else if (m <= 6) gate_go<T, D, 8>(a, s, grid, lds);
-    else gate_go<T, D, kMaxSlots + 2>(a, s, grid, lds);
+    if (m <= 2) gate_go<T, D, 4>(a, s);
+    else if (m <= 4) gate_go<T, D, 6>(a, s);
+    else if (m <= 8) gate_go<T, D, 10>(a, s);
+    else gate_go<T, D, kMaxSlots + 2>(a, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.k_eff < 2) return e;
