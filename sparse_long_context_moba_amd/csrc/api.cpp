@@ -68,7 +68,7 @@ struct Plan {
   int rows_per_run;
   // workspace offsets (bytes)
   size_t psum, kbar64, kbar32, kbar_hi, kbar_lo, norm, normmax, count, rank, offset, tile_start, qlist,
-      part_o, part_lse, total;
+      tile_map, part_o, part_lse, total;
 };
 
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -150,6 +150,7 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     P.offset = take((size_t)(P.bh * P.nb + 1) * 4);
     P.tile_start = take((size_t)(P.bh * P.nb + 1) * 4);
     P.qlist = take((size_t)P.pairs * 4);
+    P.tile_map = take((size_t)gather_grid_for(P.max_tiles) * 16);
     P.part_o = take((size_t)(P.bh * P.S * P.slots * P.D) * esz);
     P.part_lse = take((size_t)(P.bh * P.S * P.slots) * 4);
   }
@@ -312,11 +313,12 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
     pk.offset = at<int32_t>(workspace, P.offset);
     pk.tile_start = at<int32_t>(workspace, P.tile_start);
     pk.qlist = at<int32_t>(workspace, P.qlist);
+    pk.grid = gather_grid_for(P.max_tiles);
+    pk.tile_map = at<int32_t>(workspace, P.tile_map);
     MOBA_TRY(launch_pack(pk, s), "pack launch");
-    aa.offset = pk.offset;
-    aa.tile_start = pk.tile_start;
     aa.qlist = pk.qlist;
-    aa.max_tiles = P.max_tiles;
+    aa.tile_map = pk.tile_map;
+    aa.gather_grid = pk.grid;
     MOBA_TRY(launch_gather(aa, s), "gather launch");
   }
   MOBA_TRY(launch_diag_merge(aa, s), "diag launch");

@@ -114,6 +114,7 @@ template <int D>
 struct EngBF16 {
   using T = bf16;
   static constexpr bool kDMA = true;
+  static constexpr int kD = D;
   static constexpr int KC = D / 16, DT = D / 32;
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int ROWB = D * 2;       // bytes per K/V row in LDS
@@ -179,6 +180,168 @@ struct EngBF16 {
   template <int NT>
   static __device__ __forceinline__ void land(Stage<NT>&, char*, int) {
     lds_dma_wait();
+  }
+  // The same loads for K or V alone, into a buffer of TB bytes.
+  template <int NT, bool IS_V>
+  static __device__ __forceinline__ void begin_one(const bf16* p, char* buf, int tid) {
+    constexpr int NW = NT / 64, INSTS = SLOTS / 64;
+    static_assert(INSTS % NW == 0, "subtile slots must split evenly over the waves");
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
+#pragma unroll
+    for (int ii = 0; ii < INSTS / NW; ++ii) {
+      const int i = ii * NW + w;
+      const int sl = i * 64 + lane;
+      const int row = sl / CPR;
+      const int x = (sl % CPR) ^ (IS_V ? swzv(row) : swz(row));
+      lds_dma16(p + row * D + 8 * x, base + i * 1024);
+    }
+  }
+
+  // ---- the step in parts, for the pipelined stream (K one subtile ahead
+  // of V): scores of a K subtile, their row maximum, the lazy rescale, and
+  // the weights and P.V of an earlier subtile.
+  __device__ __forceinline__ void qk(const char* kbuf, int lane, f32x16 (&s)[2]) const {
+    const int h = lane >> 5, col = lane & 31;
+    const int sw = swz(col);
+    const char* r0 = kbuf + col * ROWB;
+    const char* r1 = r0 + 32 * ROWB;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(r0 + 16 * ((2 * kk + h) ^ sw));
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(r1 + 16 * ((2 * kk + h) ^ sw));
+      s[0] = mfma_bf16(a0, qf[kk], s[0]);
+      s[1] = mfma_bf16(a1, qf[kk], s[1]);
+    }
+  }
+  // Scaled (log2-domain) maximum of the query's 64 scores.
+  static __device__ __forceinline__ float rowmax(const f32x16 (&s)[2], float sl2) {
+    float a = kNegInf, b = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      a = fmaxf(a, fmaxf(s[0][r], s[0][r + 1]));
+      b = fmaxf(b, fmaxf(s[1][r], s[1][r + 1]));
+    }
+    return pair_max(fmaxf(a, b)) * sl2;
+  }
+  // Raise the reference to cover mx (see online_softmax).
+  __device__ __forceinline__ void rescale(float mx) {
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m = mn;
+    }
+  }
+  // Weights exp2(s * sl2 - m) of the scores in s, added to l, and O += P V
+  // with V from vbuf (one subtile, TB bytes).
+  __device__ __forceinline__ void expo_pv(const f32x16 (&s)[2], const char* vbuf, int lane, float sl2) {
+    const int h = lane >> 5;
+    const float nm = -m;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(s[nt][r], sl2, nm));
+        rs[r & 3] += e;
+        pb[nt][r >> 3][r & 7] = to_bf16(e);
+      }
+    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    const int j = lane & 15, half = (lane >> 4) & 1;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nt = i >> 1, g = i & 1;
+        const int d = 32 * dt + 16 * half + 4 * (j & 3);
+        const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
+        const char* a0 = vbuf + r0 * ROWB + 16 * ((d >> 3) ^ swzv(r0)) + 2 * (d & 7);
+        const char* a1 = vbuf + r1 * ROWB + 16 * ((d >> 3) ^ swzv(r1)) + 2 * (d & 7);
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = mfma_bf16(vf, pb[nt][g], o[dt]);
+      }
+  }
+  // The steady-state step of the pipelined stream, in issue order (waves
+  // issue in order, so the MFMA chains only hide the softmax arithmetic if
+  // the two are interleaved in the instruction stream): scores of the next
+  // K subtile (kbn -> sn) with the weights of the current scores sc, then
+  // O += P V from vbc with the row maximum of sn. Each chunk ends in a
+  // scheduling fence; fragments are read a few chunks ahead.
+  __device__ __forceinline__ void fused(const char* kbn, f32x16 (&sn)[2], const f32x16 (&sc)[2], const char* vbc,
+                                        int lane, float sl2, float& mxn) {
+    const int h = lane >> 5, col = lane & 31, sw = swz(col);
+    const char* kr0 = kbn + col * ROWB;
+    const char* kr1 = kr0 + 32 * ROWB;
+    // QK MFMA c: key half c % 2, k-chunk c / 2.
+    auto kfrag = [&](int c) {
+      return *reinterpret_cast<const bf16x8*>(((c & 1) ? kr1 : kr0) + 16 * ((2 * (c >> 1) + h) ^ sw));
+    };
+    const int j = lane & 15, half = (lane >> 4) & 1;
+    // P.V MFMA c: d-tile c / 4, keys 16 * (c % 4) .. +15.
+    auto vfrag = [&](int c) {
+      const int dt = c >> 2, nt = (c >> 1) & 1, g = c & 1;
+      const int d = 32 * dt + 16 * half + 4 * (j & 3);
+      const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
+      const char* a0 = vbc + r0 * ROWB + 16 * ((d >> 3) ^ swzv(r0)) + 2 * (d & 7);
+      const char* a1 = vbc + r1 * ROWB + 16 * ((d >> 3) ^ swzv(r1)) + 2 * (d & 7);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NQ = 2 * KC, NP = 4 * DT, KA = 3, VA = 2;
+    static_assert(NQ == 16 || NQ == 8, "32 score pairs over the QK chunks");
+    constexpr int EPC = 32 / NQ;  // weights per QK chunk
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    const float nm = -m;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 pb[2][2];
+    bf16x8 kq[NQ];
+#pragma unroll
+    for (int c = 0; c < KA; ++c) kq[c] = kfrag(c);
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      if (c + KA < NQ) kq[c + KA] = kfrag(c + KA);
+      sn[c & 1] = mfma_bf16(kq[c], qf[c >> 1], sn[c & 1]);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        const int x = EPC * c + u, nt = x >> 4, r = x & 15;
+        const float e = fast_exp2(__builtin_fmaf(sc[nt][r], sl2, nm));
+        rs[r & 3] += e;
+        pb[nt][r >> 3][r & 7] = to_bf16(e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    bf16x8 vq[NP];
+#pragma unroll
+    for (int c = 0; c < VA; ++c) vq[c] = vfrag(c);
+    float mx0 = kNegInf, mx1 = kNegInf;
+    constexpr int MPC = 32 / NP;  // row-max elements per P.V chunk
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      if (c + VA < NP) vq[c + VA] = vfrag(c + VA);
+      o[c >> 2] = mfma_bf16(vq[c], pb[(c >> 1) & 1][c & 1], o[c >> 2]);
+#pragma unroll
+      for (int u = 0; u < MPC; u += 2) {
+        const int x = MPC * c + u, nt = x >> 4, r = x & 15;
+        if (nt == 0) mx0 = fmaxf(mx0, fmaxf(sn[0][r], sn[0][r + 1]));
+        else mx1 = fmaxf(mx1, fmaxf(sn[1][r], sn[1][r + 1]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mxn = pair_max(fmaxf(mx0, mx1)) * sl2;
   }
 
   template <bool MASK>
@@ -426,6 +589,74 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
   }
 }
 
+// K-ahead stream for direct-load engines, unmasked subtiles only (gather):
+// each buffer holds a K subtile then a V subtile (TB bytes each). Step sub
+// loads K of sub+2 and V of sub+1, computes the scores of sub+1 while the
+// weights and P.V of sub run, and ends at the barrier that publishes the
+// loads. Buffer use: K(sub) in buf[sub % 2], V(sub) in buf[sub % 2] + TB;
+// K(sub+2) overwrites K(sub), read in the step before (or the prologue,
+// followed by its own barrier), V(sub+1) overwrites V(sub-1), read in the
+// step before.
+template <class E, int NT, bool ON, class S>
+__device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB, const typename E::T* kp,
+                                                 const typename E::T* vp, int nsub, int tid, int lane, float sl2,
+                                                 S&& start) {
+  constexpr int64_t SE = (int64_t)kSub * E::kD;
+  E::template begin_one<NT, false>(kp, bufA, tid);
+  E::template begin_one<NT, true>(vp, bufA + E::TB, tid);
+  if (nsub > 1) E::template begin_one<NT, false>(kp + SE, bufB, tid);
+  start();  // e.g. the query rows, under the first K/V loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see stream_subtiles
+  lds_dma_wait();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  float ma = kNegInf, mb = kNegInf;
+  if (ON) {
+    eng.qk(bufA, lane, sa);
+    ma = E::rowmax(sa, sl2);
+  }
+  __syncthreads();
+  // A step with a next subtile (its scores are computed here).
+  auto full = [&](int sub, char* bc, char* bn, f32x16(&sc)[2], f32x16(&sn)[2], float mc, float& mn) {
+    if (sub + 2 < nsub) E::template begin_one<NT, false>(kp + (sub + 2) * SE, bc, tid);
+    E::template begin_one<NT, true>(vp + (sub + 1) * SE, bn + E::TB, tid);
+    if (ON) {
+      eng.rescale(mc);
+      eng.fused(bn, sn, sc, bc + E::TB, lane, sl2, mn);
+    }
+    lds_dma_wait();
+    __syncthreads();
+  };
+  // The final step.
+  auto last = [&](char* bc, f32x16(&sc)[2], float mc) {
+    if (ON) {
+      eng.rescale(mc);
+      eng.expo_pv(sc, bc + E::TB, lane, sl2);
+    }
+  };
+  int sub = 0;
+  for (; sub + 2 < nsub; sub += 2) {
+    full(sub, bufA, bufB, sa, sb, ma, mb);
+    full(sub + 1, bufB, bufA, sb, sa, mb, ma);
+  }
+  if (sub + 1 < nsub) {
+    full(sub, bufA, bufB, sa, sb, ma, mb);
+    last(bufB, sb, mb);
+  } else {
+    last(bufA, sa, ma);
+  }
+}
+
+// K-ahead stream (see stream_k_ahead_t); waves without queries (on false)
+// take part in the loads and barriers only.
+template <class E, int NT, class S>
+__device__ __forceinline__ void stream_k_ahead(E& eng, char* bufA, char* bufB, const typename E::T* kp,
+                                               const typename E::T* vp, int nsub, int tid, int lane, bool on,
+                                               float sl2, S&& start) {
+  if (on) stream_k_ahead_t<E, NT, true>(eng, bufA, bufB, kp, vp, nsub, tid, lane, sl2, start);
+  else stream_k_ahead_t<E, NT, false>(eng, bufA, bufB, kp, vp, nsub, tid, lane, sl2, start);
+}
+
 // LDS for one kernel: two static subtile buffers for direct-load engines,
 // the dynamic allocation (one buffer) otherwise.
 #define MOBA_KERNEL_LDS(E)                                                   \
@@ -450,44 +681,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   MOBA_KERNEL_LDS(E)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
 
-  // Tiles are numbered per (head, block) in order; consecutive tiles share a
-  // block's K/V. Workgroups are dealt round-robin over the 8 XCDs, so give
-  // each XCD one contiguous range of tiles to keep a block's K/V in one L2.
-  const int64_t nblk = a.bh * a.n_blocks;
-  const int total = a.tile_start[nblk];
-  const int chunk = (total + 7) / 8;
-  const int li = blockIdx.x / 8;
-  if (li >= chunk) return;
-  const int L = (int)(blockIdx.x % 8) * chunk + li;
-  if (L >= total) return;
-  int64_t lo = 0, hi = nblk;  // tile_start[lo] <= L < tile_start[hi]
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (a.tile_start[mid] <= L) lo = mid;
-    else hi = mid;
-  }
-  const int64_t blk = lo;
+  // This workgroup's tile: its (head, block) and list range (written by the
+  // packing step, which also spreads tiles over the XCDs).
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 tm = *reinterpret_cast<const i32x4*>(a.tile_map + 4 * (int64_t)blockIdx.x);
+  if (tm.x < 0) return;
+  const int64_t blk = tm.x;
   const int64_t bh = blk / a.n_blocks, j = blk % a.n_blocks;
-  const int64_t e0 = a.offset[blk] + (int64_t)(L - a.tile_start[blk]) * M;
-  const int64_t e1 = min<int64_t>(a.offset[blk + 1], e0 + M);
+  const int64_t e0 = tm.y, e1 = tm.z;
   const int64_t e = e0 + 32 * w + col;
   const bool valid = e < e1;
   const bool wave_on = e0 + 32 * w < e1;
   const int slots = a.k_eff - 1;
-  const int ev = a.qlist[valid ? e : e0];
-  const int t = ev / slots;
+  int ev = 0, t = 0;
 
   E eng;
   eng.init();
   const T* q = reinterpret_cast<const T*>(a.q);
-  if (wave_on) eng.load_q(q + (bh * a.seq_len + t) * D, h);
+  // Query rows: read after the first K/V loads are queued.
+  auto load_q = [&]() {
+    ev = a.qlist[valid ? e : e0];
+    t = ev / slots;
+    if (wave_on) eng.load_q(q + (bh * a.seq_len + t) * D, h);
+  };
   const T* kp = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + j * a.block_size) * D;
   const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + j * a.block_size) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
   const int nsub = (int)(a.block_size / kSub);
-  stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, [&](const char* buf, int) {
-    if (wave_on) eng.template step<false>(buf, lane, 0, 0, sl2);
-  });
+  if constexpr (E::kDMA) {
+    stream_k_ahead<E, NT>(eng, bufA, bufB, kp, vp, nsub, tid, lane, wave_on, sl2, load_q);
+  } else {
+    load_q();
+    stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, [&](const char* buf, int) {
+      if (wave_on) eng.template step<false>(buf, lane, 0, 0, sl2);
+    });
+  }
   if (!wave_on) return;
   const float lt = pair_sum(eng.l);
   if (valid) {
@@ -606,7 +834,7 @@ hipError_t gather_t(const AttnArgs& a, hipStream_t s) {
   constexpr int lds = dyn_lds_bytes<E>();
   hipError_t e = prep_lds(kern, lds);
   if (e != hipSuccess) return e;
-  const int64_t grid = (a.max_tiles + 7) / 8 * 8;
+  const int64_t grid = a.gather_grid;
   KernelTimer timer(s, "gather_attn");
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), lds, s, a);
   return hipGetLastError();

@@ -66,6 +66,8 @@ struct PackArgs {
   int32_t* offset;            // [bh * nb + 1] exclusive scan of count
   int32_t* tile_start;        // [bh * nb + 1] exclusive scan of ceil(count / tile_m)
   int32_t* qlist;             // [pairs]: t * (k_eff - 1) + slot
+  int64_t grid;               // gather workgroups (a multiple of 8)
+  int32_t* tile_map;          // [grid][4]: per gather workgroup {block, e0, e1, 0}, block -1 if idle
 };
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_zero(void* p, int64_t n_words, hipStream_t s);
@@ -81,14 +83,16 @@ struct AttnArgs {
   bool causal;
   int k_eff;
   // gather (past blocks)
-  const int32_t* offset;
-  const int32_t* tile_start;
   const int32_t* qlist;
-  int64_t max_tiles;          // grid bound for the gather launch
+  const int32_t* tile_map;    // see PackArgs
+  int64_t gather_grid;        // gather workgroups
   void* part_o;               // [bh, S, k_eff - 1, D] in the input dtype, lane-native order
   float* part_lse;            // [bh, S, k_eff - 1], log2 domain
 };
 constexpr int kGatherTileM = 128;
+// Gather workgroups for a bound on the number of tiles (a multiple of the
+// 8 XCDs, see tile_map_kernel).
+constexpr int64_t gather_grid_for(int64_t max_tiles) { return (max_tiles + 7) / 8 * 8; }
 hipError_t launch_gather(const AttnArgs& a, hipStream_t s);
 hipError_t launch_diag_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_dense(const AttnArgs& a, hipStream_t s);

@@ -8,6 +8,8 @@
 //  pack_scan    — one workgroup: exclusive scans of the per-block query
 //                 counts (list offsets) and of ceil(count / tile_m) (gather
 //                 tile starts) over all heads and blocks.
+//  tile_map     — one thread per gather workgroup: its tile, block and
+//                 list range (see tile_map_kernel).
 //  pack_scatter — one thread per query: places each of its kept past blocks
 //                 into that block's list at offset + rank, where rank came
 //                 from the gate's atomic count. Entries are t*(k_eff-1)+slot.
@@ -56,6 +58,38 @@ __global__ __launch_bounds__(1024) void pack_scan_kernel(const int32_t* __restri
   }
 }
 
+// One thread per gather workgroup w: the tile it runs and that tile's
+// block and list range, so the gather kernel starts with one load. Tiles
+// are dealt to workgroups so that each of the 8 XCDs (workgroups go round
+// robin over them) gets one contiguous range of tiles, which keeps a
+// block's K/V in one L2: tile L = (w % 8) * chunk + w / 8.
+__global__ __launch_bounds__(256) void tile_map_kernel(PackArgs a) {
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= a.grid) return;
+  const int64_t nblk = a.bh * a.n_blocks;
+  const int64_t total = a.tile_start[nblk];
+  const int64_t chunk = (total + 7) / 8;
+  const int64_t li = w / 8, L = (w % 8) * chunk + li;
+  int32_t* out = a.tile_map + 4 * w;
+  if (li >= chunk || L >= total) {
+    out[0] = -1;
+    out[1] = out[2] = out[3] = 0;
+    return;
+  }
+  int64_t lo = 0, hi = nblk;  // the last block with tile_start <= L
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a.tile_start[mid] <= L) lo = mid;
+    else hi = mid;
+  }
+  const int32_t e0 = a.offset[lo] + (int32_t)(L - a.tile_start[lo]) * a.tile_m;
+  const int32_t e1 = min(a.offset[lo + 1], e0 + a.tile_m);
+  out[0] = (int32_t)lo;
+  out[1] = e0;
+  out[2] = e1;
+  out[3] = 0;
+}
+
 __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= a.bh * a.seq_len) return;
@@ -97,6 +131,12 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
                        a.tile_start);
   }
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    KernelTimer t(s, "tile_map");
+    hipLaunchKernelGGL(tile_map_kernel, dim3((unsigned)((a.grid + 255) / 256)), dim3(256), 0, s, a);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nq = a.bh * a.seq_len;
   {
