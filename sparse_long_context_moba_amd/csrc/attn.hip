@@ -105,7 +105,19 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
 }
+// The same with a wave-uniform base address (SGPR pair) and a 32-bit
+// per-lane byte offset, so no per-load 64-bit address arithmetic.
+__device__ __forceinline__ void lds_dma16_s(const void* base, unsigned off, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_base) : "memory");
+}
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (loads complete in issue order for this count), leaving the N most
+// recent ones in flight.
+template <int N>
+__device__ __forceinline__ void lds_dma_wait_keep() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ unsigned lds_addr(const char* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -180,6 +192,36 @@ struct EngBF16 {
   template <int NT>
   static __device__ __forceinline__ void land(Stage<NT>&, char*, int) {
     lds_dma_wait();
+  }
+  // Direct loads one wave issues for one K (or V) subtile.
+  template <int NT>
+  static constexpr int kLoadsPerWave = SLOTS / 64 / (NT / 64);
+  // Per-lane source offsets (bytes from the subtile's first row) of this
+  // wave's loads of one K (v = false) or V (v = true) subtile.
+  template <int NT>
+  struct LoadOffsets {
+    unsigned k[kLoadsPerWave<NT>], v[kLoadsPerWave<NT>];
+  };
+  template <int NT>
+  static __device__ __forceinline__ void load_offsets(LoadOffsets<NT>& lo, int tid) {
+    constexpr int NW = NT / 64;
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int ii = 0; ii < kLoadsPerWave<NT>; ++ii) {
+      const int sl = (ii * NW + w) * 64 + lane, row = sl / CPR;
+      lo.k[ii] = (unsigned)(row * D + 8 * ((sl % CPR) ^ swz(row))) * 2u;
+      lo.v[ii] = (unsigned)(row * D + 8 * ((sl % CPR) ^ swzv(row))) * 2u;
+    }
+  }
+  // The loads of one subtile from a wave-uniform base p.
+  template <int NT, bool IS_V>
+  static __device__ __forceinline__ void begin_uniform(const bf16* p, const LoadOffsets<NT>& lo, char* buf, int tid) {
+    constexpr int NW = NT / 64;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
+#pragma unroll
+    for (int ii = 0; ii < kLoadsPerWave<NT>; ++ii)
+      lds_dma16_s(p, IS_V ? lo.v[ii] : lo.k[ii], base + (ii * NW + w) * 1024);
   }
   // The same loads for K or V alone, into a buffer of TB bytes.
   template <int NT, bool IS_V>
@@ -602,9 +644,11 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
                                                  const typename E::T* vp, int nsub, int tid, int lane, float sl2,
                                                  S&& start) {
   constexpr int64_t SE = (int64_t)kSub * E::kD;
-  E::template begin_one<NT, false>(kp, bufA, tid);
-  E::template begin_one<NT, true>(vp, bufA + E::TB, tid);
-  if (nsub > 1) E::template begin_one<NT, false>(kp + SE, bufB, tid);
+  typename E::template LoadOffsets<NT> lo;
+  E::template load_offsets<NT>(lo, tid);
+  E::template begin_uniform<NT, false>(kp, lo, bufA, tid);
+  E::template begin_uniform<NT, true>(vp, lo, bufA + E::TB, tid);
+  if (nsub > 1) E::template begin_uniform<NT, false>(kp + SE, lo, bufB, tid);
   start();  // e.g. the query rows, under the first K/V loads
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see stream_subtiles
   lds_dma_wait();
@@ -617,14 +661,19 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
   }
   __syncthreads();
   // A step with a next subtile (its scores are computed here).
+  // V(sub+1) is queued before K(sub+2), and the step ends waiting for all
+  // but K(sub+2)'s loads: the next step needs K(sub+1) and V(sub+1), while
+  // K(sub+2) keeps loading through it (it is first read two steps later).
   auto full = [&](int sub, char* bc, char* bn, f32x16(&sc)[2], f32x16(&sn)[2], float mc, float& mn) {
-    if (sub + 2 < nsub) E::template begin_one<NT, false>(kp + (sub + 2) * SE, bc, tid);
-    E::template begin_one<NT, true>(vp + (sub + 1) * SE, bn + E::TB, tid);
+    const bool k2 = sub + 2 < nsub;
+    E::template begin_uniform<NT, true>(vp + (sub + 1) * SE, lo, bn + E::TB, tid);
+    if (k2) E::template begin_uniform<NT, false>(kp + (sub + 2) * SE, lo, bc, tid);
     if (ON) {
       eng.rescale(mc);
       eng.fused(bn, sn, sc, bc + E::TB, lane, sl2, mn);
     }
-    lds_dma_wait();
+    if (k2) lds_dma_wait_keep<E::template kLoadsPerWave<NT>>();
+    else lds_dma_wait();
     __syncthreads();
   };
   // The final step.
@@ -686,9 +735,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const i32x4 tm = *reinterpret_cast<const i32x4*>(a.tile_map + 4 * (int64_t)blockIdx.x);
   if (tm.x < 0) return;
-  const int64_t blk = tm.x;
+  const int64_t blk = __builtin_amdgcn_readfirstlane(tm.x);  // uniform: keeps the K/V bases in SGPRs
   const int64_t bh = blk / a.n_blocks, j = blk % a.n_blocks;
-  const int64_t e0 = tm.y, e1 = tm.z;
+  const int64_t e0 = __builtin_amdgcn_readfirstlane(tm.y), e1 = __builtin_amdgcn_readfirstlane(tm.z);
   const int64_t e = e0 + 32 * w + col;
   const bool valid = e < e1;
   const bool wave_on = e0 + 32 * w < e1;
