@@ -595,6 +595,34 @@ template <class E, int NT, class F>
 __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const typename E::T* kp,
                                                 const typename E::T* vp, int nsub, int D, int tid, F&& compute) {
   typename E::template Stage<NT> st;
+  if constexpr (E::kDMA) {
+    // Direct loads from wave-uniform bases with per-lane offsets computed
+    // once (no per-load address arithmetic).
+    typename E::template LoadOffsets<NT> lo;
+    E::template load_offsets<NT>(lo, tid);
+    auto issue = [&](int sub, char* buf) {
+      E::template begin_uniform<NT, false>(kp + sub * (int64_t)kSub * D, lo, buf, tid);
+      E::template begin_uniform<NT, true>(vp + sub * (int64_t)kSub * D, lo, buf + E::TB, tid);
+    };
+    issue(0, bufA);
+    lds_dma_wait();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query fragments too (see below)
+    __syncthreads();
+    for (int sub = 0; sub < nsub; sub += 2) {
+      const bool m1 = sub + 1 < nsub;
+      if (m1) issue(sub + 1, bufB);
+      compute(bufA, sub);
+      if (m1) lds_dma_wait();
+      __syncthreads();
+      if (!m1) break;
+      const bool m2 = sub + 2 < nsub;
+      if (m2) issue(sub + 2, bufA);
+      compute(bufB, sub + 1);
+      if (m2) lds_dma_wait();
+      __syncthreads();
+    }
+    return;
+  }
   E::template begin<NT>(st, kp, vp, bufA, tid);
   E::template land<NT>(st, bufA, tid);
   // Also tell the compiler that every vector-memory load issued so far (the
