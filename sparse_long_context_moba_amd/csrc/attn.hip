@@ -11,9 +11,10 @@
 //                 writes, per (query, slot), the normalised partial output
 //                 and its log2-sum-exp.
 //  diag_merge   — the own block. A workgroup takes 32*NW consecutive queries
-//                 of one block, attends the block's keys up to each query
-//                 (causal), then merges the query's past partials with the
-//                 log-sum-exp rule and writes o in the input dtype.
+//                 of one block, starts each query's online softmax from its
+//                 past partials (the log-sum-exp merge, done first), attends
+//                 the block's keys up to the query (causal) and writes o in
+//                 the input dtype.
 //  dense_attn   — plain full attention (causal or not) with the same engine,
 //                 the baseline MoBA is measured against.
 //
@@ -827,6 +828,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   eng.init();
   const T* q = reinterpret_cast<const T*>(a.q);
   eng.load_q(q + (bh * a.seq_len + t) * D, h);
+  if (!DENSE) {
+    // Start the online softmax from the past-block partials: with
+    // m = max lse_i and w_i = 2^(lse_i - m), the state (m, sum w_i,
+    // sum w_i o_i) is the partials' union, and the own block's keys then
+    // continue it, so the merge needs no pass after the loop (and its loads
+    // overlap the first K/V loads). l is kept on one lane of the pair,
+    // which sums it at the end.
+    const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
+    const int n = min(a.k_eff - 1, n_elig);
+    const int slots = a.k_eff - 1;
+    const int64_t rec0 = (bh * a.seq_len + t) * (int64_t)slots;
+    float mx = kNegInf;
+    for (int s = 0; s < n; ++s) mx = fmaxf(mx, a.part_lse[rec0 + s]);
+    if (n > 0) {
+      const T* po = reinterpret_cast<const T*>(a.part_o);
+      float wsum = 0.f;
+      for (int s = 0; s < n; ++s) {
+        const float ws = fast_exp2(a.part_lse[rec0 + s] - mx);
+        wsum += ws;
+        const T* src = po + (rec0 + s) * D + h * (D / 2);
+#pragma unroll
+        for (int dt = 0; dt < E::DT; ++dt) {
+          float x[16];
+          E::get16(src + 16 * dt, x);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) eng.o[dt][r] = __builtin_fmaf(ws, x[r], eng.o[dt][r]);
+        }
+      }
+      eng.m = mx;
+      eng.l = h == 0 ? wsum : 0.f;
+    }
+  }
   const T* kp = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + kb) * D;
   const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + kb) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
@@ -844,48 +877,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   });
 
-  const float lt = pair_sum(eng.l);
-  if (DENSE) {
-    const float inv = 1.f / lt;
+  // Dense, or own block continuing the partials' state: normalise once.
+  const float inv = 1.f / pair_sum(eng.l);
 #pragma unroll
-    for (int dt = 0; dt < E::DT; ++dt)
+  for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) eng.o[dt][r] *= inv;
-  } else {
-    // Merge with the past-block partials: one softmax over all chosen keys.
-    const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
-    const int n = min(a.k_eff - 1, n_elig);
-    const int slots = a.k_eff - 1;
-    const int64_t rec0 = (bh * a.seq_len + t) * (int64_t)slots;
-    const float lse_d = eng.m + fast_log2(lt);
-    float mx = lse_d;
-    for (int s = 0; s < n; ++s) mx = fmaxf(mx, a.part_lse[rec0 + s]);
-    const float wd = fast_exp2(lse_d - mx);
-    float wsum = wd;
-    const float sd = wd / lt;
-#pragma unroll
-    for (int dt = 0; dt < E::DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) eng.o[dt][r] *= sd;
-    const T* po = reinterpret_cast<const T*>(a.part_o);
-    for (int s = 0; s < n; ++s) {
-      const float ws = fast_exp2(a.part_lse[rec0 + s] - mx);
-      wsum += ws;
-      const T* src = po + (rec0 + s) * D + h * (D / 2);
-#pragma unroll
-      for (int dt = 0; dt < E::DT; ++dt) {
-        float x[16];
-        E::get16(src + 16 * dt, x);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) eng.o[dt][r] = __builtin_fmaf(ws, x[r], eng.o[dt][r]);
-      }
-    }
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int dt = 0; dt < E::DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) eng.o[dt][r] *= inv;
-  }
+    for (int r = 0; r < 16; ++r) eng.o[dt][r] *= inv;
   T* orow = reinterpret_cast<T*>(a.o) + (bh * a.seq_len + t) * D;
 #pragma unroll
   for (int dt = 0; dt < E::DT; ++dt)
