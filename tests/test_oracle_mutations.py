@@ -1,0 +1,180 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one bug in the oracle on the CPU (one function of
+oracle.moba is swapped for a wrong copy for the duration of the case) and
+runs the pin tests of test_oracle_pins.py against it; at least one of them
+must fail. The oracle itself is never modified on disk, and every swap is
+undone before the next case. A case that no pin detects means a pin is
+missing."""
+import contextlib
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moba
+from tests import test_oracle_pins as pins
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _pins():
+    """(name, callable) for every pin that exercises the method's steps."""
+    yield "hand_case", lambda: pins.test_hand_case(GOLDEN)
+    yield "pool_closed_forms", pins.test_pool_closed_forms
+    for seed in range(6):
+        for causal in (True, False):
+            yield f"subset_bruteforce[{seed},{causal}]", (
+                lambda s=seed, c=causal: pins.test_selection_matches_subset_bruteforce(s, c))
+    for seed in range(4):
+        yield f"pages_sort_rule[{seed}]", lambda s=seed: pins.test_selection_matches_pages_sort_rule(s)
+    yield "exact_tie", pins.test_exact_tie_prefers_lower_block_and_is_flagged
+    for causal in (True, False):
+        yield f"masked_dense[{causal}]", lambda c=causal: pins.test_output_matches_masked_dense_softmax(c)
+        for top_k in (8, 9, 100):
+            yield f"topk_ge_nb[{causal},{top_k}]", (
+                lambda c=causal, k=top_k: pins.test_topk_at_least_blocks_is_full_attention(c, k))
+    yield "topk1_local", pins.test_topk1_is_block_local_causal
+    yield "single_block_dense", pins.test_single_block_is_dense_causal
+    yield "block_of_one_token", pins.test_block_of_one_token_routes_to_best_past_tokens
+    yield "constant_values", pins.test_constant_values_give_constant_output_and_convex_hull
+    yield "no_future_leakage", pins.test_no_future_leakage
+    yield "permute_past_block", pins.test_permuting_a_past_block_changes_nothing_later
+
+
+@contextlib.contextmanager
+def planted(name, fn):
+    old = getattr(moba, name)
+    setattr(moba, name, fn)
+    try:
+        yield
+    finally:
+        setattr(moba, name, old)
+
+
+def _failing_pins():
+    failed = []
+    for name, pin in _pins():
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(name)
+    return failed
+
+
+# ---------------------------------------------------------------- the bugs
+_orig_pool = moba.pool_keys
+_orig_elig = moba.eligible_blocks
+_orig_select = moba.select_blocks
+_orig_keys = moba.attended_keys
+_orig_attend = moba.attend
+
+
+def pool_wrong_denominator(k, block_size):
+    # mean over Bs - 1 (an off-by-one denominator)
+    return _orig_pool(k, block_size) * block_size / max(block_size - 1, 1)
+
+
+def pool_first_key_only(k, block_size):
+    k = np.asarray(k, dtype=np.float64)
+    return k[::block_size].copy()
+
+
+def eligible_includes_own(c, n_blocks, causal):
+    # the own block is scored as well as forced
+    if causal:
+        return np.arange(c + 1, dtype=np.int64)
+    return np.arange(n_blocks, dtype=np.int64)
+
+
+def eligible_includes_next(c, n_blocks, causal):
+    # the block after the own block leaks in (future routing)
+    e = list(_orig_elig(c, n_blocks, causal))
+    if causal and c + 1 < n_blocks:
+        e.append(c + 1)
+    return np.array(e, dtype=np.int64)
+
+
+def select_ties_to_higher_index(q_t, kbar, c, top_k, causal):
+    nb = kbar.shape[0]
+    k_eff = min(top_k, nb)
+    elig = moba.eligible_blocks(c, nb, causal)
+    scores = kbar[elig] @ np.asarray(q_t, dtype=np.float64)
+    m = min(k_eff - 1, len(elig))
+    order = np.lexsort((-elig, -scores))  # higher index first among equal scores
+    chosen = elig[order[:m]]
+    flag, a, b = False, math.nan, math.nan
+    if len(elig) > k_eff - 1 >= 1:
+        a, b = float(scores[order[m - 1]]), float(scores[order[m]])
+        flag = abs(a - b) < moba.NEAR_TIE_REL * max(abs(a), abs(b))
+    sel = sorted([int(c)] + [int(j) for j in chosen])
+    idx = np.full(top_k, -1, dtype=np.int64)
+    idx[: len(sel)] = sel
+    return idx, flag, a, b
+
+
+def select_topk_excludes_own(q_t, kbar, c, top_k, causal):
+    # top_k read as "k past blocks plus the own block"
+    idx, flag, a, b = _orig_select(q_t, kbar, c, top_k + 1, causal)
+    return idx[:top_k], flag, a, b
+
+
+def select_lowest_scores(q_t, kbar, c, top_k, causal):
+    # a sign slip: the worst blocks are kept
+    return _orig_select(-np.asarray(q_t, dtype=np.float64), kbar, c, top_k, causal)
+
+
+def keys_no_causal_mask(t, idx_row, block_size, causal):
+    return _orig_keys(t, idx_row, block_size, False)
+
+
+def keys_drop_own_block(t, idx_row, block_size, causal):
+    # the own block's keys are left out (kept only when nothing else is chosen)
+    c = t // block_size
+    past = [int(j) for j in idx_row if j >= 0 and j != c]
+    return _orig_keys(t, np.array(past if past else list(idx_row)), block_size, causal)
+
+
+def attend_no_scale(q_t, k, v, keys):
+    q_t = np.asarray(q_t, dtype=np.float64)
+    return _orig_attend(q_t * math.sqrt(q_t.shape[0]), k, v, keys)
+
+
+def attend_scale_by_d(q_t, k, v, keys):
+    q_t = np.asarray(q_t, dtype=np.float64)
+    return _orig_attend(q_t / math.sqrt(q_t.shape[0]), k, v, keys)
+
+
+def attend_unnormalised(q_t, k, v, keys):
+    q_t = np.asarray(q_t, dtype=np.float64)
+    kk, vv = np.asarray(k[keys], np.float64), np.asarray(v[keys], np.float64)
+    logits = kk @ q_t / math.sqrt(q_t.shape[0])
+    return np.exp(logits - logits.max()) @ vv
+
+
+MUTATIONS = [
+    ("pool_keys", pool_wrong_denominator),
+    ("pool_keys", pool_first_key_only),
+    ("eligible_blocks", eligible_includes_own),
+    ("eligible_blocks", eligible_includes_next),
+    ("select_blocks", select_ties_to_higher_index),
+    ("select_blocks", select_topk_excludes_own),
+    ("select_blocks", select_lowest_scores),
+    ("attended_keys", keys_no_causal_mask),
+    ("attended_keys", keys_drop_own_block),
+    ("attend", attend_no_scale),
+    ("attend", attend_scale_by_d),
+    ("attend", attend_unnormalised),
+]
+
+
+def test_unmodified_oracle_passes_every_pin():
+    assert _failing_pins() == []
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f.__name__ for _, f in MUTATIONS])
+def test_planted_mistake_is_caught(name, fn):
+    with planted(name, fn):
+        failed = _failing_pins()
+    assert failed, f"no pin detects {fn.__name__} in {name}"
