@@ -67,12 +67,12 @@ def work_model(w):
 def kernel_units(w, wm):
     """(bound, algorithmic work per launch, unit) for each library kernel."""
     D, bh, nb = w.head_dim, w.batch * w.heads, w.n_blocks
-    rows_per_run = next((r for r in (256, 192, 128) if w.block_size % r == 0), 64)
     return {
         "gather_attn": ("mfma", wm["past_flops"], "flop"),
         "diag_merge": ("mfma", wm["own_flops"], "flop"),
         "gate_topk": ("mfma", wm["gate_flops"], "flop"),
-        "pool_partial": ("hbm", wm["k_bytes"] + bh * (w.seq_len // rows_per_run) * D * 8, "byte"),
+        # K read once; the pooled keys written as fp64, fp32 and a bf16 pair.
+        "pool": ("hbm", wm["k_bytes"] + bh * nb * D * (8 + 4 + 2 + 2), "byte"),
         "dense_attn": ("mfma", wm["dense_flops"], "flop"),
     }
 
@@ -89,7 +89,7 @@ KERNEL_SOURCES = {
     "gather_attn": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/common.h"],
     "diag_merge": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/common.h"],
     "gate_topk": ["sparse_long_context_moba_amd/csrc/gate.hip", "sparse_long_context_moba_amd/csrc/common.h"],
-    "pool_partial": ["sparse_long_context_moba_amd/csrc/pool.hip", "sparse_long_context_moba_amd/csrc/common.h"],
+    "pool": ["sparse_long_context_moba_amd/csrc/pool.hip", "sparse_long_context_moba_amd/csrc/common.h"],
 }
 
 

@@ -65,9 +65,8 @@ struct Plan {
   bool causal, bf16_in;
   int64_t pairs;       // (query, kept past block) pairs over all heads
   int64_t max_tiles;   // upper bound on gather tiles
-  int rows_per_run;
   // workspace offsets (bytes)
-  size_t psum, kbar64, kbar32, kbar_hi, kbar_lo, norm, normmax, count, rank, offset, tile_start, qlist,
+  size_t kbar64, kbar32, kbar_hi, kbar_lo, norm, normmax, count, rank, offset, tile_start, qlist,
       tile_map, part_o, part_lse, total;
 };
 
@@ -122,13 +121,6 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   P.pairs = per_head * P.bh;
   if (P.pairs >= (int64_t(1) << 31)) return fail(MOBA_ERR_UNSUPPORTED, "too many (query, block) pairs for int32 lists");
   P.max_tiles = P.pairs / kGatherTileM + P.bh * P.nb + 1;
-  P.rows_per_run = 64;
-  for (int r : {256, 192, 128}) {
-    if (P.Bs % r == 0) {
-      P.rows_per_run = r;
-      break;
-    }
-  }
   const size_t esz = P.bf16_in ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -137,7 +129,6 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     return at;
   };
   const size_t nbd = (size_t)(P.bh * P.nb * P.D);
-  P.psum = take((size_t)(P.bh * (P.S / P.rows_per_run) * P.D) * 8);
   P.kbar64 = take(nbd * 8);
   P.kbar32 = take(nbd * 4);
   P.kbar_hi = take(nbd * 2);
@@ -184,8 +175,9 @@ T* at(void* ws, size_t off) {
 // pool + gate: writes block_idx, counts and ranks.
 int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, void* ws, hipStream_t s,
                double* kbar64_out) {
-  MOBA_TRY(launch_zero(at<char>(ws, P.normmax), P.bh, s), "clear normmax");
-  MOBA_TRY(launch_zero(at<char>(ws, P.count), P.bh * P.nb, s), "clear counts");
+  // normmax and count are adjacent workspace pieces: one fill clears both.
+  MOBA_TRY(launch_zero(at<char>(ws, P.normmax), (int64_t)(P.count - P.normmax) / 4 + P.bh * P.nb, s),
+           "clear normmax and counts");
   PoolArgs pa{};
   pa.k = k;
   pa.bh = P.bh;
@@ -193,8 +185,6 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   pa.block_size = P.Bs;
   pa.head_dim = (int)P.D;
   pa.bf16_in = P.bf16_in;
-  pa.rows_per_run = P.rows_per_run;
-  pa.psum = at<double>(ws, P.psum);
   pa.kbar64 = kbar64_out ? kbar64_out : at<double>(ws, P.kbar64);
   pa.kbar32 = at<float>(ws, P.kbar32);
   pa.kbar_hi = at<bf16>(ws, P.kbar_hi);

@@ -755,7 +755,7 @@ constexpr int dyn_lds_bytes() {
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gather_attn_kernel(AttnArgs a) {
   using E = typename EngOf<T, D>::type;
-  constexpr int NT = 64 * NW, M = 32 * NW;
+  constexpr int NT = 64 * NW;
   MOBA_KERNEL_LDS(E)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
 

@@ -25,8 +25,6 @@ struct PoolArgs {
   int64_t bh, seq_len, block_size;
   int head_dim;
   bool bf16_in;
-  int rows_per_run;
-  double* psum;      // [bh * seq_len / rows_per_run, D]
   double* kbar64;    // [bh * nb, D]
   float* kbar32;     // [bh * nb, D]
   bf16* kbar_hi;     // [bh * nb, D]
