@@ -112,13 +112,6 @@ __device__ __forceinline__ void lds_dma16_s(const void* base, unsigned off, unsi
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_base) : "memory");
 }
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Wait until at most N of this wave's vector-memory loads are outstanding
-// (loads complete in issue order for this count), leaving the N most
-// recent ones in flight.
-template <int N>
-__device__ __forceinline__ void lds_dma_wait_keep() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 __device__ __forceinline__ unsigned lds_addr(const char* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -689,10 +682,10 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
     ma = E::rowmax(sa, sl2);
   }
   __syncthreads();
-  // A step with a next subtile (its scores are computed here).
-  // V(sub+1) is queued before K(sub+2), and the step ends waiting for all
-  // but K(sub+2)'s loads: the next step needs K(sub+1) and V(sub+1), while
-  // K(sub+2) keeps loading through it (it is first read two steps later).
+  // A step with a next subtile (its scores are computed here). Both loads
+  // it queues are read by the very next step (K(sub+2) for that step's
+  // scores, V(sub+1) for its P.V), so the step ends waiting for all of this
+  // wave's loads before the barrier that publishes them to the other waves.
   auto full = [&](int sub, char* bc, char* bn, f32x16(&sc)[2], f32x16(&sn)[2], float mc, float& mn) {
     const bool k2 = sub + 2 < nsub;
     E::template begin_uniform<NT, true>(vp + (sub + 1) * SE, lo, bn + E::TB, tid);
@@ -701,8 +694,7 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
       eng.rescale(mc);
       eng.fused(bn, sn, sc, bc + E::TB, lane, sl2, mn);
     }
-    if (k2) lds_dma_wait_keep<E::template kLoadsPerWave<NT>>();
-    else lds_dma_wait();
+    lds_dma_wait();
     __syncthreads();
   };
   // The final step.

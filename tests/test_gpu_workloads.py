@@ -52,6 +52,14 @@ def _run(name, n_rows=4096):
     say(f"[gpu] {name}: inputs ready in {time.time() - t0:.1f}s; running moba.forward")
     o, idx = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal)
     torch.cuda.synchronize()
+    # Run-to-run: every output bit and index must repeat (the path has no
+    # floating-point atomics, so any difference is a race).
+    o2, idx2 = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal)
+    torch.cuda.synchronize()
+    bits = torch.int16 if o.dtype == torch.bfloat16 else torch.int32
+    n_diff = int((o.view(bits) != o2.view(bits)).sum().item())
+    assert n_diff == 0 and torch.equal(idx, idx2), f"{name}: {n_diff} output values differ between two runs"
+    del o2, idx2
     rows = synth.sample_rows(w, n_rows)
     sel = torch.from_numpy(rows).cuda()
     o_rows = o[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
