@@ -585,9 +585,12 @@ struct EngOf<float, D> {
 // distinct objects so the compiler need not order the loads against the
 // reads of the other buffer); register-staged engines prefetch into
 // registers and use one buffer.
-template <class E, int NT, class F>
+// start() runs once the first subtile's loads are queued (work whose own
+// loads should overlap them: the query rows, the merge's partials).
+template <class E, int NT, class S, class F>
 __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const typename E::T* kp,
-                                                const typename E::T* vp, int nsub, int D, int tid, F&& compute) {
+                                                const typename E::T* vp, int nsub, int D, int tid, S&& start,
+                                                F&& compute) {
   typename E::template Stage<NT> st;
   if constexpr (E::kDMA) {
     // Direct loads from wave-uniform bases with per-lane offsets computed
@@ -599,6 +602,7 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
       E::template begin_uniform<NT, true>(vp + sub * (int64_t)kSub * D, lo, buf + E::TB, tid);
     };
     issue(0, bufA);
+    start();
     lds_dma_wait();
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query fragments too (see below)
     __syncthreads();
@@ -618,6 +622,7 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
     return;
   }
   E::template begin<NT>(st, kp, vp, bufA, tid);
+  start();
   E::template land<NT>(st, bufA, tid);
   // Also tell the compiler that every vector-memory load issued so far (the
   // query fragments) has completed, so that it emits no vmcnt waits inside
@@ -781,8 +786,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if constexpr (E::kDMA) {
     stream_k_ahead<E, NT>(eng, bufA, bufB, kp, vp, nsub, tid, lane, wave_on, sl2, load_q);
   } else {
-    load_q();
-    stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, [&](const char* buf, int) {
+    stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, load_q, [&](const char* buf, int) {
       if (wave_on) eng.template step<false>(buf, lane, 0, 0, sl2);
     });
   }
@@ -819,14 +823,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   E eng;
   eng.init();
   const T* q = reinterpret_cast<const T*>(a.q);
-  eng.load_q(q + (bh * a.seq_len + t) * D, h);
-  if (!DENSE) {
+  // Query rows, and for the own block the merge's seed: run once the first
+  // K/V loads are queued, so that their loads overlap.
+  auto start = [&]() {
+    eng.load_q(q + (bh * a.seq_len + t) * D, h);
+    if (DENSE) return;
     // Start the online softmax from the past-block partials: with
     // m = max lse_i and w_i = 2^(lse_i - m), the state (m, sum w_i,
     // sum w_i o_i) is the partials' union, and the own block's keys then
-    // continue it, so the merge needs no pass after the loop (and its loads
-    // overlap the first K/V loads). l is kept on one lane of the pair,
-    // which sums it at the end.
+    // continue it, so the merge needs no pass after the loop. l is kept on
+    // one lane of the pair, which sums it at the end.
     const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
     const int n = min(a.k_eff - 1, n_elig);
     const int slots = a.k_eff - 1;
@@ -851,7 +857,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       eng.m = mx;
       eng.l = h == 0 ? wsum : 0.f;
     }
-  }
+  };
   const T* kp = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + kb) * D;
   const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + kb) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
@@ -859,7 +865,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Subtiles entirely before the workgroup's first query need no mask; with
   // causal attention the last M/64 subtiles hold the diagonal.
   const int nfree = a.causal ? (q0 - kb) / kSub : nsub;
-  stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, [&](const char* buf, int sub) {
+  stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, start, [&](const char* buf, int sub) {
     if (sub < nfree) {
       eng.template step<false>(buf, lane, 0, 0, sl2);
     } else {
