@@ -66,7 +66,7 @@ struct Plan {
   int64_t pairs;       // (query, kept past block) pairs over all heads
   int64_t max_tiles;   // upper bound on gather tiles
   // workspace offsets (bytes)
-  size_t kbar64, kbar32, kbar_hi, kbar_lo, norm, normmax, count, rank, offset, tile_start, qlist,
+  size_t kbar64, kbar32, kbar_hi, kbar_lo, norm, count, rank, offset, tile_start, qlist,
       tile_map, part_o, part_lse, total;
 };
 
@@ -134,7 +134,6 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   P.kbar_hi = take(nbd * 2);
   P.kbar_lo = take(nbd * 2);
   P.norm = take((size_t)(P.bh * P.nb) * 4);
-  P.normmax = take((size_t)P.bh * 4);
   P.count = take((size_t)(P.bh * P.nb) * 4);
   P.rank = take((size_t)(P.bh * P.S * P.slots) * 4);
   if (need_select) {
@@ -175,9 +174,6 @@ T* at(void* ws, size_t off) {
 // pool + gate: writes block_idx, counts and ranks.
 int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, void* ws, hipStream_t s,
                double* kbar64_out) {
-  // normmax and count are adjacent workspace pieces: one fill clears both.
-  MOBA_TRY(launch_zero(at<char>(ws, P.normmax), (int64_t)(P.count - P.normmax) / 4 + P.bh * P.nb, s),
-           "clear normmax and counts");
   PoolArgs pa{};
   pa.k = k;
   pa.bh = P.bh;
@@ -190,7 +186,7 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   pa.kbar_hi = at<bf16>(ws, P.kbar_hi);
   pa.kbar_lo = at<bf16>(ws, P.kbar_lo);
   pa.norm = at<float>(ws, P.norm);
-  pa.normmax = at<unsigned>(ws, P.normmax);
+  pa.count = at<int32_t>(ws, P.count);
   MOBA_TRY(launch_pool(pa, s), "pool launch");
   if (!block_idx) return MOBA_OK;
   GateArgs ga{};
@@ -199,7 +195,7 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   ga.kbar32 = pa.kbar32;
   ga.kbar_hi = pa.kbar_hi;
   ga.kbar_lo = pa.kbar_lo;
-  ga.norm = reinterpret_cast<const float*>(pa.normmax);
+  ga.norm = pa.norm;
   ga.bh = P.bh;
   ga.seq_len = P.S;
   ga.block_size = P.Bs;

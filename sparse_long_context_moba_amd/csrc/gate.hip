@@ -582,6 +582,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
   }
   if (!wave_on) return;
 
+  // Largest norm among the wave's scanned blocks, for the rounding bound
+  // (the loads are independent and few: one per 64 blocks and lane).
+  float kmax = 0.f;
+  if (scoring) {
+    const float* nrm = a.norm + bh * NB;
+    for (int j = lane; j < jend; j += 64) kmax = fmaxf(kmax, nrm[j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off));
+  }
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     const int64_t t = tw + 32 * g + col;
@@ -605,7 +614,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
       }
       // ---- exactness check: is the cut between kept and dropped blocks
       // farther apart than twice the fast scores' rounding bound?
-      const float eps = Ops::gamma() * qnorm[g] * a.norm[bh] + 1e-30f;
+      const float eps = Ops::gamma() * qnorm[g] * kmax + 1e-30f;
       const bool amb = !(ls[m - 1] - ls[m] > 2.f * eps);
       const bool tracked = n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps;
       rescore_ambiguous<T, D, TT>(a, bh, tw + 32 * g, c, jend, amb && h == 0, tracked, lj, sel, lane, col);

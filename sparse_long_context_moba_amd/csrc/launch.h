@@ -29,8 +29,8 @@ struct PoolArgs {
   float* kbar32;     // [bh * nb, D]
   bf16* kbar_hi;     // [bh * nb, D]
   bf16* kbar_lo;     // [bh * nb, D]
-  float* norm;       // [bh * nb]
-  unsigned* normmax; // [bh], float bits of the largest block norm; zeroed before the launch
+  float* norm;       // [bh * nb] L2 norm of each pooled key, rounded up
+  int32_t* count;    // [bh * nb] the gate's per-block query counts: the pool zeroes them
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 
@@ -40,7 +40,7 @@ struct GateArgs {
   const float* kbar32;
   const bf16* kbar_hi;
   const bf16* kbar_lo;
-  const float* norm;  // [bh] largest block-mean L2 norm of the head
+  const float* norm;  // [bh * nb] L2 norm of each pooled key, rounded up
   int64_t bh, seq_len, block_size, n_blocks;
   int head_dim;
   bool bf16_in;
@@ -68,7 +68,6 @@ struct PackArgs {
   int32_t* tile_map;          // [grid][4]: per gather workgroup {block, e0, e1, 0}, block -1 if idle
 };
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
-hipError_t launch_zero(void* p, int64_t n_words, hipStream_t s);
 
 struct AttnArgs {
   const void* q;

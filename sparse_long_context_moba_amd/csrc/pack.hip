@@ -8,11 +8,11 @@
 //  pack_scan    — one workgroup: exclusive scans of the per-block query
 //                 counts (list offsets) and of ceil(count / tile_m) (gather
 //                 tile starts) over all heads and blocks.
-//  tile_map     — one thread per gather workgroup: its tile, block and
-//                 list range (see tile_map_kernel).
 //  pack_scatter — one thread per query: places each of its kept past blocks
 //                 into that block's list at offset + rank, where rank came
 //                 from the gate's atomic count. Entries are t*(k_eff-1)+slot.
+//                 The same launch writes the tile map: one thread per gather
+//                 workgroup, its tile, block and list range (see tile_map).
 #include "common.h"
 #include "launch.h"
 
@@ -58,14 +58,12 @@ __global__ __launch_bounds__(1024) void pack_scan_kernel(const int32_t* __restri
   }
 }
 
-// One thread per gather workgroup w: the tile it runs and that tile's
-// block and list range, so the gather kernel starts with one load. Tiles
-// are dealt to workgroups so that each of the 8 XCDs (workgroups go round
-// robin over them) gets one contiguous range of tiles, which keeps a
-// block's K/V in one L2: tile L = (w % 8) * chunk + w / 8.
-__global__ __launch_bounds__(256) void tile_map_kernel(PackArgs a) {
-  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (w >= a.grid) return;
+// Gather workgroup w's tile and that tile's block and list range, so the
+// gather kernel starts with one load. Tiles are dealt to workgroups so that
+// each of the 8 XCDs (workgroups go round robin over them) gets one
+// contiguous range of tiles, which keeps a block's K/V in one L2:
+// tile L = (w % 8) * chunk + w / 8.
+__device__ void tile_map(const PackArgs& a, int64_t w) {
   const int64_t nblk = a.bh * a.n_blocks;
   const int64_t total = a.tile_start[nblk];
   const int64_t chunk = (total + 7) / 8;
@@ -92,6 +90,7 @@ __global__ __launch_bounds__(256) void tile_map_kernel(PackArgs a) {
 
 __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q < a.grid) tile_map(a, q);
   if (q >= a.bh * a.seq_len) return;
   const int64_t bh = q / a.seq_len, t = q % a.seq_len;
   const int c = (int)(t / a.block_size);
@@ -109,20 +108,6 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
-}
-
-// Clears n 32-bit words with a kernel (not a memset node, so the sequence
-// stays safe to capture in a HIP graph).
-hipError_t launch_zero(void* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-  KernelTimer t(s, "zero_fill");
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   const int64_t n = a.bh * a.n_blocks;
   {
@@ -132,16 +117,11 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  {
-    KernelTimer t(s, "tile_map");
-    hipLaunchKernelGGL(tile_map_kernel, dim3((unsigned)((a.grid + 255) / 256)), dim3(256), 0, s, a);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t nq = a.bh * a.seq_len;
+  const int64_t nt = nq > a.grid ? nq : a.grid;  // threads: queries and tile-map entries
   {
     KernelTimer t(s, "pack_scatter");
-    hipLaunchKernelGGL(pack_scatter_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pack_scatter_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

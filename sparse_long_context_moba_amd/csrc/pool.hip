@@ -9,8 +9,8 @@
 // accumulates in fp64 per thread, reduces across row groups in a fixed
 // order, and writes the pooled key in fp64 (exact re-scoring), fp32, and as
 // a bf16 hi/lo pair (hi = bf16(x), lo = bf16(x - hi)) for the MFMA gate,
-// plus the block's L2 norm (rounded up) and the head's largest block norm,
-// for the gate's rounding bound. K is read exactly once; the fixed
+// plus the block's L2 norm (rounded up) for the gate's rounding bound. It
+// also clears the block's query count, which the gate's ranking fills. K is read exactly once; the fixed
 // reduction order keeps results bit-stable.
 #include "common.h"
 #include "launch.h"
@@ -79,9 +79,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   if (tid == 0) {
     const float nrm = (float)(sqrt(sq[0]) * (1.0 + 1e-6));
     a.norm[blk] = nrm;
-    // Non-negative floats order like their bit patterns: an integer max is
-    // the float max, independent of the order the blocks finish in.
-    atomicMax(a.normmax + blk / (a.seq_len / a.block_size), __float_as_uint(nrm));
+    a.count[blk] = 0;
   }
 }
 
