@@ -293,10 +293,12 @@ struct EngBF16 {
       }
     l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     const int j = lane & 15, half = (lane >> 4) & 1;
+    // Key chunks outer, d-tiles inner: consecutive MFMAs accumulate into
+    // different tiles.
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int dt = 0; dt < DT; ++dt) {
         const int nt = i >> 1, g = i & 1;
         const int d = 32 * dt + 16 * half + 4 * (j & 3);
         const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
@@ -324,9 +326,10 @@ struct EngBF16 {
       return *reinterpret_cast<const bf16x8*>(((c & 1) ? kr1 : kr0) + 16 * ((2 * (c >> 1) + h) ^ sw));
     };
     const int j = lane & 15, half = (lane >> 4) & 1;
-    // P.V MFMA c: d-tile c / 4, keys 16 * (c % 4) .. +15.
+    // P.V MFMA c: d-tile c % DT, keys 16 * (c / DT) .. +15 (consecutive
+    // MFMAs accumulate into different tiles).
     auto vfrag = [&](int c) {
-      const int dt = c >> 2, nt = (c >> 1) & 1, g = c & 1;
+      const int dt = c % DT, nt = (c / DT) >> 1, g = (c / DT) & 1;
       const int d = 32 * dt + 16 * half + 4 * (j & 3);
       const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
       const char* a0 = vbc + r0 * ROWB + 16 * ((d >> 3) ^ swzv(r0)) + 2 * (d & 7);
@@ -368,7 +371,7 @@ struct EngBF16 {
 #pragma unroll
     for (int c = 0; c < NP; ++c) {
       if (c + VA < NP) vq[c + VA] = vfrag(c + VA);
-      o[c >> 2] = mfma_bf16(vq[c], pb[(c >> 1) & 1][c & 1], o[c >> 2]);
+      o[c % DT] = mfma_bf16(vq[c], pb[(c / DT) >> 1][(c / DT) & 1], o[c % DT]);
 #pragma unroll
       for (int u = 0; u < MPC; u += 2) {
         const int x = MPC * c + u, nt = x >> 4, r = x & 15;
@@ -422,9 +425,9 @@ struct EngBF16 {
 #pragma unroll
       for (int r = 0; r < 16; ++r) pb[nt][r >> 3][r & 7] = to_bf16(s[nt][r]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[dt] = mfma_bf16(vfrag(dt, i >> 1, i & 1), pb[i >> 1][i & 1], o[dt]);
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mfma_bf16(vfrag(dt, i >> 1, i & 1), pb[i >> 1][i & 1], o[dt]);
   }
 
   // 16 output values of d-tile dt, lane-native order, to memory.

@@ -524,6 +524,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
       qnorm[g] = __builtin_sqrtf(qss) * 1.0001f;
     }
   }
+  // Largest norm among the wave's scanned blocks, for the rounding bound:
+  // the first 64 norms load now, under the scan; any others after it.
+  const int jend = a.causal ? c : NB;  // this wave's scan bound
+  const float* nrm = a.norm + bh * NB;
+  float kmax = (scoring && lane < jend) ? nrm[lane] : 0.f;
   double L[QG][TT];
   float S[QG][TT];
 #pragma unroll
@@ -533,7 +538,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
       L[g][i] = kKeyNone;
       S[g][i] = kNegInf;
     }
-  const int jend = a.causal ? c : NB;  // this wave's scan bound
   // Scan bound of the whole workgroup (its last valid query has the largest c).
   const int64_t t_last = min<int64_t>(qb + WGQ, a.seq_len) - 1;
   const int wg_jend = a.causal ? (int)(t_last / a.block_size) : NB;
@@ -582,12 +586,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
   }
   if (!wave_on) return;
 
-  // Largest norm among the wave's scanned blocks, for the rounding bound
-  // (the loads are independent and few: one per 64 blocks and lane).
-  float kmax = 0.f;
   if (scoring) {
-    const float* nrm = a.norm + bh * NB;
-    for (int j = lane; j < jend; j += 64) kmax = fmaxf(kmax, nrm[j]);
+    for (int j = lane + 64; j < jend; j += 64) kmax = fmaxf(kmax, nrm[j]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off));
   }
