@@ -137,6 +137,7 @@ def cpu_baseline(w, n_rows):
         "unit": "tokens/s",
         "cores": out["workers"],
         "kind": "oracle",
+        "near_ties": int(out["flag"].sum()),
         "sample": (f"{len(rows)} seeded query rows over {heads} heads of {w.name} (fp64 NumPy, "
                    f"{out['workers']} processes, 1 BLAS thread each); measured {out['oracle_s']:.1f} CPU-s "
                    f"(pool {out['pool_s']:.1f} s + rows); value extrapolated to a full forward "
@@ -221,6 +222,10 @@ def main():
     roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": rpeak, "unit": runit,
                 "frac": round(achieved / rpeak, 4), "traffic": measured_traffic(dom, w.name),
                 "work_per_launch": work, "work_unit": unit, "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
+    pool_hbm = None
+    if "pool" in kern and "pool" in units:
+        gbs = units["pool"][1] / (kern["pool"]["avg_ms"] * 1e-3) / 1e9
+        pool_hbm = {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     attn_gate_ms = sum(kern[n]["avg_ms"] for n in ("gate_topk", "gather_attn", "diag_merge") if n in kern)
     attn_gate_frac = (wm["gate_flops"] + wm["past_flops"] + wm["own_flops"]) / (attn_gate_ms * 1e-3) / 1e12 / peak
 
@@ -268,6 +273,7 @@ def main():
         "sparsity": {"realized": round(1 - wm["attended_keys"] / wm["dense_keys"], 4),
                      "theoretical_1_minus_k_over_nb": round(1 - w.top_k / w.n_blocks, 4)},
         "kernels_ms": {n: round(v["avg_ms"], 4) for n, v in kern.items()},
+        "pool_hbm": pool_hbm,
         "dense_causal": dense,
         "roofline": roofline,
         "cpu_baseline": cpu,
