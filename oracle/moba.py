@@ -17,7 +17,9 @@ MoBA is an approximation of attention: a block-routing heuristic followed by
 exact attention over the routed keys. The oracle therefore follows the
 method's steps in order, in float64, one query row at a time:
   1. cut the sequence into blocks of block_size tokens ([R] §3.1, [P] §4.1);
-  2. mean-pool K over each block ([P] §3.1 gating.score_fn, [S] §3);
+  2. mean-pool K over each block ([P] §3.1 gating.score_fn, [S] §3; the
+     serving article's §3 also names max pooling and the two combined as
+     engineering options, see pool_keys);
   3. score every eligible block by the inner product of the query with the
      pooled key; blocks after the query's own block are never eligible
      ([P] §3.1 causal / mask_future, [S] §3, [R] §3.2);
@@ -74,15 +76,34 @@ def theoretical_sparsity(top_k: int, n_blocks: int) -> float:
     return 1.0 - top_k / n_blocks
 
 
-def pool_keys(k: np.ndarray, block_size: int) -> np.ndarray:
-    """Mean of K over each block along the sequence ([P] §3.1 mean_pool).
+POOLINGS = ("mean", "max", "mean+max")
+
+
+def pool_keys(k: np.ndarray, block_size: int, pooling: str = "mean") -> np.ndarray:
+    """The block summary the gate scores against, per coordinate:
+
+    - "mean": the mean of K over each block along the sequence, the paper's
+      choice ([P] §3.1 mean_pool; [S] §3);
+    - "max": the largest value of each coordinate over the block's tokens,
+      which [S] §3 names as an engineering alternative that reacts to blocks
+      dense in key information;
+    - "mean+max": the two combined ([S] §3 names the combination without a
+      formula); read here as their sum, so a block's score is its mean
+      score plus its max score.
 
     k: [S, D] -> [NB, D] float64.
     """
+    if pooling not in POOLINGS:
+        raise ValueError(f"pooling must be one of {POOLINGS}, got {pooling!r}")
     k = np.asarray(k, dtype=np.float64)
     S, D = k.shape
     nb = num_blocks(S, block_size)
-    return k.reshape(nb, block_size, D).sum(axis=1) / block_size
+    blocks = k.reshape(nb, block_size, D)
+    mean = blocks.sum(axis=1) / block_size
+    if pooling == "mean":
+        return mean
+    mx = blocks.max(axis=1)
+    return mx if pooling == "max" else mean + mx
 
 
 def eligible_blocks(c: int, n_blocks: int, causal: bool) -> np.ndarray:
@@ -153,10 +174,11 @@ def attend(q_t: np.ndarray, k: np.ndarray, v: np.ndarray, keys: np.ndarray) -> n
     return (w @ vv) / w.sum()
 
 
-def forward_head(q, k, v, block_size: int, top_k: int, causal: bool = True, rows=None):
+def forward_head(q, k, v, block_size: int, top_k: int, causal: bool = True, rows=None, pooling: str = "mean"):
     """MoBA forward for one (batch, head).
 
     q, k, v: [S, D]. rows: query positions to evaluate (default: all).
+    pooling: the block summary (see pool_keys).
     Returns dict with o [R, D] float64, idx [R, top_k] int64, flag [R] bool,
     a [R], b [R], and kbar [NB, D].
     """
@@ -165,7 +187,7 @@ def forward_head(q, k, v, block_size: int, top_k: int, causal: bool = True, rows
     nb = num_blocks(S, block_size)
     if top_k < 1:
         raise ValueError(f"top_k must be >= 1, got {top_k}")
-    kbar = pool_keys(k, block_size)
+    kbar = pool_keys(k, block_size, pooling)
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.zeros((len(rows), D), np.float64)
     idx = np.zeros((len(rows), top_k), np.int64)
@@ -180,14 +202,14 @@ def forward_head(q, k, v, block_size: int, top_k: int, causal: bool = True, rows
     return {"o": o, "idx": idx, "flag": flag, "a": a, "b": b, "kbar": kbar}
 
 
-def forward(q, k, v, block_size: int, top_k: int, causal: bool = True):
+def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, pooling: str = "mean"):
     """Full MoBA forward over [B, H, S, D]. Returns (o float64, idx int64)."""
     B, H, S, D = q.shape
     o = np.zeros((B, H, S, D), np.float64)
     idx = np.zeros((B, H, S, top_k), np.int64)
     for bb in range(B):
         for hh in range(H):
-            res = forward_head(q[bb, hh], k[bb, hh], v[bb, hh], block_size, top_k, causal)
+            res = forward_head(q[bb, hh], k[bb, hh], v[bb, hh], block_size, top_k, causal, pooling=pooling)
             o[bb, hh], idx[bb, hh] = res["o"], res["idx"]
     return o, idx
 

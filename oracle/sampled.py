@@ -22,9 +22,9 @@ def _head_rows(args):
     t0 = time.perf_counter()
     q, k, v = synth.make_head(w.seed, b, h, w.seq_len, w.head_dim, w.block_size, w.dtype)
     t1 = time.perf_counter()
-    moba.pool_keys(k, w.block_size)
+    moba.pool_keys(k, w.block_size, w.pooling)
     t2 = time.perf_counter()
-    res = moba.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=ts)
+    res = moba.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=ts, pooling=w.pooling)
     t3 = time.perf_counter()
     return b, h, ts, res, t1 - t0, t2 - t1, t3 - t2
 

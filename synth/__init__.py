@@ -41,6 +41,7 @@ class Workload:
     causal: bool
     dtype: str  # "f32" or "bf16"
     seed: int
+    pooling: str = "mean"  # block summary the gate scores: "mean", "max" or "mean+max"
 
     @property
     def n_blocks(self) -> int:
@@ -57,6 +58,12 @@ WORKLOADS = {
     "long_1m": Workload("long_1m", 1, 32, 1048576, 128, 512, 3, True, "bf16", 4),
 }
 WORKLOAD_ORDER = ["tiny", "headline_32k", "coarse_32k", "long_128k", "long_1m"]
+# The headline inputs (same seed, same tensors) gated by the other block
+# summaries the serving article names next to the mean.
+WORKLOADS["headline_32k_max"] = Workload("headline_32k_max", 1, 32, 32768, 128, 512, 3, True, "bf16", 1, "max")
+WORKLOADS["headline_32k_meanmax"] = Workload("headline_32k_meanmax", 1, 32, 32768, 128, 512, 3, True, "bf16", 1,
+                                             "mean+max")
+POOLING_VARIANTS = ["headline_32k_max", "headline_32k_meanmax"]
 
 
 def _rng(seed: int, tensor: int, b: int, h: int) -> np.random.Generator:

@@ -39,7 +39,7 @@ def _as_f32(x, dtype):
 def _oracle_head(args):
     qb, kb, vb, rows, w = args
     q, k, v = (_as_f32(x, w.dtype) for x in (qb, kb, vb))
-    res = orc.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=rows)
+    res = orc.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=rows, pooling=w.pooling)
     return res, q, k, v
 
 

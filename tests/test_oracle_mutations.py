@@ -23,6 +23,8 @@ def _pins():
     """(name, callable) for every pin that exercises the method's steps."""
     yield "hand_case", lambda: pins.test_hand_case(GOLDEN)
     yield "pool_closed_forms", pins.test_pool_closed_forms
+    yield "pooling_hand_case", lambda: pins.test_pooling_hand_case(GOLDEN)
+    yield "max_pool_invariants", pins.test_max_pool_invariants
     for seed in range(6):
         for causal in (True, False):
             yield f"subset_bruteforce[{seed},{causal}]", (
@@ -71,14 +73,38 @@ _orig_keys = moba.attended_keys
 _orig_attend = moba.attend
 
 
-def pool_wrong_denominator(k, block_size):
+def pool_wrong_denominator(k, block_size, pooling="mean"):
     # mean over Bs - 1 (an off-by-one denominator)
-    return _orig_pool(k, block_size) * block_size / max(block_size - 1, 1)
+    return _orig_pool(k, block_size, pooling) * block_size / max(block_size - 1, 1)
 
 
-def pool_first_key_only(k, block_size):
+def pool_first_key_only(k, block_size, pooling="mean"):
     k = np.asarray(k, dtype=np.float64)
     return k[::block_size].copy()
+
+
+def pool_max_is_min(k, block_size, pooling="mean"):
+    # a sign slip in the max reduction
+    if pooling == "mean":
+        return _orig_pool(k, block_size)
+    k = np.asarray(k, dtype=np.float64)
+    mn = k.reshape(-1, block_size, k.shape[1]).min(axis=1)
+    return mn if pooling == "max" else _orig_pool(k, block_size) + mn
+
+
+def pool_max_over_dims(k, block_size, pooling="mean"):
+    # the max taken across coordinates instead of across the block's tokens
+    if pooling == "mean":
+        return _orig_pool(k, block_size)
+    k = np.asarray(k, dtype=np.float64)
+    blocks = k.reshape(-1, block_size, k.shape[1])
+    mx = np.repeat(blocks.max(axis=2).max(axis=1, keepdims=True), k.shape[1], axis=1)
+    return mx if pooling == "max" else _orig_pool(k, block_size) + mx
+
+
+def pool_combined_is_max(k, block_size, pooling="mean"):
+    # mean+max read as the max alone
+    return _orig_pool(k, block_size, "max" if pooling == "mean+max" else pooling)
 
 
 def eligible_includes_own(c, n_blocks, causal):
@@ -156,6 +182,9 @@ def attend_unnormalised(q_t, k, v, keys):
 MUTATIONS = [
     ("pool_keys", pool_wrong_denominator),
     ("pool_keys", pool_first_key_only),
+    ("pool_keys", pool_max_is_min),
+    ("pool_keys", pool_max_over_dims),
+    ("pool_keys", pool_combined_is_max),
     ("eligible_blocks", eligible_includes_own),
     ("eligible_blocks", eligible_includes_next),
     ("select_blocks", select_ties_to_higher_index),

@@ -108,6 +108,52 @@ def test_hand_case(golden_dir):
     np.testing.assert_allclose(res["o"][0], _sdpa(q, k, v, causal=True)[t], atol=1e-12)
 
 
+def test_pooling_hand_case(golden_dir):
+    """Mean, max and mean+max block summaries and the blocks they keep, on a
+    hand-worked case where the three disagree."""
+    g = json.load(open(os.path.join(golden_dir, "pooling_case.json")))
+    k = np.array(g["k"], np.float64)
+    Bs, t = g["block_size"], g["t"]
+    v = np.zeros_like(k)
+    for pooling, want in g["pooled"].items():
+        np.testing.assert_array_equal(moba.pool_keys(k, Bs, pooling), want, err_msg=pooling)
+    q = np.zeros((8, 2))
+    for case in g["cases"]:
+        q[t] = case["q"]
+        for pooling, want in case["idx"].items():
+            res = moba.forward_head(q, k, v, Bs, case["top_k"], True, rows=[t], pooling=pooling)
+            assert list(res["idx"][0]) == want, (pooling, case)
+    with pytest.raises(ValueError):
+        moba.pool_keys(k, Bs, "median")
+
+
+def test_max_pool_invariants():
+    """The max summary against facts that hold for any block: a constant
+    block gives its row, a token that dominates every coordinate is the max,
+    shifting or positively scaling all keys shifts or scales the max,
+    reordering tokens inside a block changes nothing, max(-k) = -min(k), and
+    the max is at least the mean (strictly where a coordinate varies)."""
+    rng = np.random.default_rng(3)
+    Bs, nb, D = 8, 5, 6
+    k = rng.standard_normal((nb * Bs, D))
+    mx = moba.pool_keys(k, Bs, "max")
+    const = np.repeat(rng.standard_normal((nb, D)), Bs, axis=0)
+    np.testing.assert_array_equal(moba.pool_keys(const, Bs, "max"), const[::Bs])
+    np.testing.assert_allclose(moba.pool_keys(const, Bs, "mean+max"), 2 * const[::Bs], rtol=1e-15, atol=1e-15)
+    dom = k.copy()
+    for j in range(nb):
+        dom[j * Bs + (j % Bs)] = np.abs(k[j * Bs:(j + 1) * Bs]).max(axis=0) + 1.0
+    np.testing.assert_array_equal(moba.pool_keys(dom, Bs, "max"), dom[[j * Bs + (j % Bs) for j in range(nb)]])
+    shift = rng.standard_normal(D)
+    np.testing.assert_allclose(moba.pool_keys(k + shift, Bs, "max"), mx + shift, atol=1e-12)
+    np.testing.assert_allclose(moba.pool_keys(2.5 * k, Bs, "max"), 2.5 * mx, atol=1e-12)
+    perm = np.concatenate([j * Bs + rng.permutation(Bs) for j in range(nb)])
+    np.testing.assert_array_equal(moba.pool_keys(k[perm], Bs, "max"), mx)
+    np.testing.assert_array_equal(moba.pool_keys(-k, Bs, "max"), -k.reshape(nb, Bs, D).min(axis=1))
+    assert (mx > moba.pool_keys(k, Bs, "mean")).all()
+    np.testing.assert_allclose(moba.pool_keys(k, Bs, "mean+max"), moba.pool_keys(k, Bs, "mean") + mx, atol=1e-12)
+
+
 # ------------------------------------------------------------------ selection
 @pytest.mark.parametrize("seed", range(6))
 @pytest.mark.parametrize("causal", [True, False])
