@@ -150,7 +150,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER + synth.POOLING_VARIANTS)
     ap.add_argument("--dense-steps", type=int, default=2, help="timed dense causal forwards (0 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=65536, help="oracle sample size (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -175,13 +175,13 @@ def main():
     t0 = time.time()
     q, k, v = upload(w, torch, args.gen_workers)
     log(f"inputs resident in HBM after {time.time() - t0:.1f}s")
-    p = moba.problem(q, w.block_size, w.top_k, w.causal)
+    p = moba.problem(q, w.block_size, w.top_k, w.causal, w.pooling)
     ws = torch.empty(moba.workspace_bytes(p), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     idx = torch.empty((w.batch, w.heads, w.seq_len, w.top_k), dtype=torch.int32, device="cuda")
 
     def step():
-        moba.forward(q, k, v, w.block_size, w.top_k, w.causal, out=o, idx=idx, workspace=ws)
+        moba.forward(q, k, v, w.block_size, w.top_k, w.causal, out=o, idx=idx, workspace=ws, pooling=w.pooling)
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
@@ -266,7 +266,7 @@ def main():
         "data": "synthetic (seeded q, v ~ N(0,1); k ~ N(0,1) + per-block N(0, 0.5^2) bias)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
                    "head_dim": w.head_dim, "block_size": w.block_size, "top_k": w.top_k,
-                   "causal": w.causal, "parallelism": "single GPU"},
+                   "causal": w.causal, "pooling": w.pooling, "parallelism": "single GPU"},
         "effective_tflops": round(eff_tflops, 2),
         "pct_peak": round(100 * eff_tflops / peak, 2),
         "attn_gate_kernels_pct_peak": round(100 * attn_gate_frac, 2),

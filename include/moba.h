@@ -2,7 +2,8 @@
  * moba.h — C ABI of libmoba.so, the MI355X (gfx950) MoBA prefill forward.
  *
  * MoBA (Mixture of Block Attention) cuts K into blocks of block_size
- * tokens, mean-pools each block, lets every query score the eligible blocks
+ * tokens, pools each block (by default its mean; see moba_pooling_t), lets
+ * every query score the eligible blocks
  * by the inner product with the pooled key, always keeps the query's own
  * block, keeps the top_k blocks in total, and runs softmax attention over
  * the keys of the chosen blocks only (causal inside the own block).
@@ -39,15 +40,23 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 1
+#define MOBA_ABI_VERSION 2
 
 typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype_t;
+
+/* The block summary the gate scores each block against ([P] §3.1 uses the
+ * mean of the block's keys along the sequence; [S] §3 names max pooling and
+ * the two combined as engineering options). Per coordinate:
+ *   MOBA_POOL_MEAN     — mean over the block's tokens (the paper's gate);
+ *   MOBA_POOL_MAX      — largest value over the block's tokens;
+ *   MOBA_POOL_MEAN_MAX — mean + max (the combination, read as their sum). */
+typedef enum { MOBA_POOL_MEAN = 0, MOBA_POOL_MAX = 1, MOBA_POOL_MEAN_MAX = 2 } moba_pooling_t;
 
 typedef enum {
   MOBA_OK = 0,
   MOBA_ERR_NULL = 1,        /* a required pointer is NULL */
   MOBA_ERR_SHAPE = 2,       /* non-positive size, or seq_len % block_size != 0 */
-  MOBA_ERR_ARG = 3,         /* top_k < 1, or another out-of-range scalar */
+  MOBA_ERR_ARG = 3,         /* top_k < 1, pooling unknown, reserved != 0 */
   MOBA_ERR_DTYPE = 4,       /* dtype is neither MOBA_F32 nor MOBA_BF16 */
   MOBA_ERR_UNSUPPORTED = 5, /* valid MoBA problem outside this build's kernel limits */
   MOBA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moba_workspace_size */
@@ -79,6 +88,8 @@ typedef struct {
   int64_t top_k;
   int32_t causal;
   int32_t dtype;
+  int32_t pooling;  /* moba_pooling_t; a zeroed field selects the mean */
+  int32_t reserved; /* must be 0 */
 } moba_problem_t;
 
 /* MOBA_ABI_VERSION of the loaded library. */
@@ -120,7 +131,8 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
 int moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
                        void* o, void* stream);
 
-/* Stage entry point: block mean-pooling only ([P] §3.1 mean_pool).
+/* Stage entry point: block pooling only ([P] §3.1 mean_pool; p->pooling
+ * selects the summary as for moba_forward).
  * kbar: device float64 [batch, heads, n_blocks, head_dim] — the pooled keys
  * the gate uses. Uses the forward's workspace. */
 int moba_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace,

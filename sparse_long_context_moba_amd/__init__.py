@@ -38,13 +38,20 @@ def _check(status: int, where: str):
         raise MobaError(status, where)
 
 
-def problem(q: torch.Tensor, block_size: int, top_k: int, causal: bool = True) -> moba_problem_t:
+POOLINGS = {"mean": 0, "max": 1, "mean+max": 2}
+
+
+def problem(q: torch.Tensor, block_size: int, top_k: int, causal: bool = True,
+            pooling: str = "mean") -> moba_problem_t:
+    if pooling not in POOLINGS:
+        raise ValueError(f"pooling must be one of {tuple(POOLINGS)}, got {pooling!r}")
     if q.dim() != 4:
         raise ValueError(f"q must be [batch, heads, seq_len, head_dim], got shape {tuple(q.shape)}")
     if q.dtype not in _DTYPES:
         raise ValueError(f"dtype must be float32 or bfloat16, got {q.dtype}")
     B, H, S, D = q.shape
-    return moba_problem_t(B, H, S, D, int(block_size), int(top_k), 1 if causal else 0, _DTYPES[q.dtype])
+    return moba_problem_t(B, H, S, D, int(block_size), int(top_k), 1 if causal else 0, _DTYPES[q.dtype],
+                          POOLINGS[pooling], 0)
 
 
 def _tensors(*ts):
@@ -77,10 +84,11 @@ def _workspace(p, device):
 
 
 def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None, idx=None,
-            workspace=None):
-    """MoBA forward. Returns (o, block_idx)."""
+            workspace=None, pooling: str = "mean"):
+    """MoBA forward. Returns (o, block_idx). pooling: the gate's block
+    summary, "mean" (the paper's), "max" or "mean+max"."""
     _tensors(q, k, v)
-    p = problem(q, block_size, top_k, causal)
+    p = problem(q, block_size, top_k, causal, pooling)
     B, H, S, D = q.shape
     o = torch.empty_like(q) if out is None else out
     bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device) if idx is None else idx
@@ -105,10 +113,10 @@ def dense(q, k, v, causal: bool = True, out=None):
     return o
 
 
-def pool(k, block_size: int):
-    """Block means of K as the gate uses them: float64 [B, H, n_blocks, D]."""
+def pool(k, block_size: int, pooling: str = "mean"):
+    """Block summaries of K as the gate uses them: float64 [B, H, n_blocks, D]."""
     _tensors(k)
-    p = problem(k, block_size, 1, True)
+    p = problem(k, block_size, 1, True, pooling)
     B, H, S, D = k.shape
     kbar = torch.empty((B, H, S // block_size if block_size > 0 else 0, D), dtype=torch.float64,
                        device=k.device)
@@ -119,10 +127,10 @@ def pool(k, block_size: int):
     return kbar
 
 
-def select(q, k, block_size: int, top_k: int, causal: bool = True):
+def select(q, k, block_size: int, top_k: int, causal: bool = True, pooling: str = "mean"):
     """Routing only: int32 [B, H, S, top_k] exactly as forward() returns it."""
     _tensors(q, k)
-    p = problem(q, block_size, top_k, causal)
+    p = problem(q, block_size, top_k, causal, pooling)
     B, H, S, D = q.shape
     bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device)
     ws, n = _workspace(p, q.device)

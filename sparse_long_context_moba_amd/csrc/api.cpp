@@ -63,6 +63,7 @@ constexpr size_t kAlign = 256;
 struct Plan {
   int64_t B, H, S, D, Bs, top_k, bh, nb, k_eff, slots;
   bool causal, bf16_in;
+  int pooling;         // moba_pooling_t
   int64_t pairs;       // (query, kept past block) pairs over all heads
   int64_t max_tiles;   // upper bound on gather tiles
   // workspace offsets (bytes)
@@ -82,6 +83,10 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     return fail(MOBA_ERR_SHAPE, "seq_len " + std::to_string(p->seq_len) + " is not a multiple of block_size " +
                                     std::to_string(p->block_size));
   if (p->top_k < 1) return fail(MOBA_ERR_ARG, "top_k must be >= 1, got " + std::to_string(p->top_k));
+  if (p->pooling != MOBA_POOL_MEAN && p->pooling != MOBA_POOL_MAX && p->pooling != MOBA_POOL_MEAN_MAX)
+    return fail(MOBA_ERR_ARG, "pooling must be MOBA_POOL_MEAN (0), MOBA_POOL_MAX (1) or MOBA_POOL_MEAN_MAX (2), got " +
+                                  std::to_string(p->pooling));
+  if (p->reserved != 0) return fail(MOBA_ERR_ARG, "reserved must be 0, got " + std::to_string(p->reserved));
   if (p->dtype != MOBA_F32 && p->dtype != MOBA_BF16)
     return fail(MOBA_ERR_DTYPE, "dtype must be MOBA_F32 (0) or MOBA_BF16 (1), got " + std::to_string(p->dtype));
   if (p->head_dim != 64 && p->head_dim != 128)
@@ -103,6 +108,7 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   P.slots = P.k_eff - 1;
   P.causal = p->causal != 0;
   P.bf16_in = p->dtype == MOBA_BF16;
+  P.pooling = p->pooling;
   if (P.bh * P.nb >= (int64_t(1) << 31))
     return fail(MOBA_ERR_UNSUPPORTED, "batch * heads * n_blocks must be below 2^31");
   if (P.slots > kMaxSlotsHost && P.k_eff < P.nb)
@@ -181,6 +187,7 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   pa.block_size = P.Bs;
   pa.head_dim = (int)P.D;
   pa.bf16_in = P.bf16_in;
+  pa.pooling = P.pooling;
   pa.kbar64 = kbar64_out ? kbar64_out : at<double>(ws, P.kbar64);
   pa.kbar32 = at<float>(ws, P.kbar32);
   pa.kbar_hi = at<bf16>(ws, P.kbar_hi);

@@ -25,6 +25,7 @@ struct PoolArgs {
   int64_t bh, seq_len, block_size;
   int head_dim;
   bool bf16_in;
+  int pooling;       // moba_pooling_t: mean, max, or mean + max per coordinate
   double* kbar64;    // [bh * nb, D]
   float* kbar32;     // [bh * nb, D]
   bf16* kbar_hi;     // [bh * nb, D]

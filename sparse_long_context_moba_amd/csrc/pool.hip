@@ -1,16 +1,19 @@
-// Block mean-pooling of K (the gate's block summary).
+// Block pooling of K: the gate's block summary.
 //
 // The gate of MoBA scores each block by the inner product of the query with
 // the mean of the block's keys along the sequence («月之暗面 MoBA 论文解读»
-// §3.1, gating.score_fn = mean_pool; the hncyxsy.com MOBA article §3).
+// §3.1, gating.score_fn = mean_pool; the hncyxsy.com MOBA article §3). The
+// article's §3 also names max pooling, and the two combined (read here as
+// their sum), as options: the same pass computes any of the three.
 //
 // One pass, bound by HBM bandwidth: one workgroup per (head, block) reads
 // the block's keys with 16-byte loads (several in flight per thread),
-// accumulates in fp64 per thread, reduces across row groups in a fixed
-// order, and writes the pooled key in fp64 (exact re-scoring), fp32, and as
-// a bf16 hi/lo pair (hi = bf16(x), lo = bf16(x - hi)) for the MFMA gate,
-// plus the block's L2 norm (rounded up) for the gate's rounding bound. It
-// also clears the block's query count, which the gate's ranking fills. K is read exactly once; the fixed
+// accumulates in fp64 (and/or takes the running max) per thread, reduces
+// across row groups in a fixed order, and writes the pooled key in fp64
+// (exact re-scoring), fp32, and as a bf16 hi/lo pair (hi = bf16(x),
+// lo = bf16(x - hi)) for the MFMA gate, plus the block's L2 norm (rounded
+// up) for the gate's rounding bound. It also clears the block's query
+// count, which the gate's ranking fills. K is read exactly once; the fixed
 // reduction order keeps results bit-stable.
 #include "common.h"
 #include "launch.h"
@@ -18,12 +21,16 @@
 namespace moba {
 
 // U rows per thread are loaded before they are accumulated (in row order).
-template <typename T, int D, int U>
+// MODE selects the summary (moba_pooling_t): 0 mean, 1 max, 2 mean + max.
+// The max is exact in any order (fp32 holds every input value).
+template <typename T, int D, int U, int MODE>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int TPR = D / VEC;         // threads per row
   constexpr int RG = 256 / TPR;        // rows per pass
-  __shared__ double red[RG][D];
+  constexpr bool SUM = MODE != 1, MAX = MODE != 0;
+  __shared__ double red[SUM ? RG : 1][D];
+  __shared__ float redm[MAX ? RG : 1][D];
   __shared__ double sq[D];
   const int tid = threadIdx.x;
   const int rg = tid / TPR, cv = tid % TPR;
@@ -31,8 +38,16 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   const int Bs = (int)a.block_size;
   const T* base = reinterpret_cast<const T*>(a.k) + blk * a.block_size * D + cv * VEC;
   double acc[VEC];
+  float mx[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+  for (int e = 0; e < VEC; ++e) {
+    acc[e] = 0.0;
+    mx[e] = -__builtin_inff();
+  }
+  auto take = [&](int e, float x) {
+    if (SUM) acc[e] += (double)x;
+    if (MAX) mx[e] = fmaxf(mx[e], x);
+  };
   for (int r0 = rg; r0 < Bs; r0 += U * RG) {
     u32x4 raw[U];
 #pragma unroll
@@ -43,33 +58,41 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
         const unsigned w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += (double)__uint_as_float(w[e] << 16);
-          acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+          take(2 * e, __uint_as_float(w[e] << 16));
+          take(2 * e + 1, __uint_as_float(w[e] & 0xffff0000u));
         }
       } else {
-        acc[0] += (double)__uint_as_float(raw[u].x);
-        acc[1] += (double)__uint_as_float(raw[u].y);
-        acc[2] += (double)__uint_as_float(raw[u].z);
-        acc[3] += (double)__uint_as_float(raw[u].w);
+        take(0, __uint_as_float(raw[u].x));
+        take(1, __uint_as_float(raw[u].y));
+        take(2, __uint_as_float(raw[u].z));
+        take(3, __uint_as_float(raw[u].w));
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) red[rg][cv * VEC + e] = acc[e];
+  for (int e = 0; e < VEC; ++e) {
+    if (SUM) red[rg][cv * VEC + e] = acc[e];
+    if (MAX) redm[rg][cv * VEC + e] = mx[e];
+  }
   __syncthreads();
   if (tid < D) {
     const int d = tid;
     double s = 0.0;
+    float m = -__builtin_inff();
 #pragma unroll
-    for (int g = 0; g < RG; ++g) s += red[g][d];
+    for (int g = 0; g < RG; ++g) {
+      if (SUM) s += red[g][d];
+      if (MAX) m = fmaxf(m, redm[g][d]);
+    }
     const double mean = s / (double)Bs;
-    a.kbar64[blk * D + d] = mean;
-    const float m32 = (float)mean;
+    const double val = MODE == 0 ? mean : MODE == 1 ? (double)m : mean + (double)m;
+    a.kbar64[blk * D + d] = val;
+    const float m32 = (float)val;
     a.kbar32[blk * D + d] = m32;
     const bf16 hi = to_bf16(m32);
     a.kbar_hi[blk * D + d] = hi;
     a.kbar_lo[blk * D + d] = to_bf16(m32 - (float)hi);
-    sq[d] = mean * mean;
+    sq[d] = val * val;
   }
   __syncthreads();
   for (int w = D / 2; w > 0; w >>= 1) {
@@ -91,8 +114,15 @@ static hipError_t pool_launch_t(const PoolArgs& a, hipStream_t s) {
   // 64 / RG >= 2; use 4 loads in flight where they divide evenly.
   const bool four = (a.block_size / RG) % 4 == 0;
   KernelTimer t(s, "pool");
-  if (four) hipLaunchKernelGGL((pool_kernel<T, D, 4>), dim3((unsigned)nblk), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((pool_kernel<T, D, 2>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)nblk);
+  switch (a.pooling * 2 + (four ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((pool_kernel<T, D, 2, 0>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((pool_kernel<T, D, 4, 0>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((pool_kernel<T, D, 2, 1>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((pool_kernel<T, D, 4, 1>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((pool_kernel<T, D, 2, 2>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((pool_kernel<T, D, 4, 2>), grid, dim3(256), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     from sparse_long_context_moba_amd import _lib
-    assert _lib.moba_abi_version() == 1
+    assert _lib.moba_abi_version() == 2
     for code in range(8):
         assert _lib.moba_status_str(code)
     assert _lib.moba_status_str(99) == "unknown status"
@@ -54,6 +54,9 @@ FAKE = 0x1000  # never dereferenced: validation fails or stops before any launch
     (dict(block_size=0), 2, "block_size"),
     (dict(seq_len=1000), 2, "multiple"),
     (dict(top_k=0), 3, "top_k"),
+    (dict(pooling=3), 3, "pooling"),
+    (dict(pooling=-1), 3, "pooling"),
+    (dict(reserved=1), 3, "reserved"),
     (dict(dtype=7), 4, "dtype"),
     (dict(head_dim=96), 5, "head_dim"),
     (dict(block_size=32, seq_len=1024), 5, "block_size"),

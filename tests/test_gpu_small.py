@@ -28,10 +28,11 @@ def _inputs(seed, B, H, S, D, Bs, dtype, bias=0.5):
     return _round(q, dtype), _round(k, dtype), _round(v, dtype)
 
 
-def _run_and_check(q, k, v, Bs, top_k, causal, dtype, label):
+def _run_and_check(q, k, v, Bs, top_k, causal, dtype, label, pooling="mean"):
     import sparse_long_context_moba_amd as moba
-    say(f"[gpu] {label}: shape={q.shape} Bs={Bs} top_k={top_k} causal={causal} {dtype}")
-    o, idx = moba.forward(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), Bs, top_k, causal)
+    say(f"[gpu] {label}: shape={q.shape} Bs={Bs} top_k={top_k} causal={causal} {dtype} pooling={pooling}")
+    o, idx = moba.forward(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), Bs, top_k, causal,
+                          pooling=pooling)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     idx = idx.cpu().numpy()
@@ -39,7 +40,7 @@ def _run_and_check(q, k, v, Bs, top_k, causal, dtype, label):
     worst = 0.0
     for b in range(B):
         for h in range(H):
-            res = orc.forward_head(q[b, h], k[b, h], v[b, h], Bs, top_k, causal)
+            res = orc.forward_head(q[b, h], k[b, h], v[b, h], Bs, top_k, causal, pooling=pooling)
             st = check_rows(o[b, h], idx[b, h], res, np.arange(S), q[b, h], k[b, h], v[b, h], Bs,
                             top_k, causal, dtype, label=f"{label} b={b} h={h}")
             worst = max(worst, st["max_err"])
@@ -126,6 +127,39 @@ def test_stage_pool_and_select():
         res = orc.forward_head(q[0, h], k[0, h], v[0, h], 256, 3, True)
         ok = (idx[0, h] == res["idx"]).all(axis=1) | res["flag"]
         assert ok.all()
+
+
+POOL_CASES = [
+    # label, seed, B, H, S, D, Bs, top_k, causal, dtype
+    ("bf16-d128-bs64-k3", 15, 1, 2, 1024, 128, 64, 3, True, "bf16"),
+    ("f32-d64-bs128-k4-noncausal", 16, 1, 2, 1024, 64, 128, 4, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("pooling", ["max", "mean+max"])
+@pytest.mark.parametrize("case", POOL_CASES, ids=[c[0] for c in POOL_CASES])
+def test_pooling_variants_parity(case, pooling):
+    """Gates scoring max-pooled or mean+max-pooled blocks: every row against
+    the oracle with the same summary."""
+    label, seed, B, H, S, D, Bs, top_k, causal, dtype = case
+    q, k, v = _inputs(seed, B, H, S, D, Bs, dtype)
+    _run_and_check(q, k, v, Bs, top_k, causal, dtype, f"{label}-{pooling}", pooling=pooling)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stage_pool_variants(dtype):
+    """The pool stage for each summary: the max is exact (a comparison of
+    input values), the mean and mean+max agree with fp64 to rounding."""
+    import sparse_long_context_moba_amd as moba
+    q, k, v = _inputs(17, 1, 2, 1024, 64, 128, dtype)
+    for pooling in ("mean", "max", "mean+max"):
+        kb = moba.pool(to_dev(k, dtype), 128, pooling).cpu().numpy()
+        for h in range(2):
+            ref = orc.pool_keys(k[0, h], 128, pooling)
+            if pooling == "max":
+                np.testing.assert_array_equal(kb[0, h], ref)
+            else:
+                np.testing.assert_allclose(kb[0, h], ref, rtol=1e-13, atol=1e-14)
 
 
 def _grouped_keys(seed, S, D, Bs, groups, jitter, dtype):

@@ -50,11 +50,11 @@ def _run(name, n_rows=4096):
     say(f"[gpu] {name}: generating and uploading inputs")
     (qd, kd, vd), host = _upload(w)
     say(f"[gpu] {name}: inputs ready in {time.time() - t0:.1f}s; running moba.forward")
-    o, idx = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal)
+    o, idx = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal, pooling=w.pooling)
     torch.cuda.synchronize()
     # Run-to-run: every output bit and index must repeat (the path has no
     # floating-point atomics, so any difference is a race).
-    o2, idx2 = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal)
+    o2, idx2 = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal, pooling=w.pooling)
     torch.cuda.synchronize()
     bits = torch.int16 if o.dtype == torch.bfloat16 else torch.int32
     n_diff = int((o.view(bits) != o2.view(bits)).sum().item())
@@ -93,6 +93,14 @@ def test_tiny_all_rows():
 
 def test_headline_32k_sampled():
     _run("headline_32k")
+
+
+def test_headline_32k_max_pooling_sampled():
+    _run("headline_32k_max")
+
+
+def test_headline_32k_meanmax_pooling_sampled():
+    _run("headline_32k_meanmax")
 
 
 def test_coarse_32k_sampled():
