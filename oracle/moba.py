@@ -38,7 +38,9 @@ Readings where the pages are silent (each is listed in the design doc):
   * gate scores are per (batch, head), raw inner products; any positive
     scale or a softmax over them is monotone and cannot change the choice;
   * top_k larger than the number of available blocks is clamped;
-  * seq_len not a multiple of block_size is an error;
+  * seq_len not a multiple of block_size: the block count is rounded up
+    and the last block is short ([S] §4 counts blocks with a ceiling
+    division; [R] §1.1's code asserts instead);
   * attention logits are scaled by 1/sqrt(head_dim);
   * non-causal mode: every other block is eligible, the own block is still
     forced, and no mask is applied inside blocks.
@@ -59,16 +61,21 @@ NEAR_TIE_REL = 1e-5
 def num_blocks(seq_len: int, block_size: int) -> int:
     """Number of key blocks ([R] §3.1: 32768 tokens in blocks of 512 -> 64).
 
-    The pages' own code asserts on a length that is not a multiple of the
-    block size ([R] §1.1); here that is a ValueError naming the parameter.
+    For a length that is not a multiple of the block size the pages
+    disagree: the code in [R] §1.1 asserts, the script in [S] §4 counts
+    blocks with a ceiling division. The ceiling is taken here: the last
+    block holds the remaining seq_len - (n - 1) * block_size tokens.
     """
     if block_size < 1:
         raise ValueError(f"block_size must be >= 1, got {block_size}")
     if seq_len < 1:
         raise ValueError(f"seq_len must be >= 1, got {seq_len}")
-    if seq_len % block_size != 0:
-        raise ValueError(f"seq_len {seq_len} is not a multiple of block_size {block_size}")
-    return seq_len // block_size
+    return -(-seq_len // block_size)
+
+
+def block_range(j: int, seq_len: int, block_size: int) -> tuple[int, int]:
+    """Token positions [lo, hi) of block j (the last block may be short)."""
+    return j * block_size, min((j + 1) * block_size, seq_len)
 
 
 def theoretical_sparsity(top_k: int, n_blocks: int) -> float:
@@ -83,7 +90,8 @@ def pool_keys(k: np.ndarray, block_size: int, pooling: str = "mean") -> np.ndarr
     """The block summary the gate scores against, per coordinate:
 
     - "mean": the mean of K over each block along the sequence, the paper's
-      choice ([P] §3.1 mean_pool; [S] §3);
+      choice ([P] §3.1 mean_pool; [S] §3); a short last block is averaged
+      over the tokens it holds;
     - "max": the largest value of each coordinate over the block's tokens,
       which [S] §3 names as an engineering alternative that reacts to blocks
       dense in key information;
@@ -98,11 +106,14 @@ def pool_keys(k: np.ndarray, block_size: int, pooling: str = "mean") -> np.ndarr
     k = np.asarray(k, dtype=np.float64)
     S, D = k.shape
     nb = num_blocks(S, block_size)
-    blocks = k.reshape(nb, block_size, D)
-    mean = blocks.sum(axis=1) / block_size
+    mean = np.zeros((nb, D))
+    mx = np.zeros((nb, D))
+    for j in range(nb):
+        lo, hi = block_range(j, S, block_size)
+        mean[j] = k[lo:hi].sum(axis=0) / (hi - lo)
+        mx[j] = k[lo:hi].max(axis=0)
     if pooling == "mean":
         return mean
-    mx = blocks.max(axis=1)
     return mx if pooling == "max" else mean + mx
 
 
@@ -147,14 +158,18 @@ def select_blocks(q_t: np.ndarray, kbar: np.ndarray, c: int, top_k: int, causal:
     return idx, flag, a, b
 
 
-def attended_keys(t: int, idx_row: np.ndarray, block_size: int, causal: bool) -> np.ndarray:
-    """Key positions query t attends: every key of every chosen block, and
-    inside its own block only keys up to t when causal ([S] §3)."""
+def attended_keys(t: int, idx_row: np.ndarray, block_size: int, causal: bool,
+                  seq_len: int | None = None) -> np.ndarray:
+    """Key positions query t attends: every key of every chosen block (a
+    short last block ends at seq_len), and inside its own block only keys
+    up to t when causal ([S] §3)."""
     keys = []
     for j in idx_row:
         if j < 0:
             continue
         lo, hi = int(j) * block_size, (int(j) + 1) * block_size
+        if seq_len is not None:
+            hi = min(hi, seq_len)
         if causal:
             hi = min(hi, t + 1)
         keys.extend(range(lo, hi))
@@ -197,7 +212,7 @@ def forward_head(q, k, v, block_size: int, top_k: int, causal: bool = True, rows
     for r, t in enumerate(rows):
         c = int(t) // block_size
         idx[r], flag[r], a[r], b[r] = select_blocks(q[t], kbar, c, top_k, causal)
-        o[r] = attend(q[t], k, v, attended_keys(int(t), idx[r], block_size, causal))
+        o[r] = attend(q[t], k, v, attended_keys(int(t), idx[r], block_size, causal, S))
     assert nb == kbar.shape[0]
     return {"o": o, "idx": idx, "flag": flag, "a": a, "b": b, "kbar": kbar}
 
@@ -217,7 +232,7 @@ def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, pooling: 
 def attend_with_idx(q_t, k, v, t: int, idx_row, block_size: int, causal: bool = True):
     """Attention of query t over a given block choice (forced-index mode),
     used where the GPU legitimately broke a near-tie the other way."""
-    return attend(q_t, k, v, attended_keys(t, np.asarray(idx_row), block_size, causal))
+    return attend(q_t, k, v, attended_keys(t, np.asarray(idx_row), block_size, causal, len(k)))
 
 
 def dense_attention(q, k, v, causal: bool = True, rows=None):
@@ -240,6 +255,8 @@ def algorithmic_flops(seq_len: int, head_dim: int, block_size: int, top_k: int,
     """
     S, D, Bs = seq_len, head_dim, block_size
     nb = num_blocks(S, Bs)
+    if S % Bs:
+        raise ValueError("the closed-form count covers whole blocks only")
     k_eff = min(top_k, nb)
     gate = 0
     keys = 0

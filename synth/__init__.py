@@ -45,7 +45,7 @@ class Workload:
 
     @property
     def n_blocks(self) -> int:
-        return self.seq_len // self.block_size
+        return -(-self.seq_len // self.block_size)
 
 
 # The five named workloads (sizes of the pages' settings: block 512 / top-k 3
@@ -88,11 +88,11 @@ def make_head(seed: int, b: int, h: int, seq_len: int, head_dim: int,
               block_size: int, dtype: str):
     """Return (q, k, v), each float32 [seq_len, head_dim], for one (b, h)."""
     S, D = seq_len, head_dim
-    nb = S // block_size
+    nb = -(-S // block_size)  # a short last block gets its own bias too
     q = _rng(seed, TENSOR_Q, b, h).standard_normal((S, D), dtype=np.float32)
     kn = _rng(seed, TENSOR_KNOISE, b, h).standard_normal((S, D), dtype=np.float32)
     bias = _rng(seed, TENSOR_KBIAS, b, h).normal(0.0, 0.5, (nb, D)).astype(np.float32)
-    kn.reshape(nb, block_size, D)[...] += bias[:, None, :]
+    kn += np.repeat(bias, block_size, axis=0)[:S]
     v = _rng(seed, TENSOR_V, b, h).standard_normal((S, D), dtype=np.float32)
     if dtype == "bf16":
         q, kn, v = round_to_bf16(q), round_to_bf16(kn), round_to_bf16(v)

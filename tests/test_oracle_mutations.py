@@ -25,6 +25,10 @@ def _pins():
     yield "pool_closed_forms", pins.test_pool_closed_forms
     yield "pooling_hand_case", lambda: pins.test_pooling_hand_case(GOLDEN)
     yield "max_pool_invariants", pins.test_max_pool_invariants
+    yield "short_block_pool", pins.test_short_last_block_counts_and_pool
+    for causal in (True, False):
+        yield f"short_block_dense[{causal}]", lambda c=causal: pins.test_short_last_block_matches_masked_dense_softmax(c)
+    yield "short_block_earlier_rows", pins.test_short_last_block_leaves_earlier_rows_alone
     for seed in range(6):
         for causal in (True, False):
             yield f"subset_bruteforce[{seed},{causal}]", (
@@ -81,6 +85,23 @@ def pool_wrong_denominator(k, block_size, pooling="mean"):
 def pool_first_key_only(k, block_size, pooling="mean"):
     k = np.asarray(k, dtype=np.float64)
     return k[::block_size].copy()
+
+
+def num_blocks_floor(seq_len, block_size):
+    # a short last block silently dropped
+    if block_size < 1:
+        raise ValueError("block_size")
+    return seq_len // block_size
+
+
+def pool_short_block_over_block_size(k, block_size, pooling="mean"):
+    # the short last block's mean divided by block_size instead of its length
+    out = _orig_pool(k, block_size, pooling)
+    S = np.asarray(k).shape[0]
+    L = S - (out.shape[0] - 1) * block_size
+    if pooling == "mean" and L < block_size:
+        out[-1] *= L / block_size
+    return out
 
 
 def pool_max_is_min(k, block_size, pooling="mean"):
@@ -151,15 +172,15 @@ def select_lowest_scores(q_t, kbar, c, top_k, causal):
     return _orig_select(-np.asarray(q_t, dtype=np.float64), kbar, c, top_k, causal)
 
 
-def keys_no_causal_mask(t, idx_row, block_size, causal):
-    return _orig_keys(t, idx_row, block_size, False)
+def keys_no_causal_mask(t, idx_row, block_size, causal, seq_len=None):
+    return _orig_keys(t, idx_row, block_size, False, seq_len)
 
 
-def keys_drop_own_block(t, idx_row, block_size, causal):
+def keys_drop_own_block(t, idx_row, block_size, causal, seq_len=None):
     # the own block's keys are left out (kept only when nothing else is chosen)
     c = t // block_size
     past = [int(j) for j in idx_row if j >= 0 and j != c]
-    return _orig_keys(t, np.array(past if past else list(idx_row)), block_size, causal)
+    return _orig_keys(t, np.array(past if past else list(idx_row)), block_size, causal, seq_len)
 
 
 def attend_no_scale(q_t, k, v, keys):
@@ -183,6 +204,8 @@ MUTATIONS = [
     ("pool_keys", pool_wrong_denominator),
     ("pool_keys", pool_first_key_only),
     ("pool_keys", pool_max_is_min),
+    ("num_blocks", num_blocks_floor),
+    ("pool_keys", pool_short_block_over_block_size),
     ("pool_keys", pool_max_over_dims),
     ("pool_keys", pool_combined_is_max),
     ("eligible_blocks", eligible_includes_own),

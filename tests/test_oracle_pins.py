@@ -28,7 +28,7 @@ def _sdpa(q, k, v, mask=None, causal=False):
 def _rand_head(seed, S, D, Bs, bias=0.5):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((S, D))
-    k = rng.standard_normal((S, D)) + np.repeat(rng.normal(0, bias, (S // Bs, D)), Bs, axis=0)
+    k = rng.standard_normal((S, D)) + np.repeat(rng.normal(0, bias, (-(-S // Bs), D)), Bs, axis=0)[:S]
     v = rng.standard_normal((S, D))
     return q, k, v
 
@@ -60,8 +60,6 @@ def test_compute_share_printed_on_pages(golden_dir):
 
 
 def test_bad_shapes_raise_naming_parameter():
-    with pytest.raises(ValueError, match="block_size"):
-        moba.num_blocks(100, 7)
     with pytest.raises(ValueError, match="block_size"):
         moba.num_blocks(100, 0)
     q, k, v = _rand_head(0, 16, 4, 4)
@@ -152,6 +150,52 @@ def test_max_pool_invariants():
     np.testing.assert_array_equal(moba.pool_keys(-k, Bs, "max"), -k.reshape(nb, Bs, D).min(axis=1))
     assert (mx > moba.pool_keys(k, Bs, "mean")).all()
     np.testing.assert_allclose(moba.pool_keys(k, Bs, "mean+max"), moba.pool_keys(k, Bs, "mean") + mx, atol=1e-12)
+
+
+# ------------------------------------------------------------ short last block
+def test_short_last_block_counts_and_pool():
+    """A length that is not a multiple of the block size: the count rounds
+    up ([S] §4's ceiling division) and the last block's summary covers only
+    its own tokens. Closed forms on a ramp k_t = (t, 1)."""
+    assert moba.num_blocks(100, 7) == 15
+    assert moba.num_blocks(64, 8) == 8 and moba.num_blocks(65, 8) == 9 and moba.num_blocks(3, 8) == 1
+    S, Bs = 20, 8
+    k = np.stack([np.arange(S, dtype=np.float64), np.ones(S)], axis=1)
+    np.testing.assert_array_equal(moba.pool_keys(k, Bs, "mean"), [[3.5, 1], [11.5, 1], [17.5, 1]])
+    np.testing.assert_array_equal(moba.pool_keys(k, Bs, "max"), [[7, 1], [15, 1], [19, 1]])
+    assert list(moba.attended_keys(19, np.array([1, 2]), Bs, False, S)) == list(range(8, 20))
+    assert list(moba.attended_keys(17, np.array([0, 2]), Bs, True, S)) == list(range(0, 8)) + [16, 17]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_short_last_block_matches_masked_dense_softmax(causal):
+    """The block mask built from the chosen blocks (the last block holds 4
+    tokens) fed to a library attention routine."""
+    S, D, Bs, top_k = 60, 8, 8, 3
+    q, k, v = _rand_head(41, S, D, Bs)
+    res = moba.forward_head(q, k, v, Bs, top_k, causal)
+    blk = np.arange(S) // Bs
+    mask = np.zeros((S, S), bool)
+    for t in range(S):
+        for j in res["idx"][t]:
+            if j >= 0:
+                mask[t, blk == j] = True
+        if causal:
+            mask[t, t + 1:] = False
+    np.testing.assert_allclose(res["o"], _sdpa(q, k, v, mask=mask), atol=1e-12)
+    full = moba.forward_head(q, k, v, Bs, 8, causal)
+    np.testing.assert_allclose(full["o"], _sdpa(q, k, v, causal=causal), atol=1e-12)
+
+
+def test_short_last_block_leaves_earlier_rows_alone():
+    """Causal: appending a partial block changes no earlier row."""
+    S, D, Bs = 60, 8, 8
+    q, k, v = _rand_head(43, S, D, Bs)
+    whole = moba.forward_head(q[:56], k[:56], v[:56], Bs, 3)
+    ragged = moba.forward_head(q, k, v, Bs, 3)
+    np.testing.assert_array_equal(ragged["idx"][:56], whole["idx"])
+    np.testing.assert_allclose(ragged["o"][:56], whole["o"], atol=1e-12)
+    assert (ragged["idx"][56:, :] >= -1).all() and (ragged["idx"][56:] == 7).any(axis=1).all()
 
 
 # ------------------------------------------------------------------ selection
