@@ -45,10 +45,11 @@ def work_model(w):
     k_eff = min(w.top_k, nb)
     gate_pairs = past_pairs = own_keys = 0
     for c in range(nb):
+        n = min(Bs, S - c * Bs)  # queries in block c (a short last block holds fewer)
         elig = c if w.causal else nb - 1
-        gate_pairs += Bs * elig
-        past_pairs += Bs * min(k_eff - 1, elig)
-        own_keys += Bs * (Bs + 1) // 2 if w.causal else Bs * Bs
+        gate_pairs += n * elig
+        past_pairs += n * min(k_eff - 1, elig)  # causal past blocks are whole blocks of Bs keys
+        own_keys += n * (n + 1) // 2 if w.causal else n * n
     dense_keys = S * (S + 1) // 2 if w.causal else S * S
     esz = 2 if w.dtype == "bf16" else 4
     return {
@@ -150,7 +151,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER + synth.POOLING_VARIANTS)
+    ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER + synth.POOLING_VARIANTS + synth.SHAPE_VARIANTS)
     ap.add_argument("--dense-steps", type=int, default=2, help="timed dense causal forwards (0 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=65536, help="oracle sample size (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,

@@ -55,7 +55,7 @@ typedef enum { MOBA_POOL_MEAN = 0, MOBA_POOL_MAX = 1, MOBA_POOL_MEAN_MAX = 2 } m
 typedef enum {
   MOBA_OK = 0,
   MOBA_ERR_NULL = 1,        /* a required pointer is NULL */
-  MOBA_ERR_SHAPE = 2,       /* non-positive size, or seq_len % block_size != 0 */
+  MOBA_ERR_SHAPE = 2,       /* non-positive size */
   MOBA_ERR_ARG = 3,         /* top_k < 1, pooling unknown, reserved != 0 */
   MOBA_ERR_DTYPE = 4,       /* dtype is neither MOBA_F32 nor MOBA_BF16 */
   MOBA_ERR_UNSUPPORTED = 5, /* valid MoBA problem outside this build's kernel limits */
@@ -64,10 +64,13 @@ typedef enum {
 } moba_status_t;
 
 /* One MoBA problem.
- *   block_size — tokens per key block ([R] §3.1, [P] §3.1). seq_len must be
- *                a multiple of it (the pages' code asserts the same, [R] §1.1).
+ *   block_size — tokens per key block ([R] §3.1, [P] §3.1). n_blocks =
+ *                ceil(seq_len / block_size): when seq_len is not a multiple
+ *                of it the last block holds the remaining tokens and its
+ *                summary covers only them ([S] §4 counts blocks with a
+ *                ceiling division; [R] §1.1's code asserts instead).
  *   top_k      — blocks each query attends, counting its own forced block
- *                ([P] §3.1, [S] §3). top_k > seq_len / block_size is clamped,
+ *                ([P] §3.1, [S] §3). top_k > n_blocks is clamped,
  *                so top_k >= the block count gives full attention.
  *   causal     — nonzero: only blocks before the query's own block may be
  *                chosen and the own block is causally masked ([P] §3.1
@@ -76,7 +79,7 @@ typedef enum {
  *   dtype      — moba_dtype_t of q, k, v and o. Arithmetic accumulates in
  *                fp32; o is rounded to the dtype (nearest, ties to even).
  * Kernel limits of this build (MOBA_ERR_UNSUPPORTED otherwise):
- *   head_dim in {64, 128}; block_size a multiple of 64;
+ *   head_dim in {64, 128}; block_size and seq_len multiples of 64;
  *   min(top_k, n_blocks) - 1 <= 16 unless top_k >= n_blocks;
  *   seq_len < 2^27; batch * heads * n_blocks < 2^31. */
 typedef struct {
@@ -123,6 +126,32 @@ int moba_workspace_size(const moba_problem_t* p, size_t* bytes);
 int moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
                  void* o, int32_t* block_idx, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/* Varlen batch: n_seqs independent sequences of different lengths in one
+ * call, each routed and attended on its own, blocks starting at its first
+ * token (the per-sequence cu_seqlens packing the pages describe for
+ * flash-attn, [R] §3.3).
+ *   cu_seqlens — HOST int64 [n_seqs + 1]: cu_seqlens[0] = 0 and sequence i
+ *                holds tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1; every
+ *                length must be >= 1 and meet the kernel limits above (a
+ *                multiple of 64; a short last block is allowed).
+ *   p          — heads, head_dim, block_size, top_k, causal, dtype and
+ *                pooling for every sequence; p->batch must equal n_seqs and
+ *                p->seq_len the total cu_seqlens[n_seqs] (both checked).
+ *   q, k, v, o — the sequences back to back, sequence i stored as
+ *                [heads, len_i, head_dim] contiguous from element
+ *                cu_seqlens[i] * heads * head_dim.
+ *   block_idx  — likewise, sequence i as [heads, len_i, top_k] from element
+ *                cu_seqlens[i] * heads * top_k.
+ *   workspace  — at least moba_workspace_size_varlen bytes; shared by the
+ *                sequences, which run one after another on the stream.
+ * Every sequence is validated before anything is launched; an error names
+ * the sequence. */
+int moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                               size_t* bytes);
+int moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                        const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Full softmax attention on the same layout (causal if p->causal), used to
  * measure MoBA's speedup over the method it approximates ([R] §1.2, [P] §1).

@@ -16,7 +16,8 @@ import torch
 from . import _lib
 from ._lib import (MOBA_BF16, MOBA_F32, moba_abi_version, moba_dense_forward, moba_forward,
                    moba_last_error, moba_pool, moba_problem_t, moba_select, moba_status_str,
-                   moba_timing_enable, moba_timing_read, moba_workspace_size)
+                   moba_timing_enable, moba_timing_read, moba_workspace_size,
+                   moba_forward_varlen, moba_workspace_size_varlen)
 
 __all__ = ["MobaError", "forward", "dense", "pool", "select", "problem", "workspace_bytes",
            "timing", "moba_abi_version", "moba_forward", "moba_dense_forward", "moba_pool",
@@ -102,6 +103,53 @@ def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None,
     return o, bi
 
 
+def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int, causal: bool = True,
+                   pooling: str = "mean"):
+    """MoBA over a varlen batch: sequences of different lengths back to back.
+
+    q, k, v: [sum_i heads * len_i, head_dim], sequence i's [heads, len_i,
+    head_dim] rows from row cu_seqlens[i] * heads (see pack_varlen).
+    cu_seqlens: host ints, cu_seqlens[0] = 0. Returns (o like q, block_idx
+    int32 [sum_i heads * len_i, top_k] in the same order)."""
+    if q.dim() != 2:
+        raise ValueError(f"q must be [tokens * heads, head_dim], got shape {tuple(q.shape)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k and v must be contiguous GPU tensors of one shape and dtype")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {q.dtype}")
+    if pooling not in POOLINGS:
+        raise ValueError(f"pooling must be one of {tuple(POOLINGS)}, got {pooling!r}")
+    cu = [int(x) for x in cu_seqlens]
+    if q.shape[0] != cu[-1] * heads:
+        raise ValueError(f"q has {q.shape[0]} rows, cu_seqlens and heads give {cu[-1] * heads}")
+    p = moba_problem_t(len(cu) - 1, int(heads), cu[-1], q.shape[1], int(block_size), int(top_k),
+                       1 if causal else 0, _DTYPES[q.dtype], POOLINGS[pooling], 0)
+    st, n = moba_workspace_size_varlen(p, cu)
+    _check(st, "moba_workspace_size_varlen")
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    bi = torch.empty((q.shape[0], int(top_k)), dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(moba_forward_varlen(p, cu, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), bi.data_ptr(),
+                                   ws.data_ptr(), n, _stream(q.device)), "moba_forward_varlen")
+    return o, bi
+
+
+def pack_varlen(seqs):
+    """[1, heads, len_i, D] tensors -> ([sum heads * len_i, D], cu_seqlens)."""
+    cu = [0]
+    for x in seqs:
+        cu.append(cu[-1] + x.shape[2])
+    return torch.cat([x.reshape(-1, x.shape[3]) for x in seqs]), cu
+
+
+def unpack_varlen(x, cu_seqlens, heads: int):
+    """Inverse of pack_varlen for an output (o or block_idx) of forward_varlen."""
+    return [x[cu_seqlens[i] * heads:cu_seqlens[i + 1] * heads].reshape(1, heads, cu_seqlens[i + 1] - cu_seqlens[i], -1)
+            for i in range(len(cu_seqlens) - 1)]
+
+
 def dense(q, k, v, causal: bool = True, out=None):
     """Full softmax attention (causal or not) with the library's dense kernel."""
     _tensors(q, k, v)
@@ -118,8 +166,8 @@ def pool(k, block_size: int, pooling: str = "mean"):
     _tensors(k)
     p = problem(k, block_size, 1, True, pooling)
     B, H, S, D = k.shape
-    kbar = torch.empty((B, H, S // block_size if block_size > 0 else 0, D), dtype=torch.float64,
-                       device=k.device)
+    nb = -(-S // block_size) if block_size > 0 else 0  # a short last block counts
+    kbar = torch.empty((B, H, nb, D), dtype=torch.float64, device=k.device)
     ws, n = _workspace(p, k.device)
     with torch.cuda.device(k.device):
         _check(moba_pool(p, k.data_ptr(), kbar.data_ptr(), ws.data_ptr(), n, _stream(k.device)),

@@ -20,6 +20,7 @@ STATUS_NAMES = {0: "MOBA_OK", 1: "MOBA_ERR_NULL", 2: "MOBA_ERR_SHAPE", 3: "MOBA_
                 7: "MOBA_ERR_DEVICE"}
 EXPORTED = ["moba_abi_version", "moba_status_str", "moba_last_error", "moba_workspace_size",
             "moba_forward", "moba_dense_forward", "moba_pool", "moba_select",
+            "moba_workspace_size_varlen", "moba_forward_varlen",
             "moba_timing_enable", "moba_timing_read"]
 
 
@@ -50,6 +51,10 @@ def _load():
         "moba_dense_forward": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
         "moba_pool": ([P, vp, vp, vp, sz, vp], ctypes.c_int),
         "moba_select": ([P, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
+        "moba_workspace_size_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                        ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+        "moba_forward_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, vp, vp, vp, vp, i32p, vp,
+                                 sz, vp], ctypes.c_int),
         "moba_timing_enable": ([ctypes.c_int], ctypes.c_int),
         "moba_timing_read": ([ctypes.POINTER(moba_kernel_time_t), ctypes.c_int,
                               ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
@@ -94,6 +99,31 @@ def moba_workspace_size(problem: moba_problem_t):
 def moba_forward(problem, q, k, v, o, block_idx, workspace, workspace_bytes, stream) -> int:
     return lib().moba_forward(ctypes.byref(problem) if problem is not None else None,
                             q, k, v, o, block_idx, workspace, workspace_bytes, stream)
+
+
+def _cu(cu_seqlens):
+    """Host int64 array for cu_seqlens (None stays NULL)."""
+    if cu_seqlens is None:
+        return None, 0
+    arr = (ctypes.c_int64 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+    return arr, len(cu_seqlens) - 1
+
+
+def moba_workspace_size_varlen(problem, cu_seqlens, n_seqs=None):
+    """-> (status, bytes); n_seqs defaults to len(cu_seqlens) - 1."""
+    arr, n = _cu(cu_seqlens)
+    out = ctypes.c_size_t(0)
+    st = lib().moba_workspace_size_varlen(ctypes.byref(problem) if problem is not None else None, arr,
+                                          n if n_seqs is None else n_seqs, ctypes.byref(out))
+    return st, out.value
+
+
+def moba_forward_varlen(problem, cu_seqlens, q, k, v, o, block_idx, workspace, workspace_bytes, stream,
+                        n_seqs=None) -> int:
+    arr, n = _cu(cu_seqlens)
+    return lib().moba_forward_varlen(ctypes.byref(problem) if problem is not None else None, arr,
+                                     n if n_seqs is None else n_seqs, q, k, v, o, block_idx, workspace,
+                                     workspace_bytes, stream)
 
 
 def moba_dense_forward(problem, q, k, v, o, stream) -> int:

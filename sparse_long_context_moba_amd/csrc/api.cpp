@@ -79,9 +79,6 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   const int64_t vals[] = {p->batch, p->heads, p->seq_len, p->head_dim, p->block_size};
   for (int i = 0; i < 5; ++i)
     if (vals[i] < 1) return fail(MOBA_ERR_SHAPE, std::string(names[i]) + " must be >= 1, got " + std::to_string(vals[i]));
-  if (p->seq_len % p->block_size != 0)
-    return fail(MOBA_ERR_SHAPE, "seq_len " + std::to_string(p->seq_len) + " is not a multiple of block_size " +
-                                    std::to_string(p->block_size));
   if (p->top_k < 1) return fail(MOBA_ERR_ARG, "top_k must be >= 1, got " + std::to_string(p->top_k));
   if (p->pooling != MOBA_POOL_MEAN && p->pooling != MOBA_POOL_MAX && p->pooling != MOBA_POOL_MEAN_MAX)
     return fail(MOBA_ERR_ARG, "pooling must be MOBA_POOL_MEAN (0), MOBA_POOL_MAX (1) or MOBA_POOL_MEAN_MAX (2), got " +
@@ -93,6 +90,8 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     return fail(MOBA_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " + std::to_string(p->head_dim));
   if (p->block_size % 64 != 0)
     return fail(MOBA_ERR_UNSUPPORTED, "block_size must be a multiple of 64, got " + std::to_string(p->block_size));
+  if (p->seq_len % 64 != 0)
+    return fail(MOBA_ERR_UNSUPPORTED, "seq_len must be a multiple of 64, got " + std::to_string(p->seq_len));
   if (p->seq_len >= (int64_t(1) << 27))
     return fail(MOBA_ERR_UNSUPPORTED, "seq_len must be below 2^27, got " + std::to_string(p->seq_len));
   Plan& P = *pl;
@@ -103,7 +102,7 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   P.Bs = p->block_size;
   P.top_k = p->top_k;
   P.bh = P.B * P.H;
-  P.nb = P.S / P.Bs;
+  P.nb = (P.S + P.Bs - 1) / P.Bs;  // a short last block holds the remainder
   P.k_eff = std::min(P.top_k, P.nb);
   P.slots = P.k_eff - 1;
   P.causal = p->causal != 0;
@@ -122,7 +121,7 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   int64_t per_head = 0;
   for (int64_t c = 0; c < P.nb; ++c) {
     const int64_t elig = P.causal ? c : P.nb - 1;
-    per_head += P.Bs * std::min(P.slots, elig);
+    per_head += std::min(P.Bs, P.S - c * P.Bs) * std::min(P.slots, elig);
   }
   P.pairs = per_head * P.bh;
   if (P.pairs >= (int64_t(1) << 31)) return fail(MOBA_ERR_UNSUPPORTED, "too many (query, block) pairs for int32 lists");
@@ -241,6 +240,82 @@ AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, v
 
 using namespace moba;
 
+namespace {
+int check_tensors(const void* q, const void* k, const void* v, const void* o, const int32_t* block_idx) {
+  if (!q) return fail(MOBA_ERR_NULL, "q is NULL");
+  if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
+  if (!v) return fail(MOBA_ERR_NULL, "v is NULL");
+  if (!o) return fail(MOBA_ERR_NULL, "o is NULL");
+  if (!block_idx) return fail(MOBA_ERR_NULL, "block_idx is NULL");
+  return MOBA_OK;
+}
+
+// The whole forward of one validated problem, queued on s.
+int run_forward(const Plan& P, const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
+                void* workspace, hipStream_t s) {
+  int st = run_select(P, q, k, block_idx, workspace, s, nullptr);
+  if (st != MOBA_OK) return st;
+  AttnArgs aa = attn_args(P, q, k, v, o);
+  aa.part_o = at<void>(workspace, P.part_o);
+  aa.part_lse = at<float>(workspace, P.part_lse);
+  if (P.pairs > 0) {
+    PackArgs pk{};
+    pk.bh = P.bh;
+    pk.seq_len = P.S;
+    pk.block_size = P.Bs;
+    pk.n_blocks = P.nb;
+    pk.causal = P.causal;
+    pk.top_k = (int)P.top_k;
+    pk.k_eff = (int)P.k_eff;
+    pk.tile_m = kGatherTileM;
+    pk.block_idx = block_idx;
+    pk.count = at<int32_t>(workspace, P.count);
+    pk.rank = at<int32_t>(workspace, P.rank);
+    pk.offset = at<int32_t>(workspace, P.offset);
+    pk.tile_start = at<int32_t>(workspace, P.tile_start);
+    pk.qlist = at<int32_t>(workspace, P.qlist);
+    pk.grid = gather_grid_for(P.max_tiles);
+    pk.tile_map = at<int32_t>(workspace, P.tile_map);
+    MOBA_TRY(launch_pack(pk, s), "pack launch");
+    aa.qlist = pk.qlist;
+    aa.tile_map = pk.tile_map;
+    aa.gather_grid = pk.grid;
+    MOBA_TRY(launch_gather(aa, s), "gather launch");
+  }
+  MOBA_TRY(launch_diag_merge(aa, s), "diag launch");
+  return MOBA_OK;
+}
+
+// Sequence i of a varlen batch as a [1, heads, len_i, head_dim] problem.
+int varlen_plans(const moba_problem_t* p, const int64_t* cu, int64_t n, std::vector<Plan>* plans) {
+  if (!p) return fail(MOBA_ERR_NULL, "problem pointer is NULL");
+  if (!cu) return fail(MOBA_ERR_NULL, "cu_seqlens is NULL");
+  if (n < 1) return fail(MOBA_ERR_ARG, "n_seqs must be >= 1, got " + std::to_string(n));
+  if (cu[0] != 0) return fail(MOBA_ERR_ARG, "cu_seqlens[0] must be 0, got " + std::to_string(cu[0]));
+  if (p->batch != n)
+    return fail(MOBA_ERR_ARG, "batch must equal n_seqs (" + std::to_string(n) + "), got " + std::to_string(p->batch));
+  if (p->seq_len != cu[n])
+    return fail(MOBA_ERR_ARG, "seq_len must equal cu_seqlens[n_seqs] (" + std::to_string(cu[n]) + "), got " +
+                                  std::to_string(p->seq_len));
+  plans->resize((size_t)n);
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t len = cu[i + 1] - cu[i];
+    if (len < 1)
+      return fail(MOBA_ERR_SHAPE, "sequence " + std::to_string(i) + " has length " + std::to_string(len) +
+                                      " (cu_seqlens must increase)");
+    moba_problem_t one = *p;
+    one.batch = 1;
+    one.seq_len = len;
+    const int st = plan_problem(&one, &(*plans)[(size_t)i], true);
+    if (st != MOBA_OK) {
+      g_err = "sequence " + std::to_string(i) + ": " + g_err;
+      return st;
+    }
+  }
+  return MOBA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int moba_abi_version(void) { return MOBA_ABI_VERSION; }
@@ -277,44 +352,53 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
   Plan P;
   int st = plan_problem(p, &P, true);
   if (st != MOBA_OK) return st;
-  if (!q) return fail(MOBA_ERR_NULL, "q is NULL");
-  if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
-  if (!v) return fail(MOBA_ERR_NULL, "v is NULL");
-  if (!o) return fail(MOBA_ERR_NULL, "o is NULL");
-  if (!block_idx) return fail(MOBA_ERR_NULL, "block_idx is NULL");
+  st = check_tensors(q, k, v, o, block_idx);
+  if (st != MOBA_OK) return st;
   st = check_ws(P, workspace, workspace_bytes);
   if (st != MOBA_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_select(P, q, k, block_idx, workspace, s, nullptr);
+  return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
+  std::vector<Plan> plans;
+  const int st = varlen_plans(p, cu_seqlens, n_seqs, &plans);
   if (st != MOBA_OK) return st;
-  AttnArgs aa = attn_args(P, q, k, v, o);
-  aa.part_o = at<void>(workspace, P.part_o);
-  aa.part_lse = at<float>(workspace, P.part_lse);
-  if (P.pairs > 0) {
-    PackArgs pk{};
-    pk.bh = P.bh;
-    pk.seq_len = P.S;
-    pk.block_size = P.Bs;
-    pk.n_blocks = P.nb;
-    pk.causal = P.causal;
-    pk.top_k = (int)P.top_k;
-    pk.k_eff = (int)P.k_eff;
-    pk.tile_m = kGatherTileM;
-    pk.block_idx = block_idx;
-    pk.count = at<int32_t>(workspace, P.count);
-    pk.rank = at<int32_t>(workspace, P.rank);
-    pk.offset = at<int32_t>(workspace, P.offset);
-    pk.tile_start = at<int32_t>(workspace, P.tile_start);
-    pk.qlist = at<int32_t>(workspace, P.qlist);
-    pk.grid = gather_grid_for(P.max_tiles);
-    pk.tile_map = at<int32_t>(workspace, P.tile_map);
-    MOBA_TRY(launch_pack(pk, s), "pack launch");
-    aa.qlist = pk.qlist;
-    aa.tile_map = pk.tile_map;
-    aa.gather_grid = pk.grid;
-    MOBA_TRY(launch_gather(aa, s), "gather launch");
+  size_t m = 0;
+  for (const Plan& P : plans) m = std::max(m, P.total);
+  *bytes = m;
+  return MOBA_OK;
+}
+
+int moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, const void* q,
+                        const void* k, const void* v, void* o, int32_t* block_idx, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  std::vector<Plan> plans;
+  int st = varlen_plans(p, cu_seqlens, n_seqs, &plans);
+  if (st != MOBA_OK) return st;
+  st = check_tensors(q, k, v, o, block_idx);
+  if (st != MOBA_OK) return st;
+  for (const Plan& P : plans) {
+    st = check_ws(P, workspace, workspace_bytes);
+    if (st != MOBA_OK) return st;
   }
-  MOBA_TRY(launch_diag_merge(aa, s), "diag launch");
+  // Every sequence is validated before the first launch; they then run in
+  // order on the one stream, sharing the workspace.
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = p->dtype == MOBA_BF16 ? 2 : 4;
+  const size_t row = (size_t)p->heads * (size_t)p->head_dim * esz;  // bytes per token of one sequence
+  for (int64_t i = 0; i < n_seqs; ++i) {
+    const size_t off = (size_t)cu_seqlens[i] * row;
+    st = run_forward(plans[(size_t)i], static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
+                     static_cast<const char*>(v) + off, static_cast<char*>(o) + off,
+                     block_idx + cu_seqlens[i] * p->heads * p->top_k, workspace, s);
+    if (st != MOBA_OK) {
+      g_err = "sequence " + std::to_string(i) + ": " + g_err;
+      return st;
+    }
+  }
   return MOBA_OK;
 }
 

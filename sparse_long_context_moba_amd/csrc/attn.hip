@@ -785,7 +785,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const T* kp = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + j * a.block_size) * D;
   const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + j * a.block_size) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
-  const int nsub = (int)(a.block_size / kSub);
+  // A short last block (seq_len not a multiple of block_size) has fewer subtiles.
+  const int nsub = (int)(min<int64_t>(a.block_size, a.seq_len - j * a.block_size) / kSub);
   if constexpr (E::kDMA) {
     stream_k_ahead<E, NT>(eng, bufA, bufB, kp, vp, nsub, tid, lane, wave_on, sl2, load_q);
   } else {
@@ -819,7 +820,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int q0 = (int)(tile * M);
   const int c = (int)(q0 / a.block_size);
   const int kb = DENSE ? 0 : (int)(c * a.block_size);
-  const int kend = a.causal ? q0 + M : (DENSE ? (int)a.seq_len : (int)(kb + a.block_size));
+  const int kend = a.causal ? q0 + M : (DENSE ? (int)a.seq_len : (int)min<int64_t>(kb + a.block_size, a.seq_len));
   const int qw0 = q0 + 32 * w;
   const int t = qw0 + col;
 
@@ -919,7 +920,7 @@ template <typename T, int D, bool DENSE>
 hipError_t diag_t(const AttnArgs& a, hipStream_t s) {
   using E = typename EngOf<T, D>::type;
   // 128-query tiles when they stay inside one block (and one sequence), else 64.
-  const bool four = DENSE ? (a.seq_len % 128 == 0) : (a.block_size % 128 == 0);
+  const bool four = a.seq_len % 128 == 0 && (DENSE || a.block_size % 128 == 0);
   const char* name = DENSE ? "dense_attn" : "diag_merge";
   constexpr int lds = dyn_lds_bytes<E>();
   if (four) {

@@ -34,9 +34,12 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ double sq[D];
   const int tid = threadIdx.x;
   const int rg = tid / TPR, cv = tid % TPR;
-  const int64_t blk = blockIdx.x;  // bh * n_blocks + j: rows blk * block_size ..
-  const int Bs = (int)a.block_size;
-  const T* base = reinterpret_cast<const T*>(a.k) + blk * a.block_size * D + cv * VEC;
+  const int64_t blk = blockIdx.x;  // bh * n_blocks + j
+  const int64_t nb = (a.seq_len + a.block_size - 1) / a.block_size;
+  const int64_t bh = blk / nb, j = blk % nb;
+  // Rows of block j; a short last block holds the remaining tokens.
+  const int Bs = (int)min<int64_t>(a.block_size, a.seq_len - j * a.block_size);
+  const T* base = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + j * a.block_size) * D + cv * VEC;
   double acc[VEC];
   float mx[VEC];
 #pragma unroll
@@ -109,10 +112,12 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 template <typename T, int D>
 static hipError_t pool_launch_t(const PoolArgs& a, hipStream_t s) {
   constexpr int RG = 256 / (D / (16 / (int)sizeof(T)));
-  const int64_t nblk = a.bh * (a.seq_len / a.block_size);
+  const int64_t nb = (a.seq_len + a.block_size - 1) / a.block_size;
+  const int64_t nblk = a.bh * nb;
+  const int64_t last = a.seq_len - (nb - 1) * a.block_size;  // rows of the last block
   // block_size is a multiple of 64, so the rows per thread are a multiple of
   // 64 / RG >= 2; use 4 loads in flight where they divide evenly.
-  const bool four = (a.block_size / RG) % 4 == 0;
+  const bool four = (a.block_size / RG) % 4 == 0 && (last / RG) % 4 == 0;
   KernelTimer t(s, "pool");
   const dim3 grid((unsigned)nblk);
   switch (a.pooling * 2 + (four ? 1 : 0)) {

@@ -64,6 +64,10 @@ WORKLOADS["headline_32k_max"] = Workload("headline_32k_max", 1, 32, 32768, 128, 
 WORKLOADS["headline_32k_meanmax"] = Workload("headline_32k_meanmax", 1, 32, 32768, 128, 512, 3, True, "bf16", 1,
                                              "mean+max")
 POOLING_VARIANTS = ["headline_32k_max", "headline_32k_meanmax"]
+# 32768 + 256 tokens: 65 blocks of 512, the last one holding 256.
+WORKLOADS["headline_33k_short_block"] = Workload("headline_33k_short_block", 1, 32, 33024, 128, 512, 3, True,
+                                                 "bf16", 5)
+SHAPE_VARIANTS = ["headline_33k_short_block"]
 
 
 def _rng(seed: int, tensor: int, b: int, h: int) -> np.random.Generator:
@@ -153,7 +157,7 @@ def sample_rows(w: Workload, n: int = 4096) -> np.ndarray:
     """
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, ROW_SAMPLE_STREAM])))
     Bs, S = w.block_size, w.seq_len
-    edges_t = sorted({0, Bs - 1, min(Bs, S - 1), S - Bs, S - 1})
+    edges_t = sorted({0, Bs - 1, min(Bs, S - 1), (w.n_blocks - 1) * Bs, S - 1})
     forced = []
     for b in {0, w.batch - 1}:
         for h in {0, w.heads - 1}:

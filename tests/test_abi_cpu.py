@@ -52,7 +52,7 @@ FAKE = 0x1000  # never dereferenced: validation fails or stops before any launch
     (dict(seq_len=0), 2, "seq_len"),
     (dict(head_dim=0), 2, "head_dim"),
     (dict(block_size=0), 2, "block_size"),
-    (dict(seq_len=1000), 2, "multiple"),
+    (dict(seq_len=1000), 5, "multiple of 64"),
     (dict(top_k=0), 3, "top_k"),
     (dict(pooling=3), 3, "pooling"),
     (dict(pooling=-1), 3, "pooling"),
@@ -109,3 +109,41 @@ def test_workspace_of_named_workloads_fits_hbm():
         st, n = _lib.moba_workspace_size(p)
         assert st == 0, _lib.moba_last_error()
         assert 0 < n < 64 << 30, (name, n)
+
+
+def test_short_last_block_is_accepted():
+    """seq_len need not be a multiple of block_size (the last block is
+    short); the kernels only need multiples of 64."""
+    from sparse_long_context_moba_amd import _lib
+    st, n = _lib.moba_workspace_size(_p(seq_len=1216, block_size=256))
+    assert st == 0 and n > 0, _lib.moba_last_error()
+
+
+def test_varlen_validation_and_workspace():
+    from sparse_long_context_moba_amd import _lib
+    cu = [0, 576, 1600, 1792]
+    p = _p(batch=3, seq_len=1792, block_size=128)
+    st, need = _lib.moba_workspace_size_varlen(p, cu)
+    assert st == 0, _lib.moba_last_error()
+    per = [_lib.moba_workspace_size(_p(batch=1, seq_len=b - a, block_size=128))[1] for a, b in zip(cu, cu[1:])]
+    assert need == max(per)
+    cases = [
+        (dict(cu=None), 1, "cu_seqlens"),
+        (dict(cu=[1, 576, 1600, 1792]), 3, "cu_seqlens[0]"),
+        (dict(p=_p(batch=2, seq_len=1792, block_size=128)), 3, "batch"),
+        (dict(p=_p(batch=3, seq_len=1700, block_size=128)), 3, "seq_len"),
+        (dict(cu=[0, 600, 1600, 1792], p=_p(batch=3, seq_len=1792, block_size=128)), 5, "sequence 0"),
+        (dict(cu=[0, 576, 576, 1792]), 2, "sequence 1"),
+    ]
+    for kw, code, word in cases:
+        c = kw.get("cu", cu)
+        pp = kw.get("p", p)
+        st, _ = _lib.moba_workspace_size_varlen(pp, c, None if c is not None else 3)
+        assert st == code, (kw, _lib.moba_last_error())
+        assert word in _lib.moba_last_error(), (kw, _lib.moba_last_error())
+        st = _lib.moba_forward_varlen(pp, c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None,
+                                      n_seqs=None if c is not None else 3)
+        assert st == code
+    # too small a workspace is rejected before any launch
+    assert _lib.moba_forward_varlen(p, cu, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 6
+    assert _lib.moba_forward_varlen(p, cu, None, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1

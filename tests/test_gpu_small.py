@@ -23,7 +23,8 @@ def _inputs(seed, B, H, S, D, Bs, dtype, bias=0.5):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, H, S, D)).astype(np.float32)
     k = rng.standard_normal((B, H, S, D)).astype(np.float32)
-    k += np.repeat(rng.normal(0, bias, (B, H, S // Bs, D)).astype(np.float32), Bs, axis=2)
+    nb = -(-S // Bs)
+    k += np.repeat(rng.normal(0, bias, (B, H, nb, D)).astype(np.float32), Bs, axis=2)[:, :, :S]
     v = rng.standard_normal((B, H, S, D)).astype(np.float32)
     return _round(q, dtype), _round(k, dtype), _round(v, dtype)
 
@@ -60,6 +61,12 @@ CASES = [
     ("bf16-d128-bs256-k3-noncausal", 8, 1, 2, 1024, 128, 256, 3, False, "bf16"),
     ("f32-d64-bs64-k8-noncausal", 9, 1, 1, 1024, 64, 64, 8, False, "f32"),
     ("bf16-d128-single-block", 10, 1, 2, 512, 128, 512, 3, True, "bf16"),
+    # seq_len not a multiple of block_size: a short last block
+    ("bf16-d128-bs256-short192", 21, 1, 2, 1216, 128, 256, 3, True, "bf16"),
+    ("bf16-d128-bs512-short256-noncausal", 22, 1, 2, 1280, 128, 512, 3, False, "bf16"),
+    ("f32-d64-bs128-short64-k4", 23, 1, 1, 576, 64, 128, 4, True, "f32"),
+    ("bf16-d64-bs192-short128-noncausal", 24, 1, 2, 704, 64, 192, 2, False, "bf16"),
+    ("bf16-d64-bs128-short64-topk-all", 25, 1, 1, 704, 64, 128, 9, True, "bf16"),
 ]
 
 
@@ -133,6 +140,7 @@ POOL_CASES = [
     # label, seed, B, H, S, D, Bs, top_k, causal, dtype
     ("bf16-d128-bs64-k3", 15, 1, 2, 1024, 128, 64, 3, True, "bf16"),
     ("f32-d64-bs128-k4-noncausal", 16, 1, 2, 1024, 64, 128, 4, False, "f32"),
+    ("bf16-d128-bs256-short192", 18, 1, 2, 1216, 128, 256, 3, True, "bf16"),
 ]
 
 
@@ -151,9 +159,10 @@ def test_stage_pool_variants(dtype):
     """The pool stage for each summary: the max is exact (a comparison of
     input values), the mean and mean+max agree with fp64 to rounding."""
     import sparse_long_context_moba_amd as moba
-    q, k, v = _inputs(17, 1, 2, 1024, 64, 128, dtype)
+    q, k, v = _inputs(17, 1, 2, 1088, 64, 128, dtype)  # 9 blocks, the last of 64 tokens
     for pooling in ("mean", "max", "mean+max"):
         kb = moba.pool(to_dev(k, dtype), 128, pooling).cpu().numpy()
+        assert kb.shape[2] == 9
         for h in range(2):
             ref = orc.pool_keys(k[0, h], 128, pooling)
             if pooling == "max":
@@ -218,3 +227,41 @@ def test_errors_raise_and_leave_outputs():
         moba.forward(qd, kd, vd, 64, 0, out=out, idx=idx)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all()) and bool((idx == 9).all())
+
+
+VARLEN_CASES = [
+    # label, seed, H, D, Bs, top_k, causal, dtype, lengths
+    ("bf16-d128-bs128-causal", 30, 2, 128, 128, 3, True, "bf16", [576, 1024, 192]),
+    ("f32-d64-bs256-noncausal", 31, 1, 64, 256, 2, False, "f32", [512, 64, 1344]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
+def test_varlen_batch(case):
+    """A varlen batch: every sequence routed and attended on its own (blocks
+    start at its first token), every row against the oracle for that
+    sequence alone, and bit-identical to one forward per sequence."""
+    import sparse_long_context_moba_amd as moba
+    label, seed, H, D, Bs, top_k, causal, dtype, lengths = case
+    seqs = [_inputs(seed + i, 1, H, n, D, Bs, dtype) for i, n in enumerate(lengths)]
+    dev = [[to_dev(x, dtype) for x in s] for s in seqs]
+    qp, cu = moba.pack_varlen([d[0] for d in dev])
+    kp, _ = moba.pack_varlen([d[1] for d in dev])
+    vp, _ = moba.pack_varlen([d[2] for d in dev])
+    say(f"[gpu] varlen {label}: lengths={lengths} cu={cu}")
+    o, idx = moba.forward_varlen(qp, kp, vp, cu, H, Bs, top_k, causal)
+    torch.cuda.synchronize()
+    os_ = moba.unpack_varlen(o, cu, H)
+    is_ = moba.unpack_varlen(idx, cu, H)
+    for i, ((q, k, v), d) in enumerate(zip(seqs, dev)):
+        o1, i1 = moba.forward(d[0], d[1], d[2], Bs, top_k, causal)
+        assert torch.equal(is_[i], i1), f"sequence {i}: indices differ from a single-sequence forward"
+        bits = torch.int16 if dtype == "bf16" else torch.int32
+        assert torch.equal(os_[i].contiguous().view(bits), o1.view(bits)), f"sequence {i}: outputs differ"
+        og = os_[i].float().cpu().numpy()
+        ig = is_[i].cpu().numpy()
+        for h in range(H):
+            res = orc.forward_head(q[0, h], k[0, h], v[0, h], Bs, top_k, causal)
+            check_rows(og[0, h], ig[0, h], res, np.arange(lengths[i]), q[0, h], k[0, h], v[0, h], Bs, top_k,
+                       causal, dtype, label=f"{label} seq={i} h={h}")
+    say(f"[gpu] varlen {label}: ok")

@@ -103,6 +103,10 @@ def test_headline_32k_meanmax_pooling_sampled():
     _run("headline_32k_meanmax")
 
 
+def test_headline_short_last_block_sampled():
+    _run("headline_33k_short_block")
+
+
 def test_coarse_32k_sampled():
     _run("coarse_32k")
 
