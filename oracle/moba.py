@@ -217,6 +217,42 @@ def forward_head(q, k, v, block_size: int, top_k: int, causal: bool = True, rows
     return {"o": o, "idx": idx, "flag": flag, "a": a, "b": b, "kbar": kbar}
 
 
+def forward_group(q, k, v, block_size: int, top_k: int, causal: bool = True, rows=None, pooling: str = "mean",
+                  shared_gate: bool = False):
+    """The query heads q [G, S, D] that read one key/value head k, v [S, D]
+    (grouped-query attention; G = 1 is plain multi-head attention).
+
+    Without a shared gate every query head routes on its own (forward_head
+    with the group's K and V). With a shared gate the group routes once: a
+    block's score is the sum over the group's heads of q_h . Kbar, i.e. the
+    summed query against the pooled key, and every head attends the blocks
+    that choice keeps ([R] §3.2 asks whether the gate is per head or shared
+    across heads and leaves it open; the sum is the plainest shared score).
+    Returns one forward_head-style dict per query head.
+    """
+    q = np.asarray(q)
+    G = q.shape[0]
+    if not shared_gate:
+        return [forward_head(q[g], k, v, block_size, top_k, causal, rows=rows, pooling=pooling) for g in range(G)]
+    S, D = q.shape[1:]
+    if top_k < 1:
+        raise ValueError(f"top_k must be >= 1, got {top_k}")
+    kbar = pool_keys(k, block_size, pooling)
+    qs = np.asarray(q, dtype=np.float64).sum(axis=0)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = [{"o": np.zeros((len(rows), D)), "idx": np.zeros((len(rows), top_k), np.int64),
+            "flag": np.zeros(len(rows), bool), "a": np.full(len(rows), np.nan), "b": np.full(len(rows), np.nan),
+            "kbar": kbar} for _ in range(G)]
+    for r, t in enumerate(rows):
+        c = int(t) // block_size
+        idx, flag, a, b = select_blocks(qs[t], kbar, c, top_k, causal)
+        keys = attended_keys(int(t), idx, block_size, causal, S)
+        for g in range(G):
+            out[g]["idx"][r], out[g]["flag"][r], out[g]["a"][r], out[g]["b"][r] = idx, flag, a, b
+            out[g]["o"][r] = attend(q[g][t], k, v, keys)
+    return out
+
+
 def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, pooling: str = "mean"):
     """Full MoBA forward over [B, H, S, D]. Returns (o float64, idx int64)."""
     B, H, S, D = q.shape

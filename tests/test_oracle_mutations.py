@@ -29,6 +29,10 @@ def _pins():
     for causal in (True, False):
         yield f"short_block_dense[{causal}]", lambda c=causal: pins.test_short_last_block_matches_masked_dense_softmax(c)
     yield "short_block_earlier_rows", pins.test_short_last_block_leaves_earlier_rows_alone
+    yield "group_per_head", pins.test_group_without_shared_gate_is_per_head
+    for causal in (True, False):
+        yield f"shared_gate_bruteforce[{causal}]", lambda c=causal: pins.test_shared_gate_matches_subset_bruteforce(c)
+    yield "shared_gate_special", pins.test_shared_gate_special_cases
     for seed in range(6):
         for causal in (True, False):
             yield f"subset_bruteforce[{seed},{causal}]", (
@@ -102,6 +106,31 @@ def pool_short_block_over_block_size(k, block_size, pooling="mean"):
     if pooling == "mean" and L < block_size:
         out[-1] *= L / block_size
     return out
+
+
+_orig_group = moba.forward_group
+
+
+def shared_gate_first_head(q, k, v, block_size, top_k, causal=True, rows=None, pooling="mean", shared_gate=False):
+    # the shared choice taken from the first head's query alone
+    if not shared_gate:
+        return _orig_group(q, k, v, block_size, top_k, causal, rows, pooling, False)
+    q = np.asarray(q)
+    lead = _orig_group(q[:1], k, v, block_size, top_k, causal, rows, pooling, True)[0]
+    out = []
+    for g in range(q.shape[0]):
+        r = dict(lead)
+        keys_rows = rows if rows is not None else np.arange(q.shape[1])
+        r["o"] = np.array([moba.attend(q[g][t], k, v, moba.attended_keys(int(t), lead["idx"][i], block_size, causal,
+                                                                            q.shape[1]))
+                           for i, t in enumerate(keys_rows)])
+        out.append(r)
+    return out
+
+
+def shared_gate_ignored(q, k, v, block_size, top_k, causal=True, rows=None, pooling="mean", shared_gate=False):
+    # every head routes on its own even when the gate is shared
+    return _orig_group(q, k, v, block_size, top_k, causal, rows, pooling, False)
 
 
 def pool_max_is_min(k, block_size, pooling="mean"):
@@ -205,6 +234,8 @@ MUTATIONS = [
     ("pool_keys", pool_first_key_only),
     ("pool_keys", pool_max_is_min),
     ("num_blocks", num_blocks_floor),
+    ("forward_group", shared_gate_first_head),
+    ("forward_group", shared_gate_ignored),
     ("pool_keys", pool_short_block_over_block_size),
     ("pool_keys", pool_max_over_dims),
     ("pool_keys", pool_combined_is_max),

@@ -408,3 +408,64 @@ def test_sample_rows_contains_edges():
     s = {tuple(r) for r in rows}
     for t in [0, 511, 512, 32767, 32768 - 512]:
         assert (0, 0, t) in s and (0, 31, t) in s
+
+
+# --------------------------------------------------- grouped heads, shared gate
+def test_group_without_shared_gate_is_per_head():
+    S, D, Bs = 64, 8, 8
+    rng = np.random.default_rng(51)
+    q = rng.standard_normal((3, S, D))
+    _, k, v = _rand_head(51, S, D, Bs)
+    out = moba.forward_group(q, k, v, Bs, 3, True)
+    for g in range(3):
+        ref = moba.forward_head(q[g], k, v, Bs, 3, True)
+        np.testing.assert_array_equal(out[g]["idx"], ref["idx"])
+        np.testing.assert_array_equal(out[g]["o"], ref["o"])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_shared_gate_matches_subset_bruteforce(causal):
+    """The shared choice maximises the group's total score: enumerate every
+    (k-1)-subset of eligible blocks and sum q_h . Kbar_j over heads and
+    blocks term by term."""
+    S, D, Bs, top_k, G = 48, 4, 8, 3, 3
+    rng = np.random.default_rng(53)
+    q = rng.standard_normal((G, S, D))
+    _, k, v = _rand_head(53, S, D, Bs)
+    out = moba.forward_group(q, k, v, Bs, top_k, causal, shared_gate=True)
+    kbar = k.reshape(S // Bs, Bs, D).mean(axis=1)
+    for t in range(S):
+        c = t // Bs
+        elig = [j for j in range(S // Bs) if (j < c if causal else j != c)]
+        m = min(top_k - 1, len(elig))
+        best, best_set = None, None
+        for sub in itertools.combinations(elig, m):
+            tot = sum(float(q[g, t] @ kbar[j]) for g in range(G) for j in sub)
+            if best is None or tot > best + 1e-12:
+                best, best_set = tot, sub
+        want = sorted(set(best_set) | {c})
+        for g in range(G):
+            assert [int(x) for x in out[g]["idx"][t] if x >= 0] == want, (t, g)
+
+
+def test_shared_gate_special_cases():
+    """One head: the shared gate is the head's own. Identical heads: the
+    summed query is a positive multiple of each, so the choice is each
+    head's own. Every head attends with its own query."""
+    S, D, Bs = 64, 8, 8
+    rng = np.random.default_rng(55)
+    q1 = rng.standard_normal((1, S, D))
+    _, k, v = _rand_head(55, S, D, Bs)
+    one = moba.forward_group(q1, k, v, Bs, 3, True, shared_gate=True)[0]
+    ref = moba.forward_head(q1[0], k, v, Bs, 3, True)
+    np.testing.assert_array_equal(one["idx"], ref["idx"])
+    np.testing.assert_allclose(one["o"], ref["o"], atol=1e-12)
+    same = np.repeat(q1, 4, axis=0)
+    out = moba.forward_group(same, k, v, Bs, 3, True, shared_gate=True)
+    for g in range(4):
+        np.testing.assert_array_equal(out[g]["idx"], ref["idx"])
+    # top_k >= n_blocks: every head gets full causal attention with its own query
+    q3 = rng.standard_normal((3, S, D))
+    full = moba.forward_group(q3, k, v, Bs, 8, True, shared_gate=True)
+    for g in range(3):
+        np.testing.assert_allclose(full[g]["o"], _sdpa(q3[g], k, v, causal=True), atol=1e-12)
