@@ -40,8 +40,12 @@ def log(msg):
 def work_model(w):
     """Algorithmic work of one forward, counted from MoBA's definition:
     gate 2*D flops per (query, eligible past block); attention 4*D flops per
-    (query, attended key), split into past blocks and the own block."""
+    (query, attended key), split into past blocks and the own block. A gate
+    shared by a group of query heads scores the group's summed query once
+    per (query position, block); pooling reads K once per key/value head."""
     S, D, Bs, nb, bh = w.seq_len, w.head_dim, w.block_size, w.n_blocks, w.batch * w.heads
+    bhkv = w.batch * w.kvh
+    gate_rows = bhkv if w.gate_shared else bh
     k_eff = min(w.top_k, nb)
     gate_pairs = past_pairs = own_keys = 0
     for c in range(nb):
@@ -53,27 +57,27 @@ def work_model(w):
     dense_keys = S * (S + 1) // 2 if w.causal else S * S
     esz = 2 if w.dtype == "bf16" else 4
     return {
-        "gate_flops": bh * 2 * D * gate_pairs,
+        "gate_flops": gate_rows * 2 * D * gate_pairs,
         "past_flops": bh * 4 * D * past_pairs * Bs,
         "own_flops": bh * 4 * D * own_keys,
         "dense_flops": bh * 4 * D * dense_keys,
         "past_pairs": bh * past_pairs,
         "attended_keys": bh * (past_pairs * Bs + own_keys),
         "dense_keys": bh * dense_keys,
-        "k_bytes": bh * S * D * esz,
-        "qkvo_bytes": 4 * bh * S * D * esz,
+        "k_bytes": bhkv * S * D * esz,
+        "qkvo_bytes": 2 * (bh + bhkv) * S * D * esz,
     }
 
 
 def kernel_units(w, wm):
     """(bound, algorithmic work per launch, unit) for each library kernel."""
-    D, bh, nb = w.head_dim, w.batch * w.heads, w.n_blocks
+    D, bhkv, nb = w.head_dim, w.batch * w.kvh, w.n_blocks
     return {
         "gather_attn": ("mfma", wm["past_flops"], "flop"),
         "diag_merge": ("mfma", wm["own_flops"], "flop"),
         "gate_topk": ("mfma", wm["gate_flops"], "flop"),
         # K read once; the pooled keys written as fp64, fp32 and a bf16 pair.
-        "pool": ("hbm", wm["k_bytes"] + bh * nb * D * (8 + 4 + 2 + 2), "byte"),
+        "pool": ("hbm", wm["k_bytes"] + bhkv * nb * D * (8 + 4 + 2 + 2), "byte"),
         "dense_attn": ("mfma", wm["dense_flops"], "flop"),
     }
 
@@ -109,15 +113,19 @@ def measured_traffic(kernel, workload):
 
 
 def upload(w, torch, workers=None):
-    shape = (w.batch, w.heads, w.seq_len, w.head_dim)
+    """q [B, H, S, D] and k, v [B, kv_heads, S, D], generated per key/value
+    head and its group of query heads."""
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    dev = [torch.empty(shape, dtype=tdt, device="cuda") for _ in range(3)]
-    for b, h, q, k, v in synth.iter_heads_parallel(w, workers):
-        for i, x in enumerate((q, k, v)):
-            t = torch.from_numpy(x)
-            dev[i][b, h].copy_(t.view(torch.bfloat16) if w.dtype == "bf16" else t)
+    G = w.group
+    q = torch.empty((w.batch, w.heads, w.seq_len, w.head_dim), dtype=tdt, device="cuda")
+    k, v = (torch.empty((w.batch, w.kvh, w.seq_len, w.head_dim), dtype=tdt, device="cuda") for _ in range(2))
+    cast = (lambda t: t.view(torch.bfloat16)) if w.dtype == "bf16" else (lambda t: t)
+    for b, hk, qh, kh, vh in synth.iter_groups_parallel(w, workers):
+        q[b, hk * G:(hk + 1) * G].copy_(cast(torch.from_numpy(qh)))
+        k[b, hk].copy_(cast(torch.from_numpy(kh)))
+        v[b, hk].copy_(cast(torch.from_numpy(vh)))
     torch.cuda.synchronize()
-    return dev
+    return q, k, v
 
 
 def cpu_baseline(w, n_rows):
@@ -151,7 +159,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER + synth.POOLING_VARIANTS + synth.SHAPE_VARIANTS)
+    ap.add_argument("--workload", default="headline_32k", choices=synth.WORKLOAD_ORDER + synth.POOLING_VARIANTS + synth.SHAPE_VARIANTS
+                    + synth.GQA_VARIANTS)
     ap.add_argument("--dense-steps", type=int, default=2, help="timed dense causal forwards (0 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=65536, help="oracle sample size (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -176,13 +185,14 @@ def main():
     t0 = time.time()
     q, k, v = upload(w, torch, args.gen_workers)
     log(f"inputs resident in HBM after {time.time() - t0:.1f}s")
-    p = moba.problem(q, w.block_size, w.top_k, w.causal, w.pooling)
+    p = moba.problem(q, w.block_size, w.top_k, w.causal, w.pooling, w.kvh, w.gate_shared)
     ws = torch.empty(moba.workspace_bytes(p), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     idx = torch.empty((w.batch, w.heads, w.seq_len, w.top_k), dtype=torch.int32, device="cuda")
 
     def step():
-        moba.forward(q, k, v, w.block_size, w.top_k, w.causal, out=o, idx=idx, workspace=ws, pooling=w.pooling)
+        moba.forward(q, k, v, w.block_size, w.top_k, w.causal, out=o, idx=idx, workspace=ws, pooling=w.pooling,
+                     gate_shared=w.gate_shared)
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
@@ -267,7 +277,8 @@ def main():
         "data": "synthetic (seeded q, v ~ N(0,1); k ~ N(0,1) + per-block N(0, 0.5^2) bias)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
                    "head_dim": w.head_dim, "block_size": w.block_size, "top_k": w.top_k,
-                   "causal": w.causal, "pooling": w.pooling, "parallelism": "single GPU"},
+                   "causal": w.causal, "pooling": w.pooling, "kv_heads": w.kvh, "gate_shared": w.gate_shared,
+                   "parallelism": "single GPU"},
         "effective_tflops": round(eff_tflops, 2),
         "pct_peak": round(100 * eff_tflops / peak, 2),
         "attn_gate_kernels_pct_peak": round(100 * attn_gate_frac, 2),

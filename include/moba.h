@@ -13,7 +13,9 @@
  *   [S] MOBA serving article, first heading «长上下文推理为什么卡在注意力这一步» (hncyxsy.com)
  *
  * Conventions for every entry point:
- *   - Tensors q, k, v, o are [batch, heads, seq_len, head_dim], contiguous,
+ *   - Tensors q and o are [batch, heads, seq_len, head_dim]; k and v are
+ *     [batch, kv_heads, seq_len, head_dim] (kv_heads = heads unless the
+ *     problem says otherwise, see moba_problem_t). All are contiguous,
  *     row-major, in device memory, of the problem's dtype (fp32 or bf16).
  *   - block_idx is int32 [batch, heads, seq_len, top_k] in device memory.
  *   - The caller owns every buffer, including the workspace; the library
@@ -40,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 2
+#define MOBA_ABI_VERSION 3
 
 typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype_t;
 
@@ -55,8 +57,8 @@ typedef enum { MOBA_POOL_MEAN = 0, MOBA_POOL_MAX = 1, MOBA_POOL_MEAN_MAX = 2 } m
 typedef enum {
   MOBA_OK = 0,
   MOBA_ERR_NULL = 1,        /* a required pointer is NULL */
-  MOBA_ERR_SHAPE = 2,       /* non-positive size */
-  MOBA_ERR_ARG = 3,         /* top_k < 1, pooling unknown, reserved != 0 */
+  MOBA_ERR_SHAPE = 2,       /* non-positive size; heads not a multiple of kv_heads */
+  MOBA_ERR_ARG = 3,         /* top_k < 1, pooling unknown, a reserved field != 0 */
   MOBA_ERR_DTYPE = 4,       /* dtype is neither MOBA_F32 nor MOBA_BF16 */
   MOBA_ERR_UNSUPPORTED = 5, /* valid MoBA problem outside this build's kernel limits */
   MOBA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moba_workspace_size */
@@ -78,6 +80,20 @@ typedef enum {
  *                eligible and no mask is applied inside blocks.
  *   dtype      — moba_dtype_t of q, k, v and o. Arithmetic accumulates in
  *                fp32; o is rounded to the dtype (nearest, ties to even).
+ *   kv_heads   — key/value heads (grouped-query attention): query head h
+ *                reads key/value head h / (heads / kv_heads), so heads must
+ *                be a multiple of it. 0 means kv_heads = heads (plain
+ *                multi-head attention). The block summaries are pooled
+ *                once per key/value head.
+ *   gate_shared— zero: every query head routes on its own scores. Nonzero:
+ *                the query heads of one key/value head route together on
+ *                the sum of their scores, sum_h q_h . kbar_j (the same as
+ *                the summed query against the pooled key), and all of them
+ *                attend the blocks that choice keeps, each with its own
+ *                query. ([R] §3.2 asks whether the gate is per head or
+ *                shared across heads and leaves it open; the sum is the
+ *                plain shared score.) block_idx then repeats the group's
+ *                choice in each of its query heads' rows.
  * Kernel limits of this build (MOBA_ERR_UNSUPPORTED otherwise):
  *   head_dim in {64, 128}; block_size and seq_len multiples of 64;
  *   min(top_k, n_blocks) - 1 <= 16 unless top_k >= n_blocks;
@@ -93,6 +109,9 @@ typedef struct {
   int32_t dtype;
   int32_t pooling;  /* moba_pooling_t; a zeroed field selects the mean */
   int32_t reserved; /* must be 0 */
+  int64_t kv_heads; /* 0 = heads; otherwise a divisor of heads */
+  int32_t gate_shared; /* 0 = per-head gate */
+  int32_t reserved2;   /* must be 0 */
 } moba_problem_t;
 
 /* MOBA_ABI_VERSION of the loaded library. */
@@ -135,12 +154,14 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
  *                holds tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1; every
  *                length must be >= 1 and meet the kernel limits above (a
  *                multiple of 64; a short last block is allowed).
- *   p          — heads, head_dim, block_size, top_k, causal, dtype and
- *                pooling for every sequence; p->batch must equal n_seqs and
+ *   p          — heads, kv_heads, head_dim, block_size, top_k, causal,
+ *                dtype, pooling and gate_shared for every sequence; p->batch must equal n_seqs and
  *                p->seq_len the total cu_seqlens[n_seqs] (both checked).
- *   q, k, v, o — the sequences back to back, sequence i stored as
+ *   q, o       — the sequences back to back, sequence i stored as
  *                [heads, len_i, head_dim] contiguous from element
  *                cu_seqlens[i] * heads * head_dim.
+ *   k, v       — likewise with kv_heads: sequence i as [kv_heads, len_i,
+ *                head_dim] from element cu_seqlens[i] * kv_heads * head_dim.
  *   block_idx  — likewise, sequence i as [heads, len_i, top_k] from element
  *                cu_seqlens[i] * heads * top_k.
  *   workspace  — at least moba_workspace_size_varlen bytes; shared by the
@@ -162,7 +183,7 @@ int moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, co
 
 /* Stage entry point: block pooling only ([P] §3.1 mean_pool; p->pooling
  * selects the summary as for moba_forward).
- * kbar: device float64 [batch, heads, n_blocks, head_dim] — the pooled keys
+ * kbar: device float64 [batch, kv_heads, n_blocks, head_dim] — the pooled keys
  * the gate uses. Uses the forward's workspace. */
 int moba_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace,
               size_t workspace_bytes, void* stream);

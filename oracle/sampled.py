@@ -20,11 +20,21 @@ def _head_rows(args):
     w, b, h, ts = args
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     t0 = time.perf_counter()
-    q, k, v = synth.make_head(w.seed, b, h, w.seq_len, w.head_dim, w.block_size, w.dtype)
+    G = w.group
+    hk = h // G
+    k, v = synth.make_kv(w.seed, b, hk, w.seq_len, w.head_dim, w.block_size, w.dtype)
+    if w.gate_shared and G > 1:
+        qs = np.stack([synth.make_q(w.seed, b, hk * G + g, w.seq_len, w.head_dim, w.dtype) for g in range(G)])
+    else:
+        qs = synth.make_q(w.seed, b, h, w.seq_len, w.head_dim, w.dtype)[None]
     t1 = time.perf_counter()
     moba.pool_keys(k, w.block_size, w.pooling)
     t2 = time.perf_counter()
-    res = moba.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=ts, pooling=w.pooling)
+    if len(qs) > 1:  # the group routes together; only head h's rows are kept
+        res = moba.forward_group(qs, k, v, w.block_size, w.top_k, w.causal, rows=ts, pooling=w.pooling,
+                                 shared_gate=True)[h % G]
+    else:
+        res = moba.forward_head(qs[0], k, v, w.block_size, w.top_k, w.causal, rows=ts, pooling=w.pooling)
     t3 = time.perf_counter()
     return b, h, ts, res, t1 - t0, t2 - t1, t3 - t2
 

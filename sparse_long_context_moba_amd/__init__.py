@@ -5,9 +5,13 @@ every step of the computation runs in the library's HIP kernels.
 
     o, idx = forward(q, k, v, block_size, top_k, causal=True)
 
-q, k, v: [batch, heads, seq_len, head_dim] contiguous CUDA tensors, float32
-or bfloat16. o has q's dtype; idx is int32 [batch, heads, seq_len, top_k]
-with each query's chosen blocks ascending (own block included), -1 padded.
+q: [batch, heads, seq_len, head_dim]; k, v: [batch, kv_heads, seq_len,
+head_dim] with heads a multiple of kv_heads (grouped-query attention; query
+head h reads key/value head h // (heads // kv_heads)); contiguous CUDA
+tensors, float32 or bfloat16. o has q's shape and dtype; idx is int32
+[batch, heads, seq_len, top_k] with each query's chosen blocks ascending
+(own block included), -1 padded. gate_shared=True routes the query heads of
+one key/value head together, on the sum of their gate scores.
 """
 from __future__ import annotations
 
@@ -43,7 +47,7 @@ POOLINGS = {"mean": 0, "max": 1, "mean+max": 2}
 
 
 def problem(q: torch.Tensor, block_size: int, top_k: int, causal: bool = True,
-            pooling: str = "mean") -> moba_problem_t:
+            pooling: str = "mean", kv_heads: int = 0, gate_shared: bool = False) -> moba_problem_t:
     if pooling not in POOLINGS:
         raise ValueError(f"pooling must be one of {tuple(POOLINGS)}, got {pooling!r}")
     if q.dim() != 4:
@@ -52,18 +56,29 @@ def problem(q: torch.Tensor, block_size: int, top_k: int, causal: bool = True,
         raise ValueError(f"dtype must be float32 or bfloat16, got {q.dtype}")
     B, H, S, D = q.shape
     return moba_problem_t(B, H, S, D, int(block_size), int(top_k), 1 if causal else 0, _DTYPES[q.dtype],
-                          POOLINGS[pooling], 0)
+                          POOLINGS[pooling], 0, int(kv_heads), 1 if gate_shared else 0, 0)
 
 
-def _tensors(*ts):
-    q = ts[0]
-    for t in ts:
+def _tensors(q, *kv):
+    """Checks q and the key/value tensors; returns kv_heads (0 if no k/v)."""
+    for t in (q, *kv):
         if not t.is_cuda:
             raise ValueError("tensors must be on a GPU device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k and v must share shape, dtype and device")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k and v must share dtype and device")
+    if not kv:
+        return 0
+    k = kv[0]
+    for t in kv:
+        if t.dim() != 4 or t.shape != k.shape:
+            raise ValueError("k and v must share one [batch, kv_heads, seq_len, head_dim] shape")
+    if q.dim() != 4 or (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]) \
+            or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise ValueError(f"k, v {tuple(k.shape)} must be [batch, kv_heads, seq_len, head_dim] with heads a "
+                         f"multiple of kv_heads, for q {tuple(q.shape)}")
+    return int(k.shape[1])
 
 
 def _stream(dev) -> int:
@@ -85,11 +100,12 @@ def _workspace(p, device):
 
 
 def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None, idx=None,
-            workspace=None, pooling: str = "mean"):
+            workspace=None, pooling: str = "mean", gate_shared: bool = False):
     """MoBA forward. Returns (o, block_idx). pooling: the gate's block
-    summary, "mean" (the paper's), "max" or "mean+max"."""
-    _tensors(q, k, v)
-    p = problem(q, block_size, top_k, causal, pooling)
+    summary, "mean" (the paper's), "max" or "mean+max". gate_shared: the
+    query heads of one key/value head route on their summed scores."""
+    hkv = _tensors(q, k, v)
+    p = problem(q, block_size, top_k, causal, pooling, hkv, gate_shared)
     B, H, S, D = q.shape
     o = torch.empty_like(q) if out is None else out
     bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device) if idx is None else idx
@@ -104,18 +120,23 @@ def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None,
 
 
 def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int, causal: bool = True,
-                   pooling: str = "mean"):
+                   pooling: str = "mean", kv_heads: int = 0, gate_shared: bool = False):
     """MoBA over a varlen batch: sequences of different lengths back to back.
 
-    q, k, v: [sum_i heads * len_i, head_dim], sequence i's [heads, len_i,
-    head_dim] rows from row cu_seqlens[i] * heads (see pack_varlen).
-    cu_seqlens: host ints, cu_seqlens[0] = 0. Returns (o like q, block_idx
-    int32 [sum_i heads * len_i, top_k] in the same order)."""
+    q: [sum_i heads * len_i, head_dim], sequence i's [heads, len_i, head_dim]
+    rows from row cu_seqlens[i] * heads (see pack_varlen); k, v likewise
+    with kv_heads (0 = heads). cu_seqlens: host ints, cu_seqlens[0] = 0.
+    Returns (o like q, block_idx int32 [sum_i heads * len_i, top_k] in the
+    same order)."""
     if q.dim() != 2:
         raise ValueError(f"q must be [tokens * heads, head_dim], got shape {tuple(q.shape)}")
+    hkv = int(kv_heads) or int(heads)
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k and v must be contiguous GPU tensors of one shape and dtype")
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 2 or t.shape[1] != q.shape[1] \
+                or t.dtype != q.dtype:
+            raise ValueError("q, k and v must be contiguous 2-D GPU tensors of one head_dim and dtype")
+    if k.shape != v.shape or k.shape[0] * heads != q.shape[0] * hkv:
+        raise ValueError(f"k, v {tuple(k.shape)} must hold kv_heads={hkv} rows per token of q {tuple(q.shape)}")
     if q.dtype not in _DTYPES:
         raise ValueError(f"dtype must be float32 or bfloat16, got {q.dtype}")
     if pooling not in POOLINGS:
@@ -124,7 +145,8 @@ def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int,
     if q.shape[0] != cu[-1] * heads:
         raise ValueError(f"q has {q.shape[0]} rows, cu_seqlens and heads give {cu[-1] * heads}")
     p = moba_problem_t(len(cu) - 1, int(heads), cu[-1], q.shape[1], int(block_size), int(top_k),
-                       1 if causal else 0, _DTYPES[q.dtype], POOLINGS[pooling], 0)
+                       1 if causal else 0, _DTYPES[q.dtype], POOLINGS[pooling], 0, int(kv_heads),
+                       1 if gate_shared else 0, 0)
     st, n = moba_workspace_size_varlen(p, cu)
     _check(st, "moba_workspace_size_varlen")
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
@@ -152,8 +174,8 @@ def unpack_varlen(x, cu_seqlens, heads: int):
 
 def dense(q, k, v, causal: bool = True, out=None):
     """Full softmax attention (causal or not) with the library's dense kernel."""
-    _tensors(q, k, v)
-    p = problem(q, q.shape[2], 1, causal)
+    hkv = _tensors(q, k, v)
+    p = problem(q, q.shape[2], 1, causal, kv_heads=hkv)
     o = torch.empty_like(q) if out is None else out
     with torch.cuda.device(q.device):
         _check(moba_dense_forward(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
@@ -175,10 +197,11 @@ def pool(k, block_size: int, pooling: str = "mean"):
     return kbar
 
 
-def select(q, k, block_size: int, top_k: int, causal: bool = True, pooling: str = "mean"):
+def select(q, k, block_size: int, top_k: int, causal: bool = True, pooling: str = "mean",
+           gate_shared: bool = False):
     """Routing only: int32 [B, H, S, top_k] exactly as forward() returns it."""
-    _tensors(q, k)
-    p = problem(q, block_size, top_k, causal, pooling)
+    hkv = _tensors(q, k)
+    p = problem(q, block_size, top_k, causal, pooling, hkv, gate_shared)
     B, H, S, D = q.shape
     bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device)
     ws, n = _workspace(p, q.device)

@@ -28,7 +28,8 @@ class moba_problem_t(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("seq_len", ctypes.c_int64),
                 ("head_dim", ctypes.c_int64), ("block_size", ctypes.c_int64),
                 ("top_k", ctypes.c_int64), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("pooling", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("pooling", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int64), ("gate_shared", ctypes.c_int32), ("reserved2", ctypes.c_int32)]
 
 
 class moba_kernel_time_t(ctypes.Structure):

@@ -62,7 +62,8 @@ constexpr size_t kAlign = 256;
 
 struct Plan {
   int64_t B, H, S, D, Bs, top_k, bh, nb, k_eff, slots;
-  bool causal, bf16_in;
+  int64_t Hkv, G, bhkv;  // key/value heads, query heads per key/value head, B * Hkv
+  bool causal, bf16_in, shared;
   int pooling;         // moba_pooling_t
   int64_t pairs;       // (query, kept past block) pairs over all heads
   int64_t max_tiles;   // upper bound on gather tiles
@@ -84,6 +85,11 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     return fail(MOBA_ERR_ARG, "pooling must be MOBA_POOL_MEAN (0), MOBA_POOL_MAX (1) or MOBA_POOL_MEAN_MAX (2), got " +
                                   std::to_string(p->pooling));
   if (p->reserved != 0) return fail(MOBA_ERR_ARG, "reserved must be 0, got " + std::to_string(p->reserved));
+  if (p->reserved2 != 0) return fail(MOBA_ERR_ARG, "reserved2 must be 0, got " + std::to_string(p->reserved2));
+  if (p->kv_heads < 0) return fail(MOBA_ERR_SHAPE, "kv_heads must be >= 0 (0 = heads), got " + std::to_string(p->kv_heads));
+  if (p->kv_heads > 0 && p->heads % p->kv_heads != 0)
+    return fail(MOBA_ERR_SHAPE, "heads (" + std::to_string(p->heads) + ") must be a multiple of kv_heads (" +
+                                    std::to_string(p->kv_heads) + ")");
   if (p->dtype != MOBA_F32 && p->dtype != MOBA_BF16)
     return fail(MOBA_ERR_DTYPE, "dtype must be MOBA_F32 (0) or MOBA_BF16 (1), got " + std::to_string(p->dtype));
   if (p->head_dim != 64 && p->head_dim != 128)
@@ -102,6 +108,10 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   P.Bs = p->block_size;
   P.top_k = p->top_k;
   P.bh = P.B * P.H;
+  P.Hkv = p->kv_heads > 0 ? p->kv_heads : P.H;
+  P.G = P.H / P.Hkv;
+  P.bhkv = P.B * P.Hkv;
+  P.shared = p->gate_shared != 0;
   P.nb = (P.S + P.Bs - 1) / P.Bs;  // a short last block holds the remainder
   P.k_eff = std::min(P.top_k, P.nb);
   P.slots = P.k_eff - 1;
@@ -133,12 +143,13 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     off += up(bytes);
     return at;
   };
-  const size_t nbd = (size_t)(P.bh * P.nb * P.D);
+  // Block summaries per key/value head; counts per query head.
+  const size_t nbd = (size_t)(P.bhkv * P.nb * P.D);
   P.kbar64 = take(nbd * 8);
   P.kbar32 = take(nbd * 4);
   P.kbar_hi = take(nbd * 2);
   P.kbar_lo = take(nbd * 2);
-  P.norm = take((size_t)(P.bh * P.nb) * 4);
+  P.norm = take((size_t)(P.bhkv * P.nb) * 4);
   P.count = take((size_t)(P.bh * P.nb) * 4);
   P.rank = take((size_t)(P.bh * P.S * P.slots) * 4);
   if (need_select) {
@@ -181,7 +192,8 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
                double* kbar64_out) {
   PoolArgs pa{};
   pa.k = k;
-  pa.bh = P.bh;
+  pa.bh = P.bhkv;
+  pa.group = (int)P.G;
   pa.seq_len = P.S;
   pa.block_size = P.Bs;
   pa.head_dim = (int)P.D;
@@ -214,6 +226,8 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   ga.block_idx = block_idx;
   ga.count = at<int32_t>(ws, P.count);
   ga.rank = at<int32_t>(ws, P.rank);
+  ga.group = (int)P.G;
+  ga.shared = P.shared;
   MOBA_TRY(launch_gate(ga, s), "gate launch");
   return MOBA_OK;
 }
@@ -232,6 +246,7 @@ AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, v
   aa.bf16_in = P.bf16_in;
   aa.causal = P.causal;
   aa.k_eff = (int)P.k_eff;
+  aa.group = (int)P.G;
   return aa;
 }
 
@@ -388,11 +403,13 @@ int moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int6
   // order on the one stream, sharing the workspace.
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t esz = p->dtype == MOBA_BF16 ? 2 : 4;
-  const size_t row = (size_t)p->heads * (size_t)p->head_dim * esz;  // bytes per token of one sequence
+  // Bytes per token of one sequence: all query heads, all key/value heads.
+  const size_t row = (size_t)p->heads * (size_t)p->head_dim * esz;
+  const size_t kv_row = (size_t)plans[0].Hkv * (size_t)p->head_dim * esz;
   for (int64_t i = 0; i < n_seqs; ++i) {
-    const size_t off = (size_t)cu_seqlens[i] * row;
-    st = run_forward(plans[(size_t)i], static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
-                     static_cast<const char*>(v) + off, static_cast<char*>(o) + off,
+    const size_t off = (size_t)cu_seqlens[i] * row, kv_off = (size_t)cu_seqlens[i] * kv_row;
+    st = run_forward(plans[(size_t)i], static_cast<const char*>(q) + off, static_cast<const char*>(k) + kv_off,
+                     static_cast<const char*>(v) + kv_off, static_cast<char*>(o) + off,
                      block_idx + cu_seqlens[i] * p->heads * p->top_k, workspace, s);
     if (st != MOBA_OK) {
       g_err = "sequence " + std::to_string(i) + ": " + g_err;

@@ -782,8 +782,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     t = ev / slots;
     if (wave_on) eng.load_q(q + (bh * a.seq_len + t) * D, h);
   };
-  const T* kp = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + j * a.block_size) * D;
-  const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + j * a.block_size) * D;
+  // Keys and values of the query head's key/value head (grouped-query attention).
+  const int64_t kvh = bh / a.group;
+  const T* kp = reinterpret_cast<const T*>(a.k) + (kvh * a.seq_len + j * a.block_size) * D;
+  const T* vp = reinterpret_cast<const T*>(a.v) + (kvh * a.seq_len + j * a.block_size) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
   // A short last block (seq_len not a multiple of block_size) has fewer subtiles.
   const int nsub = (int)(min<int64_t>(a.block_size, a.seq_len - j * a.block_size) / kSub);
@@ -862,8 +864,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       eng.l = h == 0 ? wsum : 0.f;
     }
   };
-  const T* kp = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + kb) * D;
-  const T* vp = reinterpret_cast<const T*>(a.v) + (bh * a.seq_len + kb) * D;
+  const int64_t kvh = bh / a.group;  // the query head's key/value head
+  const T* kp = reinterpret_cast<const T*>(a.k) + (kvh * a.seq_len + kb) * D;
+  const T* vp = reinterpret_cast<const T*>(a.v) + (kvh * a.seq_len + kb) * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
   const int nsub = (kend - kb) / kSub;
   // Subtiles entirely before the workgroup's first query need no mask; with

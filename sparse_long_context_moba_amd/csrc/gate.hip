@@ -206,8 +206,8 @@ struct GateOps<bf16, D> {
   static constexpr int CPR = D / 8;             // chunks per row
   static constexpr int CH = kTileB * CPR;       // chunks per tile of hi (or lo)
   static constexpr int NLD = 2 * CH / 256;
-  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t bh, int j0, int tid) {
-    const int64_t head = bh * a.n_blocks * D;
+  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t kvh, int j0, int tid) {
+    const int64_t head = kvh * a.n_blocks * D;
     if (j0 + kTileB <= a.n_blocks) {
       // Whole tile: a uniform base and a fixed per-thread offset.
       const bf16* hi = a.kbar_hi + head + (int64_t)j0 * D;
@@ -293,6 +293,29 @@ struct GateOps<float, D> {
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) f[kk] = qrow[2 * kk + h];
   }
+  // Shared gate: the fp32 sum of the group's ng query rows (added in head
+  // order), rows head_stride elements apart. Returns sum_h ||q_h|| over
+  // both lane halves, which bounds the summed query's norm and, times
+  // ng * 2^-24, the rounding of the fp32 sum's dot products.
+  template <typename TQ>
+  __device__ float load_sum(const TQ* qrow, int64_t head_stride, int ng, int h) {
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) f[kk] = 0.f;
+    float norms = 0.f;
+    for (int g = 0; g < ng; ++g) {
+      const TQ* r = qrow + g * head_stride;
+      float ss = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) {
+        const float x = (float)r[2 * kk + h];
+        f[kk] += x;
+        ss = __builtin_fmaf(x, x, ss);
+      }
+      ss += shfl_xor32(ss);
+      norms += __builtin_sqrtf(ss);
+    }
+    return norms;
+  }
   __device__ float sumsq() const {
     float s = 0.f;
 #pragma unroll
@@ -305,8 +328,8 @@ struct GateOps<float, D> {
   static constexpr int CPR = D / 2;
   static constexpr int CH = kTileB * CPR;
   static constexpr int NLD = CH / 256;
-  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t bh, int j0, int tid) {
-    const float* head = a.kbar32 + bh * a.n_blocks * D;
+  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t kvh, int j0, int tid) {
+    const float* head = a.kbar32 + kvh * a.n_blocks * D;
     if (j0 + kTileB <= a.n_blocks) {
       const float* base = head + (int64_t)j0 * D;
 #pragma unroll
@@ -371,17 +394,20 @@ constexpr int gate_waves() {
 }
 
 // fp64 re-scoring of the wave's ambiguous queries (lanes with `amb` set,
-// lane half 0), one query at a time by the whole wave. The queries share c
+// lane half 0), one query at a time by the whole wave. A query's fp64
+// vector is the sum of its rows in the nq query heads from qh0 (one head
+// unless the gate is shared); the pooled keys are those of key head kvh.
+// The queries share c
 // and the eligible set. Candidates are the query's tracked list, or every
 // eligible block when its rounding band reaches past the list (`tracked`
 // false). 64 lanes split each candidate's dot product into D/8 slices of 8
 // coordinates and sum the slices in a fixed order (deterministic). The
 // query in lane column L gets the exact top-TT in sel.
-template <typename T, int D, int TT>
-__device__ void rescore_ambiguous(const GateArgs& a, int64_t bh, int64_t tg, int c, int jend, bool amb,
-                                  bool tracked, const int (&lj)[TT], int (&sel)[TT], int lane, int col) {
+template <typename TQ, int D, int TT>
+__device__ void rescore_ambiguous(const GateArgs& a, int64_t qh0, int nq, int64_t kvh, int64_t tg, int c, int jend,
+                                  bool amb, bool tracked, const int (&lj)[TT], int (&sel)[TT], int lane, int col) {
   uint64_t pend = __builtin_amdgcn_ballot_w64(amb);
-  const double* kb64 = a.kbar64 + bh * a.n_blocks * (int64_t)D;
+  const double* kb64 = a.kbar64 + kvh * a.n_blocks * (int64_t)D;
   constexpr int SL = D / 8;    // 8-coordinate slices per candidate
   constexpr int G = 64 / SL;   // candidates per pass
   const int gi = lane / SL, sl = lane % SL;
@@ -389,11 +415,17 @@ __device__ void rescore_ambiguous(const GateArgs& a, int64_t bh, int64_t tg, int
     const int ln = __builtin_ctzll(pend);
     pend &= pend - 1;
     const bool trk = __builtin_amdgcn_readlane((int)tracked, ln);
-    // This lane's slice of the ambiguous query's coordinates, in fp64.
-    const T* qL = reinterpret_cast<const T*>(a.q) + (bh * a.seq_len + tg + ln) * D + 8 * sl;
+    // This lane's slice of the ambiguous query's coordinates, summed over
+    // the heads in fp64.
+    const TQ* qL = reinterpret_cast<const TQ*>(a.q) + (qh0 * a.seq_len + tg + ln) * D + 8 * sl;
     double qd[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) qd[e] = (double)(float)qL[e];
+    for (int g = 1; g < nq; ++g) {
+      const TQ* qg = qL + g * a.seq_len * D;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qd[e] += (double)(float)qg[e];
+    }
     int cj[TT];
 #pragma unroll
     for (int i = 0; i < TT; ++i) cj[i] = __builtin_amdgcn_readlane(lj[i], ln);
@@ -484,10 +516,14 @@ __device__ void write_row(int32_t* row, const int (&sel)[TT], bool scoring, int 
 
 }  // namespace
 
-template <typename T, int D, int TT>
+// T is the type the scores are computed in (the MFMA path), TQ the stored
+// query type. SHARED: one workgroup row of queries per key/value head, the
+// scores being those of the group's summed query (T = float then).
+template <typename T, typename TQ, int D, int TT, bool SHARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT>()))) void gate_topk_kernel(
     GateArgs a) {
   using Ops = GateOps<T, D>;
+  static_assert(SHARED || sizeof(T) == sizeof(TQ), "a per-head gate scores in the query's own type");
   constexpr int QG = gate_groups<T, D, TT>();
   constexpr int WQ = 32 * QG;       // queries per wave
   constexpr int WGQ = 4 * WQ;       // queries per workgroup
@@ -497,7 +533,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
   const int64_t wg_per_head = (a.seq_len + WGQ - 1) / WGQ;
   // Within a head, workgroups run latest queries first: they scan the most
   // blocks (causal), so the short ones fill the tail of the launch.
-  const int64_t bh = blockIdx.x / wg_per_head;
+  // Per-head gate: grp is a query head and reads key head grp / group.
+  // Shared gate: grp is a key/value head and routes its group of query heads.
+  const int64_t grp = blockIdx.x / wg_per_head;
+  const int64_t kvh = SHARED ? grp : grp / a.group;
+  const int64_t qh0 = SHARED ? grp * a.group : grp;
+  const int nq = SHARED ? a.group : 1;
   const int64_t qb = (wg_per_head - 1 - blockIdx.x % wg_per_head) * WGQ;
   // The wave's queries t0 .. t0 + WQ - 1 (group g, lane column col: query
   // t0 + 32 g + col) lie in one block, as block_size is a multiple of 64 and
@@ -518,16 +559,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
   for (int g = 0; g < QG; ++g) {
     qnorm[g] = 0.f;
     if (scoring) {
-      qf[g].load(reinterpret_cast<const T*>(a.q) + (bh * a.seq_len + tw + 32 * g + col) * D, h);
-      float qss = qf[g].sumsq();
-      qss += shfl_xor32(qss);
-      qnorm[g] = __builtin_sqrtf(qss) * 1.0001f;
+      const TQ* qrow = reinterpret_cast<const TQ*>(a.q) + (qh0 * a.seq_len + tw + 32 * g + col) * D;
+      if constexpr (SHARED) {
+        qnorm[g] = qf[g].template load_sum<TQ>(qrow, a.seq_len * D, nq, h) * 1.0001f;
+      } else {
+        qf[g].load(qrow, h);
+        float qss = qf[g].sumsq();
+        qss += shfl_xor32(qss);
+        qnorm[g] = __builtin_sqrtf(qss) * 1.0001f;
+      }
     }
   }
   // Largest norm among the wave's scanned blocks, for the rounding bound:
   // the first 64 norms load now, under the scan; any others after it.
   const int jend = a.causal ? c : NB;  // this wave's scan bound
-  const float* nrm = a.norm + bh * NB;
+  const float* nrm = a.norm + kvh * NB;
   float kmax = (scoring && lane < jend) ? nrm[lane] : 0.f;
   double L[QG][TT];
   float S[QG][TT];
@@ -552,17 +598,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
   typename Ops::Chunk stg[Ops::NLD];
   f32x16 acc_a[QG], acc_b[QG];
   if (ntiles > 0) {
-    Ops::fetch(stg, a, bh, 0, tid);
+    Ops::fetch(stg, a, kvh, 0, tid);
     Ops::put(tile, stg, tid);
   }
   __syncthreads();
-  if (ntiles > 1) Ops::fetch(stg, a, bh, kTileB, tid);
+  if (ntiles > 1) Ops::fetch(stg, a, kvh, kTileB, tid);
   if (my_tiles > 0) Ops::template scores<QG>(tile, col, h, qf, acc_a);
   auto step = [&](int i, f32x16(&cur)[QG], f32x16(&nxt)[QG]) {
     char* next_buf = tile + ((i + 1) & 1) * Ops::TILE_BYTES;
     if (i + 1 < ntiles) Ops::put(next_buf, stg, tid);
     __syncthreads();
-    if (i + 2 < ntiles) Ops::fetch(stg, a, bh, (i + 2) * kTileB, tid);
+    if (i + 2 < ntiles) Ops::fetch(stg, a, kvh, (i + 2) * kTileB, tid);
     const bool do_next = i + 1 < my_tiles, do_cur = i < my_tiles;
     const int jt = i * kTileB, tis = i % kSegTiles;
     const int jb = jt + 4 * h;
@@ -594,7 +640,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     const int64_t t = tw + 32 * g + col;
-    int32_t* idx_row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
     int sel[TT];
     if (scoring) {
       // Merge the two lane halves (keys are distinct, so both halves end
@@ -614,12 +659,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<
       }
       // ---- exactness check: is the cut between kept and dropped blocks
       // farther apart than twice the fast scores' rounding bound?
-      const float eps = Ops::gamma() * qnorm[g] * kmax + 1e-30f;
+      // A shared gate's fp32 query sum adds at most (nq - 1) roundings of
+      // 2^-24 per coordinate, covered by nq * 2^-22 against sum_h ||q_h||.
+      const float gam = Ops::gamma() + (SHARED ? (float)nq * 2.3841858e-07f : 0.f);
+      const float eps = gam * qnorm[g] * kmax + 1e-30f;
       const bool amb = !(ls[m - 1] - ls[m] > 2.f * eps);
       const bool tracked = n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps;
-      rescore_ambiguous<T, D, TT>(a, bh, tw + 32 * g, c, jend, amb && h == 0, tracked, lj, sel, lane, col);
+      rescore_ambiguous<TQ, D, TT>(a, qh0, nq, kvh, tw + 32 * g, c, jend, amb && h == 0, tracked, lj, sel, lane,
+                                   col);
     }
-    if (h == 0) write_row<TT>(idx_row, sel, scoring, m, c, a.causal ? c + 1 : NB, a.top_k);
+    if (h == 0)
+      for (int hq = 0; hq < nq; ++hq)
+        write_row<TT>(a.block_idx + ((qh0 + hq) * a.seq_len + t) * a.top_k, sel, scoring, m, c,
+                      a.causal ? c + 1 : NB, a.top_k);
   }
 }
 
@@ -678,26 +730,35 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
   }
 }
 
-template <typename T, int D, int TT>
+template <typename T, typename TQ, int D, int TT, bool SHARED>
 static void gate_go(const GateArgs& a, hipStream_t s) {
   constexpr int WGQ = 4 * 32 * gate_groups<T, D, TT>();  // queries per workgroup
   const int64_t wg_per_head = (a.seq_len + WGQ - 1) / WGQ;
-  const dim3 grid((unsigned)(a.bh * wg_per_head));
+  const int64_t rows = SHARED ? a.bh / a.group : a.bh;
+  const dim3 grid((unsigned)(rows * wg_per_head));
   const int lds = 2 * GateOps<T, D>::TILE_BYTES;
-  hipLaunchKernelGGL((gate_topk_kernel<T, D, TT>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gate_topk_kernel<T, TQ, D, TT, SHARED>), grid, dim3(256), lds, s, a);
 }
 
+template <typename T, typename TQ, int D, bool SHARED>
+static void gate_pick(const GateArgs& a, hipStream_t s) {
+  // The list tracks m + 2 or more blocks so that a rounding band at the
+  // cut usually ends inside it.
+  const int m = a.k_eff - 1;
+  if (m <= 2) gate_go<T, TQ, D, 4, SHARED>(a, s);
+  else if (m <= 4) gate_go<T, TQ, D, 6, SHARED>(a, s);
+  else if (m <= 8) gate_go<T, TQ, D, 10, SHARED>(a, s);
+  else gate_go<T, TQ, D, kMaxSlots + 2, SHARED>(a, s);
+}
+
+// T: the stored dtype. A shared gate of a group of more than one head
+// scores the fp32 sum of its queries on the fp32 path.
 template <typename T, int D>
 static hipError_t gate_launch_t(const GateArgs& a, hipStream_t s) {
-  const int m = a.k_eff - 1;
   {
-    // The list tracks m + 2 or more blocks so that a rounding band at the
-    // cut usually ends inside it.
     KernelTimer timer(s, "gate_topk");
-    if (m <= 2) gate_go<T, D, 4>(a, s);
-    else if (m <= 4) gate_go<T, D, 6>(a, s);
-    else if (m <= 8) gate_go<T, D, 10>(a, s);
-    else gate_go<T, D, kMaxSlots + 2>(a, s);
+    if (a.shared && a.group > 1) gate_pick<float, T, D, true>(a, s);
+    else gate_pick<T, T, D, false>(a, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.k_eff < 2) return e;

@@ -31,7 +31,8 @@ struct PoolArgs {
   bf16* kbar_hi;     // [bh * nb, D]
   bf16* kbar_lo;     // [bh * nb, D]
   float* norm;       // [bh * nb] L2 norm of each pooled key, rounded up
-  int32_t* count;    // [bh * nb] the gate's per-block query counts: the pool zeroes them
+  int32_t* count;    // [bh * group * nb] the gate's per-block query counts: the pool zeroes them
+  int group;         // query heads per key/value head (bh counts key/value heads here)
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 
@@ -51,6 +52,8 @@ struct GateArgs {
   int32_t* block_idx;  // [bh, S, top_k]
   int32_t* count;      // [bh * nb], zeroed before the launch
   int32_t* rank;       // [bh, S, k_eff - 1]: position of (t, slot) in its block's list
+  int group;           // query heads per key/value head: query head bh pools key head bh / group
+  bool shared;         // the group routes once, on the sum of its heads' scores
 };
 hipError_t launch_gate(const GateArgs& a, hipStream_t s);
 
@@ -86,6 +89,7 @@ struct AttnArgs {
   int64_t gather_grid;        // gather workgroups
   void* part_o;               // [bh, S, k_eff - 1, D] in the input dtype, lane-native order
   float* part_lse;            // [bh, S, k_eff - 1], log2 domain
+  int group;                  // query heads per key/value head: k, v of query head bh are head bh / group
 };
 constexpr int kGatherTileM = 128;
 // Gather workgroups for a bound on the number of tiles (a multiple of the

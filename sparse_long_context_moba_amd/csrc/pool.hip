@@ -13,7 +13,8 @@
 // (exact re-scoring), fp32, and as a bf16 hi/lo pair (hi = bf16(x),
 // lo = bf16(x - hi)) for the MFMA gate, plus the block's L2 norm (rounded
 // up) for the gate's rounding bound. It also clears the block's query
-// count, which the gate's ranking fills. K is read exactly once; the fixed
+// counts (one per query head reading this key/value head), which the gate's
+// ranking fills. K is read exactly once; the fixed
 // reduction order keeps results bit-stable.
 #include "common.h"
 #include "launch.h"
@@ -105,8 +106,9 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   if (tid == 0) {
     const float nrm = (float)(sqrt(sq[0]) * (1.0 + 1e-6));
     a.norm[blk] = nrm;
-    a.count[blk] = 0;
   }
+  // Every query head that reads this key/value head keeps its own list.
+  for (int g = tid; g < a.group; g += 256) a.count[(bh * a.group + g) * nb + j] = 0;
 }
 
 template <typename T, int D>

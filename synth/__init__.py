@@ -42,10 +42,20 @@ class Workload:
     dtype: str  # "f32" or "bf16"
     seed: int
     pooling: str = "mean"  # block summary the gate scores: "mean", "max" or "mean+max"
+    kv_heads: int = 0      # key/value heads (grouped-query attention); 0 = heads
+    gate_shared: bool = False  # a group of query heads routes on its summed scores
 
     @property
     def n_blocks(self) -> int:
         return -(-self.seq_len // self.block_size)
+
+    @property
+    def kvh(self) -> int:
+        return self.kv_heads or self.heads
+
+    @property
+    def group(self) -> int:
+        return self.heads // self.kvh
 
 
 # The five named workloads (sizes of the pages' settings: block 512 / top-k 3
@@ -68,6 +78,14 @@ POOLING_VARIANTS = ["headline_32k_max", "headline_32k_meanmax"]
 WORKLOADS["headline_33k_short_block"] = Workload("headline_33k_short_block", 1, 32, 33024, 128, 512, 3, True,
                                                  "bf16", 5)
 SHAPE_VARIANTS = ["headline_33k_short_block"]
+# Grouped-query attention at the headline shape: 32 query heads over 8
+# key/value heads, each query head routing on its own or each group of four
+# routing once on its summed scores.
+WORKLOADS["headline_32k_gqa4"] = Workload("headline_32k_gqa4", 1, 32, 32768, 128, 512, 3, True, "bf16", 6,
+                                          kv_heads=8)
+WORKLOADS["headline_32k_gqa4_shared"] = Workload("headline_32k_gqa4_shared", 1, 32, 32768, 128, 512, 3, True,
+                                                 "bf16", 6, kv_heads=8, gate_shared=True)
+GQA_VARIANTS = ["headline_32k_gqa4", "headline_32k_gqa4_shared"]
 
 
 def _rng(seed: int, tensor: int, b: int, h: int) -> np.random.Generator:
@@ -88,21 +106,45 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return (x.view(np.uint32) >> 16).astype(np.uint16).view(np.int16)
 
 
-def make_head(seed: int, b: int, h: int, seq_len: int, head_dim: int,
-              block_size: int, dtype: str):
-    """Return (q, k, v), each float32 [seq_len, head_dim], for one (b, h)."""
+def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return x
+
+
+def make_q(seed: int, b: int, h: int, seq_len: int, head_dim: int, dtype: str):
+    """q of query head (b, h), float32 [seq_len, head_dim]."""
+    q = _rng(seed, TENSOR_Q, b, h).standard_normal((seq_len, head_dim), dtype=np.float32)
+    return _cast(q, dtype)
+
+
+def make_kv(seed: int, b: int, h: int, seq_len: int, head_dim: int, block_size: int, dtype: str):
+    """(k, v) of key/value head (b, h), each float32 [seq_len, head_dim]."""
     S, D = seq_len, head_dim
     nb = -(-S // block_size)  # a short last block gets its own bias too
-    q = _rng(seed, TENSOR_Q, b, h).standard_normal((S, D), dtype=np.float32)
     kn = _rng(seed, TENSOR_KNOISE, b, h).standard_normal((S, D), dtype=np.float32)
     bias = _rng(seed, TENSOR_KBIAS, b, h).normal(0.0, 0.5, (nb, D)).astype(np.float32)
     kn += np.repeat(bias, block_size, axis=0)[:S]
     v = _rng(seed, TENSOR_V, b, h).standard_normal((S, D), dtype=np.float32)
-    if dtype == "bf16":
-        q, kn, v = round_to_bf16(q), round_to_bf16(kn), round_to_bf16(v)
-    elif dtype != "f32":
-        raise ValueError(f"unknown dtype {dtype!r}")
-    return q, kn, v
+    return _cast(kn, dtype), _cast(v, dtype)
+
+
+def make_head(seed: int, b: int, h: int, seq_len: int, head_dim: int,
+              block_size: int, dtype: str):
+    """Return (q, k, v), each float32 [seq_len, head_dim], for one (b, h)."""
+    q = make_q(seed, b, h, seq_len, head_dim, dtype)
+    return (q, *make_kv(seed, b, h, seq_len, head_dim, block_size, dtype))
+
+
+def make_group(w: "Workload", b: int, hk: int):
+    """(q [group, S, D] of the query heads hk * group .. + group - 1, k, v of
+    key/value head hk). With kv_heads = heads this is make_head of (b, hk)."""
+    G = w.group
+    q = np.stack([make_q(w.seed, b, hk * G + g, w.seq_len, w.head_dim, w.dtype) for g in range(G)])
+    k, v = make_kv(w.seed, b, hk, w.seq_len, w.head_dim, w.block_size, w.dtype)
+    return q, k, v
 
 
 def make_inputs(w: Workload, heads=None):
@@ -127,6 +169,31 @@ def _head_job(args):
     if w.dtype == "bf16":
         return b, h, bf16_bits(q), bf16_bits(k), bf16_bits(v)
     return b, h, q, k, v
+
+
+def _group_job(args):
+    w, b, hk = args
+    q, k, v = make_group(w, b, hk)
+    if w.dtype == "bf16":
+        return b, hk, bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    return b, hk, q, k, v
+
+
+def iter_groups_parallel(w: Workload, workers: int | None = None):
+    """Yield (b, hk, q [group, S, D], k, v) per key/value head, generated in
+    worker processes (bf16 workloads as int16 bit patterns, like
+    iter_heads_parallel)."""
+    jobs = [(w, b, hk) for b in range(w.batch) for hk in range(w.kvh)]
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    if workers <= 1 or len(jobs) == 1:
+        for j in jobs:
+            yield _group_job(j)
+        return
+    import multiprocessing as mp
+    with mp.get_context("fork").Pool(workers) as pool:
+        for out in pool.imap(_group_job, jobs, chunksize=1):
+            yield out
 
 
 def iter_heads_parallel(w: Workload, workers: int | None = None):

@@ -34,9 +34,12 @@ def to_dev(x: np.ndarray, dtype: str):
     return t.cuda()
 
 
-def check_rows(gpu_o, gpu_idx, res, rows_t, q, k, v, block_size, top_k, causal, dtype, label=""):
+def check_rows(gpu_o, gpu_idx, res, rows_t, q, k, v, block_size, top_k, causal, dtype, label="", q_gate=None):
     """Compare GPU rows (o [R, D], idx [R, top_k]) of one head with the
-    oracle's forward_head result `res` for the same rows. Returns stats."""
+    oracle's forward_head result `res` for the same rows. Returns stats.
+    q_gate: the query the gate scores with, if not q (a shared gate scores
+    the group's summed query)."""
+    q_gate = q if q_gate is None else q_gate
     tol = TOL[dtype]
     kbar = res["kbar"]
     n_flag = n_tie_diff = 0
@@ -54,7 +57,7 @@ def check_rows(gpu_o, gpu_idx, res, rows_t, q, k, v, block_size, top_k, causal, 
             a, b = res["a"][r], res["b"][r]
             tau = orc.NEAR_TIE_REL * max(abs(a), abs(b))
             elig = set(int(j) for j in orc.eligible_blocks(c, kbar.shape[0], causal))
-            s = {j: float(kbar[j] @ q[t]) for j in elig}
+            s = {j: float(kbar[j] @ np.asarray(q_gate[t], np.float64)) for j in elig}
             chosen = set(j for j in gi if j >= 0)
             assert c in chosen, f"{label} t={t}: own block missing"
             assert all(s[j] <= a + tau or j in chosen for j in elig), f"{label} t={t}: dropped a clear winner"

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     from sparse_long_context_moba_amd import _lib
-    assert _lib.moba_abi_version() == 2
+    assert _lib.moba_abi_version() == 3
     for code in range(8):
         assert _lib.moba_status_str(code)
     assert _lib.moba_status_str(99) == "unknown status"
@@ -57,6 +57,10 @@ FAKE = 0x1000  # never dereferenced: validation fails or stops before any launch
     (dict(pooling=3), 3, "pooling"),
     (dict(pooling=-1), 3, "pooling"),
     (dict(reserved=1), 3, "reserved"),
+    (dict(reserved2=1), 3, "reserved2"),
+    (dict(kv_heads=-1), 2, "kv_heads"),
+    (dict(heads=4, kv_heads=3), 2, "multiple of kv_heads"),
+    (dict(heads=2, kv_heads=4), 2, "multiple of kv_heads"),
     (dict(dtype=7), 4, "dtype"),
     (dict(head_dim=96), 5, "head_dim"),
     (dict(block_size=32, seq_len=1024), 5, "block_size"),
@@ -147,3 +151,30 @@ def test_varlen_validation_and_workspace():
     # too small a workspace is rejected before any launch
     assert _lib.moba_forward_varlen(p, cu, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 6
     assert _lib.moba_forward_varlen(p, cu, None, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+
+
+def test_struct_layout_matches_header():
+    """moba_problem_t: six int64, four int32, one int64, two int32 = 80 bytes,
+    kv_heads at byte 64."""
+    from sparse_long_context_moba_amd._lib import moba_problem_t
+    assert ctypes.sizeof(moba_problem_t) == 80
+    assert moba_problem_t.kv_heads.offset == 64
+    assert moba_problem_t.gate_shared.offset == 72
+
+
+def test_grouped_query_heads_workspace():
+    """Key/value heads shrink the pooled-key arrays only: per-query-head
+    buffers (counts, ranks, lists, partials) keep their size, and a shared
+    gate needs no extra workspace."""
+    from sparse_long_context_moba_amd import _lib
+    st, mha = _lib.moba_workspace_size(_p(heads=8))
+    st2, gqa = _lib.moba_workspace_size(_p(heads=8, kv_heads=2))
+    st3, sh = _lib.moba_workspace_size(_p(heads=8, kv_heads=2, gate_shared=1))
+    st4, same = _lib.moba_workspace_size(_p(heads=8, kv_heads=8))
+    assert st == st2 == st3 == st4 == 0, _lib.moba_last_error()
+    assert gqa < mha and sh == gqa and same == mha
+    # pooled keys: fp64 + fp32 + bf16 hi/lo per coordinate, and an fp32 norm, per (kv head, block)
+    nb, D = 1024 // 256, 128
+    up = lambda x: (x + 255) // 256 * 256
+    saved = sum(up(8 * nb * D * e) - up(2 * nb * D * e) for e in (8, 4, 2, 2)) + up(8 * nb * 4) - up(2 * nb * 4)
+    assert mha - gqa == saved

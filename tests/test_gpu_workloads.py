@@ -16,18 +16,21 @@ pytestmark = pytest.mark.gpu
 
 
 def _upload(w):
-    """Generate the workload's inputs per head on the host (worker processes)
-    and copy them into device tensors; keep the host copies for the oracle."""
-    shape = (w.batch, w.heads, w.seq_len, w.head_dim)
+    """Generate the workload's inputs per key/value head and its group of
+    query heads on the host (worker processes) and copy them into device
+    tensors; keep the host copies for the oracle, keyed by (b, kv head)."""
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    dev = [torch.empty(shape, dtype=tdt, device="cuda") for _ in range(3)]
+    G = w.group
+    qd = torch.empty((w.batch, w.heads, w.seq_len, w.head_dim), dtype=tdt, device="cuda")
+    kd, vd = (torch.empty((w.batch, w.kvh, w.seq_len, w.head_dim), dtype=tdt, device="cuda") for _ in range(2))
     host = {}
-    for b, h, q, k, v in synth.iter_heads_parallel(w):
-        for i, x in enumerate((q, k, v)):
-            t = torch.from_numpy(x)
-            dev[i][b, h].copy_(t.view(torch.bfloat16) if w.dtype == "bf16" else t)
-        host[(b, h)] = (q, k, v)
-    return dev, host
+    cast = (lambda t: t.view(torch.bfloat16)) if w.dtype == "bf16" else (lambda t: t)
+    for b, hk, q, k, v in synth.iter_groups_parallel(w):
+        qd[b, hk * G:(hk + 1) * G].copy_(cast(torch.from_numpy(q)))
+        kd[b, hk].copy_(cast(torch.from_numpy(k)))
+        vd[b, hk].copy_(cast(torch.from_numpy(v)))
+        host[(b, hk)] = (q, k, v)
+    return (qd, kd, vd), host
 
 
 def _as_f32(x, dtype):
@@ -37,10 +40,17 @@ def _as_f32(x, dtype):
 
 
 def _oracle_head(args):
-    qb, kb, vb, rows, w = args
-    q, k, v = (_as_f32(x, w.dtype) for x in (qb, kb, vb))
-    res = orc.forward_head(q, k, v, w.block_size, w.top_k, w.causal, rows=rows, pooling=w.pooling)
-    return res, q, k, v
+    """Oracle rows of query head g of a group (all G heads' queries given)."""
+    qb, kb, vb, g, rows, w = args
+    qs, k, v = (_as_f32(x, w.dtype) for x in (qb, kb, vb))
+    if w.gate_shared:
+        res = orc.forward_group(qs, k, v, w.block_size, w.top_k, w.causal, rows=rows, pooling=w.pooling,
+                                shared_gate=True)[g]
+        q_gate = qs.astype(np.float64).sum(axis=0)
+    else:
+        res = orc.forward_head(qs[g], k, v, w.block_size, w.top_k, w.causal, rows=rows, pooling=w.pooling)
+        q_gate = None
+    return res, qs[g], k, v, q_gate
 
 
 def _run(name, n_rows=4096):
@@ -50,11 +60,12 @@ def _run(name, n_rows=4096):
     say(f"[gpu] {name}: generating and uploading inputs")
     (qd, kd, vd), host = _upload(w)
     say(f"[gpu] {name}: inputs ready in {time.time() - t0:.1f}s; running moba.forward")
-    o, idx = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal, pooling=w.pooling)
+    kw = dict(pooling=w.pooling, gate_shared=w.gate_shared)
+    o, idx = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal, **kw)
     torch.cuda.synchronize()
     # Run-to-run: every output bit and index must repeat (the path has no
     # floating-point atomics, so any difference is a race).
-    o2, idx2 = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal, pooling=w.pooling)
+    o2, idx2 = moba.forward(qd, kd, vd, w.block_size, w.top_k, w.causal, **kw)
     torch.cuda.synchronize()
     bits = torch.int16 if o.dtype == torch.bfloat16 else torch.int32
     n_diff = int((o.view(bits) != o2.view(bits)).sum().item())
@@ -73,12 +84,13 @@ def _run(name, n_rows=4096):
     stats = {"rows": 0, "max_err": 0.0, "flagged": 0, "tie_diff": 0}
     import multiprocessing as mp
     keys = sorted(groups)
-    jobs = [(*host[bh], rows[groups[bh], 2], w) for bh in keys]
+    G = w.group
+    jobs = [(*host[(bh[0], bh[1] // G)], bh[1] % G, rows[groups[bh], 2], w) for bh in keys]
     with mp.get_context("fork").Pool(min(16, len(jobs))) as pool:
-        for bh, (res, q, k, v) in zip(keys, pool.imap(_oracle_head, jobs)):
+        for bh, (res, q, k, v, q_gate) in zip(keys, pool.imap(_oracle_head, jobs)):
             ii = groups[bh]
             st = check_rows(o_rows[ii], idx_rows[ii], res, rows[ii, 2], q, k, v, w.block_size,
-                            w.top_k, w.causal, w.dtype, label=f"{name} b={bh[0]} h={bh[1]}")
+                            w.top_k, w.causal, w.dtype, label=f"{name} b={bh[0]} h={bh[1]}", q_gate=q_gate)
             stats["rows"] += st["rows"]
             stats["max_err"] = max(stats["max_err"], st["max_err"])
             stats["flagged"] += st["flagged"]
@@ -105,6 +117,14 @@ def test_headline_32k_meanmax_pooling_sampled():
 
 def test_headline_short_last_block_sampled():
     _run("headline_33k_short_block")
+
+
+def test_headline_gqa4_per_head_sampled():
+    _run("headline_32k_gqa4")
+
+
+def test_headline_gqa4_shared_gate_sampled():
+    _run("headline_32k_gqa4_shared")
 
 
 def test_coarse_32k_sampled():
