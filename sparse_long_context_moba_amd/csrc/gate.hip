@@ -17,7 +17,9 @@
 // the pooled keys as the A operand (rows = blocks) and the queries as the
 // B operand (columns = queries), so lane l holds 16 block scores of query
 // l%32. The pooled keys enter as a bf16 hi/lo pair (two MFMA passes, fp32
-// accumulate); fp32 inputs use fp32 MFMA on the fp32 means. The MFMAs of
+// accumulate); fp32 inputs use fp32 MFMA on the fp32 means. A gate shared
+// by a group of query heads scores the group's summed query (fp32, split
+// into a bf16 hi/lo pair: three MFMA passes). The MFMAs of
 // tile i+1 are interleaved in the instruction stream with the selection
 // work of tile i (waves issue in order).
 //
@@ -293,29 +295,6 @@ struct GateOps<float, D> {
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) f[kk] = qrow[2 * kk + h];
   }
-  // Shared gate: the fp32 sum of the group's ng query rows (added in head
-  // order), rows head_stride elements apart. Returns sum_h ||q_h|| over
-  // both lane halves, which bounds the summed query's norm and, times
-  // ng * 2^-24, the rounding of the fp32 sum's dot products.
-  template <typename TQ>
-  __device__ float load_sum(const TQ* qrow, int64_t head_stride, int ng, int h) {
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk) f[kk] = 0.f;
-    float norms = 0.f;
-    for (int g = 0; g < ng; ++g) {
-      const TQ* r = qrow + g * head_stride;
-      float ss = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        const float x = (float)r[2 * kk + h];
-        f[kk] += x;
-        ss = __builtin_fmaf(x, x, ss);
-      }
-      ss += shfl_xor32(ss);
-      norms += __builtin_sqrtf(ss);
-    }
-    return norms;
-  }
   __device__ float sumsq() const {
     float s = 0.f;
 #pragma unroll
@@ -379,6 +358,112 @@ struct GateOps<float, D> {
   static __device__ constexpr float gamma() { return (2 * D + 16) * 2.3841858e-07f + 1.5258789e-05f; }
 };
 
+// Shared gate: the group's summed query, taken in fp32 and split into a
+// bf16 pair (hi = bf16(x), lo = bf16(x - hi)), against the pooled keys' bf16
+// pair: three MFMA products (hi.hi, hi.lo, lo.hi; lo.lo is below 2^-16 of
+// the score and left to the rounding bound). The tile staging is the
+// per-head bf16 one.
+template <int D>
+struct GateOpsSplitQ : GateOps<bf16, D> {
+  using Base = GateOps<bf16, D>;
+  static constexpr int KC = Base::KC, KR = Base::KR;
+  bf16x8 f[KC];  // hi
+  bf16x8 g[KC];  // lo
+  // Sum of the ng query rows (head order) in fp32, split into hi/lo.
+  // Returns sum_h ||q_h|| over both lane halves.
+  template <typename TQ>
+  __device__ float load_sum(const TQ* qrow, int64_t head_stride, int ng, int h) {
+    float x[KC][8];
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[kk][e] = 0.f;
+    float norms = 0.f;
+    for (int gh = 0; gh < ng; ++gh) {
+      const TQ* r = qrow + gh * head_stride;
+      float ss = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = (float)r[16 * kk + 8 * h + e];
+          x[kk][e] += y;
+          ss = __builtin_fmaf(y, y, ss);
+        }
+      ss += shfl_xor32(ss);
+      norms += __builtin_sqrtf(ss);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16 hi = to_bf16(x[kk][e]);
+        f[kk][e] = hi;
+        g[kk][e] = to_bf16(x[kk][e] - (float)hi);
+      }
+    return norms;
+  }
+  static constexpr int QG_MAX = 1;
+  template <int QG>
+  static __device__ void scores(const char* lds, int col, int h, const GateOpsSplitQ (&qf)[QG],
+                                f32x16 (&acc)[QG]) {
+    static_assert(QG == 1, "one query group");
+    const bf16* hi = reinterpret_cast<const bf16*>(lds) + col * KR + 8 * h;
+    const bf16* lo = hi + kTileB * KR;
+    acc[0] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(hi + 16 * kk);
+      acc[0] = mfma_bf16(af, qf[0].f[kk], acc[0]);
+      acc[0] = mfma_bf16(af, qf[0].g[kk], acc[0]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(lo + 16 * kk);
+      acc[0] = mfma_bf16(af, qf[0].f[kk], acc[0]);
+    }
+  }
+  // Issue order as in the per-head gate: two MFMAs per hi fragment, one per
+  // lo fragment, each with an even share of the selection's VALU work.
+  template <int QG, int TT>
+  static __device__ __forceinline__ void interleave() {
+    constexpr int NF = 2 * KC;
+    constexpr int VALU = 16 * QG * (TT + 1) + 16;
+    constexpr int PER = (VALU + NF - 1) / NF;
+    constexpr int AHEAD = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int fr = 0; fr < KC; ++fr) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int fr = KC; fr < NF; ++fr) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+      if (fr + AHEAD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  // Relative rounding bound: the pooled keys' hi/lo residual, the summed
+  // query's hi/lo residual and the omitted lo.lo product (each <= 2^-16,
+  // taken as 2^-15), 3D+16 fp32 accumulation steps at 2^-22 each and the
+  // segment key truncation (2^-16). The fp32 sum of the heads' queries is
+  // added by the caller.
+  static __device__ constexpr float gamma() {
+    return 3 * 3.0517578e-05f + (3 * D + 16) * 2.3841858e-07f + 1.5258789e-05f;
+  }
+};
+
+template <bool C, typename A, typename B>
+struct pick_type {
+  using type = A;
+};
+template <typename A, typename B>
+struct pick_type<false, A, B> {
+  using type = B;
+};
+
 // 32-query groups per wave. A second group would give independent MFMA and
 // selection chains and halve the LDS fragment reads, but with the pipelined
 // accumulators it does not fit the register file without spills; one group
@@ -387,10 +472,11 @@ template <typename T, int D, int TT>
 __host__ __device__ constexpr int gate_groups() {
   return 1;
 }
-// Waves per SIMD the register budget is set for.
-template <typename T, int D, int TT>
+// Waves per SIMD the register budget is set for (a shared gate holds two
+// query fragments).
+template <typename T, int D, int TT, bool SHARED = false>
 constexpr int gate_waves() {
-  return (sizeof(T) == 2 && TT <= 6) ? 3 : 2;
+  return (sizeof(T) == 2 && TT <= 6 && !SHARED) ? 3 : 2;
 }
 
 // fp64 re-scoring of the wave's ambiguous queries (lanes with `amb` set,
@@ -518,11 +604,13 @@ __device__ void write_row(int32_t* row, const int (&sel)[TT], bool scoring, int 
 
 // T is the type the scores are computed in (the MFMA path), TQ the stored
 // query type. SHARED: one workgroup row of queries per key/value head, the
-// scores being those of the group's summed query (T = float then).
+// scores being those of the group's summed query (bf16 MFMA on its hi/lo
+// split, T = bf16).
 template <typename T, typename TQ, int D, int TT, bool SHARED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT>()))) void gate_topk_kernel(
-    GateArgs a) {
-  using Ops = GateOps<T, D>;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT, SHARED>()))) void
+gate_topk_kernel(GateArgs a) {
+  using Ops = typename pick_type<SHARED, GateOpsSplitQ<D>, GateOps<T, D>>::type;
+  static_assert(!SHARED || sizeof(T) == 2, "a shared gate scores on the bf16 pair");
   static_assert(SHARED || sizeof(T) == sizeof(TQ), "a per-head gate scores in the query's own type");
   constexpr int QG = gate_groups<T, D, TT>();
   constexpr int WQ = 32 * QG;       // queries per wave
@@ -752,12 +840,12 @@ static void gate_pick(const GateArgs& a, hipStream_t s) {
 }
 
 // T: the stored dtype. A shared gate of a group of more than one head
-// scores the fp32 sum of its queries on the fp32 path.
+// scores the fp32 sum of its queries, split into a bf16 pair.
 template <typename T, int D>
 static hipError_t gate_launch_t(const GateArgs& a, hipStream_t s) {
   {
     KernelTimer timer(s, "gate_topk");
-    if (a.shared && a.group > 1) gate_pick<float, T, D, true>(a, s);
+    if (a.shared && a.group > 1) gate_pick<bf16, T, D, true>(a, s);
     else gate_pick<T, T, D, false>(a, s);
   }
   hipError_t e = hipGetLastError();
