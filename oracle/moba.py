@@ -30,6 +30,8 @@ method's steps in order, in float64, one query row at a time:
      indices by score with a stable descending sort and keeps the first k);
   5. attend over the keys of the chosen blocks only, causal inside the
      query's own block ([S] §3), with one softmax over that whole key set.
+The backward (backward_head) differentiates step 5 with the choice of
+steps 3-4 held fixed (see its docstring for why that is the gradient).
 
 Readings where the pages are silent (each is listed in the design doc):
   * top_k counts the forced current block ([P] §3.1: each query attends
@@ -269,6 +271,72 @@ def attend_with_idx(q_t, k, v, t: int, idx_row, block_size: int, causal: bool = 
     """Attention of query t over a given block choice (forced-index mode),
     used where the GPU legitimately broke a near-tie the other way."""
     return attend(q_t, k, v, attended_keys(t, np.asarray(idx_row), block_size, causal, len(k)))
+
+
+def attend_lse(q_t: np.ndarray, k: np.ndarray, keys: np.ndarray) -> float:
+    """Natural-log log-sum-exp of the scaled logits q k_u / sqrt(D) over the
+    attended keys: the softmax normaliser a backward pass reuses."""
+    q_t = np.asarray(q_t, dtype=np.float64)
+    logits = np.asarray(k[keys], dtype=np.float64) @ q_t / math.sqrt(q_t.shape[0])
+    mx = logits.max()
+    return float(mx + math.log(np.exp(logits - mx).sum()))
+
+
+def attend_grad(q_t: np.ndarray, k: np.ndarray, v: np.ndarray, keys: np.ndarray, do_t: np.ndarray):
+    """Gradients of o = softmax(l) V_U, l_u = q . k_u / sqrt(D), for an
+    upstream gradient do (the textbook softmax-attention backward, float64):
+
+        p = softmax(l);  dV_u = p_u do;  dp_u = do . v_u;
+        dl_u = p_u (dp_u - do . o);  dq = sum_u dl_u k_u / sqrt(D);
+        dk_u = dl_u q / sqrt(D).
+
+    Returns (dq [D], dk [len(keys), D], dv [len(keys), D])."""
+    q_t = np.asarray(q_t, dtype=np.float64)
+    do_t = np.asarray(do_t, dtype=np.float64)
+    kk = np.asarray(k[keys], dtype=np.float64)
+    vv = np.asarray(v[keys], dtype=np.float64)
+    scale = 1.0 / math.sqrt(q_t.shape[0])
+    logits = kk @ q_t * scale
+    w = np.exp(logits - logits.max())
+    p = w / w.sum()
+    o = p @ vv
+    dv = np.outer(p, do_t)
+    dp = vv @ do_t
+    dl = p * (dp - do_t @ o)
+    dq = (dl @ kk) * scale
+    dk = np.outer(dl, q_t) * scale
+    return dq, dk, dv
+
+
+def backward_head(q, k, v, do, idx, block_size: int, causal: bool = True):
+    """MoBA backward for one (batch, head): the gradients of o with respect
+    to q, k and v for the upstream gradient do, with the block choice idx
+    [S, top_k] (as forward_head returns it) held fixed.
+
+    The pages use MoBA in training and fine-tuning ([S] §3 on SFT with MoBA
+    layers; [P] §2) but give no gradient. Read here: the routing is a top-k
+    over block scores, piecewise constant in q and k, so its derivative is
+    zero wherever the choice is not tied; and the gate's scores do not
+    weight the output (unchosen blocks get exactly 0, chosen ones are not
+    scaled), so no gradient flows through the pooled keys. What remains is
+    the gradient of one softmax attention per query over its attended keys.
+
+    Returns (dq, dk, dv, lse): float64 [S, D] each and the per-query
+    natural-log log-sum-exp [S] of the scaled logits."""
+    q = np.asarray(q)
+    S, D = q.shape
+    dq = np.zeros((S, D))
+    dk = np.zeros((S, D))
+    dv = np.zeros((S, D))
+    lse = np.zeros(S)
+    for t in range(S):
+        keys = attended_keys(t, np.asarray(idx[t]), block_size, causal, S)
+        gq, gk, gv = attend_grad(q[t], k, v, keys, do[t])
+        dq[t] = gq
+        np.add.at(dk, keys, gk)
+        np.add.at(dv, keys, gv)
+        lse[t] = attend_lse(q[t], k, keys)
+    return dq, dk, dv, lse
 
 
 def dense_attention(q, k, v, causal: bool = True, rows=None):

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import moba
+from tests import test_oracle_backward as bwd
 from tests import test_oracle_pins as pins
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -33,6 +34,12 @@ def _pins():
     for causal in (True, False):
         yield f"shared_gate_bruteforce[{causal}]", lambda c=causal: pins.test_shared_gate_matches_subset_bruteforce(c)
     yield "shared_gate_special", pins.test_shared_gate_special_cases
+    yield "backward_finite_differences", lambda: bwd.test_backward_matches_finite_differences(True, 8)
+    for causal in (True, False):
+        yield f"backward_masked_autograd[{causal}]", lambda c=causal: bwd.test_backward_matches_masked_autograd(c)
+    yield "backward_dense", lambda: bwd.test_backward_topk_covering_all_blocks_is_dense(True)
+    yield "backward_invariants", bwd.test_backward_invariants
+    yield "backward_lse", bwd.test_lse_matches_torch_logsumexp
     for seed in range(6):
         for causal in (True, False):
             yield f"subset_bruteforce[{seed},{causal}]", (
@@ -79,6 +86,8 @@ _orig_elig = moba.eligible_blocks
 _orig_select = moba.select_blocks
 _orig_keys = moba.attended_keys
 _orig_attend = moba.attend
+_orig_grad = moba.attend_grad
+_orig_lse = moba.attend_lse
 
 
 def pool_wrong_denominator(k, block_size, pooling="mean"):
@@ -229,7 +238,53 @@ def attend_unnormalised(q_t, k, v, keys):
     return np.exp(logits - logits.max()) @ vv
 
 
+def _grad_parts(q_t, k, v, keys, do_t):
+    q_t = np.asarray(q_t, dtype=np.float64)
+    do_t = np.asarray(do_t, dtype=np.float64)
+    kk, vv = np.asarray(k[keys], np.float64), np.asarray(v[keys], np.float64)
+    scale = 1.0 / math.sqrt(q_t.shape[0])
+    logits = kk @ q_t * scale
+    w = np.exp(logits - logits.max())
+    return q_t, do_t, kk, vv, scale, w, w / w.sum()
+
+
+def grad_drop_delta(q_t, k, v, keys, do_t):
+    # the softmax Jacobian's do . o term is dropped
+    q_t, do_t, kk, vv, scale, w, p = _grad_parts(q_t, k, v, keys, do_t)
+    dl = p * (vv @ do_t)
+    return (dl @ kk) * scale, np.outer(dl, q_t) * scale, np.outer(p, do_t)
+
+
+def grad_dq_unscaled(q_t, k, v, keys, do_t):
+    dq, dk, dv = _orig_grad(q_t, k, v, keys, do_t)
+    return dq * math.sqrt(np.asarray(q_t).shape[0]), dk, dv
+
+
+def grad_dv_unnormalised(q_t, k, v, keys, do_t):
+    q_t, do_t, kk, vv, scale, w, p = _grad_parts(q_t, k, v, keys, do_t)
+    dq, dk, _ = _orig_grad(q_t, k, v, keys, do_t)
+    return dq, dk, np.outer(w, do_t)
+
+
+def grad_dk_from_keys(q_t, k, v, keys, do_t):
+    # dk built from the keys instead of the query
+    q_t, do_t, kk, vv, scale, w, p = _grad_parts(q_t, k, v, keys, do_t)
+    dq, _, dv = _orig_grad(q_t, k, v, keys, do_t)
+    dl = p * (vv @ do_t - do_t @ (p @ vv))
+    return dq, dl[:, None] * kk * scale, dv
+
+
+def lse_unscaled(q_t, k, keys):
+    q_t = np.asarray(q_t, dtype=np.float64)
+    return _orig_lse(q_t * math.sqrt(q_t.shape[0]), k, keys)
+
+
 MUTATIONS = [
+    ("attend_grad", grad_drop_delta),
+    ("attend_grad", grad_dq_unscaled),
+    ("attend_grad", grad_dv_unnormalised),
+    ("attend_grad", grad_dk_from_keys),
+    ("attend_lse", lse_unscaled),
     ("pool_keys", pool_wrong_denominator),
     ("pool_keys", pool_first_key_only),
     ("pool_keys", pool_max_is_min),
