@@ -843,6 +843,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int n = min(a.k_eff - 1, n_elig);
     const int slots = a.k_eff - 1;
     const int64_t rec0 = (bh * a.seq_len + t) * (int64_t)slots;
+    if constexpr (sizeof(T) == 2) {
+      if (n > 0 && n <= 2) {
+        // One or two past blocks (top_k <= 3): every load of both slots is
+        // requested before any is used, so the merge waits one memory
+        // round trip, not one per load; the arithmetic and its order are
+        // those of the general loop below.
+        const bf16* po = reinterpret_cast<const bf16*>(a.part_o);
+        const bf16* src0 = po + rec0 * D + h * (D / 2);
+        const float l0 = a.part_lse[rec0];
+        const float l1 = n > 1 ? a.part_lse[rec0 + 1] : kNegInf;
+        bf16x8 x0[2 * E::DT], x1[2 * E::DT];
+#pragma unroll
+        for (int i = 0; i < 2 * E::DT; ++i) x0[i] = *reinterpret_cast<const bf16x8*>(src0 + 8 * i);
+        if (n > 1) {
+#pragma unroll
+          for (int i = 0; i < 2 * E::DT; ++i) x1[i] = *reinterpret_cast<const bf16x8*>(src0 + D + 8 * i);
+        }
+        const float mx = fmaxf(fmaxf(kNegInf, l0), l1);
+        const float w0 = fast_exp2(l0 - mx);
+        float wsum = 0.f;
+        wsum += w0;
+#pragma unroll
+        for (int dt = 0; dt < E::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) eng.o[dt][r] = __builtin_fmaf(w0, (float)x0[2 * dt + r / 8][r % 8], eng.o[dt][r]);
+        if (n > 1) {
+          const float w1 = fast_exp2(l1 - mx);
+          wsum += w1;
+#pragma unroll
+          for (int dt = 0; dt < E::DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              eng.o[dt][r] = __builtin_fmaf(w1, (float)x1[2 * dt + r / 8][r % 8], eng.o[dt][r]);
+        }
+        eng.m = mx;
+        eng.l = h == 0 ? wsum : 0.f;
+        return;
+      }
+    }
     float mx = kNegInf;
     for (int s = 0; s < n; ++s) mx = fmaxf(mx, a.part_lse[rec0 + s]);
     if (n > 0) {
