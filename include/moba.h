@@ -146,6 +146,37 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
                  void* o, int32_t* block_idx, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* moba_forward that also writes, per query, the natural-log log-sum-exp of
+ * its scaled logits q.k_u / sqrt(head_dim) over every key it attended (the
+ * softmax normaliser a backward pass reuses).
+ *   lse — device float32 [batch, heads, seq_len]; must not be NULL.
+ * Everything else as moba_forward (same workspace size). */
+int moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                     void* o, int32_t* block_idx, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* MoBA backward (bf16 inputs only; MOBA_ERR_UNSUPPORTED otherwise): the
+ * gradients of o with respect to q, k and v for the upstream gradient dout,
+ * with the forward's block choice held fixed. The routing is a top-k over
+ * block scores, constant between ties, and the gate's scores do not weight
+ * the output, so no gradient flows through the block summaries; what
+ * remains is, per query, the gradient of one softmax attention over its
+ * attended keys. MoBA is used in training and fine-tuning ([S] §3, [P] §2);
+ * the pages give no gradient, this is the plain reading.
+ *   q, k, v, o, block_idx — the forward's inputs and outputs (same problem);
+ *   lse   — device float32 [batch, heads, seq_len] from moba_forward_lse;
+ *   dout  — device, like o: the upstream gradient;
+ *   dq    — output, like q; dk, dv — outputs, like k and v (summed over the
+ *           query heads of each key/value head).
+ *   workspace — at least moba_backward_workspace_size bytes, 256-byte
+ *           aligned, contents on entry irrelevant.
+ * Deterministic: no floating-point atomics; dq sums its per-block parts in
+ * a fixed order. */
+int moba_backward_workspace_size(const moba_problem_t* p, size_t* bytes);
+int moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk,
+                  void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Varlen batch: n_seqs independent sequences of different lengths in one
  * call, each routed and attended on its own, blocks starting at its first
  * token (the per-sequence cu_seqlens packing the pages describe for

@@ -18,10 +18,11 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (MOBA_BF16, MOBA_F32, moba_abi_version, moba_dense_forward, moba_forward,
+from ._lib import (MOBA_BF16, MOBA_F32, moba_abi_version, moba_dense_forward, moba_forward, moba_forward_lse,
                    moba_last_error, moba_pool, moba_problem_t, moba_select, moba_status_str,
                    moba_timing_enable, moba_timing_read, moba_workspace_size,
-                   moba_forward_varlen, moba_workspace_size_varlen)
+                   moba_forward_varlen, moba_workspace_size_varlen, moba_backward,
+                   moba_backward_workspace_size)
 
 __all__ = ["MobaError", "forward", "dense", "pool", "select", "problem", "workspace_bytes",
            "timing", "moba_abi_version", "moba_forward", "moba_dense_forward", "moba_pool",
@@ -100,10 +101,12 @@ def _workspace(p, device):
 
 
 def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None, idx=None,
-            workspace=None, pooling: str = "mean", gate_shared: bool = False):
-    """MoBA forward. Returns (o, block_idx). pooling: the gate's block
-    summary, "mean" (the paper's), "max" or "mean+max". gate_shared: the
-    query heads of one key/value head route on their summed scores."""
+            workspace=None, pooling: str = "mean", gate_shared: bool = False, return_lse: bool = False):
+    """MoBA forward. Returns (o, block_idx), or (o, block_idx, lse) with
+    return_lse (float32 [B, H, S], the natural-log log-sum-exp of each
+    query's scaled logits over its attended keys). pooling: the gate's
+    block summary, "mean" (the paper's), "max" or "mean+max". gate_shared:
+    the query heads of one key/value head route on their summed scores."""
     hkv = _tensors(q, k, v)
     p = problem(q, block_size, top_k, causal, pooling, hkv, gate_shared)
     B, H, S, D = q.shape
@@ -114,9 +117,37 @@ def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None,
     else:
         ws, n = workspace, workspace.numel()
     with torch.cuda.device(q.device):
+        if return_lse:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+            _check(moba_forward_lse(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), bi.data_ptr(),
+                                    lse.data_ptr(), ws.data_ptr(), n, _stream(q.device)), "moba_forward_lse")
+            return o, bi, lse
         _check(moba_forward(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), bi.data_ptr(),
                             ws.data_ptr(), n, _stream(q.device)), "moba_forward")
     return o, bi
+
+
+def backward(q, k, v, o, dout, idx, lse, block_size: int, top_k: int, causal: bool = True):
+    """MoBA backward (bf16): (dq, dk, dv) for the upstream gradient dout,
+    with the forward's block choice idx held fixed; o and lse from
+    forward(..., return_lse=True)."""
+    hkv = _tensors(q, k, v)
+    _tensors(q, o, dout)
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if not (idx.is_cuda and idx.is_contiguous() and idx.dtype == torch.int32 and lse.is_cuda
+            and lse.is_contiguous() and lse.dtype == torch.float32):
+        raise ValueError("idx must be contiguous int32 and lse contiguous float32 on the GPU")
+    p = problem(q, block_size, top_k, causal, "mean", hkv)
+    st, n = moba_backward_workspace_size(p)
+    _check(st, "moba_backward_workspace_size")
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        _check(moba_backward(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                             idx.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             ws.data_ptr(), n, _stream(q.device)), "moba_backward")
+    return dq, dk, dv
 
 
 def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int, causal: bool = True,

@@ -19,8 +19,9 @@ STATUS_NAMES = {0: "MOBA_OK", 1: "MOBA_ERR_NULL", 2: "MOBA_ERR_SHAPE", 3: "MOBA_
                 4: "MOBA_ERR_DTYPE", 5: "MOBA_ERR_UNSUPPORTED", 6: "MOBA_ERR_WORKSPACE",
                 7: "MOBA_ERR_DEVICE"}
 EXPORTED = ["moba_abi_version", "moba_status_str", "moba_last_error", "moba_workspace_size",
-            "moba_forward", "moba_dense_forward", "moba_pool", "moba_select",
+            "moba_forward", "moba_forward_lse", "moba_dense_forward", "moba_pool", "moba_select",
             "moba_workspace_size_varlen", "moba_forward_varlen",
+            "moba_backward_workspace_size", "moba_backward",
             "moba_timing_enable", "moba_timing_read"]
 
 
@@ -49,6 +50,7 @@ def _load():
         "moba_last_error": ([], ctypes.c_char_p),
         "moba_workspace_size": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moba_forward": ([P, vp, vp, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
+        "moba_forward_lse": ([P, vp, vp, vp, vp, i32p, vp, vp, sz, vp], ctypes.c_int),
         "moba_dense_forward": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
         "moba_pool": ([P, vp, vp, vp, sz, vp], ctypes.c_int),
         "moba_select": ([P, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
@@ -56,6 +58,8 @@ def _load():
                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moba_forward_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, vp, vp, vp, vp, i32p, vp,
                                  sz, vp], ctypes.c_int),
+        "moba_backward_workspace_size": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+        "moba_backward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "moba_timing_enable": ([ctypes.c_int], ctypes.c_int),
         "moba_timing_read": ([ctypes.POINTER(moba_kernel_time_t), ctypes.c_int,
                               ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
@@ -102,6 +106,11 @@ def moba_forward(problem, q, k, v, o, block_idx, workspace, workspace_bytes, str
                             q, k, v, o, block_idx, workspace, workspace_bytes, stream)
 
 
+def moba_forward_lse(problem, q, k, v, o, block_idx, lse, workspace, workspace_bytes, stream) -> int:
+    return lib().moba_forward_lse(ctypes.byref(problem) if problem is not None else None,
+                                  q, k, v, o, block_idx, lse, workspace, workspace_bytes, stream)
+
+
 def _cu(cu_seqlens):
     """Host int64 array for cu_seqlens (None stays NULL)."""
     if cu_seqlens is None:
@@ -139,6 +148,18 @@ def moba_pool(problem, k, kbar, workspace, workspace_bytes, stream) -> int:
 def moba_select(problem, q, k, block_idx, workspace, workspace_bytes, stream) -> int:
     return lib().moba_select(ctypes.byref(problem) if problem is not None else None, q, k, block_idx,
                            workspace, workspace_bytes, stream)
+
+
+def moba_backward_workspace_size(problem):
+    """-> (status, bytes)"""
+    n = ctypes.c_size_t(0)
+    st = lib().moba_backward_workspace_size(ctypes.byref(problem) if problem is not None else None, ctypes.byref(n))
+    return st, n.value
+
+
+def moba_backward(problem, q, k, v, o, dout, block_idx, lse, dq, dk, dv, workspace, workspace_bytes, stream) -> int:
+    return lib().moba_backward(ctypes.byref(problem) if problem is not None else None, q, k, v, o, dout, block_idx,
+                               lse, dq, dk, dv, workspace, workspace_bytes, stream)
 
 
 def moba_timing_enable(enable: bool) -> int:

@@ -164,6 +164,30 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
   return MOBA_OK;
 }
 
+// Backward workspace: the forward's plan (its lists and tiles are rebuilt
+// from block_idx) plus delta and the log2-domain log-sum-exp per query, the
+// past-block dq partials and the own-block dq, all fp32.
+struct BwdPlan {
+  size_t delta, lse2, dq_part, dq_own, chunk_counts, total;
+};
+BwdPlan plan_backward(const Plan& P) {
+  BwdPlan B;
+  size_t off = P.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up(bytes);
+    return at;
+  };
+  const size_t rows = (size_t)(P.bh * P.S);
+  B.delta = take(rows * 4);
+  B.lse2 = take(rows * 4);
+  B.dq_part = take(rows * (size_t)P.slots * (size_t)P.D * 4);
+  B.dq_own = take(rows * (size_t)P.D * 4);
+  B.chunk_counts = take((size_t)P.bh * (size_t)((P.S + kRankChunk - 1) / kRankChunk) * (size_t)P.nb * 4);
+  B.total = off;
+  return B;
+}
+
 int check_ws(const Plan& P, void* ws, size_t bytes) {
   if (bytes < P.total)
     return fail(MOBA_ERR_WORKSPACE, "workspace_bytes " + std::to_string(bytes) + " < required " + std::to_string(P.total));
@@ -267,10 +291,11 @@ int check_tensors(const void* q, const void* k, const void* v, const void* o, co
 
 // The whole forward of one validated problem, queued on s.
 int run_forward(const Plan& P, const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
-                void* workspace, hipStream_t s) {
+                void* workspace, hipStream_t s, float* lse = nullptr) {
   int st = run_select(P, q, k, block_idx, workspace, s, nullptr);
   if (st != MOBA_OK) return st;
   AttnArgs aa = attn_args(P, q, k, v, o);
+  aa.lse_out = lse;
   aa.part_o = at<void>(workspace, P.part_o);
   aa.part_lse = at<float>(workspace, P.part_lse);
   if (P.pairs > 0) {
@@ -372,6 +397,124 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
   st = check_ws(P, workspace, workspace_bytes);
   if (st != MOBA_OK) return st;
   return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                     int32_t* block_idx, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan P;
+  int st = plan_problem(p, &P, true);
+  if (st != MOBA_OK) return st;
+  st = check_tensors(q, k, v, o, block_idx);
+  if (st != MOBA_OK) return st;
+  if (!lse) return fail(MOBA_ERR_NULL, "lse is NULL");
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != MOBA_OK) return st;
+  return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream), lse);
+}
+
+static int plan_backward_problem(const moba_problem_t* p, Plan* P, BwdPlan* B) {
+  const int st = plan_problem(p, P, true);
+  if (st != MOBA_OK) return st;
+  if (!P->bf16_in) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports bf16 inputs only (dtype MOBA_BF16)");
+  if (P->nb > 16384) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports at most 16384 blocks");
+  *B = plan_backward(*P);
+  return MOBA_OK;
+}
+
+int moba_backward_workspace_size(const moba_problem_t* p, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
+  Plan P;
+  BwdPlan B;
+  const int st = plan_backward_problem(p, &P, &B);
+  if (st != MOBA_OK) return st;
+  *bytes = B.total;
+  return MOBA_OK;
+}
+
+int moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk, void* dv,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan P;
+  BwdPlan B;
+  int st = plan_backward_problem(p, &P, &B);
+  if (st != MOBA_OK) return st;
+  const void* ins[] = {q, k, v, o, dout, block_idx, lse, dq, dk, dv};
+  const char* names[] = {"q", "k", "v", "o", "dout", "block_idx", "lse", "dq", "dk", "dv"};
+  for (int i = 0; i < 10; ++i)
+    if (!ins[i]) return fail(MOBA_ERR_NULL, std::string(names[i]) + " is NULL");
+  if (workspace_bytes < B.total)
+    return fail(MOBA_ERR_WORKSPACE, "workspace_bytes " + std::to_string(workspace_bytes) + " < required " +
+                                        std::to_string(B.total));
+  if (!workspace) return fail(MOBA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(MOBA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  BwdArgs ba{};
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.o = o;
+  ba.dout = dout;
+  ba.lse = lse;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.bh = P.bh;
+  ba.seq_len = P.S;
+  ba.block_size = P.Bs;
+  ba.n_blocks = P.nb;
+  ba.head_dim = (int)P.D;
+  ba.causal = P.causal;
+  ba.k_eff = (int)P.k_eff;
+  ba.group = (int)P.G;
+  ba.delta = at<float>(workspace, B.delta);
+  ba.lse2 = at<float>(workspace, B.lse2);
+  ba.dq_part = at<float>(workspace, B.dq_part);
+  ba.dq_own = at<float>(workspace, B.dq_own);
+  if (P.pairs > 0) {
+    // The forward's varlen lists, rebuilt from block_idx in a fixed order
+    // (dk and dv sum over them): counts, ranks, offsets, lists, tiles.
+    int32_t* count = at<int32_t>(workspace, P.count);
+    GateArgs ga{};
+    ga.bh = P.bh;
+    ga.seq_len = P.S;
+    ga.block_size = P.Bs;
+    ga.n_blocks = P.nb;
+    ga.top_k = (int)P.top_k;
+    ga.k_eff = (int)P.k_eff;
+    ga.block_idx = const_cast<int32_t*>(block_idx);
+    ga.count = count;
+    ga.rank = at<int32_t>(workspace, P.rank);
+    ga.group = (int)P.G;
+    MOBA_TRY(launch_rank(ga, s, at<int32_t>(workspace, B.chunk_counts)), "rank launch");
+    PackArgs pk{};
+    pk.bh = P.bh;
+    pk.seq_len = P.S;
+    pk.block_size = P.Bs;
+    pk.n_blocks = P.nb;
+    pk.causal = P.causal;
+    pk.top_k = (int)P.top_k;
+    pk.k_eff = (int)P.k_eff;
+    pk.tile_m = kGatherTileM;
+    pk.block_idx = block_idx;
+    pk.count = count;
+    pk.rank = ga.rank;
+    pk.offset = at<int32_t>(workspace, P.offset);
+    pk.tile_start = at<int32_t>(workspace, P.tile_start);
+    pk.qlist = at<int32_t>(workspace, P.qlist);
+    pk.grid = gather_grid_for(P.max_tiles);
+    pk.tile_map = at<int32_t>(workspace, P.tile_map);
+    MOBA_TRY(launch_pack(pk, s), "pack launch");
+    ba.qlist = pk.qlist;
+    ba.offset = pk.offset;
+    ba.tile_map = pk.tile_map;
+    ba.gather_grid = pk.grid;
+  }
+  MOBA_TRY(launch_backward(ba, s), "backward launch");
+  return MOBA_OK;
 }
 
 int moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, size_t* bytes) {

@@ -922,7 +922,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   });
 
   // Dense, or own block continuing the partials' state: normalise once.
-  const float inv = 1.f / pair_sum(eng.l);
+  const float lt = pair_sum(eng.l);
+  const float inv = 1.f / lt;
+  // The natural-log log-sum-exp of the query's scaled logits over every key
+  // it attended (m and l are in the log2 domain), for a backward pass.
+  if (a.lse_out && h == 0) a.lse_out[bh * a.seq_len + t] = (eng.m + fast_log2(lt)) * 0.69314718f;
 #pragma unroll
   for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
@@ -993,6 +997,416 @@ hipError_t launch_diag_merge(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_dense(const AttnArgs& a, hipStream_t s) {
   if (a.bf16_in) return a.head_dim == 128 ? diag_t<bf16, 128, true>(a, s) : diag_t<bf16, 64, true>(a, s);
   return a.head_dim == 128 ? diag_t<float, 128, true>(a, s) : diag_t<float, 64, true>(a, s);
+}
+
+
+// ================================================================ backward
+// MoBA backward for bf16 inputs, the block choice of the forward held fixed
+// (a top-k over block scores has no gradient off ties, and the gate's
+// scores do not weight the output): per query, the gradient of one softmax
+// attention over its attended keys. With l = q.k / sqrt(D), p = exp(l - lse),
+// delta = do . o:  dv_u += p_u do,  ds_u = p_u (do . v_u - delta),
+// dq += ds_u k_u / sqrt(D),  dk_u += ds_u q / sqrt(D).
+//
+// Kernels (each step single-buffered: load a 64-row subtile to LDS, wait,
+// compute, barrier):
+//  bwd_prep    — delta and the log-sum-exp in the log2 domain per query;
+//  dq_past     — block-major like gather_attn (the forward's lists and
+//                tiles): per key subtile S^T = K Q^T and dP^T = V dO^T on
+//                the forward's score path, then dQ^T += K^T dS^T on its P.V
+//                path (K read through the LDS transpose load); one fp32
+//                partial per (query, slot);
+//  dq_own      — the own block, 64 queries per workgroup, causal mask;
+//  dq_reduce   — dq = own + the slots' partials, in slot order (no atomics);
+//  dkv         — key-major: a workgroup holds 64 keys of one block (32 per
+//                wave, as the B operand the way the forward holds queries)
+//                and streams 64-row subtiles of the queries that attend
+//                them: the block's own queries, then its listed queries
+//                (gathered rows), for every query head of the key/value
+//                head. PASS 0 accumulates dV^T += dO^T P, PASS 1
+//                dK^T += Q^T dS (both on the P.V path); together they would
+//                not fit the register file.
+namespace {
+
+// C[row][lane column] for 64 LDS rows (K-swizzled layout) against the B
+// fragments b (32 columns, one per lane column): the forward's score step.
+template <int D>
+__device__ __forceinline__ void mm_rows(const char* buf, int lane, const bf16x8 (&b)[D / 16], f32x16 (&c)[2]) {
+  using E = EngBF16<D>;
+  const int h = lane >> 5, col = lane & 31, sw = E::swz(col);
+  const char* r0 = buf + col * E::ROWB;
+  const char* r1 = r0 + 32 * E::ROWB;
+  c[0] = f32x16{};
+  c[1] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(r0 + 16 * ((2 * kk + h) ^ sw));
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(r1 + 16 * ((2 * kk + h) ^ sw));
+    c[0] = mfma_bf16(a0, b[kk], c[0]);
+    c[1] = mfma_bf16(a1, b[kk], c[1]);
+  }
+}
+
+// acc^T[d][lane column] += sum over the 64 rows of T[row][d] x[row][column],
+// T in LDS (V-swizzled layout, read transposed), x in the C layout of
+// mm_rows (rounded to bf16): the forward's P.V step.
+template <int D>
+__device__ __forceinline__ void mm_trans(const char* buf, int lane, const f32x16 (&x)[2], f32x16 (&acc)[D / 32]) {
+  using E = EngBF16<D>;
+  const int h = lane >> 5, j = lane & 15, half = (lane >> 4) & 1;
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pb[nt][r >> 3][r & 7] = to_bf16(x[nt][r]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int nt = i >> 1, g = i & 1;
+      const int d = 32 * dt + 16 * half + 4 * (j & 3);
+      const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
+      const char* a0 = buf + r0 * E::ROWB + 16 * ((d >> 3) ^ E::swzv(r0)) + 2 * (d & 7);
+      const char* a1 = buf + r1 * E::ROWB + 16 * ((d >> 3) ^ E::swzv(r1)) + 2 * (d & 7);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[dt] = mfma_bf16(vf, pb[nt][g], acc[dt]);
+    }
+}
+
+// A row's D/16 B fragments for this lane half (like EngBF16::load_q).
+template <int D>
+__device__ __forceinline__ void load_frags(bf16x8 (&f)[D / 16], const bf16* row, int h) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) f[kk] = *reinterpret_cast<const bf16x8*>(row + 16 * kk + 8 * h);
+}
+
+// acc (C layout of mm_trans: lane column = row of dst, element r = coordinate
+// 32 dt + crow(r, h)) times scale, to a row of dst in fp32 or bf16.
+template <int D>
+__device__ __forceinline__ void store_row_f32(float* dst, const f32x16 (&acc)[D / 32], int h, float scale) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * rg + 4 * h) =
+          f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
+                acc[dt][4 * rg + 3] * scale};
+}
+template <int D>
+__device__ __forceinline__ void store_row_bf16(bf16* dst, const f32x16 (&acc)[D / 32], int h, float scale) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      EngBF16<D>::put4(dst + 32 * dt + 8 * rg + 4 * h, acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale,
+                       acc[dt][4 * rg + 2] * scale, acc[dt][4 * rg + 3] * scale);
+}
+
+// 64 rows of src (rows[i] = row index, from LDS) into buf, K-swizzled
+// (V = false) or V-swizzled (V = true), by direct HBM -> LDS loads.
+template <int D, int NT, bool V>
+__device__ __forceinline__ void load_rows(const bf16* src, const int* rows, char* buf, int tid) {
+  using E = EngBF16<D>;
+  constexpr int NW = NT / 64, INSTS = E::SLOTS / 64;
+  static_assert(INSTS % NW == 0, "subtile slots must split evenly over the waves");
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
+#pragma unroll
+  for (int ii = 0; ii < INSTS / NW; ++ii) {
+    const int i = ii * NW + w;
+    const int sl = i * 64 + lane;
+    const int row = sl / E::CPR;
+    const int x = (sl % E::CPR) ^ (V ? E::swzv(row) : E::swz(row));
+    lds_dma16(src + (int64_t)rows[row] * D + 8 * x, base + i * 1024);
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int tid = threadIdx.x, sub = tid & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const int64_t n = a.bh * a.seq_len;
+  const int D = a.head_dim, per = D / 16;
+  float sum = 0.f;
+  if (row < n) {
+    const bf16* o = reinterpret_cast<const bf16*>(a.o) + row * D + sub * per;
+    const bf16* g = reinterpret_cast<const bf16*>(a.dout) + row * D + sub * per;
+    for (int e = 0; e < per; ++e) sum = __builtin_fmaf((float)o[e], (float)g[e], sum);
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
+  if (row < n && sub == 0) {
+    a.delta[row] = sum;
+    a.lse2[row] = a.lse[row] * kLog2e;
+  }
+}
+
+// One key subtile of a dq workgroup: p and ds from the scores, dq^T += K^T ds.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_step(const char* bk, const char* bv, const char* bkt, int lane,
+                                        const bf16x8 (&qf)[D / 16], const bf16x8 (&gf)[D / 16], float lse2,
+                                        float delta, float sl2, int key0, int t, f32x16 (&acc)[D / 32]) {
+  const int h = lane >> 5;
+  f32x16 s[2], dp[2];
+  mm_rows<D>(bk, lane, qf, s);
+  mm_rows<D>(bv, lane, gf, dp);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(__builtin_fmaf(s[nt][r], sl2, -lse2));
+      if (MASK && key0 + 32 * nt + crow(r, h) > t) p = 0.f;
+      s[nt][r] = p * (dp[nt][r] - delta);
+    }
+  mm_trans<D>(bkt, lane, s, acc);
+}
+
+// Past blocks: one gather tile (a block and up to 128 listed queries).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_past_kernel(BwdArgs a) {
+  using E = EngBF16<D>;
+  constexpr int NT = 256, KC = D / 16, DT = D / 32;
+  __shared__ __align__(16) char bk[E::TB], bv[E::TB], bkt[E::TB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 tm = *reinterpret_cast<const i32x4*>(a.tile_map + 4 * (int64_t)blockIdx.x);
+  if (tm.x < 0) return;
+  const int64_t blk = __builtin_amdgcn_readfirstlane(tm.x);
+  const int64_t bh = blk / a.n_blocks, j = blk % a.n_blocks;
+  const int64_t e0 = __builtin_amdgcn_readfirstlane(tm.y), e1 = __builtin_amdgcn_readfirstlane(tm.z);
+  const int64_t e = e0 + 32 * w + col;
+  const bool valid = e < e1, wave_on = e0 + 32 * w < e1;
+  const int slots = a.k_eff - 1;
+  const int ev = a.qlist[valid ? e : e0];
+  const int t = ev / slots;
+  const int64_t row = bh * a.seq_len + t;
+  bf16x8 qf[KC], gf[KC];
+  load_frags<D>(qf, reinterpret_cast<const bf16*>(a.q) + row * D, h);
+  load_frags<D>(gf, reinterpret_cast<const bf16*>(a.dout) + row * D, h);
+  const float lse2 = a.lse2[row], delta = a.delta[row];
+  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
+  const int64_t kvh = bh / a.group;
+  const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + j * a.block_size) * D;
+  const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + j * a.block_size) * D;
+  const int nsub = (int)(min<int64_t>(a.block_size, a.seq_len - j * a.block_size) / kSub);
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  for (int sub = 0; sub < nsub; ++sub) {
+    E::template begin_one<NT, false>(kp + (int64_t)sub * kSub * D, bk, tid);
+    E::template begin_one<NT, false>(vp + (int64_t)sub * kSub * D, bv, tid);
+    E::template begin_one<NT, true>(kp + (int64_t)sub * kSub * D, bkt, tid);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
+    lds_dma_wait();
+    __syncthreads();
+    if (wave_on) dq_step<D, false>(bk, bv, bkt, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+    __syncthreads();
+  }
+  if (valid) store_row_f32<D>(a.dq_part + ((bh * a.seq_len * slots) + ev) * D, acc, h, 1.f / __builtin_sqrtf((float)D));
+}
+
+// The own block: 64 consecutive queries of one head.
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
+  using E = EngBF16<D>;
+  constexpr int NT = 128, KC = D / 16, DT = D / 32;
+  __shared__ __align__(16) char bk[E::TB], bv[E::TB], bkt[E::TB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int64_t ntile = a.seq_len / 64;
+  const int64_t bh = blockIdx.x / ntile;
+  const int q0 = (int)((blockIdx.x % ntile) * 64);
+  const int c = (int)(q0 / a.block_size);
+  const int kb = (int)(c * a.block_size);
+  const int kend = a.causal ? q0 + 64 : (int)min<int64_t>(kb + a.block_size, a.seq_len);
+  const int t = q0 + 32 * w + col;
+  const int64_t row = bh * a.seq_len + t;
+  bf16x8 qf[KC], gf[KC];
+  load_frags<D>(qf, reinterpret_cast<const bf16*>(a.q) + row * D, h);
+  load_frags<D>(gf, reinterpret_cast<const bf16*>(a.dout) + row * D, h);
+  const float lse2 = a.lse2[row], delta = a.delta[row];
+  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
+  const int64_t kvh = bh / a.group;
+  const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + kb) * D;
+  const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + kb) * D;
+  const int nsub = (kend - kb) / kSub;
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  for (int sub = 0; sub < nsub; ++sub) {
+    E::template begin_one<NT, false>(kp + (int64_t)sub * kSub * D, bk, tid);
+    E::template begin_one<NT, false>(vp + (int64_t)sub * kSub * D, bv, tid);
+    E::template begin_one<NT, true>(kp + (int64_t)sub * kSub * D, bkt, tid);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_dma_wait();
+    __syncthreads();
+    const int key0 = kb + sub * kSub;
+    if (a.causal && key0 + kSub > q0 + 32 * w) {
+      if (key0 <= q0 + 32 * w + 31) dq_step<D, true>(bk, bv, bkt, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
+    } else {
+      dq_step<D, false>(bk, bv, bkt, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+    }
+    __syncthreads();
+  }
+  store_row_f32<D>(a.dq_own + row * D, acc, h, 1.f / __builtin_sqrtf((float)D));
+}
+
+// dq = own-block part + the past slots' partials (slot order), to bf16.
+__global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a) {
+  const int D = a.head_dim, tpr = D / 4;  // threads per row, 4 coordinates each
+  const int rows_per = 256 / tpr;
+  const int64_t row = (int64_t)blockIdx.x * rows_per + threadIdx.x / tpr;
+  if (row >= a.bh * a.seq_len) return;
+  const int d = 4 * (threadIdx.x % tpr);
+  const int64_t t = row % a.seq_len;
+  const int c = (int)(t / a.block_size);
+  const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
+  const int slots = a.k_eff - 1;
+  const int n = min(slots, n_elig);
+  f32x4 x = *reinterpret_cast<const f32x4*>(a.dq_own + row * D + d);
+  for (int s = 0; s < n; ++s) {
+    const f32x4 y = *reinterpret_cast<const f32x4*>(a.dq_part + (row * slots + s) * D + d);
+    x += y;
+  }
+  bf16x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = to_bf16(x[e]);
+  *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.dq) + row * D + d) = o;
+}
+
+// dK (PASS 1) or dV (PASS 0) for 64 keys of one block of one key/value head.
+template <int D, int PASS>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dkv_kernel(BwdArgs a) {
+  using E = EngBF16<D>;
+  constexpr int NT = 128, KC = D / 16, DT = D / 32;
+  __shared__ __align__(16) char bq[E::TB], bx[E::TB], by[PASS == 1 ? E::TB : 16];
+  __shared__ int rows[64];
+  __shared__ float lse2s[64], deltas[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int64_t nchunk = a.block_size / kSub;
+  const int64_t kc = blockIdx.x % nchunk;
+  const int64_t j = (blockIdx.x / nchunk) % a.n_blocks;
+  const int64_t kvh = blockIdx.x / (nchunk * a.n_blocks);
+  const int64_t k0 = j * a.block_size + kc * kSub;
+  if (k0 >= a.seq_len) return;  // past the end of a short last block
+  const int u = (int)k0 + 32 * w + col;  // this lane's key
+  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + u) * D;
+  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + u) * D;
+  bf16x8 kf[KC], vf[PASS == 1 ? KC : 1];
+  load_frags<D>(kf, krow, h);
+  if constexpr (PASS == 1) load_frags<D>(vf, vrow, h);
+  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
+  const int slots = a.k_eff - 1;
+  const int64_t jend = min<int64_t>((j + 1) * a.block_size, a.seq_len);
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // One 64-row subtile of query head bh: rows from row_of(i) (valid when
+  // i < n), causal mask against the keys when MASK.
+  auto subtile = [&](int64_t bh, int n, bool mask, auto&& row_of) {
+    if (tid < 64) {
+      const bool ok = tid < n;
+      const int t = row_of(ok ? tid : 0);
+      rows[tid] = t;
+      lse2s[tid] = ok ? a.lse2[bh * a.seq_len + t] : __builtin_inff();
+      deltas[tid] = ok ? a.delta[bh * a.seq_len + t] : 0.f;
+    }
+    __syncthreads();
+    const bf16* qb = reinterpret_cast<const bf16*>(a.q) + bh * a.seq_len * D;
+    const bf16* gb = reinterpret_cast<const bf16*>(a.dout) + bh * a.seq_len * D;
+    load_rows<D, NT, false>(qb, rows, bq, tid);
+    if constexpr (PASS == 0) {
+      load_rows<D, NT, true>(gb, rows, bx, tid);   // dO^T for dV
+    } else {
+      load_rows<D, NT, false>(gb, rows, bx, tid);  // dO for dP
+      load_rows<D, NT, true>(qb, rows, by, tid);   // Q^T for dK
+    }
+    lds_dma_wait();
+    __syncthreads();
+    f32x16 s[2];
+    mm_rows<D>(bq, lane, kf, s);
+    f32x16 dp[2];
+    if constexpr (PASS == 1) mm_rows<D>(bx, lane, vf, dp);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int r0 = 32 * nt + 8 * rg + 4 * h;  // rows of elements 4 rg .. 4 rg + 3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          float p = fast_exp2(__builtin_fmaf(s[nt][r], sl2, -l4[e]));
+          if (mask && u > rows[r0 + e]) p = 0.f;
+          if constexpr (PASS == 0) s[nt][r] = p;
+          else s[nt][r] = p * (dp[nt][r] - d4[e]);
+        }
+      }
+    mm_trans<D>(PASS == 0 ? bx : by, lane, s, acc);
+    __syncthreads();
+  };
+  for (int g = 0; g < a.group; ++g) {
+    const int64_t bh = kvh * a.group + g;
+    // The block's own queries: those at or after the keys (causal), or all.
+    const int64_t qs = a.causal ? k0 : j * a.block_size;
+    for (int64_t t0 = qs; t0 < jend; t0 += 64) {
+      const int n = (int)min<int64_t>(64, jend - t0);
+      subtile(bh, n, a.causal, [&](int i) { return (int)(t0 + i); });
+    }
+    // Its listed queries (past-block routing of later, or other, queries).
+    if (slots > 0) {
+      const int32_t* lst = a.qlist + a.offset[bh * a.n_blocks + j];
+      const int cnt = a.offset[bh * a.n_blocks + j + 1] - a.offset[bh * a.n_blocks + j];
+      for (int i0 = 0; i0 < cnt; i0 += 64) {
+        const int n = min(64, cnt - i0);
+        subtile(bh, n, false, [&](int i) { return lst[i0 + i] / slots; });
+      }
+    }
+  }
+  bf16* dst = reinterpret_cast<bf16*>(PASS == 0 ? a.dv : a.dk) + (kvh * a.seq_len + u) * D;
+  store_row_bf16<D>(dst, acc, h, PASS == 0 ? 1.f : 1.f / __builtin_sqrtf((float)D));
+}
+
+template <int D>
+hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = a.bh * a.seq_len;
+  {
+    KernelTimer t(s, "bwd_prep");
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.k_eff > 1 && a.gather_grid > 0) {
+    KernelTimer t(s, "bwd_dq_past");
+    hipLaunchKernelGGL(dq_past_kernel<D>, dim3((unsigned)a.gather_grid), dim3(256), 0, s, a);
+  }
+  {
+    KernelTimer t(s, "bwd_dq_own");
+    hipLaunchKernelGGL(dq_own_kernel<D>, dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), 0, s, a);
+  }
+  {
+    KernelTimer t(s, "bwd_dq_reduce");
+    const int rows_per = 256 / (D / 4);
+    hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((rows + rows_per - 1) / rows_per)), dim3(256), 0, s, a);
+  }
+  const int64_t nchunk = a.block_size / kSub;
+  const int64_t kv_wgs = (a.bh / a.group) * a.n_blocks * nchunk;
+  {
+    KernelTimer t(s, "bwd_dv");
+    hipLaunchKernelGGL((dkv_kernel<D, 0>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+  }
+  {
+    KernelTimer t(s, "bwd_dk");
+    hipLaunchKernelGGL((dkv_kernel<D, 1>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? backward_t<128>(a, s) : backward_t<64>(a, s);
 }
 
 }  // namespace moba

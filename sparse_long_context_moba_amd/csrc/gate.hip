@@ -56,6 +56,7 @@ constexpr int kNoBlock = 0x7fffffff;
 constexpr int kTileB = 32;          // pooled keys per LDS tile
 constexpr int kLdsBinsMax = 8192;   // per-workgroup histogram bins kept in LDS
 constexpr int kRankQ = 1024;        // queries per rank workgroup
+static_assert(kRankQ == kRankChunk, "rank chunk of the ordered ranks");
 
 // Strict order: higher score first, then lower block index.
 __device__ __forceinline__ bool better64(double s1, int j1, double s2, int j2) {
@@ -856,6 +857,100 @@ static hipError_t gate_launch_t(const GateArgs& a, hipStream_t s) {
     KernelTimer timer(s, "rank");
     hipLaunchKernelGGL(rank_kernel, dim3((unsigned)rank_wgs), dim3(256), rank_lds, s, a);
   }
+  return hipGetLastError();
+}
+
+// Ranks in a fixed order (for sums over a block's list that must not
+// depend on scheduling): chunk_count counts each chunk's picks per block,
+// chunk_scan turns them into per-chunk bases (and the block totals in
+// count), and rank_ordered numbers the picks of a chunk in the order
+// (64-query group, column of block_idx, lane) with wave ballots: lanes
+// with the same block in one column get consecutive ranks by lane.
+__global__ __launch_bounds__(256) void chunk_count_kernel(GateArgs a, int32_t* cc, int64_t nchunk) {
+  extern __shared__ __align__(16) char smem[];
+  int* bins = reinterpret_cast<int*>(smem);
+  const int NB = (int)a.n_blocks;
+  const int64_t bh = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+  for (int i = threadIdx.x; i < NB; i += 256) bins[i] = 0;
+  __syncthreads();
+  for (int qq = threadIdx.x; qq < kRankQ; qq += 256) {
+    const int64_t t = ch * kRankQ + qq;
+    if (t >= a.seq_len) break;
+    const int c = (int)(t / a.block_size);
+    const int32_t* row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
+    for (int i = 0; i < a.top_k; ++i) {
+      const int j = row[i];
+      if (j < 0) break;
+      if (j != c) atomicAdd(bins + j, 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NB; i += 256) cc[(bh * nchunk + ch) * NB + i] = bins[i];
+}
+
+__global__ __launch_bounds__(256) void chunk_scan_kernel(GateArgs a, int32_t* cc, int64_t nchunk) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int NB = (int)a.n_blocks;
+  if (id >= a.bh * NB) return;
+  const int64_t bh = id / NB, j = id % NB;
+  int32_t run = 0;
+  for (int64_t ch = 0; ch < nchunk; ++ch) {
+    int32_t* p = cc + (bh * nchunk + ch) * NB + j;
+    const int32_t n = *p;
+    *p = run;
+    run += n;
+  }
+  a.count[id] = run;
+}
+
+__global__ __launch_bounds__(64) void rank_ordered_kernel(GateArgs a, const int32_t* cc, int64_t nchunk) {
+  extern __shared__ __align__(16) char smem[];
+  int* bins = reinterpret_cast<int*>(smem);
+  const int NB = (int)a.n_blocks;
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+  const int slots = a.k_eff - 1;
+  for (int i = lane; i < NB; i += 64) bins[i] = cc[(bh * nchunk + ch) * NB + i];
+  __syncthreads();
+  for (int g = 0; g < kRankQ; g += 64) {
+    const int64_t t = ch * kRankQ + g + lane;
+    const bool on = t < a.seq_len;
+    const int c = on ? (int)(t / a.block_size) : -1;
+    const int32_t* row = a.block_idx + (bh * a.seq_len + (on ? t : 0)) * a.top_k;
+    int32_t* rk = a.rank + (bh * a.seq_len + (on ? t : 0)) * (int64_t)slots;
+    int s = 0;          // this lane's past-block index so far
+    bool done = !on;    // a -1 ends the row
+    for (int i = 0; i < a.top_k; ++i) {
+      int j = done ? -1 : row[i];
+      if (j < 0) done = true;
+      const bool pick = !done && j != c;
+      uint64_t todo = __builtin_amdgcn_ballot_w64(pick);
+      while (todo) {
+        const int leader = __builtin_ctzll(todo);
+        const int jl = __builtin_amdgcn_readlane(j, leader);
+        const uint64_t same = __builtin_amdgcn_ballot_w64(pick && j == jl);
+        const int base = bins[jl];
+        if (pick && j == jl) rk[s] = base + __builtin_popcountll(same & ((1ull << lane) - 1));
+        __syncthreads();  // every lane has read bins[jl] before it moves
+        if (lane == leader) bins[jl] = base + __builtin_popcountll(same);
+        __syncthreads();
+        todo &= ~same;
+      }
+      if (pick) ++s;
+    }
+  }
+}
+
+hipError_t launch_rank(const GateArgs& a, hipStream_t s, int32_t* chunk_counts) {
+  if (a.k_eff < 2) return hipSuccess;
+  const int64_t nchunk = (a.seq_len + kRankQ - 1) / kRankQ;
+  const int lds = (int)a.n_blocks * 4;
+  if (lds > 65536) return hipErrorInvalidValue;
+  KernelTimer timer(s, "rank_ordered");
+  hipLaunchKernelGGL(chunk_count_kernel, dim3((unsigned)(a.bh * nchunk)), dim3(256), lds, s, a, chunk_counts, nchunk);
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3((unsigned)((a.bh * a.n_blocks + 255) / 256)), dim3(256), 0, s, a,
+                     chunk_counts, nchunk);
+  hipLaunchKernelGGL(rank_ordered_kernel, dim3((unsigned)(a.bh * nchunk)), dim3(64), lds, s, a, chunk_counts, nchunk);
   return hipGetLastError();
 }
 

@@ -90,6 +90,7 @@ struct AttnArgs {
   void* part_o;               // [bh, S, k_eff - 1, D] in the input dtype, lane-native order
   float* part_lse;            // [bh, S, k_eff - 1], log2 domain
   int group;                  // query heads per key/value head: k, v of query head bh are head bh / group
+  float* lse_out;             // optional [bh, S]: natural-log log-sum-exp per query (own-block kernel)
 };
 constexpr int kGatherTileM = 128;
 // Gather workgroups for a bound on the number of tiles (a multiple of the
@@ -98,5 +99,37 @@ constexpr int64_t gather_grid_for(int64_t max_tiles) { return (max_tiles + 7) / 
 hipError_t launch_gather(const AttnArgs& a, hipStream_t s);
 hipError_t launch_diag_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_dense(const AttnArgs& a, hipStream_t s);
+
+// Backward (bf16 inputs): gradients with the forward's block choice fixed.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;            // [bh, S] natural-log log-sum-exp from the forward
+  void* dq;                    // [bh, S, D]
+  void* dk;                    // [bh / group, S, D]
+  void* dv;                    // [bh / group, S, D]
+  int64_t bh, seq_len, block_size, n_blocks;
+  int head_dim;
+  bool causal;
+  int k_eff;
+  int group;                   // query heads per key/value head
+  const int32_t* qlist;        // per-block query lists (as for the forward's gather)
+  const int32_t* offset;       // [bh * nb + 1] list offsets
+  const int32_t* tile_map;     // gather tiles
+  int64_t gather_grid;
+  float* delta;                // [bh, S] do . o
+  float* lse2;                 // [bh, S] log-sum-exp in the log2 domain
+  float* dq_part;              // [bh, S, k_eff - 1, D] past-block dq partials
+  float* dq_own;               // [bh, S, D] own-block dq
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+// Ranks of a given block_idx in a fixed order, and the per-block counts
+// (a.count), for the backward; chunk_counts: [bh, ceil(S / 1024), nb] int32
+// scratch. Needs n_blocks <= 16384.
+constexpr int64_t kRankChunk = 1024;
+hipError_t launch_rank(const GateArgs& a, hipStream_t s, int32_t* chunk_counts);
 
 }  // namespace moba

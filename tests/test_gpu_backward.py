@@ -1,0 +1,87 @@
+"""GPU parity of the MoBA backward (bf16) against the fp64 oracle's
+backward_head, every row and every key, with the GPU forward's block
+choice held fixed on both sides (the gradient is defined for a given
+choice). Also the forward's log-sum-exp output against the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moba as orc
+from tests.parity import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# Tolerances (bf16 inputs, fp32 accumulation, P and dS rounded to bf16 for
+# the MFMA products, as P is in the forward): the error of a gradient entry
+# is a sum of per-key terms each off by about 2^-8 of its size, so it is
+# bounded relative to the tensor's own scale: max |err| <= 2e-2 * max |ref|.
+REL = 2e-2
+LSE_TOL = 1e-4  # fp32 log-sum-exp of logits of size ~10: rounding ~1e-6
+
+
+def _round(x):
+    import synth
+    return synth.round_to_bf16(x)
+
+
+def _inputs(seed, B, H, Hkv, S, D, Bs, bias=0.5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    nb = -(-S // Bs)
+    k += np.repeat(rng.normal(0, bias, (B, Hkv, nb, D)).astype(np.float32), Bs, axis=2)[:, :, :S]
+    v = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    do = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    return _round(q), _round(k), _round(v), _round(do)
+
+
+CASES = [
+    # label, seed, B, H, Hkv, S, D, Bs, top_k, causal, shared
+    ("d128-bs128-k3", 70, 1, 2, 2, 1024, 128, 128, 3, True, False),
+    ("d64-bs64-k4-noncausal", 71, 1, 2, 2, 512, 64, 64, 4, False, False),
+    ("d128-bs256-short192", 72, 1, 2, 2, 1216, 128, 256, 3, True, False),
+    ("d128-k1", 73, 1, 1, 1, 512, 128, 128, 1, True, False),
+    ("d64-topk-all", 74, 1, 1, 1, 512, 64, 64, 9, True, False),
+    ("d128-gqa2-shared", 75, 1, 4, 2, 1024, 128, 128, 3, True, True),
+    ("d128-gqa4-per-head-b2", 76, 2, 4, 1, 512, 128, 128, 2, True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(case):
+    import sparse_long_context_moba_amd as moba
+    label, seed, B, H, Hkv, S, D, Bs, top_k, causal, shared = case
+    q, k, v, do = _inputs(seed, B, H, Hkv, S, D, Bs)
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    say(f"[gpu] backward {label}: q={q.shape} kv={k.shape} Bs={Bs} top_k={top_k} causal={causal} shared={shared}")
+    o, idx, lse = moba.forward(qd, kd, vd, Bs, top_k, causal, gate_shared=shared, return_lse=True)
+    dq, dk, dv = moba.backward(qd, kd, vd, o, dod, idx, lse, Bs, top_k, causal)
+    dq2, dk2, dv2 = moba.backward(qd, kd, vd, o, dod, idx, lse, Bs, top_k, causal)
+    torch.cuda.synchronize()
+    for x, y in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), "backward is not run-to-run bit-identical"
+    idx = idx.cpu().numpy()
+    lse = lse.cpu().numpy()
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    G = H // Hkv
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0, "lse": 0.0}
+    for b in range(B):
+        for hk in range(Hkv):
+            rdk = np.zeros((S, D))
+            rdv = np.zeros((S, D))
+            for g in range(G):
+                h = hk * G + g
+                gq, gk, gv, glse = orc.backward_head(q[b, h], k[b, hk], v[b, hk], do[b, h], idx[b, h], Bs, causal)
+                rdk += gk
+                rdv += gv
+                e_lse = np.abs(lse[b, h] - glse).max()
+                assert e_lse <= LSE_TOL, f"{label} b={b} h={h}: lse error {e_lse:.3e}"
+                e = np.abs(dq[b, h] - gq).max()
+                assert e <= REL * np.abs(gq).max(), f"{label} b={b} h={h}: dq error {e:.3e} (scale {np.abs(gq).max():.3e})"
+                worst["dq"] = max(worst["dq"], e / np.abs(gq).max())
+                worst["lse"] = max(worst["lse"], e_lse)
+            for name, got, ref in (("dk", dk[b, hk], rdk), ("dv", dv[b, hk], rdv)):
+                e = np.abs(got - ref).max()
+                assert e <= REL * np.abs(ref).max(), f"{label} b={b} kv={hk}: {name} error {e:.3e} (scale {np.abs(ref).max():.3e})"
+                worst[name] = max(worst[name], e / np.abs(ref).max())
+    say(f"[gpu] backward {label}: ok, max error / scale: " + ", ".join(f"{n}={v:.2e}" for n, v in worst.items()))
