@@ -154,6 +154,68 @@ def cpu_baseline(w, n_rows):
     }
 
 
+def backward_bench(args, w, wm, q, k, v, moba, torch):
+    """One step = one moba_backward over the workload (the forward's o,
+    block_idx and log-sum-exp resident in HBM, a seeded upstream gradient).
+    Algorithmic work: 10*D flops per (query, attended key), the five
+    D-length products of a softmax-attention backward (scores, dP, dQ, dK,
+    dV); the kernels recompute the scores once more per pass."""
+    if w.dtype != "bf16":
+        print("the backward is built for bf16 workloads only", file=sys.stderr)
+        sys.exit(2)
+    o, idx, lse = moba.forward(q, k, v, w.block_size, w.top_k, w.causal, pooling=w.pooling,
+                               gate_shared=w.gate_shared, return_lse=True)
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    dout = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+
+    def bstep():
+        moba.backward(q, k, v, o, dout, idx, lse, w.block_size, w.top_k, w.causal)
+
+    for _ in range(args.warmup):
+        bstep()
+    torch.cuda.synchronize()
+    log(f"backward warmup {args.warmup} done; timing {args.steps} steps")
+    with moba.timing() as tm:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            bstep()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms = 1e3 * elapsed / args.steps
+    kern = {n: {"launches": c, "avg_ms": tot / c} for n, c, tot in tm.rows}
+    log("kernels: " + ", ".join(f"{n} {x['avg_ms']:.3f}ms" for n, x in kern.items()))
+    D, bh = w.head_dim, w.batch * w.heads
+    past_keys = wm["past_flops"] // (4 * D)
+    own_keys = wm["own_flops"] // (4 * D)
+    flops = 10 * D * (past_keys + own_keys)
+    # per-kernel algorithmic work: dq kernels 6*D per pair (scores, dP, dQ);
+    # the dV pass 4*D (scores, dV), the dK pass 6*D (scores, dP, dK).
+    units = {"bwd_dq_past": 6 * D * past_keys, "bwd_dq_own": 6 * D * own_keys,
+             "bwd_dv": 4 * D * (past_keys + own_keys), "bwd_dk": 6 * D * (past_keys + own_keys)}
+    dom = max((n for n in kern if n in units), key=lambda n: kern[n]["avg_ms"])
+    ach = units[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "MoBA bwd tokens/sec + effective TFLOP/s (% bf16 MFMA peak)",
+        "value": round(w.batch * w.seq_len / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (the forward's recipe; upstream gradient ~ N(0,1))",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kvh, "seq_len": w.seq_len,
+                   "head_dim": D, "block_size": w.block_size, "top_k": w.top_k, "causal": w.causal,
+                   "parallelism": "single GPU"},
+        "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "pct_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {n: round(x["avg_ms"], 4) for n, x in kern.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "work_per_launch": units[dom], "work_unit": "flop",
+                     "avg_launch_ms": round(kern[dom]["avg_ms"], 4)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +228,9 @@ def main():
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a plain device copy whose "
                          "HBM counters calibrate FETCH_SIZE/WRITE_SIZE readings)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the MoBA backward (dq, dk, dv for a fixed block choice) instead of the forward "
+                         "and print its own JSON line (bf16 workloads)")
     ap.add_argument("--gen-workers", type=int, default=None,
                     help="processes generating the inputs (default: one per core, up to 16; use 1 under a profiler)")
     args = ap.parse_args()
@@ -203,6 +268,8 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {n} bytes done")
         del src, dst
+    if args.backward:
+        return backward_bench(args, w, wm, q, k, v, moba, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

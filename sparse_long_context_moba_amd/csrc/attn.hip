@@ -1128,12 +1128,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const int tid = threadIdx.x, sub = tid & 15;
   const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
   const int64_t n = a.bh * a.seq_len;
-  const int D = a.head_dim, per = D / 16;
+  const int D = a.head_dim;
   float sum = 0.f;
   if (row < n) {
-    const bf16* o = reinterpret_cast<const bf16*>(a.o) + row * D + sub * per;
-    const bf16* g = reinterpret_cast<const bf16*>(a.dout) + row * D + sub * per;
-    for (int e = 0; e < per; ++e) sum = __builtin_fmaf((float)o[e], (float)g[e], sum);
+    // 16 lanes per row, one 16-byte (D = 128) or 8-byte (D = 64) load each.
+    const bf16* o = reinterpret_cast<const bf16*>(a.o) + row * D;
+    const bf16* g = reinterpret_cast<const bf16*>(a.dout) + row * D;
+    if (D == 128) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + 8 * sub);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(g + 8 * sub);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum = __builtin_fmaf((float)x[e], (float)y[e], sum);
+    } else {
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(o + 4 * sub);
+      const bf16x4 y = *reinterpret_cast<const bf16x4*>(g + 4 * sub);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum = __builtin_fmaf((float)x[e], (float)y[e], sum);
+    }
   }
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);

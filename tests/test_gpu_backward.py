@@ -85,3 +85,54 @@ def test_backward_parity(case):
                 assert e <= REL * np.abs(ref).max(), f"{label} b={b} kv={hk}: {name} error {e:.3e} (scale {np.abs(ref).max():.3e})"
                 worst[name] = max(worst[name], e / np.abs(ref).max())
     say(f"[gpu] backward {label}: ok, max error / scale: " + ", ".join(f"{n}={v:.2e}" for n, v in worst.items()))
+
+
+def test_backward_headline_sampled():
+    """headline_32k (32 heads, 32768 tokens, block 512, top_k 3) at full
+    size, in the launch configuration bench.py --backward times: dq on 256
+    seeded sampled rows (plus edge rows), and dk, dv on every key of two
+    blocks (the first and the last) of the first and the last head, each
+    summed by the oracle over every query that attends those keys."""
+    import synth
+    import sparse_long_context_moba_amd as moba
+    w = synth.WORKLOADS["headline_32k"]
+    S, D, Bs = w.seq_len, w.head_dim, w.block_size
+    say("[gpu] backward headline_32k: generating inputs")
+    q = torch.empty((1, w.heads, S, D), dtype=torch.bfloat16, device="cuda")
+    k, v = (torch.empty_like(q) for _ in range(2))
+    host = {}
+    for b, hk, qh, kh, vh in synth.iter_groups_parallel(w):
+        for dst, x in ((q, qh), (k, kh[None]), (v, vh[None])):
+            dst[b, hk:hk + 1].copy_(torch.from_numpy(x).view(torch.bfloat16))
+        host[hk] = tuple((x.view(np.uint16).astype(np.uint32) << 16).view(np.float32) for x in (qh[0], kh, vh))
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    dout = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o, idx, lse = moba.forward(q, k, v, Bs, w.top_k, w.causal, return_lse=True)
+    dq, dk, dv = moba.backward(q, k, v, o, dout, idx, lse, Bs, w.top_k, w.causal)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    for h in (0, w.heads - 1):
+        qh, kh, vh = host[h]
+        doh = dout[0, h].float().cpu().numpy()
+        ih = idx[0, h].cpu().numpy()
+        dqh, dkh, dvh = (x[0, h].float().cpu().numpy() for x in (dq, dk, dv))
+        rows = np.unique(np.concatenate([rng.choice(S, 256, replace=False), [0, Bs - 1, Bs, S - 1]]))
+        ref = np.stack([orc.attend_grad(qh[t], kh, vh, orc.attended_keys(int(t), ih[t], Bs, True, S), doh[t])[0]
+                        for t in rows])
+        e = np.abs(dqh[rows] - ref).max()
+        assert e <= REL * np.abs(ref).max(), f"h={h}: dq error {e:.3e} (scale {np.abs(ref).max():.3e})"
+        for j in (0, S // Bs - 1):
+            lo, hi = j * Bs, (j + 1) * Bs
+            users = np.nonzero((ih == j).any(axis=1))[0]
+            rdk = np.zeros((Bs, D))
+            rdv = np.zeros((Bs, D))
+            for t in users:
+                keys = orc.attended_keys(int(t), ih[t], Bs, True, S)
+                _, gk, gv = orc.attend_grad(qh[t], kh, vh, keys, doh[t])
+                sel = (keys >= lo) & (keys < hi)
+                rdk[keys[sel] - lo] += gk[sel]
+                rdv[keys[sel] - lo] += gv[sel]
+            for name, got, r in (("dk", dkh[lo:hi], rdk), ("dv", dvh[lo:hi], rdv)):
+                e = np.abs(got - r).max()
+                assert e <= REL * np.abs(r).max(), f"h={h} block={j}: {name} error {e:.3e} (scale {np.abs(r).max():.3e})"
+            say(f"[gpu] backward headline_32k h={h} block={j}: {len(users)} queries attend it; ok")
