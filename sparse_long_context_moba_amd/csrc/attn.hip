@@ -1018,8 +1018,9 @@ hipError_t launch_dense(const AttnArgs& a, hipStream_t s) {
 //                partial per (query, slot);
 //  dq_own      — the own block, 64 queries per workgroup, causal mask;
 //  dq_reduce   — dq = own + the slots' partials, in slot order (no atomics);
-//  dkv         — key-major: a workgroup holds 64 keys of one block (32 per
-//                wave, as the B operand the way the forward holds queries)
+//  dkv         — key-major: a workgroup holds 128 (or 64) keys of one
+//                block (32 per wave, as the B operand the way the forward
+//                holds queries)
 //                and streams 64-row subtiles of the queries that attend
 //                them: the block's own queries, then its listed queries
 //                (gathered rows), for every query head of the key/value
@@ -1286,20 +1287,21 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a) {
   *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.dq) + row * D + d) = o;
 }
 
-// dK (PASS 1) or dV (PASS 0) for 64 keys of one block of one key/value head.
-template <int D, int PASS>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dkv_kernel(BwdArgs a) {
+// dK (PASS 1) or dV (PASS 0) for 32 * NW keys of one block of one
+// key/value head.
+template <int D, int PASS, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dkv_kernel(BwdArgs a) {
   using E = EngBF16<D>;
-  constexpr int NT = 128, KC = D / 16, DT = D / 32;
+  constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, KEYS = 32 * NW;
   __shared__ __align__(16) char bq[E::TB], bx[E::TB], by[PASS == 1 ? E::TB : 16];
   __shared__ int rows[64];
   __shared__ float lse2s[64], deltas[64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int64_t nchunk = a.block_size / kSub;
+  const int64_t nchunk = a.block_size / KEYS;
   const int64_t kc = blockIdx.x % nchunk;
   const int64_t j = (blockIdx.x / nchunk) % a.n_blocks;
   const int64_t kvh = blockIdx.x / (nchunk * a.n_blocks);
-  const int64_t k0 = j * a.block_size + kc * kSub;
+  const int64_t k0 = j * a.block_size + kc * KEYS;
   if (k0 >= a.seq_len) return;  // past the end of a short last block
   const int u = (int)k0 + 32 * w + col;  // this lane's key
   const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + u) * D;
@@ -1318,7 +1320,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   auto subtile = [&](int64_t bh, int n, bool mask, auto&& row_of) {
     if (tid < 64) {
       const bool ok = tid < n;
-      const int t = row_of(ok ? tid : 0);
+      const int t = row_of(ok ? tid : 0);  // a padding row repeats a valid one
       rows[tid] = t;
       lse2s[tid] = ok ? a.lse2[bh * a.seq_len + t] : __builtin_inff();
       deltas[tid] = ok ? a.delta[bh * a.seq_len + t] : 0.f;
@@ -1402,15 +1404,20 @@ hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
     const int rows_per = 256 / (D / 4);
     hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((rows + rows_per - 1) / rows_per)), dim3(256), 0, s, a);
   }
-  const int64_t nchunk = a.block_size / kSub;
-  const int64_t kv_wgs = (a.bh / a.group) * a.n_blocks * nchunk;
+  // 128 keys per workgroup where every block length is a multiple of 128,
+  // else 64.
+  const int64_t last = a.seq_len - (a.n_blocks - 1) * a.block_size;
+  const bool wide = a.block_size % 128 == 0 && last % 128 == 0;
+  const int64_t kv_wgs = (a.bh / a.group) * a.n_blocks * (a.block_size / (wide ? 128 : 64));
   {
     KernelTimer t(s, "bwd_dv");
-    hipLaunchKernelGGL((dkv_kernel<D, 0>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+    if (wide) hipLaunchKernelGGL((dkv_kernel<D, 0, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dkv_kernel<D, 0, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
   }
   {
     KernelTimer t(s, "bwd_dk");
-    hipLaunchKernelGGL((dkv_kernel<D, 1>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+    if (wide) hipLaunchKernelGGL((dkv_kernel<D, 1, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dkv_kernel<D, 1, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
   }
   return hipGetLastError();
 }
