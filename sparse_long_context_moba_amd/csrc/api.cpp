@@ -165,10 +165,10 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
 }
 
 // Backward workspace: the forward's plan (its lists and tiles are rebuilt
-// from block_idx) plus delta and the log2-domain log-sum-exp per query, the
-// past-block dq partials and the own-block dq, all fp32.
+// from block_idx) plus delta and the log2-domain log-sum-exp per query and
+// the past-block dq partials, all fp32, and the ordered ranks' chunk counts.
 struct BwdPlan {
-  size_t delta, lse2, dq_part, dq_own, chunk_counts, total;
+  size_t delta, lse2, dq_part, chunk_counts, total;
 };
 BwdPlan plan_backward(const Plan& P) {
   BwdPlan B;
@@ -182,7 +182,6 @@ BwdPlan plan_backward(const Plan& P) {
   B.delta = take(rows * 4);
   B.lse2 = take(rows * 4);
   B.dq_part = take(rows * (size_t)P.slots * (size_t)P.D * 4);
-  B.dq_own = take(rows * (size_t)P.D * 4);
   B.chunk_counts = take((size_t)P.bh * (size_t)((P.S + kRankChunk - 1) / kRankChunk) * (size_t)P.nb * 4);
   B.total = off;
   return B;
@@ -473,7 +472,6 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
   ba.delta = at<float>(workspace, B.delta);
   ba.lse2 = at<float>(workspace, B.lse2);
   ba.dq_part = at<float>(workspace, B.dq_part);
-  ba.dq_own = at<float>(workspace, B.dq_own);
   if (P.pairs > 0) {
     // The forward's varlen lists, rebuilt from block_idx in a fixed order
     // (dk and dv sum over them): counts, ranks, offsets, lists, tiles.

@@ -1016,8 +1016,9 @@ hipError_t launch_dense(const AttnArgs& a, hipStream_t s) {
 //                the forward's score path, then dQ^T += K^T dS^T on its P.V
 //                path (K read through the LDS transpose load); one fp32
 //                partial per (query, slot);
-//  dq_own      — the own block, 64 queries per workgroup, causal mask;
-//  dq_reduce   — dq = own + the slots' partials, in slot order (no atomics);
+//  dq_own      — the own block, 64 queries per workgroup, causal mask; it
+//                then adds the slots' partials in slot order and writes dq
+//                (no atomics);
 //  dkv         — key-major: a workgroup holds 128 (or 64) keys of one
 //                block (32 per wave, as the B operand the way the forward
 //                holds queries)
@@ -1261,30 +1262,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     __syncthreads();
   }
-  store_row_f32<D>(a.dq_own + row * D, acc, h, 1.f / __builtin_sqrtf((float)D));
-}
-
-// dq = own-block part + the past slots' partials (slot order), to bf16.
-__global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a) {
-  const int D = a.head_dim, tpr = D / 4;  // threads per row, 4 coordinates each
-  const int rows_per = 256 / tpr;
-  const int64_t row = (int64_t)blockIdx.x * rows_per + threadIdx.x / tpr;
-  if (row >= a.bh * a.seq_len) return;
-  const int d = 4 * (threadIdx.x % tpr);
-  const int64_t t = row % a.seq_len;
-  const int c = (int)(t / a.block_size);
+  // dq = own-block part + the past slots' partials (written by dq_past, an
+  // earlier launch) in slot order, rounded once to bf16.
+  const float scale = 1.f / __builtin_sqrtf((float)D);
   const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
   const int slots = a.k_eff - 1;
   const int n = min(slots, n_elig);
-  f32x4 x = *reinterpret_cast<const f32x4*>(a.dq_own + row * D + d);
-  for (int s = 0; s < n; ++s) {
-    const f32x4 y = *reinterpret_cast<const f32x4*>(a.dq_part + (row * slots + s) * D + d);
-    x += y;
-  }
-  bf16x4 o;
+  bf16* dst = reinterpret_cast<bf16*>(a.dq) + row * D;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = to_bf16(x[e]);
-  *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.dq) + row * D + d) = o;
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = 32 * dt + 8 * rg + 4 * h;
+      f32x4 x = f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
+                      acc[dt][4 * rg + 3] * scale};
+      for (int sl = 0; sl < n; ++sl) x += *reinterpret_cast<const f32x4*>(a.dq_part + (row * slots + sl) * D + d);
+      E::put4(dst + d, x[0], x[1], x[2], x[3]);
+    }
 }
 
 // dK (PASS 1) or dV (PASS 0) for 32 * NW keys of one block of one
@@ -1398,11 +1392,6 @@ hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
   {
     KernelTimer t(s, "bwd_dq_own");
     hipLaunchKernelGGL(dq_own_kernel<D>, dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), 0, s, a);
-  }
-  {
-    KernelTimer t(s, "bwd_dq_reduce");
-    const int rows_per = 256 / (D / 4);
-    hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((rows + rows_per - 1) / rows_per)), dim3(256), 0, s, a);
   }
   // 128 keys per workgroup where every block length is a multiple of 128,
   // else 64.

@@ -123,7 +123,6 @@ struct BwdArgs {
   float* delta;                // [bh, S] do . o
   float* lse2;                 // [bh, S] log-sum-exp in the log2 domain
   float* dq_part;              // [bh, S, k_eff - 1, D] past-block dq partials
-  float* dq_own;               // [bh, S, D] own-block dq
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 // Ranks of a given block_idx in a fixed order, and the per-block counts
