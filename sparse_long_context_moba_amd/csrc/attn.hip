@@ -1014,7 +1014,8 @@ hipError_t launch_dense(const AttnArgs& a, hipStream_t s) {
 //  dq_past     — block-major like gather_attn (the forward's lists and
 //                tiles): per key subtile S^T = K Q^T and dP^T = V dO^T on
 //                the forward's score path, then dQ^T += K^T dS^T on its P.V
-//                path (K read through the LDS transpose load); one fp32
+//                path (the same K copy read through the LDS transpose
+//                load); subtiles double-buffered; one fp32
 //                partial per (query, slot);
 //  dq_own      — the own block, 64 queries per workgroup, causal mask; it
 //                then adds the slots' partials in slot order and writes dq
@@ -1050,9 +1051,10 @@ __device__ __forceinline__ void mm_rows(const char* buf, int lane, const bf16x8 
 }
 
 // acc^T[d][lane column] += sum over the 64 rows of T[row][d] x[row][column],
-// T in LDS (V-swizzled layout, read transposed), x in the C layout of
-// mm_rows (rounded to bf16): the forward's P.V step.
-template <int D>
+// T in LDS read transposed, V-swizzled (VSW; conflict-free) or K-swizzled
+// (two-way bank conflicts on these reads, but the same copy serves mm_rows),
+// x in the C layout of mm_rows (rounded to bf16): the forward's P.V step.
+template <int D, bool VSW = true>
 __device__ __forceinline__ void mm_trans(const char* buf, int lane, const f32x16 (&x)[2], f32x16 (&acc)[D / 32]) {
   using E = EngBF16<D>;
   const int h = lane >> 5, j = lane & 15, half = (lane >> 4) & 1;
@@ -1068,8 +1070,9 @@ __device__ __forceinline__ void mm_trans(const char* buf, int lane, const f32x16
       const int nt = i >> 1, g = i & 1;
       const int d = 32 * dt + 16 * half + 4 * (j & 3);
       const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
-      const char* a0 = buf + r0 * E::ROWB + 16 * ((d >> 3) ^ E::swzv(r0)) + 2 * (d & 7);
-      const char* a1 = buf + r1 * E::ROWB + 16 * ((d >> 3) ^ E::swzv(r1)) + 2 * (d & 7);
+      const int s0 = VSW ? E::swzv(r0) : E::swz(r0), s1 = VSW ? E::swzv(r1) : E::swz(r1);
+      const char* a0 = buf + r0 * E::ROWB + 16 * ((d >> 3) ^ s0) + 2 * (d & 7);
+      const char* a1 = buf + r1 * E::ROWB + 16 * ((d >> 3) ^ s1) + 2 * (d & 7);
       const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
       const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1158,7 +1161,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 
 // One key subtile of a dq workgroup: p and ds from the scores, dq^T += K^T ds.
 template <int D, bool MASK>
-__device__ __forceinline__ void dq_step(const char* bk, const char* bv, const char* bkt, int lane,
+__device__ __forceinline__ void dq_step(const char* bk, const char* bv, int lane,
                                         const bf16x8 (&qf)[D / 16], const bf16x8 (&gf)[D / 16], float lse2,
                                         float delta, float sl2, int key0, int t, f32x16 (&acc)[D / 32]) {
   const int h = lane >> 5;
@@ -1173,7 +1176,7 @@ __device__ __forceinline__ void dq_step(const char* bk, const char* bv, const ch
       if (MASK && key0 + 32 * nt + crow(r, h) > t) p = 0.f;
       s[nt][r] = p * (dp[nt][r] - delta);
     }
-  mm_trans<D>(bkt, lane, s, acc);
+  mm_trans<D, false>(bk, lane, s, acc);
 }
 
 // Past blocks: one gather tile (a block and up to 128 listed queries).
@@ -1181,7 +1184,7 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_past_kernel(BwdArgs a) {
   using E = EngBF16<D>;
   constexpr int NT = 256, KC = D / 16, DT = D / 32;
-  __shared__ __align__(16) char bk[E::TB], bv[E::TB], bkt[E::TB];
+  __shared__ __align__(16) char bk0[E::TB], bv0[E::TB], bk1[E::TB], bv1[E::TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const i32x4 tm = *reinterpret_cast<const i32x4*>(a.tile_map + 4 * (int64_t)blockIdx.x);
@@ -1207,14 +1210,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // Double-buffered: the loads of subtile sub + 1 run under the compute of
+  // sub (buffer sub & 1); each step ends waiting for them, then the barrier.
+  E::template begin_one<NT, false>(kp, bk0, tid);
+  E::template begin_one<NT, false>(vp, bv0, tid);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
+  lds_dma_wait();
+  __syncthreads();
   for (int sub = 0; sub < nsub; ++sub) {
-    E::template begin_one<NT, false>(kp + (int64_t)sub * kSub * D, bk, tid);
-    E::template begin_one<NT, false>(vp + (int64_t)sub * kSub * D, bv, tid);
-    E::template begin_one<NT, true>(kp + (int64_t)sub * kSub * D, bkt, tid);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
+    const bool odd = sub & 1;
+    if (sub + 1 < nsub) {
+      E::template begin_one<NT, false>(kp + (int64_t)(sub + 1) * kSub * D, odd ? bk0 : bk1, tid);
+      E::template begin_one<NT, false>(vp + (int64_t)(sub + 1) * kSub * D, odd ? bv0 : bv1, tid);
+    }
+    if (wave_on) dq_step<D, false>(odd ? bk1 : bk0, odd ? bv1 : bv0, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
     lds_dma_wait();
-    __syncthreads();
-    if (wave_on) dq_step<D, false>(bk, bv, bkt, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
     __syncthreads();
   }
   if (valid) store_row_f32<D>(a.dq_part + ((bh * a.seq_len * slots) + ev) * D, acc, h, 1.f / __builtin_sqrtf((float)D));
@@ -1225,7 +1235,9 @@ template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
   using E = EngBF16<D>;
   constexpr int NT = 128, KC = D / 16, DT = D / 32;
-  __shared__ __align__(16) char bk[E::TB], bv[E::TB], bkt[E::TB];
+  // Single-buffered (32 KB), so that four of these two-wave workgroups
+  // share a compute unit.
+  __shared__ __align__(16) char bk[E::TB], bv[E::TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   const int64_t ntile = a.seq_len / 64;
   const int64_t bh = blockIdx.x / ntile;
@@ -1250,15 +1262,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   for (int sub = 0; sub < nsub; ++sub) {
     E::template begin_one<NT, false>(kp + (int64_t)sub * kSub * D, bk, tid);
     E::template begin_one<NT, false>(vp + (int64_t)sub * kSub * D, bv, tid);
-    E::template begin_one<NT, true>(kp + (int64_t)sub * kSub * D, bkt, tid);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
     lds_dma_wait();
     __syncthreads();
     const int key0 = kb + sub * kSub;
     if (a.causal && key0 + kSub > q0 + 32 * w) {
-      if (key0 <= q0 + 32 * w + 31) dq_step<D, true>(bk, bv, bkt, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
+      if (key0 <= q0 + 32 * w + 31) dq_step<D, true>(bk, bv, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
     } else {
-      dq_step<D, false>(bk, bv, bkt, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+      dq_step<D, false>(bk, bv, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
     }
     __syncthreads();
   }
