@@ -178,3 +178,31 @@ def test_grouped_query_heads_workspace():
     up = lambda x: (x + 255) // 256 * 256
     saved = sum(up(8 * nb * D * e) - up(2 * nb * D * e) for e in (8, 4, 2, 2)) + up(8 * nb * 4) - up(2 * nb * 4)
     assert mha - gqa == saved
+
+
+def test_backward_and_lse_validation():
+    """moba_forward_lse and moba_backward validate on the host like
+    moba_forward: bf16 only for the backward, every pointer named, the
+    workspace size checked before anything is launched."""
+    from sparse_long_context_moba_amd import _lib
+    st, need = _lib.moba_backward_workspace_size(_p())
+    st_f, fwd = _lib.moba_workspace_size(_p())
+    assert st == 0 and st_f == 0 and need > fwd, _lib.moba_last_error()
+    st, _ = _lib.moba_backward_workspace_size(_p(dtype=0))
+    assert st == 5 and "bf16" in _lib.moba_last_error()
+    st, _ = _lib.moba_backward_workspace_size(_p(top_k=0))
+    assert st == 3
+    names = ["q", "k", "v", "o", "dout", "block_idx", "lse", "dq", "dk", "dv"]
+    for i, name in enumerate(names):
+        args = [FAKE] * 10
+        args[i] = None
+        st = _lib.moba_backward(_p(), *args, FAKE, need, None)
+        assert st == 1 and name in _lib.moba_last_error(), (name, _lib.moba_last_error())
+    assert _lib.moba_backward(_p(), *([FAKE] * 10), FAKE, need - 1, None) == 6
+    assert _lib.moba_backward(_p(), *([FAKE] * 10), FAKE + 8, need, None) == 6
+    assert _lib.moba_backward(_p(dtype=0), *([FAKE] * 10), FAKE, need, None) == 5
+    # the forward with the log-sum-exp: same workspace as the forward, lse required
+    assert _lib.moba_forward_lse(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, fwd, None) == 1
+    assert "lse" in _lib.moba_last_error()
+    assert _lib.moba_forward_lse(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwd - 1, None) == 6
+    assert _lib.moba_forward_lse(_p(top_k=0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwd, None) == 3
