@@ -1231,20 +1231,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 }
 
 // The own block: 64 consecutive queries of one head.
-template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
   using E = EngBF16<D>;
-  constexpr int NT = 128, KC = D / 16, DT = D / 32;
-  // Single-buffered (32 KB), so that four of these two-wave workgroups
-  // share a compute unit.
+  constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, M = 32 * NW;
+  // Single-buffered (32 KB), so that several workgroups share a compute unit.
   __shared__ __align__(16) char bk[E::TB], bv[E::TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int64_t ntile = a.seq_len / 64;
+  const int64_t ntile = a.seq_len / M;
   const int64_t bh = blockIdx.x / ntile;
-  const int q0 = (int)((blockIdx.x % ntile) * 64);
+  const int q0 = (int)((blockIdx.x % ntile) * M);
   const int c = (int)(q0 / a.block_size);
   const int kb = (int)(c * a.block_size);
-  const int kend = a.causal ? q0 + 64 : (int)min<int64_t>(kb + a.block_size, a.seq_len);
+  const int kend = a.causal ? q0 + M : (int)min<int64_t>(kb + a.block_size, a.seq_len);
   const int t = q0 + 32 * w + col;
   const int64_t row = bh * a.seq_len + t;
   bf16x8 qf[KC], gf[KC];
@@ -1402,7 +1401,11 @@ hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
   }
   {
     KernelTimer t(s, "bwd_dq_own");
-    hipLaunchKernelGGL(dq_own_kernel<D>, dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), 0, s, a);
+    // 128 queries per workgroup where tiles of 128 stay inside one block.
+    if (a.seq_len % 128 == 0 && a.block_size % 128 == 0)
+      hipLaunchKernelGGL((dq_own_kernel<D, 4>), dim3((unsigned)(a.bh * (a.seq_len / 128))), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dq_own_kernel<D, 2>), dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), 0, s, a);
   }
   // 128 keys per workgroup where every block length is a multiple of 128,
   // else 64.
