@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 3
+#define MOBA_ABI_VERSION 4
 
 typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype_t;
 

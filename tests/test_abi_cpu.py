@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     from sparse_long_context_moba_amd import _lib
-    assert _lib.moba_abi_version() == 3
+    assert _lib.moba_abi_version() == 4
     for code in range(8):
         assert _lib.moba_status_str(code)
     assert _lib.moba_status_str(99) == "unknown status"
