@@ -165,10 +165,11 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
 }
 
 // Backward workspace: the forward's plan (its lists and tiles are rebuilt
-// from block_idx) plus delta and the log2-domain log-sum-exp per query and
-// the past-block dq partials, all fp32, and the ordered ranks' chunk counts.
+// from block_idx) plus delta and the log2-domain log-sum-exp per query, the
+// past-block dq partials, all fp32, the ordered ranks' chunk counts, and per
+// list position its query row, log-sum-exp and delta.
 struct BwdPlan {
-  size_t delta, lse2, dq_part, chunk_counts, total;
+  size_t delta, lse2, dq_part, chunk_counts, lt, ll, ld, total;
 };
 BwdPlan plan_backward(const Plan& P) {
   BwdPlan B;
@@ -183,6 +184,9 @@ BwdPlan plan_backward(const Plan& P) {
   B.lse2 = take(rows * 4);
   B.dq_part = take(rows * (size_t)P.slots * (size_t)P.D * 4);
   B.chunk_counts = take((size_t)P.bh * (size_t)((P.S + kRankChunk - 1) / kRankChunk) * (size_t)P.nb * 4);
+  B.lt = take((size_t)P.pairs * 4);
+  B.ll = take((size_t)P.pairs * 4);
+  B.ld = take((size_t)P.pairs * 4);
   B.total = off;
   return B;
 }
@@ -472,6 +476,9 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
   ba.delta = at<float>(workspace, B.delta);
   ba.lse2 = at<float>(workspace, B.lse2);
   ba.dq_part = at<float>(workspace, B.dq_part);
+  ba.lt = at<int32_t>(workspace, B.lt);
+  ba.ll = at<float>(workspace, B.ll);
+  ba.ld = at<float>(workspace, B.ld);
   if (P.pairs > 0) {
     // The forward's varlen lists, rebuilt from block_idx in a fixed order
     // (dk and dv sum over them): counts, ranks, offsets, lists, tiles.

@@ -123,6 +123,9 @@ struct BwdArgs {
   float* delta;                // [bh, S] do . o
   float* lse2;                 // [bh, S] log-sum-exp in the log2 domain
   float* dq_part;              // [bh, S, k_eff - 1, D] past-block dq partials
+  int32_t* lt;                 // [pairs] per list position: the query row
+  float* ll;                   // [pairs] its log-sum-exp (log2 domain)
+  float* ld;                   // [pairs] its delta
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 // Ranks of a given block_idx in a fixed order, and the per-block counts
