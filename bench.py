@@ -91,8 +91,10 @@ def source_digest(files):
 
 
 KERNEL_SOURCES = {
-    "gather_attn": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/common.h"],
-    "diag_merge": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/common.h"],
+    "gather_attn": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/engine.h",
+                    "sparse_long_context_moba_amd/csrc/common.h"],
+    "diag_merge": ["sparse_long_context_moba_amd/csrc/attn.hip", "sparse_long_context_moba_amd/csrc/engine.h",
+                   "sparse_long_context_moba_amd/csrc/common.h"],
     "gate_topk": ["sparse_long_context_moba_amd/csrc/gate.hip", "sparse_long_context_moba_amd/csrc/common.h"],
     "pool": ["sparse_long_context_moba_amd/csrc/pool.hip", "sparse_long_context_moba_amd/csrc/common.h"],
 }

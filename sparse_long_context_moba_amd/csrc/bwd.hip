@@ -1,0 +1,638 @@
+// MoBA backward kernels (bf16 inputs) on the attention engine of
+// engine.h; the launch sequence is in api.cpp (moba_backward).
+#include "engine.h"
+
+namespace moba {
+
+// ================================================================ backward
+// MoBA backward for bf16 inputs, the block choice of the forward held fixed
+// (a top-k over block scores has no gradient off ties, and the gate's
+// scores do not weight the output): per query, the gradient of one softmax
+// attention over its attended keys. With l = q.k / sqrt(D), p = exp(l - lse),
+// delta = do . o:  dv_u += p_u do,  ds_u = p_u (do . v_u - delta),
+// dq += ds_u k_u / sqrt(D),  dk_u += ds_u q / sqrt(D).
+//
+// Kernels (each step single-buffered: load a 64-row subtile to LDS, wait,
+// compute, barrier):
+//  bwd_prep    — delta and the log-sum-exp in the log2 domain per query;
+//  dq_past     — block-major like gather_attn (the forward's lists and
+//                tiles): per key subtile S^T = K Q^T and dP^T = V dO^T on
+//                the forward's score path, then dQ^T += K^T dS^T on its P.V
+//                path (the same K copy read through the LDS transpose
+//                load); subtiles double-buffered; one fp32
+//                partial per (query, slot);
+//  dq_own      — the own block, 64 queries per workgroup, causal mask; it
+//                then adds the slots' partials in slot order and writes dq
+//                (no atomics);
+//  dkv         — key-major: a workgroup holds 128 (or 64) keys of one
+//                block (32 per wave, as the B operand the way the forward
+//                holds queries)
+//                and streams 64-row subtiles of the queries that attend
+//                them: the block's own queries, then its listed queries
+//                (gathered rows), for every query head of the key/value
+//                head. PASS 0 accumulates dV^T += dO^T P, PASS 1
+//                dK^T += Q^T dS (both on the P.V path); together they would
+//                not fit the register file.
+namespace {
+
+// C[row][lane column] for 64 LDS rows (K-swizzled layout) against the B
+// fragments b (32 columns, one per lane column): the forward's score step.
+template <int D>
+__device__ __forceinline__ void mm_rows(const char* buf, int lane, const bf16x8 (&b)[D / 16], f32x16 (&c)[2]) {
+  using E = EngBF16<D>;
+  const int h = lane >> 5, col = lane & 31, sw = E::swz(col);
+  const char* r0 = buf + col * E::ROWB;
+  const char* r1 = r0 + 32 * E::ROWB;
+  c[0] = f32x16{};
+  c[1] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(r0 + 16 * ((2 * kk + h) ^ sw));
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(r1 + 16 * ((2 * kk + h) ^ sw));
+    c[0] = mfma_bf16(a0, b[kk], c[0]);
+    c[1] = mfma_bf16(a1, b[kk], c[1]);
+  }
+}
+
+// acc^T[d][lane column] += sum over the 64 rows of T[row][d] x[row][column],
+// T in LDS read transposed, V-swizzled (VSW; conflict-free) or K-swizzled
+// (two-way bank conflicts on these reads, but the same copy serves mm_rows),
+// x in the C layout of mm_rows (rounded to bf16): the forward's P.V step.
+template <int D, bool VSW = true>
+__device__ __forceinline__ void mm_trans(const char* buf, int lane, const f32x16 (&x)[2], f32x16 (&acc)[D / 32]) {
+  using E = EngBF16<D>;
+  const int h = lane >> 5, j = lane & 15, half = (lane >> 4) & 1;
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pb[nt][r >> 3][r & 7] = to_bf16(x[nt][r]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int nt = i >> 1, g = i & 1;
+      const int d = 32 * dt + 16 * half + 4 * (j & 3);
+      const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
+      const int s0 = VSW ? E::swzv(r0) : E::swz(r0), s1 = VSW ? E::swzv(r1) : E::swz(r1);
+      const char* a0 = buf + r0 * E::ROWB + 16 * ((d >> 3) ^ s0) + 2 * (d & 7);
+      const char* a1 = buf + r1 * E::ROWB + 16 * ((d >> 3) ^ s1) + 2 * (d & 7);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[dt] = mfma_bf16(vf, pb[nt][g], acc[dt]);
+    }
+}
+
+// A row's D/16 B fragments for this lane half (like EngBF16::load_q).
+template <int D>
+__device__ __forceinline__ void load_frags(bf16x8 (&f)[D / 16], const bf16* row, int h) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) f[kk] = *reinterpret_cast<const bf16x8*>(row + 16 * kk + 8 * h);
+}
+
+// acc (C layout of mm_trans: lane column = row of dst, element r = coordinate
+// 32 dt + crow(r, h)) times scale, to a row of dst in fp32 or bf16.
+template <int D>
+__device__ __forceinline__ void store_row_f32(float* dst, const f32x16 (&acc)[D / 32], int h, float scale) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * rg + 4 * h) =
+          f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
+                acc[dt][4 * rg + 3] * scale};
+}
+template <int D>
+__device__ __forceinline__ void store_row_bf16(bf16* dst, const f32x16 (&acc)[D / 32], int h, float scale) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      EngBF16<D>::put4(dst + 32 * dt + 8 * rg + 4 * h, acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale,
+                       acc[dt][4 * rg + 2] * scale, acc[dt][4 * rg + 3] * scale);
+}
+
+// 64 rows of src (rows[i] = row index, from LDS) into buf, K-swizzled
+// (V = false) or V-swizzled (V = true), by direct HBM -> LDS loads.
+template <int D, int NT, bool V>
+__device__ __forceinline__ void load_rows(const bf16* src, const int* rows, char* buf, int tid) {
+  using E = EngBF16<D>;
+  constexpr int NW = NT / 64, INSTS = E::SLOTS / 64;
+  static_assert(INSTS % NW == 0, "subtile slots must split evenly over the waves");
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
+#pragma unroll
+  for (int ii = 0; ii < INSTS / NW; ++ii) {
+    const int i = ii * NW + w;
+    const int sl = i * 64 + lane;
+    const int row = sl / E::CPR;
+    const int x = (sl % E::CPR) ^ (V ? E::swzv(row) : E::swz(row));
+    lds_dma16(src + (int64_t)rows[row] * D + 8 * x, base + i * 1024);
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int tid = threadIdx.x, sub = tid & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const int64_t n = a.bh * a.seq_len;
+  const int D = a.head_dim;
+  float sum = 0.f;
+  if (row < n) {
+    // 16 lanes per row, one 16-byte (D = 128) or 8-byte (D = 64) load each.
+    const bf16* o = reinterpret_cast<const bf16*>(a.o) + row * D;
+    const bf16* g = reinterpret_cast<const bf16*>(a.dout) + row * D;
+    if (D == 128) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + 8 * sub);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(g + 8 * sub);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum = __builtin_fmaf((float)x[e], (float)y[e], sum);
+    } else {
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(o + 4 * sub);
+      const bf16x4 y = *reinterpret_cast<const bf16x4*>(g + 4 * sub);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum = __builtin_fmaf((float)x[e], (float)y[e], sum);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
+  if (row < n && sub == 0) {
+    a.delta[row] = sum;
+    a.lse2[row] = a.lse[row] * kLog2e;
+  }
+}
+
+// One key subtile of a dq workgroup: p and ds from the scores, dq^T += K^T ds.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_step(const char* bk, const char* bv, int lane,
+                                        const bf16x8 (&qf)[D / 16], const bf16x8 (&gf)[D / 16], float lse2,
+                                        float delta, float sl2, int key0, int t, f32x16 (&acc)[D / 32]) {
+  const int h = lane >> 5;
+  f32x16 s[2], dp[2];
+  mm_rows<D>(bk, lane, qf, s);
+  mm_rows<D>(bv, lane, gf, dp);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(__builtin_fmaf(s[nt][r], sl2, -lse2));
+      if (MASK && key0 + 32 * nt + crow(r, h) > t) p = 0.f;
+      s[nt][r] = p * (dp[nt][r] - delta);
+    }
+  mm_trans<D, false>(bk, lane, s, acc);
+}
+
+// Past blocks: one gather tile (a block and up to 128 listed queries).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_past_kernel(BwdArgs a) {
+  using E = EngBF16<D>;
+  constexpr int NT = 256, KC = D / 16, DT = D / 32;
+  __shared__ __align__(16) char bk0[E::TB], bv0[E::TB], bk1[E::TB], bv1[E::TB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 tm = *reinterpret_cast<const i32x4*>(a.tile_map + 4 * (int64_t)blockIdx.x);
+  if (tm.x < 0) return;
+  const int64_t blk = __builtin_amdgcn_readfirstlane(tm.x);
+  const int64_t bh = blk / a.n_blocks, j = blk % a.n_blocks;
+  const int64_t e0 = __builtin_amdgcn_readfirstlane(tm.y), e1 = __builtin_amdgcn_readfirstlane(tm.z);
+  const int64_t e = e0 + 32 * w + col;
+  const bool valid = e < e1, wave_on = e0 + 32 * w < e1;
+  const int slots = a.k_eff - 1;
+  const int ev = a.qlist[valid ? e : e0];
+  const int t = ev / slots;
+  const int64_t row = bh * a.seq_len + t;
+  bf16x8 qf[KC], gf[KC];
+  load_frags<D>(qf, reinterpret_cast<const bf16*>(a.q) + row * D, h);
+  load_frags<D>(gf, reinterpret_cast<const bf16*>(a.dout) + row * D, h);
+  const float lse2 = a.lse2[row], delta = a.delta[row];
+  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
+  const int64_t kvh = bh / a.group;
+  const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + j * a.block_size) * D;
+  const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + j * a.block_size) * D;
+  const int nsub = (int)(min<int64_t>(a.block_size, a.seq_len - j * a.block_size) / kSub);
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // Double-buffered: the loads of subtile sub + 1 run under the compute of
+  // sub (buffer sub & 1); each step ends waiting for them, then the barrier.
+  E::template begin_one<NT, false>(kp, bk0, tid);
+  E::template begin_one<NT, false>(vp, bv0, tid);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
+  lds_dma_wait();
+  __syncthreads();
+  for (int sub = 0; sub < nsub; ++sub) {
+    const bool odd = sub & 1;
+    if (sub + 1 < nsub) {
+      E::template begin_one<NT, false>(kp + (int64_t)(sub + 1) * kSub * D, odd ? bk0 : bk1, tid);
+      E::template begin_one<NT, false>(vp + (int64_t)(sub + 1) * kSub * D, odd ? bv0 : bv1, tid);
+    }
+    if (wave_on) dq_step<D, false>(odd ? bk1 : bk0, odd ? bv1 : bv0, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+    lds_dma_wait();
+    __syncthreads();
+  }
+  if (valid) store_row_f32<D>(a.dq_part + ((bh * a.seq_len * slots) + ev) * D, acc, h, 1.f / __builtin_sqrtf((float)D));
+}
+
+// The own block: 64 consecutive queries of one head.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
+  using E = EngBF16<D>;
+  constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, M = 32 * NW;
+  // Single-buffered (32 KB), so that several workgroups share a compute unit.
+  __shared__ __align__(16) char bk[E::TB], bv[E::TB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int64_t ntile = a.seq_len / M;
+  const int64_t bh = blockIdx.x / ntile;
+  const int q0 = (int)((blockIdx.x % ntile) * M);
+  const int c = (int)(q0 / a.block_size);
+  const int kb = (int)(c * a.block_size);
+  const int kend = a.causal ? q0 + M : (int)min<int64_t>(kb + a.block_size, a.seq_len);
+  const int t = q0 + 32 * w + col;
+  const int64_t row = bh * a.seq_len + t;
+  bf16x8 qf[KC], gf[KC];
+  load_frags<D>(qf, reinterpret_cast<const bf16*>(a.q) + row * D, h);
+  load_frags<D>(gf, reinterpret_cast<const bf16*>(a.dout) + row * D, h);
+  const float lse2 = a.lse2[row], delta = a.delta[row];
+  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
+  const int64_t kvh = bh / a.group;
+  const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + kb) * D;
+  const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + kb) * D;
+  const int nsub = (kend - kb) / kSub;
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  for (int sub = 0; sub < nsub; ++sub) {
+    E::template begin_one<NT, false>(kp + (int64_t)sub * kSub * D, bk, tid);
+    E::template begin_one<NT, false>(vp + (int64_t)sub * kSub * D, bv, tid);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
+    lds_dma_wait();
+    __syncthreads();
+    const int key0 = kb + sub * kSub;
+    if (a.causal && key0 + kSub > q0 + 32 * w) {
+      if (key0 <= q0 + 32 * w + 31) dq_step<D, true>(bk, bv, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
+    } else {
+      dq_step<D, false>(bk, bv, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+    }
+    __syncthreads();
+  }
+  // dq = own-block part + the past slots' partials (written by dq_past, an
+  // earlier launch) in slot order, rounded once to bf16.
+  const float scale = 1.f / __builtin_sqrtf((float)D);
+  const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
+  const int slots = a.k_eff - 1;
+  const int n = min(slots, n_elig);
+  bf16* dst = reinterpret_cast<bf16*>(a.dq) + row * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = 32 * dt + 8 * rg + 4 * h;
+      f32x4 x = f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
+                      acc[dt][4 * rg + 3] * scale};
+      for (int sl = 0; sl < n; ++sl) x += *reinterpret_cast<const f32x4*>(a.dq_part + (row * slots + sl) * D + d);
+      E::put4(dst + d, x[0], x[1], x[2], x[3]);
+    }
+}
+
+// Per list position (the forward's lists, rebuilt in a fixed order): the
+// query row, its log-sum-exp and its delta, stored contiguously so that the
+// dK/dV passes read a subtile's metadata with one independent load each.
+__global__ __launch_bounds__(256) void list_meta_kernel(BwdArgs a) {
+  const int64_t lst = blockIdx.x;  // bh * n_blocks + j
+  const int64_t bh = lst / a.n_blocks;
+  const int slots = a.k_eff - 1;
+  const int o0 = a.offset[lst], o1 = a.offset[lst + 1];
+  for (int pos = o0 + (int)threadIdx.x; pos < o1; pos += 256) {
+    const int t = a.qlist[pos] / slots;
+    a.lt[pos] = t;
+    a.ll[pos] = a.lse2[bh * a.seq_len + t];
+    a.ld[pos] = a.delta[bh * a.seq_len + t];
+  }
+}
+
+// dV (PASS 0; dK is dk_kernel) for 32 * NW keys of one block of one
+// key/value head. The 64-row query subtiles that attend those keys (for
+// every query head of the group: the block's own queries at or after the
+// keys, then its listed queries) are numbered 0 .. N-1 and software
+// pipelined over two LDS buffer sets: while subtile i is computed from one
+// set, the rows of i + 1 load into the other, and wave 0 holds the row
+// numbers, log-sum-exps and deltas of i + 2 in registers. Q and dO are
+// staged once each (K-swizzled); the dK and dV products read them
+// transposed from the same copy.
+template <int D, int PASS, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dkv_kernel(BwdArgs a) {
+  using E = EngBF16<D>;
+  constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, KEYS = 32 * NW;
+  __shared__ __align__(16) char bq[2][E::TB], bx[2][E::TB];
+  __shared__ int rows[2][64];
+  __shared__ float lse2s[2][64], deltas[2][64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  // Blocks in order, all heads of a block together: early blocks are in
+  // the most lists (causal routing), so the longest workgroups start first.
+  const int64_t nchunk = a.block_size / KEYS;
+  const int64_t nkv = a.bh / a.group;
+  const int64_t kc = blockIdx.x % nchunk;
+  const int64_t kvh = (blockIdx.x / nchunk) % nkv;
+  const int64_t j = blockIdx.x / (nchunk * nkv);
+  const int64_t k0 = j * a.block_size + kc * KEYS;
+  if (k0 >= a.seq_len) return;  // past the end of a short last block
+  const int u = (int)k0 + 32 * w + col;  // this lane's key
+  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + u) * D;
+  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + u) * D;
+  bf16x8 kf[KC], vf[PASS == 1 ? KC : 1];
+  load_frags<D>(kf, krow, h);
+  if constexpr (PASS == 1) load_frags<D>(vf, vrow, h);
+  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
+  const int slots = a.k_eff - 1;
+  const int64_t jend = min<int64_t>((j + 1) * a.block_size, a.seq_len);
+  const int64_t qs = a.causal ? k0 : j * a.block_size;  // first own query that sees the keys
+  const int n_own = (int)((jend - qs + 63) / 64);
+  // Subtile i: (query head, own or listed, first row or list position, rows).
+  struct Sub {
+    int64_t bh;
+    int64_t first;
+    int n;
+    bool own;
+  };
+  auto sub_at = [&](int i) {
+    Sub d{};
+    for (int g = 0; g < a.group; ++g) {
+      const int64_t bh = kvh * a.group + g;
+      if (i < n_own) {
+        d.bh = bh;
+        d.own = true;
+        d.first = qs + 64 * (int64_t)i;
+        d.n = (int)min<int64_t>(64, jend - d.first);
+        return d;
+      }
+      i -= n_own;
+      int64_t o0 = 0, cnt = 0;
+      if (slots > 0) {
+        o0 = a.offset[bh * a.n_blocks + j];
+        cnt = a.offset[bh * a.n_blocks + j + 1] - o0;
+      }
+      const int n_list = (int)((cnt + 63) / 64);
+      if (i < n_list) {
+        d.bh = bh;
+        d.own = false;
+        d.first = o0 + 64 * (int64_t)i;
+        d.n = (int)min<int64_t>(64, cnt - 64 * (int64_t)i);
+        return d;
+      }
+      i -= n_list;
+    }
+    return d;
+  };
+  int total = 0;
+  for (int g = 0; g < a.group; ++g) {
+    const int64_t bh = kvh * a.group + g;
+    int64_t cnt = 0;
+    if (slots > 0) cnt = a.offset[bh * a.n_blocks + j + 1] - a.offset[bh * a.n_blocks + j];
+    total += n_own + (int)((cnt + 63) / 64);
+  }
+  // Wave 0's registers: row number, log-sum-exp and delta of its lane's row
+  // of a subtile (a padding row repeats the first row with weight 0).
+  int mt = 0;
+  float ml = 0.f, md = 0.f;
+  auto meta_load = [&](const Sub& d) {
+    const bool ok = lane < d.n;
+    const int64_t i = d.first + (ok ? lane : 0);
+    if (d.own) {
+      mt = (int)i;
+      ml = a.lse2[d.bh * a.seq_len + i];
+      md = a.delta[d.bh * a.seq_len + i];
+    } else {
+      mt = a.lt[i];
+      ml = a.ll[i];
+      md = a.ld[i];
+    }
+    if (!ok) {
+      ml = __builtin_inff();
+      md = 0.f;
+    }
+  };
+  auto meta_store = [&](int x) {
+    rows[x][lane] = mt;
+    lse2s[x][lane] = ml;
+    deltas[x][lane] = md;
+  };
+  auto rows_in = [&](const Sub& d, int x) {
+    const bf16* qb = reinterpret_cast<const bf16*>(a.q) + d.bh * a.seq_len * D;
+    const bf16* gb = reinterpret_cast<const bf16*>(a.dout) + d.bh * a.seq_len * D;
+    load_rows<D, NT, false>(qb, rows[x], bq[x], tid);
+    load_rows<D, NT, false>(gb, rows[x], bx[x], tid);
+  };
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  auto compute = [&](const Sub& d, int x) {
+    const bool mask = d.own && a.causal;
+    f32x16 s[2];
+    mm_rows<D>(bq[x], lane, kf, s);
+    f32x16 dp[2];
+    if constexpr (PASS == 1) mm_rows<D>(bx[x], lane, vf, dp);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int r0 = 32 * nt + 8 * rg + 4 * h;  // rows of elements 4 rg .. 4 rg + 3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[x][r0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&deltas[x][r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          float p = fast_exp2(__builtin_fmaf(s[nt][r], sl2, -l4[e]));
+          if (mask && u > rows[x][r0 + e]) p = 0.f;
+          if constexpr (PASS == 0) s[nt][r] = p;
+          else s[nt][r] = p * (dp[nt][r] - d4[e]);
+        }
+      }
+    // dV^T += dO^T P or dK^T += Q^T dS, read transposed from the K-swizzled copy.
+    mm_trans<D, false>(PASS == 0 ? bx[x] : bq[x], lane, s, acc);
+  };
+  // Prologue: metadata of 0 stored, rows of 0 loading, metadata of 1 in
+  // wave 0's registers.
+  Sub cur = sub_at(0);
+  if (w == 0) {
+    meta_load(cur);
+    meta_store(0);
+  }
+  __syncthreads();
+  rows_in(cur, 0);
+  Sub nxt = total > 1 ? sub_at(1) : Sub{};
+  if (w == 0 && total > 1) meta_load(nxt);
+  for (int i = 0; i < total; ++i) {
+    const int x = i & 1;
+    // Wave 0 publishes the metadata of i + 1, requested during step i - 1
+    // (set x ^ 1 was last read by step i - 1, before its closing barrier).
+    if (w == 0 && i + 1 < total) meta_store(x ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows of i, loaded during step i - 1
+    lds_dma_wait();
+    __syncthreads();
+    // Under the compute of i: the rows of i + 1 and the metadata of i + 2.
+    Sub nn{};
+    if (i + 2 < total) nn = sub_at(i + 2);
+    if (i + 1 < total) rows_in(nxt, x ^ 1);
+    if (w == 0 && i + 2 < total) meta_load(nn);
+    compute(cur, x);
+    __syncthreads();  // set x is free for step i + 1's metadata and rows
+    cur = nxt;
+    nxt = nn;
+  }
+  bf16* dst = reinterpret_cast<bf16*>(PASS == 0 ? a.dv : a.dk) + (kvh * a.seq_len + u) * D;
+  store_row_bf16<D>(dst, acc, h, PASS == 0 ? 1.f : 1.f / __builtin_sqrtf((float)D));
+}
+
+// dK (launched with PASS = 1; PASS = 0 would give dV) for 32 * NW keys of
+// one block of one key/value head, single-buffered: each 64-row query
+// subtile is staged (row numbers, log-sum-exps, deltas, then the rows of
+// Q, dO and Q^T) and then computed. For dK this beats the pipelined
+// dkv_kernel, which spills registers in this pass (same-box A/B at
+// headline_32k: 1.75-1.79 against 1.94 ms; for dV the pipelined kernel
+// wins, 1.47 against 1.49-1.54 ms).
+template <int D, int PASS, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dk_kernel(BwdArgs a) {
+  using E = EngBF16<D>;
+  constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, KEYS = 32 * NW;
+  __shared__ __align__(16) char bq[E::TB], bx[E::TB], by[PASS == 1 ? E::TB : 16];
+  __shared__ int rows[64];
+  __shared__ float lse2s[64], deltas[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  // Blocks in order, all heads of a block together: early blocks are in
+  // the most lists (causal routing), so the longest workgroups start first.
+  const int64_t nchunk = a.block_size / KEYS;
+  const int64_t nkv = a.bh / a.group;
+  const int64_t kc = blockIdx.x % nchunk;
+  const int64_t kvh = (blockIdx.x / nchunk) % nkv;
+  const int64_t j = blockIdx.x / (nchunk * nkv);
+  const int64_t k0 = j * a.block_size + kc * KEYS;
+  if (k0 >= a.seq_len) return;  // past the end of a short last block
+  const int u = (int)k0 + 32 * w + col;  // this lane's key
+  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + u) * D;
+  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + u) * D;
+  bf16x8 kf[KC], vf[PASS == 1 ? KC : 1];
+  load_frags<D>(kf, krow, h);
+  if constexpr (PASS == 1) load_frags<D>(vf, vrow, h);
+  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
+  const int slots = a.k_eff - 1;
+  const int64_t jend = min<int64_t>((j + 1) * a.block_size, a.seq_len);
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // One 64-row subtile of query head bh: rows from row_of(i) (valid when
+  // i < n), causal mask against the keys when MASK.
+  auto subtile = [&](int64_t bh, int n, bool mask, auto&& row_of) {
+    if (tid < 64) {
+      const bool ok = tid < n;
+      const int t = row_of(ok ? tid : 0);  // a padding row repeats a valid one
+      rows[tid] = t;
+      lse2s[tid] = ok ? a.lse2[bh * a.seq_len + t] : __builtin_inff();
+      deltas[tid] = ok ? a.delta[bh * a.seq_len + t] : 0.f;
+    }
+    __syncthreads();
+    const bf16* qb = reinterpret_cast<const bf16*>(a.q) + bh * a.seq_len * D;
+    const bf16* gb = reinterpret_cast<const bf16*>(a.dout) + bh * a.seq_len * D;
+    load_rows<D, NT, false>(qb, rows, bq, tid);
+    if constexpr (PASS == 0) {
+      load_rows<D, NT, true>(gb, rows, bx, tid);   // dO^T for dV
+    } else {
+      load_rows<D, NT, false>(gb, rows, bx, tid);  // dO for dP
+      load_rows<D, NT, true>(qb, rows, by, tid);   // Q^T for dK
+    }
+    lds_dma_wait();
+    __syncthreads();
+    f32x16 s[2];
+    mm_rows<D>(bq, lane, kf, s);
+    f32x16 dp[2];
+    if constexpr (PASS == 1) mm_rows<D>(bx, lane, vf, dp);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int r0 = 32 * nt + 8 * rg + 4 * h;  // rows of elements 4 rg .. 4 rg + 3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          float p = fast_exp2(__builtin_fmaf(s[nt][r], sl2, -l4[e]));
+          if (mask && u > rows[r0 + e]) p = 0.f;
+          if constexpr (PASS == 0) s[nt][r] = p;
+          else s[nt][r] = p * (dp[nt][r] - d4[e]);
+        }
+      }
+    mm_trans<D>(PASS == 0 ? bx : by, lane, s, acc);
+    __syncthreads();
+  };
+  for (int g = 0; g < a.group; ++g) {
+    const int64_t bh = kvh * a.group + g;
+    // The block's own queries: those at or after the keys (causal), or all.
+    const int64_t qs = a.causal ? k0 : j * a.block_size;
+    for (int64_t t0 = qs; t0 < jend; t0 += 64) {
+      const int n = (int)min<int64_t>(64, jend - t0);
+      subtile(bh, n, a.causal, [&](int i) { return (int)(t0 + i); });
+    }
+    // Its listed queries (past-block routing of later, or other, queries).
+    if (slots > 0) {
+      const int32_t* lst = a.qlist + a.offset[bh * a.n_blocks + j];
+      const int cnt = a.offset[bh * a.n_blocks + j + 1] - a.offset[bh * a.n_blocks + j];
+      for (int i0 = 0; i0 < cnt; i0 += 64) {
+        const int n = min(64, cnt - i0);
+        subtile(bh, n, false, [&](int i) { return lst[i0 + i] / slots; });
+      }
+    }
+  }
+  bf16* dst = reinterpret_cast<bf16*>(PASS == 0 ? a.dv : a.dk) + (kvh * a.seq_len + u) * D;
+  store_row_bf16<D>(dst, acc, h, PASS == 0 ? 1.f : 1.f / __builtin_sqrtf((float)D));
+}
+
+template <int D>
+hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = a.bh * a.seq_len;
+  {
+    KernelTimer t(s, "bwd_prep");
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.k_eff > 1 && a.gather_grid > 0) {
+    KernelTimer t(s, "bwd_list_meta");
+    hipLaunchKernelGGL(list_meta_kernel, dim3((unsigned)(a.bh * a.n_blocks)), dim3(256), 0, s, a);
+  }
+  if (a.k_eff > 1 && a.gather_grid > 0) {
+    KernelTimer t(s, "bwd_dq_past");
+    hipLaunchKernelGGL(dq_past_kernel<D>, dim3((unsigned)a.gather_grid), dim3(256), 0, s, a);
+  }
+  {
+    KernelTimer t(s, "bwd_dq_own");
+    // 128 queries per workgroup where tiles of 128 stay inside one block.
+    if (a.seq_len % 128 == 0 && a.block_size % 128 == 0)
+      hipLaunchKernelGGL((dq_own_kernel<D, 4>), dim3((unsigned)(a.bh * (a.seq_len / 128))), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dq_own_kernel<D, 2>), dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), 0, s, a);
+  }
+  // 128 keys per workgroup where every block length is a multiple of 128,
+  // else 64.
+  const int64_t last = a.seq_len - (a.n_blocks - 1) * a.block_size;
+  const bool wide = a.block_size % 128 == 0 && last % 128 == 0;
+  const int64_t kv_wgs = (a.bh / a.group) * a.n_blocks * (a.block_size / (wide ? 128 : 64));
+  {
+    KernelTimer t(s, "bwd_dv");
+    if (wide) hipLaunchKernelGGL((dkv_kernel<D, 0, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dkv_kernel<D, 0, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+  }
+  {
+    KernelTimer t(s, "bwd_dk");
+    if (wide) hipLaunchKernelGGL((dk_kernel<D, 1, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dk_kernel<D, 1, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? backward_t<128>(a, s) : backward_t<64>(a, s);
+}
+
+}  // namespace moba
