@@ -12,27 +12,29 @@ namespace moba {
 // delta = do . o:  dv_u += p_u do,  ds_u = p_u (do . v_u - delta),
 // dq += ds_u k_u / sqrt(D),  dk_u += ds_u q / sqrt(D).
 //
-// Kernels (each step single-buffered: load a 64-row subtile to LDS, wait,
-// compute, barrier):
+// Kernels:
 //  bwd_prep    — delta and the log-sum-exp in the log2 domain per query;
+//  list_meta   — per list position its query row, log-sum-exp and delta,
+//                contiguous (one independent load per row for dK/dV);
 //  dq_past     — block-major like gather_attn (the forward's lists and
-//                tiles): per key subtile S^T = K Q^T and dP^T = V dO^T on
+//                tiles): per 64-key subtile S^T = K Q^T and dP^T = V dO^T on
 //                the forward's score path, then dQ^T += K^T dS^T on its P.V
 //                path (the same K copy read through the LDS transpose
-//                load); subtiles double-buffered; one fp32
-//                partial per (query, slot);
-//  dq_own      — the own block, 64 queries per workgroup, causal mask; it
-//                then adds the slots' partials in slot order and writes dq
-//                (no atomics);
-//  dkv         — key-major: a workgroup holds 128 (or 64) keys of one
-//                block (32 per wave, as the B operand the way the forward
-//                holds queries)
-//                and streams 64-row subtiles of the queries that attend
-//                them: the block's own queries, then its listed queries
-//                (gathered rows), for every query head of the key/value
-//                head. PASS 0 accumulates dV^T += dO^T P, PASS 1
-//                dK^T += Q^T dS (both on the P.V path); together they would
-//                not fit the register file.
+//                load); subtiles double-buffered; one fp32 partial per
+//                (query, slot);
+//  dq_own      — the own block, 128 (or 64) queries per workgroup, causal
+//                mask, single-buffered; it then adds the slots' partials in
+//                slot order and writes dq (no atomics);
+//  dkv, dk     — key-major: a workgroup holds 128 (or 64) keys of one block
+//                (32 per wave, as the B operand the way the forward holds
+//                queries) and streams 64-row subtiles of the queries that
+//                attend them: the block's own queries, then its listed
+//                queries (gathered rows), for every query head of the
+//                key/value head; blocks in order, heaviest first. dkv
+//                (software-pipelined over two buffer sets) accumulates
+//                dV^T += dO^T P, dk (single-buffered) dK^T += Q^T dS, both
+//                on the P.V path; one pass for both would not fit the
+//                register file.
 namespace {
 
 // C[row][lane column] for 64 LDS rows (K-swizzled layout) against the B
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   if (valid) store_row_f32<D>(a.dq_part + ((bh * a.seq_len * slots) + ev) * D, acc, h, 1.f / __builtin_sqrtf((float)D));
 }
 
-// The own block: 64 consecutive queries of one head.
+// The own block: 32 * NW consecutive queries of one head.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
   using E = EngBF16<D>;
