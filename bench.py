@@ -214,7 +214,26 @@ def backward_bench(args, w, wm, q, k, v, moba, torch):
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "work_per_launch": units[dom], "work_unit": "flop",
                      "avg_launch_ms": round(kern[dom]["avg_ms"], 4)},
+        "cpu_baseline": None,
     }
+    if args.cpu_rows > 0:
+        from oracle import sampled
+        n = min(args.cpu_rows, 16384)
+        log(f"cpu baseline: oracle backward on {n} sampled rows")
+        rows = synth.sample_rows(w, n)
+        pool_s, row_s, nrows, heads, workers = sampled.oracle_backward_rows(w, rows)
+        cpu_s = pool_s + row_s
+        bh = w.batch * w.heads
+        full_wall = (pool_s / heads * bh + row_s / nrows * bh * w.seq_len) / workers
+        line["cpu_baseline"] = {
+            "value": w.batch * w.seq_len / full_wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": (f"{nrows} seeded query rows over {heads} heads of {w.name}: routing plus the fp64 "
+                       f"softmax-attention gradient of each row (NumPy, {workers} processes, 1 BLAS thread each); "
+                       f"measured {cpu_s:.1f} CPU-s (pooling {pool_s:.1f} s + rows); value extrapolated to every head "
+                       f"and row ({bh} heads x {w.seq_len}) "
+                       f"= {full_wall:.1f} s wall"),
+        }
+        log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} tokens/s on {workers} cores")
     print(json.dumps(line), flush=True)
 
 

@@ -84,3 +84,45 @@ def oracle_rows(w: "synth.Workload", rows: np.ndarray, workers: int | None = Non
     out["wall_s"] = time.perf_counter() - t0
     out["workers"] = workers
     return out
+
+
+def _head_grad_rows(args):
+    """Oracle backward work for sampled rows of one head: each row's routing
+    and its softmax-attention gradient (dq for the row and its dk, dv
+    contributions), with a seeded upstream gradient. Timing only."""
+    w, b, h, ts = args
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    G = w.group
+    k, v = synth.make_kv(w.seed, b, h // G, w.seq_len, w.head_dim, w.block_size, w.dtype)
+    q = synth.make_q(w.seed, b, h, w.seq_len, w.head_dim, w.dtype)
+    do = np.random.default_rng(np.random.SeedSequence([w.seed, 1000, b, h])).standard_normal(q.shape)
+    t0 = time.perf_counter()
+    kbar = moba.pool_keys(k, w.block_size, w.pooling)
+    t1 = time.perf_counter()
+    for t in ts:
+        c = int(t) // w.block_size
+        idx, _, _, _ = moba.select_blocks(q[t], kbar, c, w.top_k, w.causal)
+        keys = moba.attended_keys(int(t), idx, w.block_size, w.causal, w.seq_len)
+        moba.attend_grad(q[t], k, v, keys, do[t])
+    return t1 - t0, time.perf_counter() - t1, len(ts)
+
+
+def oracle_backward_rows(w: "synth.Workload", rows: np.ndarray, workers: int | None = None):
+    """Times the oracle's backward on sampled rows (b, h, t); returns
+    (pool_seconds, row_seconds, rows, heads, workers): one pooling pass per
+    sampled head, and the rows' routing and gradients."""
+    rows = np.asarray(rows, dtype=np.int64)
+    groups = {}
+    for b, h, t in rows:
+        groups.setdefault((int(b), int(h)), []).append(int(t))
+    jobs = [(w, b, h, np.array(ts, np.int64)) for (b, h), ts in groups.items()]
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    workers = max(1, min(workers, len(jobs)))
+    if workers == 1:
+        res = list(map(_head_grad_rows, jobs))
+    else:
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(workers) as pool:
+            res = pool.map(_head_grad_rows, jobs)
+    return sum(r[0] for r in res), sum(r[1] for r in res), sum(r[2] for r in res), len(jobs), workers
