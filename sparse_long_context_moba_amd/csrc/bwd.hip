@@ -23,7 +23,7 @@ namespace moba {
 //                load); subtiles double-buffered; one fp32 partial per
 //                (query, slot);
 //  dq_own      — the own block, 128 (or 64) queries per workgroup, causal
-//                mask, single-buffered; it then adds the slots' partials in
+//                mask, double-buffered; it then adds the slots' partials in
 //                slot order and writes dq (no atomics);
 //  dkv, dk     — key-major: a workgroup holds 128 (or 64) keys of one block
 //                (32 per wave, as the B operand the way the forward holds
@@ -241,8 +241,9 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
   using E = EngBF16<D>;
   constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, M = 32 * NW;
-  // Single-buffered (32 KB), so that several workgroups share a compute unit.
-  __shared__ __align__(16) char bk[E::TB], bv[E::TB];
+  // Double-buffered (64 KB): registers already limit a compute unit to two
+  // of these workgroups (four waves each), which the LDS still holds.
+  __shared__ __align__(16) char bk0[E::TB], bv0[E::TB], bk1[E::TB], bv1[E::TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   const int64_t ntile = a.seq_len / M;
   const int64_t bh = blockIdx.x / ntile;
@@ -264,18 +265,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  E::template begin_one<NT, false>(kp, bk0, tid);
+  E::template begin_one<NT, false>(vp, bv0, tid);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
+  lds_dma_wait();
+  __syncthreads();
   for (int sub = 0; sub < nsub; ++sub) {
-    E::template begin_one<NT, false>(kp + (int64_t)sub * kSub * D, bk, tid);
-    E::template begin_one<NT, false>(vp + (int64_t)sub * kSub * D, bv, tid);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
-    lds_dma_wait();
-    __syncthreads();
+    // Subtile sub is in buffer sub & 1; sub + 1 loads into the other one
+    // (last read in step sub - 1, before its barrier).
+    const bool odd = sub & 1;
+    if (sub + 1 < nsub) {
+      E::template begin_one<NT, false>(kp + (int64_t)(sub + 1) * kSub * D, odd ? bk0 : bk1, tid);
+      E::template begin_one<NT, false>(vp + (int64_t)(sub + 1) * kSub * D, odd ? bv0 : bv1, tid);
+    }
+    const char* bk = odd ? bk1 : bk0;
+    const char* bv = odd ? bv1 : bv0;
     const int key0 = kb + sub * kSub;
     if (a.causal && key0 + kSub > q0 + 32 * w) {
       if (key0 <= q0 + 32 * w + 31) dq_step<D, true>(bk, bv, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
     } else {
       dq_step<D, false>(bk, bv, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
     }
+    lds_dma_wait();
     __syncthreads();
   }
   // dq = own-block part + the past slots' partials (written by dq_past, an
