@@ -296,6 +296,29 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int slots = a.k_eff - 1;
   const int n = min(slots, n_elig);
   bf16* dst = reinterpret_cast<bf16*>(a.dq) + row * D;
+  const float* p0 = a.dq_part + (row * slots) * D;
+  if (n <= 2) {
+    // One or two past blocks (top_k <= 3): every partial is requested
+    // before any is added (one memory round trip); slot order kept (the
+    // own part's scaling may fuse with the first addition).
+    f32x4 y0[DT * 4], y1[DT * 4];
+#pragma unroll
+    for (int i = 0; i < DT * 4; ++i) {
+      const int d = 32 * (i / 4) + 8 * (i % 4) + 4 * h;
+      if (n > 0) y0[i] = *reinterpret_cast<const f32x4*>(p0 + d);
+      if (n > 1) y1[i] = *reinterpret_cast<const f32x4*>(p0 + D + d);
+    }
+#pragma unroll
+    for (int i = 0; i < DT * 4; ++i) {
+      const int dt = i / 4, rg = i % 4, d = 32 * dt + 8 * rg + 4 * h;
+      f32x4 x = f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
+                      acc[dt][4 * rg + 3] * scale};
+      if (n > 0) x += y0[i];
+      if (n > 1) x += y1[i];
+      E::put4(dst + d, x[0], x[1], x[2], x[3]);
+    }
+    return;
+  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -303,7 +326,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int d = 32 * dt + 8 * rg + 4 * h;
       f32x4 x = f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
                       acc[dt][4 * rg + 3] * scale};
-      for (int sl = 0; sl < n; ++sl) x += *reinterpret_cast<const f32x4*>(a.dq_part + (row * slots + sl) * D + d);
+      for (int sl = 0; sl < n; ++sl) x += *reinterpret_cast<const f32x4*>(p0 + sl * D + d);
       E::put4(dst + d, x[0], x[1], x[2], x[3]);
     }
 }
