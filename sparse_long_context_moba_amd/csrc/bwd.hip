@@ -522,16 +522,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // dK (launched with PASS = 1; PASS = 0 would give dV) for 32 * NW keys of
 // one block of one key/value head, single-buffered: each 64-row query
-// subtile is staged (row numbers, log-sum-exps, deltas, then the rows of
-// Q, dO and Q^T) and then computed. For dK this beats the pipelined
-// dkv_kernel, which spills registers in this pass (same-box A/B at
-// headline_32k: 1.75-1.79 against 1.94 ms; for dV the pipelined kernel
-// wins, 1.47 against 1.49-1.54 ms).
+// subtile is staged (row numbers, log-sum-exps and deltas, for listed rows
+// from list_meta_kernel's contiguous arrays, then the rows of Q and dO,
+// K-swizzled) and then computed; dK^T += Q^T dS reads Q transposed from
+// its one copy. For dK this beats the pipelined dkv_kernel, which spills
+// registers in this pass (same-box A/B at headline_32k: 1.75-1.79 against
+// 1.94 ms; for dV the pipelined kernel wins, 1.47 against 1.49-1.54 ms),
+// and it beats this kernel with double-buffered metadata (12-24 registers
+// spilled: 2.16-2.33 against 1.67-1.69 ms).
 template <int D, int PASS, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dk_kernel(BwdArgs a) {
   using E = EngBF16<D>;
   constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, KEYS = 32 * NW;
-  __shared__ __align__(16) char bq[E::TB], bx[E::TB], by[PASS == 1 ? E::TB : 16];
+  __shared__ __align__(16) char bq[E::TB], bx[E::TB];
   __shared__ int rows[64];
   __shared__ float lse2s[64], deltas[64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
@@ -558,13 +561,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   // One 64-row subtile of query head bh: rows from row_of(i) (valid when
   // i < n), causal mask against the keys when MASK.
-  auto subtile = [&](int64_t bh, int n, bool mask, auto&& row_of) {
+  auto subtile = [&](int64_t bh, int n, bool own, int64_t first) {
+    const bool mask = own && a.causal;
     if (tid < 64) {
       const bool ok = tid < n;
-      const int t = row_of(ok ? tid : 0);  // a padding row repeats a valid one
+      const int64_t i = first + (ok ? tid : 0);  // a padding row repeats a valid one
+      int t;
+      float l, dl;
+      if (own) {
+        t = (int)i;
+        l = a.lse2[bh * a.seq_len + i];
+        dl = a.delta[bh * a.seq_len + i];
+      } else {  // list position: one independent load each
+        t = a.lt[i];
+        l = a.ll[i];
+        dl = a.ld[i];
+      }
       rows[tid] = t;
-      lse2s[tid] = ok ? a.lse2[bh * a.seq_len + t] : __builtin_inff();
-      deltas[tid] = ok ? a.delta[bh * a.seq_len + t] : 0.f;
+      lse2s[tid] = ok ? l : __builtin_inff();
+      deltas[tid] = ok ? dl : 0.f;
     }
     __syncthreads();
     const bf16* qb = reinterpret_cast<const bf16*>(a.q) + bh * a.seq_len * D;
@@ -574,7 +589,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       load_rows<D, NT, true>(gb, rows, bx, tid);   // dO^T for dV
     } else {
       load_rows<D, NT, false>(gb, rows, bx, tid);  // dO for dP
-      load_rows<D, NT, true>(qb, rows, by, tid);   // Q^T for dK
     }
     lds_dma_wait();
     __syncthreads();
@@ -598,7 +612,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           else s[nt][r] = p * (dp[nt][r] - d4[e]);
         }
       }
-    mm_trans<D>(PASS == 0 ? bx : by, lane, s, acc);
+    if constexpr (PASS == 0) mm_trans<D>(bx, lane, s, acc);
+    else mm_trans<D, false>(bq, lane, s, acc);
     __syncthreads();
   };
   for (int g = 0; g < a.group; ++g) {
@@ -607,16 +622,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int64_t qs = a.causal ? k0 : j * a.block_size;
     for (int64_t t0 = qs; t0 < jend; t0 += 64) {
       const int n = (int)min<int64_t>(64, jend - t0);
-      subtile(bh, n, a.causal, [&](int i) { return (int)(t0 + i); });
+      subtile(bh, n, true, t0);
     }
     // Its listed queries (past-block routing of later, or other, queries).
     if (slots > 0) {
-      const int32_t* lst = a.qlist + a.offset[bh * a.n_blocks + j];
-      const int cnt = a.offset[bh * a.n_blocks + j + 1] - a.offset[bh * a.n_blocks + j];
-      for (int i0 = 0; i0 < cnt; i0 += 64) {
-        const int n = min(64, cnt - i0);
-        subtile(bh, n, false, [&](int i) { return lst[i0 + i] / slots; });
-      }
+      const int64_t o0 = a.offset[bh * a.n_blocks + j];
+      const int cnt = a.offset[bh * a.n_blocks + j + 1] - o0;
+      for (int i0 = 0; i0 < cnt; i0 += 64) subtile(bh, min(64, cnt - i0), false, o0 + i0);
     }
   }
   bf16* dst = reinterpret_cast<bf16*>(PASS == 0 ? a.dv : a.dk) + (kvh * a.seq_len + u) * D;
