@@ -559,8 +559,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  // One 64-row subtile of query head bh: rows from row_of(i) (valid when
-  // i < n), causal mask against the keys when MASK.
+  // One 64-row subtile of query head bh, n valid rows from `first`: own
+  // rows are consecutive queries (masked against the keys when causal),
+  // listed rows are list positions.
   auto subtile = [&](int64_t bh, int n, bool own, int64_t first) {
     const bool mask = own && a.causal;
     if (tid < 64) {
