@@ -183,7 +183,7 @@ BwdPlan plan_backward(const Plan& P) {
   B.delta = take(rows * 4);
   B.lse2 = take(rows * 4);
   B.dq_part = take(rows * (size_t)P.slots * (size_t)P.D * 4);
-  B.chunk_counts = take((size_t)P.bh * (size_t)((P.S + kRankChunk - 1) / kRankChunk) * (size_t)P.nb * 4);
+  B.chunk_counts = take((size_t)P.bh * (size_t)((P.S + rank_chunk(P.S) - 1) / rank_chunk(P.S)) * (size_t)P.nb * 4);
   B.lt = take((size_t)P.pairs * 4);
   B.ll = take((size_t)P.pairs * 4);
   B.ld = take((size_t)P.pairs * 4);

@@ -56,7 +56,6 @@ constexpr int kNoBlock = 0x7fffffff;
 constexpr int kTileB = 32;          // pooled keys per LDS tile
 constexpr int kLdsBinsMax = 8192;   // per-workgroup histogram bins kept in LDS
 constexpr int kRankQ = 1024;        // queries per rank workgroup
-static_assert(kRankQ == kRankChunk, "rank chunk of the ordered ranks");
 
 // Strict order: higher score first, then lower block index.
 __device__ __forceinline__ bool better64(double s1, int j1, double s2, int j2) {
@@ -866,15 +865,15 @@ static hipError_t gate_launch_t(const GateArgs& a, hipStream_t s) {
 // count), and rank_ordered numbers the picks of a chunk in the order
 // (64-query group, column of block_idx, lane) with wave ballots: lanes
 // with the same block in one column get consecutive ranks by lane.
-__global__ __launch_bounds__(256) void chunk_count_kernel(GateArgs a, int32_t* cc, int64_t nchunk) {
+__global__ __launch_bounds__(256) void chunk_count_kernel(GateArgs a, int32_t* cc, int64_t nchunk, int qchunk) {
   extern __shared__ __align__(16) char smem[];
   int* bins = reinterpret_cast<int*>(smem);
   const int NB = (int)a.n_blocks;
   const int64_t bh = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
   for (int i = threadIdx.x; i < NB; i += 256) bins[i] = 0;
   __syncthreads();
-  for (int qq = threadIdx.x; qq < kRankQ; qq += 256) {
-    const int64_t t = ch * kRankQ + qq;
+  for (int qq = threadIdx.x; qq < qchunk; qq += 256) {
+    const int64_t t = ch * qchunk + qq;
     if (t >= a.seq_len) break;
     const int c = (int)(t / a.block_size);
     const int32_t* row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
@@ -893,17 +892,29 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(GateArgs a, int32_t* cc
   const int NB = (int)a.n_blocks;
   if (id >= a.bh * NB) return;
   const int64_t bh = id / NB, j = id % NB;
+  int32_t* p = cc + bh * nchunk * NB + j;  // chunk ch at p[ch * NB]
   int32_t run = 0;
-  for (int64_t ch = 0; ch < nchunk; ++ch) {
-    int32_t* p = cc + (bh * nchunk + ch) * NB + j;
-    const int32_t n = *p;
-    *p = run;
+  int64_t ch = 0;
+  // Eight counts requested before the first of their bases is stored.
+  for (; ch + 8 <= nchunk; ch += 8) {
+    int32_t n[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) n[u] = p[(ch + u) * NB];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      p[(ch + u) * NB] = run;
+      run += n[u];
+    }
+  }
+  for (; ch < nchunk; ++ch) {
+    const int32_t n = p[ch * NB];
+    p[ch * NB] = run;
     run += n;
   }
   a.count[id] = run;
 }
 
-__global__ __launch_bounds__(64) void rank_ordered_kernel(GateArgs a, const int32_t* cc, int64_t nchunk) {
+__global__ __launch_bounds__(64) void rank_ordered_kernel(GateArgs a, const int32_t* cc, int64_t nchunk, int qchunk) {
   extern __shared__ __align__(16) char smem[];
   int* bins = reinterpret_cast<int*>(smem);
   const int NB = (int)a.n_blocks;
@@ -912,8 +923,8 @@ __global__ __launch_bounds__(64) void rank_ordered_kernel(GateArgs a, const int3
   const int slots = a.k_eff - 1;
   for (int i = lane; i < NB; i += 64) bins[i] = cc[(bh * nchunk + ch) * NB + i];
   __syncthreads();
-  for (int g = 0; g < kRankQ; g += 64) {
-    const int64_t t = ch * kRankQ + g + lane;
+  for (int g = 0; g < qchunk; g += 64) {
+    const int64_t t = ch * qchunk + g + lane;
     const bool on = t < a.seq_len;
     const int c = on ? (int)(t / a.block_size) : -1;
     const int32_t* row = a.block_idx + (bh * a.seq_len + (on ? t : 0)) * a.top_k;
@@ -943,14 +954,17 @@ __global__ __launch_bounds__(64) void rank_ordered_kernel(GateArgs a, const int3
 
 hipError_t launch_rank(const GateArgs& a, hipStream_t s, int32_t* chunk_counts) {
   if (a.k_eff < 2) return hipSuccess;
-  const int64_t nchunk = (a.seq_len + kRankQ - 1) / kRankQ;
+  const int qchunk = (int)rank_chunk(a.seq_len);
+  const int64_t nchunk = (a.seq_len + qchunk - 1) / qchunk;
   const int lds = (int)a.n_blocks * 4;
   if (lds > 65536) return hipErrorInvalidValue;
   KernelTimer timer(s, "rank_ordered");
-  hipLaunchKernelGGL(chunk_count_kernel, dim3((unsigned)(a.bh * nchunk)), dim3(256), lds, s, a, chunk_counts, nchunk);
+  hipLaunchKernelGGL(chunk_count_kernel, dim3((unsigned)(a.bh * nchunk)), dim3(256), lds, s, a, chunk_counts, nchunk,
+                     qchunk);
   hipLaunchKernelGGL(chunk_scan_kernel, dim3((unsigned)((a.bh * a.n_blocks + 255) / 256)), dim3(256), 0, s, a,
                      chunk_counts, nchunk);
-  hipLaunchKernelGGL(rank_ordered_kernel, dim3((unsigned)(a.bh * nchunk)), dim3(64), lds, s, a, chunk_counts, nchunk);
+  hipLaunchKernelGGL(rank_ordered_kernel, dim3((unsigned)(a.bh * nchunk)), dim3(64), lds, s, a, chunk_counts, nchunk,
+                     qchunk);
   return hipGetLastError();
 }
 

@@ -129,9 +129,12 @@ struct BwdArgs {
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 // Ranks of a given block_idx in a fixed order, and the per-block counts
-// (a.count), for the backward; chunk_counts: [bh, ceil(S / 1024), nb] int32
-// scratch. Needs n_blocks <= 16384.
-constexpr int64_t kRankChunk = 1024;
+// (a.count), for the backward; chunk_counts: [bh, ceil(S / rank_chunk(S)),
+// nb] int32 scratch. Needs n_blocks <= 16384. Queries per chunk: 256 while
+// a sequence has at most 128 chunks (more waves for short sequences), else
+// 1024 (bounded scratch and scan length for long ones); a multiple of 64, so
+// the rank order, by 64-query group, does not depend on it.
+inline int64_t rank_chunk(int64_t seq_len) { return seq_len <= 128 * 256 ? 256 : 1024; }
 hipError_t launch_rank(const GateArgs& a, hipStream_t s, int32_t* chunk_counts);
 
 }  // namespace moba
