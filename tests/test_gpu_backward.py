@@ -87,17 +87,15 @@ def test_backward_parity(case):
     say(f"[gpu] backward {label}: ok, max error / scale: " + ", ".join(f"{n}={v:.2e}" for n, v in worst.items()))
 
 
-def test_backward_headline_sampled():
-    """headline_32k (32 heads, 32768 tokens, block 512, top_k 3) at full
-    size, in the launch configuration bench.py --backward times: dq on 256
-    seeded sampled rows (plus edge rows), and dk, dv on every key of two
-    blocks (the first and the last) of the first and the last head, each
-    summed by the oracle over every query that attends those keys."""
+def _check_sampled(w):
+    """dq on 256 seeded sampled rows (plus edge rows), and dk, dv on every
+    key of two blocks (the first and the last) of the first and the last
+    head, each summed by the oracle over every query that attends those
+    keys."""
     import synth
     import sparse_long_context_moba_amd as moba
-    w = synth.WORKLOADS["headline_32k"]
     S, D, Bs = w.seq_len, w.head_dim, w.block_size
-    say("[gpu] backward headline_32k: generating inputs")
+    say(f"[gpu] backward {w.name}: generating inputs")
     q = torch.empty((1, w.heads, S, D), dtype=torch.bfloat16, device="cuda")
     k, v = (torch.empty_like(q) for _ in range(2))
     host = {}
@@ -135,4 +133,19 @@ def test_backward_headline_sampled():
             for name, got, r in (("dk", dkh[lo:hi], rdk), ("dv", dvh[lo:hi], rdv)):
                 e = np.abs(got - r).max()
                 assert e <= REL * np.abs(r).max(), f"h={h} block={j}: {name} error {e:.3e} (scale {np.abs(r).max():.3e})"
-            say(f"[gpu] backward headline_32k h={h} block={j}: {len(users)} queries attend it; ok")
+            say(f"[gpu] backward {w.name} h={h} block={j}: {len(users)} queries attend it; ok")
+
+
+def test_backward_headline_sampled():
+    """headline_32k (32 heads, 32768 tokens, block 512, top_k 3) at full
+    size, in the launch configuration bench.py --backward times."""
+    import synth
+    _check_sampled(synth.WORKLOADS["headline_32k"])
+
+
+def test_backward_64k_two_heads_sampled():
+    """65536 tokens, 2 heads, block 512, top_k 3: past 32768 tokens the
+    ordered ranks of the backward's lists take 1024-query chunks (256 up to
+    that length), so this covers the other chunk size."""
+    import synth
+    _check_sampled(synth.Workload("bwd_64k_2h", 1, 2, 65536, 128, 512, 3, True, "bf16", 21))
