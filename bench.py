@@ -130,6 +130,21 @@ def upload(w, torch, workers=None):
     return q, k, v
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) and the cores this
+    process may run on."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return name, len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, n_rows):
     """The fp64 oracle on a bounded seeded sample of the workload, on this
     host's cores; extrapolated to a full forward (pool every head + every
@@ -143,14 +158,18 @@ def cpu_baseline(w, n_rows):
     bh = w.batch * w.heads
     cpu_seconds = pool_per_head * bh + row_s * bh * w.seq_len
     full_wall = cpu_seconds / out["workers"]
+    model, affinity = cpu_model()
     return {
         "value": w.batch * w.seq_len / full_wall,
         "unit": "tokens/s",
         "cores": out["workers"],
         "kind": "oracle",
+        "cpu_model": model,
+        "affinity_cores": affinity,
         "near_ties": int(out["flag"].sum()),
         "sample": (f"{len(rows)} seeded query rows over {heads} heads of {w.name} (fp64 NumPy, "
-                   f"{out['workers']} processes, 1 BLAS thread each); measured {out['oracle_s']:.1f} CPU-s "
+                   f"{out['workers']} processes, 1 BLAS thread each, on {model}; {affinity} cores in this "
+                   f"process's affinity, of which one GPU's host share is 16); measured {out['oracle_s']:.1f} CPU-s "
                    f"(pool {out['pool_s']:.1f} s + rows); value extrapolated to a full forward "
                    f"({bh} heads x {w.seq_len} rows) = {full_wall:.1f} s wall"),
     }

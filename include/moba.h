@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 4
+#define MOBA_ABI_VERSION 5
 
 typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype_t;
 
@@ -118,7 +118,7 @@ typedef struct {
 int moba_abi_version(void);
 
 /* Static text for a status code (never NULL). */
-const char* moba_status_str(int status);
+const char* moba_status_str(moba_status_t status);
 
 /* Detail of the last failing call on this thread, naming the bad
  * parameter ("" after a successful call). Valid until the next call. */
@@ -126,7 +126,7 @@ const char* moba_last_error(void);
 
 /* Bytes of device workspace moba_forward needs for *p (host only, no HIP
  * call). Fails with the same codes as moba_forward's validation. */
-int moba_workspace_size(const moba_problem_t* p, size_t* bytes);
+moba_status_t moba_workspace_size(const moba_problem_t* p, size_t* bytes);
 
 /* MoBA prefill forward ([P] §3.1, [S] §3; steps listed at the top).
  *   q, k, v  — inputs (see conventions); read only.
@@ -142,7 +142,7 @@ int moba_workspace_size(const moba_problem_t* p, size_t* bytes);
  * Gate scores are selected exactly: a query whose fast (MFMA) scores leave
  * the cut between kept and dropped blocks inside their rounding bound is
  * re-scored in fp64. */
-int moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
+moba_status_t moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
                  void* o, int32_t* block_idx, void* workspace, size_t workspace_bytes,
                  void* stream);
 
@@ -151,7 +151,7 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
  * softmax normaliser a backward pass reuses).
  *   lse — device float32 [batch, heads, seq_len]; must not be NULL.
  * Everything else as moba_forward (same workspace size). */
-int moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v,
+moba_status_t moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v,
                      void* o, int32_t* block_idx, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
@@ -163,7 +163,15 @@ int moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, cons
  * remains is, per query, the gradient of one softmax attention over its
  * attended keys. MoBA is used in training and fine-tuning ([S] §3, [P] §2);
  * the pages give no gradient, this is the plain reading.
- *   q, k, v, o, block_idx — the forward's inputs and outputs (same problem);
+ *   q, k, v, o, block_idx — the forward's inputs and outputs (same problem).
+ *           A block_idx row is read up to its first -1; entries that do not
+ *           name a past block the query may attend (outside 0..n_blocks-1,
+ *           its own block, a later block under causal routing) are
+ *           skipped, and only the first min(top_k, n_blocks) - 1 (at most
+ *           the eligible count) past entries are used. The own block is
+ *           always attended. A row the forward wrote is used as is; an
+ *           edited row gets the gradient of the blocks that remain, which
+ *           is that of the forward only if lse matches them;
  *   lse   — device float32 [batch, heads, seq_len] from moba_forward_lse;
  *   dout  — device, like o: the upstream gradient;
  *   dq    — output, like q; dk, dv — outputs, like k and v (summed over the
@@ -172,8 +180,8 @@ int moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, cons
  *           aligned, contents on entry irrelevant.
  * Deterministic: no floating-point atomics; dq sums its per-block parts in
  * a fixed order. */
-int moba_backward_workspace_size(const moba_problem_t* p, size_t* bytes);
-int moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+moba_status_t moba_backward_workspace_size(const moba_problem_t* p, size_t* bytes);
+moba_status_t moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk,
                   void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -199,30 +207,54 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
  *                sequences, which run one after another on the stream.
  * Every sequence is validated before anything is launched; an error names
  * the sequence. */
-int moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+moba_status_t moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
                                size_t* bytes);
-int moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+moba_status_t moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
                         const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Full softmax attention on the same layout (causal if p->causal), used to
- * measure MoBA's speedup over the method it approximates ([R] §1.2, [P] §1).
- * block_size and top_k are ignored apart from validation of their sign;
- * seq_len must be a multiple of 64. Needs no workspace. */
-int moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
-                       void* o, void* stream);
+/* Full causal softmax attention on the same layout, the method MoBA
+ * approximates: with top_k covering every block MoBA becomes exactly this,
+ * the switch to full attention [R] §1.2 describes for short inputs; MoBA's
+ * speedup is measured against it ([P] §1 quotes the speedup over full
+ * attention at 1M and 10M tokens).
+ *   q, k, v — as for moba_forward (kv_heads honoured); o — output like q.
+ * p->causal is ignored (always causal); block_size, top_k and pooling are
+ * validated for sign only. Limits: head_dim in {64, 128}, seq_len a
+ * multiple of 64. Needs no workspace; errors as for moba_forward. */
+moba_status_t moba_dense_causal_forward(const moba_problem_t* p, const void* q, const void* k,
+                                        const void* v, void* o, void* stream);
 
-/* Stage entry point: block pooling only ([P] §3.1 mean_pool; p->pooling
- * selects the summary as for moba_forward).
- * kbar: device float64 [batch, kv_heads, n_blocks, head_dim] — the pooled keys
- * the gate uses. Uses the forward's workspace. */
-int moba_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace,
-              size_t workspace_bytes, void* stream);
+/* moba_dense_causal_forward with the mask taken from p->causal (zero: full
+ * non-causal attention, which MoBA equals when it keeps every block without
+ * a causal mask). */
+moba_status_t moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                                 void* o, void* stream);
 
-/* Stage entry point: pooling, gate scores and top-k selection only; writes
- * block_idx exactly as moba_forward does. Uses the forward's workspace. */
-int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* block_idx,
-                void* workspace, size_t workspace_bytes, void* stream);
+/* Stage entry point (test/debug): the block summaries alone, step 1 of the
+ * forward. Each block's keys are mean-pooled along the sequence ([P] §3.1,
+ * gating score_fn mean_pool; [S] §3), or max / mean+max pooled per
+ * p->pooling ([S] §3 names them as options).
+ *   k    — device keys [batch, kv_heads, seq_len, head_dim];
+ *   kbar — output, device float64 [batch, kv_heads, n_blocks, head_dim]:
+ *          the pooled keys the gate scores against (a short last block
+ *          pooled over the tokens it holds).
+ * Uses the forward's workspace (moba_workspace_size). Errors as for
+ * moba_forward, plus MOBA_ERR_NULL for a NULL kbar. */
+moba_status_t moba_debug_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Stage entry point (test/debug): pooling, the gate and the top-k choice
+ * alone, steps 1-3 of the forward. Each query scores the eligible blocks by
+ * its inner product with their pooled keys, future blocks masked ([P] §3.1
+ * causal / mask_future), keeps its own block ([S] §3 force_current_block)
+ * and the best top_k - 1 scored blocks, ties to the lower index (the
+ * stable descending sort of [P] §4.1's routing check).
+ *   q, k      — as for moba_forward;
+ *   block_idx — output, exactly the block_idx moba_forward writes.
+ * Uses the forward's workspace; errors as for moba_forward. */
+moba_status_t moba_debug_gate_topk(const moba_problem_t* p, const void* q, const void* k, int32_t* block_idx,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing with HIP events on the launching stream.
  * moba_timing_enable(1) creates an event pool (host call, not for use under
@@ -237,8 +269,8 @@ typedef struct {
   double total_ms;
 } moba_kernel_time_t;
 
-int moba_timing_enable(int enable);
-int moba_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries);
+moba_status_t moba_timing_enable(int enable);
+moba_status_t moba_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries);
 
 #ifdef __cplusplus
 }

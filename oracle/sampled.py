@@ -51,6 +51,7 @@ def oracle_rows(w: "synth.Workload", rows: np.ndarray, workers: int | None = Non
         groups.setdefault((int(b), int(h)), []).append((i, int(t)))
     jobs = [(w, b, h, np.array([t for _, t in lst], np.int64)) for (b, h), lst in groups.items()]
     if workers is None:
+        # Every affinity core, up to the 16-core host share one GPU gets.
         workers = min(16, len(os.sched_getaffinity(0)))
     workers = max(1, min(workers, len(jobs)))
     n = len(rows)
@@ -117,6 +118,7 @@ def oracle_backward_rows(w: "synth.Workload", rows: np.ndarray, workers: int | N
         groups.setdefault((int(b), int(h)), []).append(int(t))
     jobs = [(w, b, h, np.array(ts, np.int64)) for (b, h), ts in groups.items()]
     if workers is None:
+        # Every affinity core, up to the 16-core host share one GPU gets.
         workers = min(16, len(os.sched_getaffinity(0)))
     workers = max(1, min(workers, len(jobs)))
     if workers == 1:

@@ -18,15 +18,16 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (MOBA_BF16, MOBA_F32, moba_abi_version, moba_dense_forward, moba_forward, moba_forward_lse,
-                   moba_last_error, moba_pool, moba_problem_t, moba_select, moba_status_str,
+from ._lib import (MOBA_BF16, MOBA_F32, moba_abi_version, moba_dense_causal_forward, moba_dense_forward,
+                   moba_forward, moba_forward_lse, moba_last_error, moba_debug_pool, moba_problem_t,
+                   moba_debug_gate_topk, moba_status_str,
                    moba_timing_enable, moba_timing_read, moba_workspace_size,
                    moba_forward_varlen, moba_workspace_size_varlen, moba_backward,
                    moba_backward_workspace_size)
 
 __all__ = ["MobaError", "forward", "dense", "pool", "select", "problem", "workspace_bytes",
-           "timing", "moba_abi_version", "moba_forward", "moba_dense_forward", "moba_pool",
-           "moba_select", "moba_workspace_size", "moba_status_str", "moba_last_error",
+           "timing", "moba_abi_version", "moba_forward", "moba_dense_causal_forward", "moba_dense_forward",
+           "moba_debug_pool", "moba_debug_gate_topk", "moba_workspace_size", "moba_status_str", "moba_last_error",
            "moba_timing_enable", "moba_timing_read", "moba_problem_t"]
 
 _DTYPES = {torch.float32: MOBA_F32, torch.bfloat16: MOBA_BF16}
@@ -82,6 +83,39 @@ def _tensors(q, *kv):
     return int(k.shape[1])
 
 
+def check_buffer(t, name: str, shape, dtype, device):
+    """A caller-supplied output or input buffer must have exactly this shape,
+    dtype and device and be contiguous: the kernels index it from those
+    sizes, so a smaller or differently typed buffer would be read or written
+    out of bounds. Returns t; raises ValueError naming the buffer."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def check_workspace(ws, need: int, device) -> int:
+    """A caller-supplied workspace: a contiguous tensor on the device with at
+    least `need` bytes. Returns its size in bytes (numel * element size)."""
+    if not isinstance(ws, torch.Tensor):
+        raise ValueError(f"workspace must be a tensor, got {type(ws).__name__}")
+    if ws.device != torch.device(device):
+        raise ValueError(f"workspace must be on {device}, got {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    n = ws.numel() * ws.element_size()
+    if n < need:
+        raise ValueError(f"workspace holds {n} bytes, the problem needs {need}")
+    return n
+
+
 def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -110,12 +144,14 @@ def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None,
     hkv = _tensors(q, k, v)
     p = problem(q, block_size, top_k, causal, pooling, hkv, gate_shared)
     B, H, S, D = q.shape
-    o = torch.empty_like(q) if out is None else out
-    bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device) if idx is None else idx
+    o = torch.empty_like(q) if out is None else check_buffer(out, "out", q.shape, q.dtype, q.device)
+    idx_shape = (B, H, S, int(top_k))
+    bi = torch.empty(idx_shape, dtype=torch.int32, device=q.device) if idx is None else \
+        check_buffer(idx, "idx", idx_shape, torch.int32, q.device)
     if workspace is None:
         ws, n = _workspace(p, q.device)
     else:
-        ws, n = workspace, workspace.numel()
+        ws, n = workspace, check_workspace(workspace, workspace_bytes(p), q.device)
     with torch.cuda.device(q.device):
         if return_lse:
             lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
@@ -133,11 +169,11 @@ def backward(q, k, v, o, dout, idx, lse, block_size: int, top_k: int, causal: bo
     forward(..., return_lse=True)."""
     hkv = _tensors(q, k, v)
     _tensors(q, o, dout)
-    if o.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("o and dout must have q's shape")
-    if not (idx.is_cuda and idx.is_contiguous() and idx.dtype == torch.int32 and lse.is_cuda
-            and lse.is_contiguous() and lse.dtype == torch.float32):
-        raise ValueError("idx must be contiguous int32 and lse contiguous float32 on the GPU")
+    check_buffer(o, "o", q.shape, q.dtype, q.device)
+    check_buffer(dout, "dout", q.shape, q.dtype, q.device)
+    B, H, S, D = q.shape
+    check_buffer(idx, "idx", (B, H, S, int(top_k)), torch.int32, q.device)
+    check_buffer(lse, "lse", (B, H, S), torch.float32, q.device)
     p = problem(q, block_size, top_k, causal, "mean", hkv)
     st, n = moba_backward_workspace_size(p)
     _check(st, "moba_backward_workspace_size")
@@ -204,13 +240,16 @@ def unpack_varlen(x, cu_seqlens, heads: int):
 
 
 def dense(q, k, v, causal: bool = True, out=None):
-    """Full softmax attention (causal or not) with the library's dense kernel."""
+    """Full softmax attention (causal or not) with the library's dense
+    kernel: moba_dense_causal_forward, or moba_dense_forward without the
+    causal mask."""
     hkv = _tensors(q, k, v)
     p = problem(q, q.shape[2], 1, causal, kv_heads=hkv)
-    o = torch.empty_like(q) if out is None else out
+    o = torch.empty_like(q) if out is None else check_buffer(out, "out", q.shape, q.dtype, q.device)
+    fn, name = (moba_dense_causal_forward, "moba_dense_causal_forward") if causal else \
+        (moba_dense_forward, "moba_dense_forward")
     with torch.cuda.device(q.device):
-        _check(moba_dense_forward(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                  _stream(q.device)), "moba_dense_forward")
+        _check(fn(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _stream(q.device)), name)
     return o
 
 
@@ -223,8 +262,8 @@ def pool(k, block_size: int, pooling: str = "mean"):
     kbar = torch.empty((B, H, nb, D), dtype=torch.float64, device=k.device)
     ws, n = _workspace(p, k.device)
     with torch.cuda.device(k.device):
-        _check(moba_pool(p, k.data_ptr(), kbar.data_ptr(), ws.data_ptr(), n, _stream(k.device)),
-               "moba_pool")
+        _check(moba_debug_pool(p, k.data_ptr(), kbar.data_ptr(), ws.data_ptr(), n, _stream(k.device)),
+               "moba_debug_pool")
     return kbar
 
 
@@ -237,8 +276,8 @@ def select(q, k, block_size: int, top_k: int, causal: bool = True, pooling: str 
     bi = torch.empty((B, H, S, int(top_k)), dtype=torch.int32, device=q.device)
     ws, n = _workspace(p, q.device)
     with torch.cuda.device(q.device):
-        _check(moba_select(p, q.data_ptr(), k.data_ptr(), bi.data_ptr(), ws.data_ptr(), n,
-                           _stream(q.device)), "moba_select")
+        _check(moba_debug_gate_topk(p, q.data_ptr(), k.data_ptr(), bi.data_ptr(), ws.data_ptr(), n,
+                                    _stream(q.device)), "moba_debug_gate_topk")
     return bi
 
 

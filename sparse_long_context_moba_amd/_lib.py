@@ -19,7 +19,8 @@ STATUS_NAMES = {0: "MOBA_OK", 1: "MOBA_ERR_NULL", 2: "MOBA_ERR_SHAPE", 3: "MOBA_
                 4: "MOBA_ERR_DTYPE", 5: "MOBA_ERR_UNSUPPORTED", 6: "MOBA_ERR_WORKSPACE",
                 7: "MOBA_ERR_DEVICE"}
 EXPORTED = ["moba_abi_version", "moba_status_str", "moba_last_error", "moba_workspace_size",
-            "moba_forward", "moba_forward_lse", "moba_dense_forward", "moba_pool", "moba_select",
+            "moba_forward", "moba_forward_lse", "moba_dense_causal_forward", "moba_dense_forward",
+            "moba_debug_pool", "moba_debug_gate_topk",
             "moba_workspace_size_varlen", "moba_forward_varlen",
             "moba_backward_workspace_size", "moba_backward",
             "moba_timing_enable", "moba_timing_read"]
@@ -51,9 +52,10 @@ def _load():
         "moba_workspace_size": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moba_forward": ([P, vp, vp, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
         "moba_forward_lse": ([P, vp, vp, vp, vp, i32p, vp, vp, sz, vp], ctypes.c_int),
+        "moba_dense_causal_forward": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
         "moba_dense_forward": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
-        "moba_pool": ([P, vp, vp, vp, sz, vp], ctypes.c_int),
-        "moba_select": ([P, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
+        "moba_debug_pool": ([P, vp, vp, vp, sz, vp], ctypes.c_int),
+        "moba_debug_gate_topk": ([P, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
         "moba_workspace_size_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moba_forward_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, vp, vp, vp, vp, i32p, vp,
@@ -136,18 +138,23 @@ def moba_forward_varlen(problem, cu_seqlens, q, k, v, o, block_idx, workspace, w
                                      workspace_bytes, stream)
 
 
+def moba_dense_causal_forward(problem, q, k, v, o, stream) -> int:
+    return lib().moba_dense_causal_forward(ctypes.byref(problem) if problem is not None else None, q, k, v, o,
+                                           stream)
+
+
 def moba_dense_forward(problem, q, k, v, o, stream) -> int:
     return lib().moba_dense_forward(ctypes.byref(problem) if problem is not None else None, q, k, v, o, stream)
 
 
-def moba_pool(problem, k, kbar, workspace, workspace_bytes, stream) -> int:
-    return lib().moba_pool(ctypes.byref(problem) if problem is not None else None, k, kbar, workspace,
-                         workspace_bytes, stream)
+def moba_debug_pool(problem, k, kbar, workspace, workspace_bytes, stream) -> int:
+    return lib().moba_debug_pool(ctypes.byref(problem) if problem is not None else None, k, kbar, workspace,
+                                 workspace_bytes, stream)
 
 
-def moba_select(problem, q, k, block_idx, workspace, workspace_bytes, stream) -> int:
-    return lib().moba_select(ctypes.byref(problem) if problem is not None else None, q, k, block_idx,
-                           workspace, workspace_bytes, stream)
+def moba_debug_gate_topk(problem, q, k, block_idx, workspace, workspace_bytes, stream) -> int:
+    return lib().moba_debug_gate_topk(ctypes.byref(problem) if problem is not None else None, q, k, block_idx,
+                                      workspace, workspace_bytes, stream)
 
 
 def moba_backward_workspace_size(problem):

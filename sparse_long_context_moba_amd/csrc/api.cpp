@@ -359,11 +359,9 @@ int varlen_plans(const moba_problem_t* p, const int64_t* cu, int64_t n, std::vec
 }
 }  // namespace
 
-extern "C" {
+namespace {
 
-int moba_abi_version(void) { return MOBA_ABI_VERSION; }
-
-const char* moba_status_str(int status) {
+const char* status_text(int status) {
   switch (status) {
     case MOBA_OK: return "ok";
     case MOBA_ERR_NULL: return "null pointer";
@@ -377,9 +375,7 @@ const char* moba_status_str(int status) {
   }
 }
 
-const char* moba_last_error(void) { return g_err.c_str(); }
-
-int moba_workspace_size(const moba_problem_t* p, size_t* bytes) {
+int impl_workspace_size(const moba_problem_t* p, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
   Plan P;
@@ -389,7 +385,7 @@ int moba_workspace_size(const moba_problem_t* p, size_t* bytes) {
   return MOBA_OK;
 }
 
-int moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+int impl_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
                  int32_t* block_idx, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Plan P;
@@ -402,7 +398,7 @@ int moba_forward(const moba_problem_t* p, const void* q, const void* k, const vo
   return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream));
 }
 
-int moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+int impl_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
                      int32_t* block_idx, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Plan P;
@@ -416,7 +412,7 @@ int moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, cons
   return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream), lse);
 }
 
-static int plan_backward_problem(const moba_problem_t* p, Plan* P, BwdPlan* B) {
+int plan_backward_problem(const moba_problem_t* p, Plan* P, BwdPlan* B) {
   const int st = plan_problem(p, P, true);
   if (st != MOBA_OK) return st;
   if (!P->bf16_in) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports bf16 inputs only (dtype MOBA_BF16)");
@@ -425,7 +421,7 @@ static int plan_backward_problem(const moba_problem_t* p, Plan* P, BwdPlan* B) {
   return MOBA_OK;
 }
 
-int moba_backward_workspace_size(const moba_problem_t* p, size_t* bytes) {
+int impl_backward_workspace_size(const moba_problem_t* p, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
   Plan P;
@@ -436,7 +432,7 @@ int moba_backward_workspace_size(const moba_problem_t* p, size_t* bytes) {
   return MOBA_OK;
 }
 
-int moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+int impl_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk, void* dv,
                   void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
@@ -473,6 +469,8 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
   ba.causal = P.causal;
   ba.k_eff = (int)P.k_eff;
   ba.group = (int)P.G;
+  ba.block_idx = block_idx;
+  ba.top_k = (int)P.top_k;
   ba.delta = at<float>(workspace, B.delta);
   ba.lse2 = at<float>(workspace, B.lse2);
   ba.dq_part = at<float>(workspace, B.dq_part);
@@ -488,6 +486,7 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
     ga.seq_len = P.S;
     ga.block_size = P.Bs;
     ga.n_blocks = P.nb;
+    ga.causal = P.causal;
     ga.top_k = (int)P.top_k;
     ga.k_eff = (int)P.k_eff;
     ga.block_idx = const_cast<int32_t*>(block_idx);
@@ -522,7 +521,7 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
   return MOBA_OK;
 }
 
-int moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, size_t* bytes) {
+int impl_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
   std::vector<Plan> plans;
@@ -534,7 +533,7 @@ int moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlen
   return MOBA_OK;
 }
 
-int moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, const void* q,
+int impl_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, const void* q,
                         const void* k, const void* v, void* o, int32_t* block_idx, void* workspace,
                         size_t workspace_bytes, void* stream) {
   g_err.clear();
@@ -567,13 +566,14 @@ int moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int6
   return MOBA_OK;
 }
 
-int moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
-                       void* stream) {
+int impl_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                       void* stream, bool force_causal) {
   g_err.clear();
   if (!p) return fail(MOBA_ERR_NULL, "problem pointer is NULL");
   // Dense attention ignores the block structure: validate it as a problem
   // whose only block is the whole sequence.
   moba_problem_t d = *p;
+  if (force_causal) d.causal = 1;
   if (d.seq_len >= 1) d.block_size = d.seq_len % 64 == 0 ? 64 : d.seq_len;
   if (d.top_k < 1) return fail(MOBA_ERR_ARG, "top_k must be >= 1, got " + std::to_string(p->top_k));
   d.top_k = 1;
@@ -593,7 +593,7 @@ int moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, co
   return MOBA_OK;
 }
 
-int moba_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace, size_t workspace_bytes,
+int impl_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace, size_t workspace_bytes,
               void* stream) {
   g_err.clear();
   Plan P;
@@ -606,7 +606,7 @@ int moba_pool(const moba_problem_t* p, const void* k, double* kbar, void* worksp
   return run_select(P, nullptr, k, nullptr, workspace, static_cast<hipStream_t>(stream), kbar);
 }
 
-int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* block_idx, void* workspace,
+int impl_select(const moba_problem_t* p, const void* q, const void* k, int32_t* block_idx, void* workspace,
                 size_t workspace_bytes, void* stream) {
   g_err.clear();
   Plan P;
@@ -620,7 +620,7 @@ int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* 
   return run_select(P, q, k, block_idx, workspace, static_cast<hipStream_t>(stream), nullptr);
 }
 
-int moba_timing_enable(int enable) {
+int impl_timing_enable(int enable) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_tmu);
   if (enable && g_events.empty()) {
@@ -637,7 +637,7 @@ int moba_timing_enable(int enable) {
   return MOBA_OK;
 }
 
-int moba_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries) {
+int impl_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries) {
   g_err.clear();
   if (!n_entries) return fail(MOBA_ERR_NULL, "n_entries is NULL");
   std::lock_guard<std::mutex> lk(g_tmu);
@@ -661,6 +661,79 @@ int moba_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries) {
   *n_entries = (int)agg.size();
   for (int i = 0; i < (int)agg.size() && i < max_entries; ++i) out[i] = agg[i];
   return MOBA_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ the C ABI
+extern "C" {
+
+static inline moba_status_t st_(int s) { return static_cast<moba_status_t>(s); }
+
+int moba_abi_version(void) { return MOBA_ABI_VERSION; }
+
+const char* moba_status_str(moba_status_t status) { return status_text(static_cast<int>(status)); }
+
+const char* moba_last_error(void) { return g_err.c_str(); }
+
+moba_status_t moba_workspace_size(const moba_problem_t* p, size_t* bytes) { return st_(impl_workspace_size(p, bytes)); }
+
+moba_status_t moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                           int32_t* block_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  return st_(impl_forward(p, q, k, v, o, block_idx, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                               int32_t* block_idx, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return st_(impl_forward_lse(p, q, k, v, o, block_idx, lse, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_backward_workspace_size(const moba_problem_t* p, size_t* bytes) {
+  return st_(impl_backward_workspace_size(p, bytes));
+}
+
+moba_status_t moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk,
+                            void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return st_(impl_backward(p, q, k, v, o, dout, block_idx, lse, dq, dk, dv, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                                         size_t* bytes) {
+  return st_(impl_workspace_size_varlen(p, cu_seqlens, n_seqs, bytes));
+}
+
+moba_status_t moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                                  const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return st_(impl_forward_varlen(p, cu_seqlens, n_seqs, q, k, v, o, block_idx, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_dense_causal_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                                        void* o, void* stream) {
+  return st_(impl_dense_forward(p, q, k, v, o, stream, true));
+}
+
+moba_status_t moba_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                                 void* stream) {
+  return st_(impl_dense_forward(p, q, k, v, o, stream, false));
+}
+
+moba_status_t moba_debug_pool(const moba_problem_t* p, const void* k, double* kbar, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return st_(impl_pool(p, k, kbar, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_debug_gate_topk(const moba_problem_t* p, const void* q, const void* k, int32_t* block_idx,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return st_(impl_select(p, q, k, block_idx, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_timing_enable(int enable) { return st_(impl_timing_enable(enable)); }
+
+moba_status_t moba_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries) {
+  return st_(impl_timing_read(out, max_entries, n_entries));
 }
 
 }  // extern "C"

@@ -292,9 +292,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // dq = own-block part + the past slots' partials (written by dq_past, an
   // earlier launch) in slot order, rounded once to bf16.
   const float scale = 1.f / __builtin_sqrtf((float)D);
-  const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
+  // The row's past blocks, counted as the list-building kernels count them
+  // (the same validity test and cap), so exactly the partials dq_past wrote.
   const int slots = a.k_eff - 1;
-  const int n = min(slots, n_elig);
+  const int cap = past_cap(c, a.n_blocks, a.causal, a.k_eff);
+  int n = 0;
+  {
+    const int32_t* ir = a.block_idx + row * a.top_k;
+    for (int i = 0; i < a.top_k && n < cap; ++i) {
+      const int j = ir[i];
+      if (j < 0) break;
+      n += routed_past_block(j, c, a.n_blocks, a.causal) ? 1 : 0;
+    }
+  }
   bf16* dst = reinterpret_cast<bf16*>(a.dq) + row * D;
   const float* p0 = a.dq_part + (row * slots) * D;
   if (n <= 2) {

@@ -50,6 +50,22 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short u) {
 // Round to nearest even fp32 -> bf16 (inputs here are finite).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 
+// Whether entry j of a block_idx row of a query in block c names a past
+// block that query attends: a valid index other than its own block, and
+// not a later block under causal routing. Every kernel that turns a
+// block_idx row into list entries (ranks, counts, scatter, the backward's
+// partial count) skips entries failing this test in the same way and takes
+// at most past_cap of them (the first ones; a -1 ends the row), so no row,
+// even one edited by a caller, yields more list entries than the exact
+// pair count the workspace is sized for.
+__device__ __forceinline__ bool routed_past_block(int j, int c, int64_t n_blocks, bool causal) {
+  return j >= 0 && j < n_blocks && j != c && (!causal || j < c);
+}
+// Past blocks a query in block c keeps: min(k_eff - 1, eligible blocks).
+__device__ __forceinline__ int past_cap(int c, int64_t n_blocks, bool causal, int k_eff) {
+  return min(k_eff - 1, causal ? c : (int)n_blocks - 1);
+}
+
 template <typename T>
 struct io;
 template <>

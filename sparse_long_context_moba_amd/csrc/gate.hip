@@ -787,11 +787,12 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
     const int c = (int)(t / a.block_size);
     const int32_t* row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
     int32_t* rk = a.rank + (bh * a.seq_len + t) * (int64_t)slots;
+    const int cap = past_cap(c, NB, a.causal, a.k_eff);
     int s = 0;
-    for (int i = 0; i < a.top_k; ++i) {
+    for (int i = 0; i < a.top_k && s < cap; ++i) {
       const int j = row[i];
       if (j < 0) break;
-      if (j == c) continue;
+      if (!routed_past_block(j, c, NB, a.causal)) continue;
       rk[s++] = lds_bins ? atomicAdd(bins + j, 1) : atomicAdd(cnt + j, 1);
     }
   }
@@ -808,11 +809,12 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
     const int c = (int)(t / a.block_size);
     const int32_t* row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
     int32_t* rk = a.rank + (bh * a.seq_len + t) * (int64_t)slots;
+    const int cap = past_cap(c, NB, a.causal, a.k_eff);
     int s = 0;
-    for (int i = 0; i < a.top_k; ++i) {
+    for (int i = 0; i < a.top_k && s < cap; ++i) {
       const int j = row[i];
       if (j < 0) break;
-      if (j == c) continue;
+      if (!routed_past_block(j, c, NB, a.causal)) continue;
       rk[s++] += bins[j];
     }
   }
@@ -877,10 +879,14 @@ __global__ __launch_bounds__(256) void chunk_count_kernel(GateArgs a, int32_t* c
     if (t >= a.seq_len) break;
     const int c = (int)(t / a.block_size);
     const int32_t* row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
-    for (int i = 0; i < a.top_k; ++i) {
+    const int cap = past_cap(c, NB, a.causal, a.k_eff);
+    int s = 0;
+    for (int i = 0; i < a.top_k && s < cap; ++i) {
       const int j = row[i];
       if (j < 0) break;
-      if (j != c) atomicAdd(bins + j, 1);
+      if (!routed_past_block(j, c, NB, a.causal)) continue;
+      atomicAdd(bins + j, 1);
+      ++s;
     }
   }
   __syncthreads();
@@ -934,7 +940,7 @@ __global__ __launch_bounds__(64) void rank_ordered_kernel(GateArgs a, const int3
     for (int i = 0; i < a.top_k; ++i) {
       int j = done ? -1 : row[i];
       if (j < 0) done = true;
-      const bool pick = !done && j != c;
+      const bool pick = !done && s < past_cap(c, NB, a.causal, a.k_eff) && routed_past_block(j, c, NB, a.causal);
       uint64_t todo = __builtin_amdgcn_ballot_w64(pick);
       while (todo) {
         const int leader = __builtin_ctzll(todo);

@@ -116,6 +116,8 @@ struct BwdArgs {
   bool causal;
   int k_eff;
   int group;                   // query heads per key/value head
+  const int32_t* block_idx;    // [bh, S, top_k] the forward's block choice
+  int top_k;                   // columns of block_idx
   const int32_t* qlist;        // per-block query lists (as for the forward's gather)
   const int32_t* offset;       // [bh * nb + 1] list offsets
   const int32_t* tile_map;     // gather tiles

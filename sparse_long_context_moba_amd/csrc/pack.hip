@@ -97,11 +97,12 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
   const int slots = a.k_eff - 1;
   const int32_t* row = a.block_idx + q * a.top_k;
   const int32_t* rk = a.rank + q * slots;
+  const int cap = past_cap(c, a.n_blocks, a.causal, a.k_eff);
   int s = 0;
-  for (int i = 0; i < a.top_k; ++i) {
+  for (int i = 0; i < a.top_k && s < cap; ++i) {
     const int j = row[i];
     if (j < 0) break;
-    if (j == c) continue;
+    if (!routed_past_block(j, c, a.n_blocks, a.causal)) continue;
     const int64_t blk = bh * a.n_blocks + j;
     a.qlist[a.offset[blk] + rk[s]] = (int32_t)(t * slots + s);
     ++s;

@@ -28,9 +28,45 @@ def test_exports_every_declared_function():
     assert sorted(_lib.EXPORTED) == names
 
 
+# The boundary's entry points: the forward with its workspace query, the
+# dense causal baseline, the two stage (debug) entry points and the status
+# text; each must be declared in include/moba.h and exported by the library.
+BOUNDARY = ["moba_abi_version", "moba_workspace_size", "moba_forward", "moba_dense_causal_forward",
+            "moba_status_str", "moba_debug_pool", "moba_debug_gate_topk"]
+
+
+def test_boundary_entry_points_are_declared_and_exported():
+    from sparse_long_context_moba_amd import _lib
+    names = _header_functions()
+    for n in BOUNDARY:
+        assert n in names, f"{n} not declared in include/moba.h"
+        fn = getattr(_lib.lib(), n)
+        assert fn is not None
+
+
+def test_boundary_entry_points_validate_through_ctypes():
+    """Each boundary entry point, called through ctypes with a bad argument,
+    returns its status code before any launch."""
+    from sparse_long_context_moba_amd import _lib
+    st, need = _lib.moba_workspace_size(_p())
+    assert st == 0
+    assert _lib.moba_dense_causal_forward(_p(), None, FAKE, FAKE, FAKE, None) == 1
+    assert _lib.moba_dense_causal_forward(_p(head_dim=96), FAKE, FAKE, FAKE, FAKE, None) == 5
+    assert "head_dim" in _lib.moba_last_error()
+    # p->causal does not matter to the causal baseline: still validated the same way
+    assert _lib.moba_dense_causal_forward(_p(causal=0, dtype=9), FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert _lib.moba_debug_pool(_p(), None, FAKE, FAKE, need, None) == 1
+    assert _lib.moba_debug_pool(_p(top_k=0), FAKE, FAKE, FAKE, need, None) == 3
+    assert _lib.moba_debug_pool(_p(), FAKE, FAKE, FAKE, need - 1, None) == 6
+    assert _lib.moba_debug_gate_topk(_p(), FAKE, None, FAKE, FAKE, need, None) == 1
+    assert _lib.moba_debug_gate_topk(_p(block_size=96), FAKE, FAKE, FAKE, FAKE, need, None) == 5
+    assert _lib.moba_debug_gate_topk(_p(), FAKE, FAKE, FAKE, None, need, None) == 6
+    assert _lib.moba_status_str(0) == "ok"
+
+
 def test_abi_version_and_status_strings():
     from sparse_long_context_moba_amd import _lib
-    assert _lib.moba_abi_version() == 4
+    assert _lib.moba_abi_version() == 5
     for code in range(8):
         assert _lib.moba_status_str(code)
     assert _lib.moba_status_str(99) == "unknown status"
@@ -91,8 +127,8 @@ def test_null_pointers_and_workspace():
     assert _lib.moba_forward(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, need, None) == 6
     assert _lib.moba_dense_forward(_p(seq_len=1000, block_size=1000), FAKE, FAKE, FAKE, FAKE, None) == 5
     assert _lib.moba_dense_forward(_p(), None, FAKE, FAKE, FAKE, None) == 1
-    assert _lib.moba_pool(_p(), FAKE, None, FAKE, need, None) == 1
-    assert _lib.moba_select(_p(), FAKE, FAKE, None, FAKE, need, None) == 1
+    assert _lib.moba_debug_pool(_p(), FAKE, None, FAKE, need, None) == 1
+    assert _lib.moba_debug_gate_topk(_p(), FAKE, FAKE, None, FAKE, need, None) == 1
 
 
 def test_topk_beyond_blocks_is_clamped_not_an_error():
@@ -206,3 +242,38 @@ def test_backward_and_lse_validation():
     assert "lse" in _lib.moba_last_error()
     assert _lib.moba_forward_lse(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwd - 1, None) == 6
     assert _lib.moba_forward_lse(_p(top_k=0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwd, None) == 3
+
+
+def test_python_buffer_checks_reject_wrong_buffers():
+    """forward() and backward() check caller-supplied buffers before any
+    call: a wrong shape, dtype, device or layout raises ValueError naming the
+    buffer (checked here with CPU tensors standing for the device)."""
+    import torch
+    import sparse_long_context_moba_amd as moba
+    q = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
+    cpu = torch.device("cpu")
+    ok = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
+    assert moba.check_buffer(ok, "out", q.shape, q.dtype, cpu) is ok
+    bad = [
+        (torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16), "shape"),
+        (torch.zeros(1, 2, 128, 64, dtype=torch.float32), "bfloat16"),
+        (torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16).transpose(2, 3), "contiguous"),
+        (torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16, device="meta"), "cpu"),
+        (None, "tensor"),
+    ]
+    for t, word in bad:
+        with pytest.raises(ValueError, match=word):
+            moba.check_buffer(t, "out", q.shape, q.dtype, cpu)
+    idx_shape = (1, 2, 128, 3)
+    with pytest.raises(ValueError, match="idx"):
+        moba.check_buffer(torch.zeros(idx_shape, dtype=torch.int64), "idx", idx_shape, torch.int32, cpu)
+    with pytest.raises(ValueError, match="idx"):
+        moba.check_buffer(torch.zeros((1, 2, 128, 2), dtype=torch.int32), "idx", idx_shape, torch.int32, cpu)
+    with pytest.raises(ValueError, match="lse"):
+        moba.check_buffer(torch.zeros((1, 2, 127), dtype=torch.float32), "lse", (1, 2, 128), torch.float32, cpu)
+    ws = torch.zeros(100, dtype=torch.float32)
+    assert moba.check_workspace(ws, 400, cpu) == 400
+    with pytest.raises(ValueError, match="needs 401"):
+        moba.check_workspace(ws, 401, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        moba.check_workspace(torch.zeros(200, dtype=torch.uint8)[::2], 10, cpu)

@@ -149,3 +149,75 @@ def test_backward_64k_two_heads_sampled():
     that length), so this covers the other chunk size."""
     import synth
     _check_sampled(synth.Workload("bwd_64k_2h", 1, 2, 65536, 128, 512, 3, True, "bf16", 21))
+
+
+def _edit_rows(idx, Bs):
+    """block_idx rows rewritten with entries the backward must skip (out of
+    range, negative after the valid ones, the own block repeated, future
+    blocks, a fourth past block beyond the cap) and the valid past blocks
+    reordered, so that the blocks the backward keeps are exactly the
+    original ones. idx: int [S, 4] of one head, causal, top_k 4."""
+    out = idx.copy()
+    S = idx.shape[0]
+    for t in range(S):
+        c = t // Bs
+        row = [int(j) for j in idx[t] if j >= 0]
+        past = [j for j in row if j != c]
+        if c == 0:
+            out[t] = [0, 7, 5, 99]
+        elif c == 1:
+            out[t] = [1, 0, 1, 4000]
+        elif c == 2:
+            out[t] = [2, past[1], past[0], -3]
+        elif t % 2 == 0 or c == 3:
+            out[t] = [c, past[2], past[0], past[1]]
+        else:
+            extra = next(j for j in range(c) if j not in past)
+            out[t] = [past[0], past[1], past[2], extra]
+    return out
+
+
+def _kept_past_blocks(row, c, n_blocks, k_eff, causal=True):
+    """The documented reading of a row: up to the first -1, skip entries that
+    name no past block the query may attend, keep the first
+    min(k_eff - 1, eligible) of the rest."""
+    cap = min(k_eff - 1, c if causal else n_blocks - 1)
+    kept = []
+    for j in row:
+        if j < 0 or len(kept) >= cap:
+            break
+        if j < n_blocks and j != c and (not causal or j < c):
+            kept.append(int(j))
+    return kept
+
+
+def test_backward_skips_entries_that_name_no_past_block():
+    """A block_idx edited by the caller: entries that name no past block the
+    query may attend are skipped and at most min(top_k, n_blocks) - 1 past
+    blocks per row are used, in the same way by every kernel that reads the
+    rows. With edits that keep the same past blocks, the gradients equal
+    the oracle's for the forward's own choice."""
+    import sparse_long_context_moba_amd as moba
+    B, H, S, D, Bs, top_k = 1, 2, 2048, 128, 256, 4
+    q, k, v, do = _inputs(77, B, H, H, S, D, Bs)
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o, idx, lse = moba.forward(qd, kd, vd, Bs, top_k, True, return_lse=True)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    edited = np.stack([_edit_rows(idx_h[0, h], Bs) for h in range(H)])[None].astype(np.int32)
+    nb = S // Bs
+    for h in range(H):
+        for t in range(S):
+            c = t // Bs
+            orig = sorted(j for j in idx_h[0, h, t] if 0 <= j != c)
+            assert sorted(_kept_past_blocks(edited[0, h, t], c, nb, top_k)) == orig, (h, t)
+    say(f"[gpu] backward with edited block_idx rows: S={S} Bs={Bs} top_k={top_k}")
+    dq, dk, dv = moba.backward(qd, kd, vd, o, dod, torch.from_numpy(edited).cuda(), lse, Bs, top_k, True)
+    torch.cuda.synchronize()
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    for h in range(H):
+        gq, gk, gv, _ = orc.backward_head(q[0, h], k[0, h], v[0, h], do[0, h], idx_h[0, h], Bs, True)
+        for name, got, ref in (("dq", dq[0, h], gq), ("dk", dk[0, h], gk), ("dv", dv[0, h], gv)):
+            e = np.abs(got - ref).max()
+            assert e <= REL * np.abs(ref).max(), f"h={h}: {name} error {e:.3e} (scale {np.abs(ref).max():.3e})"
+    say("[gpu] backward with edited rows: ok")

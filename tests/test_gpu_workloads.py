@@ -99,6 +99,57 @@ def _run(name, n_rows=4096):
     assert stats["rows"] == len(rows)
 
 
+def _oracle_dense_rows(args):
+    qb, kb, vb, rows, dtype, causal = args
+    q, k, v = (_as_f32(x, dtype) for x in (qb, kb, vb))
+    return orc.dense_attention(q, k, v, causal, rows=rows)
+
+
+def _run_dense(name, n_rows=4096):
+    """The dense kernel (the speedup's denominator) at a workload's full
+    size, in the launch bench.py times: sampled rows against the oracle's
+    plain softmax attention."""
+    import sparse_long_context_moba_amd as moba
+    w = synth.WORKLOADS[name]
+    t0 = time.time()
+    say(f"[gpu] dense {name}: generating and uploading inputs")
+    (qd, kd, vd), host = _upload(w)
+    say(f"[gpu] dense {name}: inputs ready in {time.time() - t0:.1f}s; running moba.dense")
+    o = moba.dense(qd, kd, vd, w.causal)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, n_rows)
+    sel = torch.from_numpy(rows).cuda()
+    o_rows = o[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
+    del o, qd, kd, vd
+    torch.cuda.empty_cache()
+    say(f"[gpu] dense {name}: done; oracle on {len(rows)} rows")
+    groups = {}
+    for i, (b, h, t) in enumerate(rows):
+        groups.setdefault((int(b), int(h)), []).append(i)
+    keys = sorted(groups)
+    G = w.group
+    jobs = []
+    for b, h in keys:
+        qg, kh, vh = host[(b, h // G)]
+        jobs.append((qg[h % G], kh, vh, rows[groups[(b, h)], 2], w.dtype, w.causal))
+    import multiprocessing as mp
+    worst = 0.0
+    tol = 2e-2 if w.dtype == "bf16" else 1e-4
+    with mp.get_context("fork").Pool(min(16, len(jobs))) as pool:
+        for bh, ref in zip(keys, pool.imap(_oracle_dense_rows, jobs)):
+            ii = groups[bh]
+            err = np.abs(o_rows[ii].astype(np.float64) - ref).max(axis=1)
+            worst = max(worst, float(err.max()))
+            bad = np.nonzero(err > tol)[0]
+            assert len(bad) == 0, (f"dense {name} b={bh[0]} h={bh[1]} t={rows[ii][bad[0], 2]}: "
+                                   f"max|o - oracle| = {err[bad[0]]:.3e} > {tol}")
+    say(f"[gpu] dense {name}: ok, {len(rows)} rows, max_err={worst:.3e} in {time.time() - t0:.1f}s")
+
+
+def test_dense_headline_32k_sampled():
+    _run_dense("headline_32k")
+
+
 def test_tiny_all_rows():
     _run("tiny", n_rows=4096)
 

@@ -53,6 +53,9 @@ def _pins():
             yield f"topk_ge_nb[{causal},{top_k}]", (
                 lambda c=causal, k=top_k: pins.test_topk_at_least_blocks_is_full_attention(c, k))
     yield "topk1_local", pins.test_topk1_is_block_local_causal
+    for causal in (True, False):
+        yield f"dense_sdpa[{causal}]", lambda c=causal: pins.test_dense_attention_matches_library_sdpa(c)
+    yield "dense_is_moba_all_blocks", pins.test_dense_attention_is_moba_keeping_every_block
     yield "single_block_dense", pins.test_single_block_is_dense_causal
     yield "block_of_one_token", pins.test_block_of_one_token_routes_to_best_past_tokens
     yield "constant_values", pins.test_constant_values_give_constant_output_and_convex_hull
@@ -88,6 +91,7 @@ _orig_keys = moba.attended_keys
 _orig_attend = moba.attend
 _orig_grad = moba.attend_grad
 _orig_lse = moba.attend_lse
+_orig_dense = moba.dense_attention
 
 
 def pool_wrong_denominator(k, block_size, pooling="mean"):
@@ -238,6 +242,26 @@ def attend_unnormalised(q_t, k, v, keys):
     return np.exp(logits - logits.max()) @ vv
 
 
+def dense_drops_diagonal(q, k, v, causal=True, rows=None):
+    # each query attends only the keys before it, not itself
+    S, D = q.shape
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), D))
+    for r, t in enumerate(rows):
+        out[r] = moba.attend(q[t], k, v, np.arange(int(t) if causal else S, dtype=np.int64))
+    return out
+
+
+def dense_ignores_causal(q, k, v, causal=True, rows=None):
+    return _orig_dense(q, k, v, False, rows)
+
+
+def dense_ignores_rows(q, k, v, causal=True, rows=None):
+    # the requested rows are evaluated as if they were the first ones
+    n = q.shape[0] if rows is None else len(rows)
+    return _orig_dense(q, k, v, causal)[:n]
+
+
 def _grad_parts(q_t, k, v, keys, do_t):
     q_t = np.asarray(q_t, dtype=np.float64)
     do_t = np.asarray(do_t, dtype=np.float64)
@@ -280,6 +304,9 @@ def lse_unscaled(q_t, k, keys):
 
 
 MUTATIONS = [
+    ("dense_attention", dense_drops_diagonal),
+    ("dense_attention", dense_ignores_causal),
+    ("dense_attention", dense_ignores_rows),
     ("attend_grad", grad_drop_delta),
     ("attend_grad", grad_dq_unscaled),
     ("attend_grad", grad_dv_unnormalised),

@@ -317,6 +317,31 @@ def test_single_block_is_dense_causal():
     np.testing.assert_allclose(res["o"], _sdpa(q, k, v, causal=True), atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_attention_matches_library_sdpa(causal):
+    """The dense baseline the speedup is measured against («MoBA 复现代码跑不通…»
+    §1.2: short inputs switch to plain full attention) equals torch's
+    scaled_dot_product_attention in float64, causal or not, on every row and
+    on a scattered subset of rows (first, last and interior ones)."""
+    S, D = 72, 16
+    q, k, v = _rand_head(29, S, D, 8)
+    ref = _sdpa(q, k, v, causal=causal)
+    np.testing.assert_allclose(moba.dense_attention(q, k, v, causal), ref, atol=1e-12)
+    rows = np.array([S - 1, 0, 37, 1, 36])
+    np.testing.assert_allclose(moba.dense_attention(q, k, v, causal, rows=rows), ref[rows], atol=1e-12)
+
+
+def test_dense_attention_is_moba_keeping_every_block():
+    """With top_k covering every block MoBA attends all keys up to the query
+    (the pages' seamless switch to full attention), so it equals the dense
+    baseline row for row; both are also compared with the library above."""
+    S, D, Bs = 64, 8, 16
+    q, k, v = _rand_head(31, S, D, Bs)
+    for causal in (True, False):
+        res = moba.forward_head(q, k, v, Bs, S // Bs, causal)
+        np.testing.assert_allclose(moba.dense_attention(q, k, v, causal), res["o"], atol=1e-12)
+
+
 def test_block_of_one_token_routes_to_best_past_tokens():
     """block_size 1: each query keeps itself plus the top_k - 1 past tokens by
     q.k (computed with torch.topk on continuous data, no ties)."""
