@@ -144,6 +144,7 @@ def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None,
     hkv = _tensors(q, k, v)
     p = problem(q, block_size, top_k, causal, pooling, hkv, gate_shared)
     B, H, S, D = q.shape
+    need = workspace_bytes(p)  # validates the problem through the library first
     o = torch.empty_like(q) if out is None else check_buffer(out, "out", q.shape, q.dtype, q.device)
     idx_shape = (B, H, S, int(top_k))
     bi = torch.empty(idx_shape, dtype=torch.int32, device=q.device) if idx is None else \
@@ -151,7 +152,7 @@ def forward(q, k, v, block_size: int, top_k: int, causal: bool = True, out=None,
     if workspace is None:
         ws, n = _workspace(p, q.device)
     else:
-        ws, n = workspace, check_workspace(workspace, workspace_bytes(p), q.device)
+        ws, n = workspace, check_workspace(workspace, need, q.device)
     with torch.cuda.device(q.device):
         if return_lse:
             lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
@@ -169,14 +170,14 @@ def backward(q, k, v, o, dout, idx, lse, block_size: int, top_k: int, causal: bo
     forward(..., return_lse=True)."""
     hkv = _tensors(q, k, v)
     _tensors(q, o, dout)
+    p = problem(q, block_size, top_k, causal, "mean", hkv)
+    st, n = moba_backward_workspace_size(p)  # validates the problem through the library first
+    _check(st, "moba_backward_workspace_size")
     check_buffer(o, "o", q.shape, q.dtype, q.device)
     check_buffer(dout, "dout", q.shape, q.dtype, q.device)
     B, H, S, D = q.shape
     check_buffer(idx, "idx", (B, H, S, int(top_k)), torch.int32, q.device)
     check_buffer(lse, "lse", (B, H, S), torch.float32, q.device)
-    p = problem(q, block_size, top_k, causal, "mean", hkv)
-    st, n = moba_backward_workspace_size(p)
-    _check(st, "moba_backward_workspace_size")
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     with torch.cuda.device(q.device):
