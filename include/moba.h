@@ -19,7 +19,9 @@
  *     row-major, in device memory, of the problem's dtype (fp32 or bf16).
  *   - block_idx is int32 [batch, heads, seq_len, top_k] in device memory.
  *   - The caller owns every buffer, including the workspace; the library
- *     never allocates device memory and keeps no per-call state.
+ *     never allocates device memory and keeps no per-call state (one
+ *     exception: moba_forward_noalloc works in a scratch array compiled
+ *     into the library, see there).
  *   - stream is a hipStream_t (NULL = the null stream). Work is queued on
  *     it and the call returns without synchronising; a device fault shows
  *     at the caller's next synchronisation.
@@ -42,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 5
+#define MOBA_ABI_VERSION 6
 
 typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype_t;
 
@@ -145,6 +147,30 @@ moba_status_t moba_workspace_size(const moba_problem_t* p, size_t* bytes);
 moba_status_t moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,
                  void* o, int32_t* block_idx, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/* Bytes of the device scratch array moba_forward_noalloc works in (one
+ * copy per GPU the library runs on, held until the process ends). */
+#define MOBA_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* moba_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace taken from a scratch
+ * array compiled into the library instead of a caller buffer. The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the array's device address on the calling thread's current
+ * device (which must be the stream's device) is looked up on that device's
+ * first call and kept.
+ *   q, k, v, o, block_idx, stream — as for moba_forward.
+ * Limit: problems whose moba_workspace_size exceeds
+ * MOBA_NOALLOC_SCRATCH_BYTES fail with MOBA_ERR_WORKSPACE before anything
+ * is launched (256 MiB holds, for example, 32 heads x 8192 tokens or
+ * 8 heads x 32768 tokens at head_dim 128, block 512, top_k 3, bf16).
+ * Every call on one GPU shares that GPU's array and nothing in it has to
+ * start cleared (the forward writes each byte it reads); calls that overlap
+ * on one GPU (different streams or threads without ordering between them)
+ * race on it and must be serialised by the caller. */
+moba_status_t moba_forward_noalloc(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                                   void* o, int32_t* block_idx, void* stream);
 
 /* moba_forward that also writes, per query, the natural-log log-sum-exp of
  * its scaled logits q.k_u / sqrt(head_dim) over every key it attended (the

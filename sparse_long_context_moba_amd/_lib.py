@@ -19,7 +19,7 @@ STATUS_NAMES = {0: "MOBA_OK", 1: "MOBA_ERR_NULL", 2: "MOBA_ERR_SHAPE", 3: "MOBA_
                 4: "MOBA_ERR_DTYPE", 5: "MOBA_ERR_UNSUPPORTED", 6: "MOBA_ERR_WORKSPACE",
                 7: "MOBA_ERR_DEVICE"}
 EXPORTED = ["moba_abi_version", "moba_status_str", "moba_last_error", "moba_workspace_size",
-            "moba_forward", "moba_forward_lse", "moba_dense_causal_forward", "moba_dense_forward",
+            "moba_forward", "moba_forward_noalloc", "moba_forward_lse", "moba_dense_causal_forward", "moba_dense_forward",
             "moba_debug_pool", "moba_debug_gate_topk",
             "moba_workspace_size_varlen", "moba_forward_varlen",
             "moba_backward_workspace_size", "moba_backward",
@@ -51,6 +51,7 @@ def _load():
         "moba_last_error": ([], ctypes.c_char_p),
         "moba_workspace_size": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moba_forward": ([P, vp, vp, vp, vp, i32p, vp, sz, vp], ctypes.c_int),
+        "moba_forward_noalloc": ([P, vp, vp, vp, vp, i32p, vp], ctypes.c_int),
         "moba_forward_lse": ([P, vp, vp, vp, vp, i32p, vp, vp, sz, vp], ctypes.c_int),
         "moba_dense_causal_forward": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
         "moba_dense_forward": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -106,6 +107,14 @@ def moba_workspace_size(problem: moba_problem_t):
 def moba_forward(problem, q, k, v, o, block_idx, workspace, workspace_bytes, stream) -> int:
     return lib().moba_forward(ctypes.byref(problem) if problem is not None else None,
                             q, k, v, o, block_idx, workspace, workspace_bytes, stream)
+
+
+def moba_forward_noalloc(problem, q, k, v, o, block_idx, stream) -> int:
+    return lib().moba_forward_noalloc(ctypes.byref(problem) if problem is not None else None,
+                                      q, k, v, o, block_idx, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # MOBA_NOALLOC_SCRATCH_BYTES in include/moba.h
 
 
 def moba_forward_lse(problem, q, k, v, o, block_idx, lse, workspace, workspace_bytes, stream) -> int:

@@ -665,6 +665,58 @@ int impl_timing_read(moba_kernel_time_t* out, int max_entries, int* n_entries) {
 
 }  // namespace
 
+// ------------------------------------------------ allocation-free forward
+// The workspace of moba_forward_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends. In host code `scratch` only
+// names the symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept, and only that
+// address is passed to kernels.
+static __device__ __align__(256) char scratch[MOBA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device ordinal; nullptr until looked up
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  MOBA_TRY(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev >= (int)g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[(size_t)dev]) {
+    void* ptr = nullptr;
+    MOBA_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign != 0)
+      return fail(MOBA_ERR_DEVICE, "the scratch array's device address is NULL or not 256-byte aligned");
+    g_scratch_ptr[(size_t)dev] = ptr;
+  }
+  *out = g_scratch_ptr[(size_t)dev];
+  return MOBA_OK;
+}
+
+int impl_forward_noalloc(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                         int32_t* block_idx, void* stream) {
+  g_err.clear();
+  Plan P;
+  int st = plan_problem(p, &P, true);
+  if (st != MOBA_OK) return st;
+  st = check_tensors(q, k, v, o, block_idx);
+  if (st != MOBA_OK) return st;
+  if (P.total > (size_t)MOBA_NOALLOC_SCRATCH_BYTES)
+    return fail(MOBA_ERR_WORKSPACE, "problem needs " + std::to_string(P.total) +
+                                        " bytes of scratch, above the " +
+                                        std::to_string((size_t)MOBA_NOALLOC_SCRATCH_BYTES) +
+                                        " bytes moba_forward_noalloc holds per GPU; use moba_forward with a "
+                                        "caller-allocated workspace");
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != MOBA_OK) return st;
+  // Nothing in the scratch needs clearing: the forward never reads a byte
+  // of its workspace before writing it (the pool kernel zeroes the block
+  // counts the gate's ranking then fills).
+  return run_forward(P, q, k, v, o, block_idx, ws, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
 // ------------------------------------------------------------ the C ABI
 extern "C" {
 
@@ -681,6 +733,11 @@ moba_status_t moba_workspace_size(const moba_problem_t* p, size_t* bytes) { retu
 moba_status_t moba_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
                            int32_t* block_idx, void* workspace, size_t workspace_bytes, void* stream) {
   return st_(impl_forward(p, q, k, v, o, block_idx, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_forward_noalloc(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                                   int32_t* block_idx, void* stream) {
+  return st_(impl_forward_noalloc(p, q, k, v, o, block_idx, stream));
 }
 
 moba_status_t moba_forward_lse(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,

@@ -66,7 +66,7 @@ def test_boundary_entry_points_validate_through_ctypes():
 
 def test_abi_version_and_status_strings():
     from sparse_long_context_moba_amd import _lib
-    assert _lib.moba_abi_version() == 5
+    assert _lib.moba_abi_version() == 6
     for code in range(8):
         assert _lib.moba_status_str(code)
     assert _lib.moba_status_str(99) == "unknown status"
