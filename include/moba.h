@@ -96,10 +96,14 @@ typedef enum {
  *                shared across heads and leaves it open; the sum is the
  *                plain shared score.) block_idx then repeats the group's
  *                choice in each of its query heads' rows.
+ * Any seq_len >= 1 is accepted: the last block, and the last tile of
+ * queries and keys, may be partial (padding rows are masked, and loads
+ * never leave the sequence).
  * Kernel limits of this build (MOBA_ERR_UNSUPPORTED otherwise):
- *   head_dim in {64, 128}; block_size and seq_len multiples of 64;
+ *   head_dim in {64, 128}; block_size a multiple of 64;
  *   min(top_k, n_blocks) - 1 <= 16 unless top_k >= n_blocks;
- *   seq_len < 2^27; batch * heads * n_blocks < 2^31. */
+ *   seq_len < 2^27; heads * blocks over the batch < 2^31;
+ *   heads * tokens over the batch * (min(top_k, n_blocks) - 1) < 2^31. */
 typedef struct {
   int64_t batch;
   int64_t heads;
@@ -181,7 +185,8 @@ moba_status_t moba_forward_lse(const moba_problem_t* p, const void* q, const voi
                      void* o, int32_t* block_idx, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
-/* MoBA backward (bf16 inputs only; MOBA_ERR_UNSUPPORTED otherwise): the
+/* MoBA backward (bf16 inputs and seq_len a multiple of 64 only;
+ * MOBA_ERR_UNSUPPORTED otherwise): the
  * gradients of o with respect to q, k and v for the upstream gradient dout,
  * with the forward's block choice held fixed. The routing is a top-k over
  * block scores, constant between ties, and the gate's scores do not weight
@@ -214,11 +219,14 @@ moba_status_t moba_backward(const moba_problem_t* p, const void* q, const void* 
 /* Varlen batch: n_seqs independent sequences of different lengths in one
  * call, each routed and attended on its own, blocks starting at its first
  * token (the per-sequence cu_seqlens packing the pages describe for
- * flash-attn, [R] §3.3).
+ * flash-attn, [R] §3.3). The batch runs as one launch chain, the same
+ * kernels and launch count as a single sequence: every kernel finds its
+ * sequence in a small table of per-sequence prefix sums (tokens, blocks,
+ * tiles) that the call copies into the workspace.
  *   cu_seqlens — HOST int64 [n_seqs + 1]: cu_seqlens[0] = 0 and sequence i
  *                holds tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1; every
- *                length must be >= 1 and meet the kernel limits above (a
- *                multiple of 64; a short last block is allowed).
+ *                length must be >= 1 (any length; a short last block and
+ *                a partial last tile are allowed) and below 2^27.
  *   p          — heads, kv_heads, head_dim, block_size, top_k, causal,
  *                dtype, pooling and gate_shared for every sequence; p->batch must equal n_seqs and
  *                p->seq_len the total cu_seqlens[n_seqs] (both checked).
@@ -229,10 +237,11 @@ moba_status_t moba_backward(const moba_problem_t* p, const void* q, const void* 
  *                head_dim] from element cu_seqlens[i] * kv_heads * head_dim.
  *   block_idx  — likewise, sequence i as [heads, len_i, top_k] from element
  *                cu_seqlens[i] * heads * top_k.
- *   workspace  — at least moba_workspace_size_varlen bytes; shared by the
- *                sequences, which run one after another on the stream.
+ *   workspace  — at least moba_workspace_size_varlen bytes (the lists and
+ *                partials of all sequences at once, plus the table).
  * Every sequence is validated before anything is launched; an error names
- * the sequence. */
+ * the sequence. The table goes to the device with hipMemcpyAsync from host
+ * memory (ordered on the stream). */
 moba_status_t moba_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
                                size_t* bytes);
 moba_status_t moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
@@ -245,9 +254,9 @@ moba_status_t moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seq
  * speedup is measured against it ([P] §1 quotes the speedup over full
  * attention at 1M and 10M tokens).
  *   q, k, v — as for moba_forward (kv_heads honoured); o — output like q.
- * p->causal is ignored (always causal); block_size, top_k and pooling are
- * validated for sign only. Limits: head_dim in {64, 128}, seq_len a
- * multiple of 64. Needs no workspace; errors as for moba_forward. */
+ * p->causal is ignored (always causal); block_size and top_k are
+ * validated for sign only. Limits: head_dim in {64, 128}; any seq_len
+ * below 2^27. Needs no workspace; errors as for moba_forward. */
 moba_status_t moba_dense_causal_forward(const moba_problem_t* p, const void* q, const void* k,
                                         const void* v, void* o, void* stream);
 

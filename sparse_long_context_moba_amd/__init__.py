@@ -189,7 +189,8 @@ def backward(q, k, v, o, dout, idx, lse, block_size: int, top_k: int, causal: bo
 
 def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int, causal: bool = True,
                    pooling: str = "mean", kv_heads: int = 0, gate_shared: bool = False):
-    """MoBA over a varlen batch: sequences of different lengths back to back.
+    """MoBA over a varlen batch: sequences of different lengths (any length
+    >= 1) back to back, run as one launch chain.
 
     q: [sum_i heads * len_i, head_dim], sequence i's [heads, len_i, head_dim]
     rows from row cu_seqlens[i] * heads (see pack_varlen); k, v likewise

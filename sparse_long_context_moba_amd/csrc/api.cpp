@@ -60,21 +60,29 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+// One launch chain: a batch of n_seq sequences, all of length S (uniform)
+// or of the lengths in `lens` (a varlen batch), each with heads query heads
+// and Hkv key/value heads.
 struct Plan {
-  int64_t B, H, S, D, Bs, top_k, bh, nb, k_eff, slots;
+  int64_t B, H, S, D, Bs, top_k, bh, nb, k_eff, slots;  // S, nb, bh: the uniform batch's
   int64_t Hkv, G, bhkv;  // key/value heads, query heads per key/value head, B * Hkv
   bool causal, bf16_in, shared;
   int pooling;         // moba_pooling_t
+  // the sequences
+  bool uniform;
+  int64_t n_seq, T, nb_total, max_nb, w64, w128, w1024;  // totals over the sequences
+  std::vector<int64_t> tab;  // varlen: the sequence table (rows of kSeqCols prefix sums)
   int64_t pairs;       // (query, kept past block) pairs over all heads
   int64_t max_tiles;   // upper bound on gather tiles
   // workspace offsets (bytes)
   size_t kbar64, kbar32, kbar_hi, kbar_lo, norm, count, rank, offset, tile_start, qlist,
-      tile_map, part_o, part_lse, total;
+      tile_map, part_o, part_lse, seq_tab, total;
 };
 
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
+// Fields every problem shares; seq_len is checked by the caller.
+int plan_common(const moba_problem_t* p, Plan* pl) {
   if (!p) return fail(MOBA_ERR_NULL, "problem pointer is NULL");
   const char* names[] = {"batch", "heads", "seq_len", "head_dim", "block_size"};
   const int64_t vals[] = {p->batch, p->heads, p->seq_len, p->head_dim, p->block_size};
@@ -96,46 +104,100 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     return fail(MOBA_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " + std::to_string(p->head_dim));
   if (p->block_size % 64 != 0)
     return fail(MOBA_ERR_UNSUPPORTED, "block_size must be a multiple of 64, got " + std::to_string(p->block_size));
-  if (p->seq_len % 64 != 0)
-    return fail(MOBA_ERR_UNSUPPORTED, "seq_len must be a multiple of 64, got " + std::to_string(p->seq_len));
-  if (p->seq_len >= (int64_t(1) << 27))
-    return fail(MOBA_ERR_UNSUPPORTED, "seq_len must be below 2^27, got " + std::to_string(p->seq_len));
   Plan& P = *pl;
   P.B = p->batch;
   P.H = p->heads;
-  P.S = p->seq_len;
   P.D = p->head_dim;
   P.Bs = p->block_size;
   P.top_k = p->top_k;
-  P.bh = P.B * P.H;
   P.Hkv = p->kv_heads > 0 ? p->kv_heads : P.H;
   P.G = P.H / P.Hkv;
   P.bhkv = P.B * P.Hkv;
+  P.bh = P.B * P.H;
   P.shared = p->gate_shared != 0;
-  P.nb = (P.S + P.Bs - 1) / P.Bs;  // a short last block holds the remainder
-  P.k_eff = std::min(P.top_k, P.nb);
-  P.slots = P.k_eff - 1;
   P.causal = p->causal != 0;
   P.bf16_in = p->dtype == MOBA_BF16;
   P.pooling = p->pooling;
-  if (P.bh * P.nb >= (int64_t(1) << 31))
-    return fail(MOBA_ERR_UNSUPPORTED, "batch * heads * n_blocks must be below 2^31");
-  if (P.slots > kMaxSlotsHost && P.k_eff < P.nb)
-    return fail(MOBA_ERR_UNSUPPORTED, "top_k " + std::to_string(P.top_k) + " keeps more than " +
-                                          std::to_string(kMaxSlotsHost) + " past blocks per query; use top_k <= " +
-                                          std::to_string(kMaxSlotsHost + 1) + " or top_k >= n_blocks (" +
-                                          std::to_string(P.nb) + ")");
-  if (P.S * std::max<int64_t>(P.slots, 1) >= (int64_t(1) << 31))
-    return fail(MOBA_ERR_UNSUPPORTED, "seq_len * (min(top_k, n_blocks) - 1) must be below 2^31");
-  // Exact pair count: every query in block c keeps min(k_eff - 1, eligible) past blocks.
-  int64_t per_head = 0;
-  for (int64_t c = 0; c < P.nb; ++c) {
-    const int64_t elig = P.causal ? c : P.nb - 1;
-    per_head += std::min(P.Bs, P.S - c * P.Bs) * std::min(P.slots, elig);
+  return MOBA_OK;
+}
+
+// (query, kept past block) pairs of one head of a sequence of len tokens.
+int64_t head_pairs(const Plan& P, int64_t len) {
+  const int64_t nb = (len + P.Bs - 1) / P.Bs;
+  int64_t n = 0;
+  for (int64_t c = 0; c < nb; ++c) {
+    const int64_t elig = P.causal ? c : nb - 1;
+    n += std::min(P.Bs, len - c * P.Bs) * std::min(P.slots, elig);
   }
-  P.pairs = per_head * P.bh;
+  return n;
+}
+
+// The sequences: lens == nullptr for B sequences of S tokens (P.S set),
+// else n lengths (a varlen batch). Sets totals, limits and the workspace.
+int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const char* what) {
+  P.uniform = lens == nullptr;
+  P.n_seq = n;
+  auto len_of = [&](int64_t i) { return lens ? lens[i] : P.S; };
+  P.T = P.nb_total = P.max_nb = P.w64 = P.w128 = P.w1024 = 0;
+  if (!P.uniform) P.tab.assign((size_t)(n + 1) * kSeqCols, 0);
+  for (int64_t i = 0; i <= n; ++i) {
+    if (!P.uniform) {
+      int64_t* row = &P.tab[(size_t)i * kSeqCols];
+      row[kSeqTok] = P.T;
+      row[kSeqBlk] = P.nb_total;
+      row[kSeqW64] = P.w64;
+      row[kSeqW128] = P.w128;
+      row[kSeqW1024] = P.w1024;
+    }
+    if (i == n) break;
+    const int64_t L = len_of(i);
+    if (L >= (int64_t(1) << 27))
+      return fail(MOBA_ERR_UNSUPPORTED, std::string(what) + " must be below 2^27, got " + std::to_string(L));
+    const int64_t nbi = seq_units(kSeqBlk, L, P.Bs);
+    P.T += L;
+    P.nb_total += nbi;
+    P.max_nb = std::max(P.max_nb, nbi);
+    P.w64 += seq_units(kSeqW64, L, P.Bs);
+    P.w128 += seq_units(kSeqW128, L, P.Bs);
+    P.w1024 += seq_units(kSeqW1024, L, P.Bs);
+    if (P.uniform) break;  // every sequence alike: scale below
+  }
+  if (P.uniform) {
+    P.T *= n;
+    P.nb = P.nb_total;
+    P.nb_total *= n;
+    P.w64 *= n;
+    P.w128 *= n;
+    P.w1024 *= n;
+  }
+  // k_eff - 1 past-block slots per query row: a sequence with fewer blocks
+  // keeps min(top_k - 1, eligible) <= its own count of them.
+  P.k_eff = std::min(P.top_k, P.max_nb);
+  P.slots = P.k_eff - 1;
+  if (P.H * P.nb_total >= (int64_t(1) << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "heads * blocks (over all sequences) must be below 2^31");
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t nbi = seq_units(kSeqBlk, len_of(i), P.Bs);
+    const int64_t si = std::min(P.top_k, nbi) - 1;
+    if (si > kMaxSlotsHost && P.top_k < nbi)
+      return fail(MOBA_ERR_UNSUPPORTED, "top_k " + std::to_string(P.top_k) + " keeps more than " +
+                                            std::to_string(kMaxSlotsHost) + " past blocks per query; use top_k <= " +
+                                            std::to_string(kMaxSlotsHost + 1) + " or top_k >= n_blocks (" +
+                                            std::to_string(nbi) + ")");
+    if (P.uniform) break;
+  }
+  if (P.H * P.T * std::max<int64_t>(P.slots, 1) >= (int64_t(1) << 31))
+    return fail(MOBA_ERR_UNSUPPORTED,
+                "heads * tokens * (min(top_k, n_blocks) - 1) must be below 2^31 (int32 list entries)");
+  // Exact pair count: every query in block c keeps min(k_eff - 1, eligible) past blocks.
+  P.pairs = 0;
+  if (P.uniform) {
+    P.pairs = head_pairs(P, P.S) * P.H * n;
+  } else {
+    for (int64_t i = 0; i < n; ++i) P.pairs += head_pairs(P, lens[i]) * P.H;
+  }
   if (P.pairs >= (int64_t(1) << 31)) return fail(MOBA_ERR_UNSUPPORTED, "too many (query, block) pairs for int32 lists");
-  P.max_tiles = P.pairs / kGatherTileM + P.bh * P.nb + 1;
+  P.max_tiles = P.pairs / kGatherTileM + P.H * P.nb_total + 1;
   const size_t esz = P.bf16_in ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -144,24 +206,42 @@ int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
     return at;
   };
   // Block summaries per key/value head; counts per query head.
-  const size_t nbd = (size_t)(P.bhkv * P.nb * P.D);
-  P.kbar64 = take(nbd * 8);
-  P.kbar32 = take(nbd * 4);
-  P.kbar_hi = take(nbd * 2);
-  P.kbar_lo = take(nbd * 2);
-  P.norm = take((size_t)(P.bhkv * P.nb) * 4);
-  P.count = take((size_t)(P.bh * P.nb) * 4);
-  P.rank = take((size_t)(P.bh * P.S * P.slots) * 4);
+  const size_t kvb = (size_t)(P.Hkv * P.nb_total), qb = (size_t)(P.H * P.nb_total);
+  const size_t rows = (size_t)(P.H * P.T);
+  P.kbar64 = take(kvb * P.D * 8);
+  P.kbar32 = take(kvb * P.D * 4);
+  P.kbar_hi = take(kvb * P.D * 2);
+  P.kbar_lo = take(kvb * P.D * 2);
+  P.norm = take(kvb * 4);
+  P.count = take(qb * 4);
+  P.rank = take(rows * P.slots * 4);
+  P.seq_tab = P.uniform ? 0 : take(P.tab.size() * 8);
   if (need_select) {
-    P.offset = take((size_t)(P.bh * P.nb + 1) * 4);
-    P.tile_start = take((size_t)(P.bh * P.nb + 1) * 4);
+    P.offset = take((qb + 1) * 4);
+    P.tile_start = take((qb + 1) * 4);
     P.qlist = take((size_t)P.pairs * 4);
     P.tile_map = take((size_t)gather_grid_for(P.max_tiles) * 16);
-    P.part_o = take((size_t)(P.bh * P.S * P.slots * P.D) * esz);
-    P.part_lse = take((size_t)(P.bh * P.S * P.slots) * 4);
+    P.part_o = take(rows * P.slots * P.D * esz);
+    P.part_lse = take(rows * P.slots * 4);
   }
   P.total = off;
   return MOBA_OK;
+}
+
+// A batch of equal-length sequences ([batch, heads, seq_len, head_dim]).
+int plan_problem(const moba_problem_t* p, Plan* pl, bool need_select) {
+  int st = plan_common(p, pl);
+  if (st != MOBA_OK) return st;
+  pl->S = p->seq_len;
+  return plan_seqs(*pl, nullptr, p->batch, need_select, "seq_len");
+}
+
+Seqs seqs_of(const Plan& P, void* ws) {
+  Seqs q;
+  q.tab = P.uniform ? nullptr : reinterpret_cast<const int64_t*>(static_cast<char*>(ws) + P.seq_tab);
+  q.n = P.n_seq;
+  q.len = P.uniform ? P.S : 0;
+  return q;
 }
 
 // Backward workspace: the forward's plan (its lists and tiles are rebuilt
@@ -217,11 +297,17 @@ T* at(void* ws, size_t off) {
 // pool + gate: writes block_idx, counts and ranks.
 int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, void* ws, hipStream_t s,
                double* kbar64_out) {
+  const Seqs sq = seqs_of(P, ws);
+  if (!P.uniform)
+    MOBA_TRY(hipMemcpyAsync(static_cast<char*>(ws) + P.seq_tab, P.tab.data(), P.tab.size() * sizeof(int64_t),
+                            hipMemcpyHostToDevice, s),
+             "sequence table copy");
   PoolArgs pa{};
   pa.k = k;
-  pa.bh = P.bhkv;
+  pa.sq = sq;
+  pa.kv_heads = P.Hkv;
+  pa.kv_blocks = P.Hkv * P.nb_total;
   pa.group = (int)P.G;
-  pa.seq_len = P.S;
   pa.block_size = P.Bs;
   pa.head_dim = (int)P.D;
   pa.bf16_in = P.bf16_in;
@@ -241,10 +327,13 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   ga.kbar_hi = pa.kbar_hi;
   ga.kbar_lo = pa.kbar_lo;
   ga.norm = pa.norm;
-  ga.bh = P.bh;
-  ga.seq_len = P.S;
+  ga.sq = sq;
+  ga.heads = P.H;
+  ga.kv_heads = P.Hkv;
   ga.block_size = P.Bs;
-  ga.n_blocks = P.nb;
+  ga.max_nb = P.max_nb;
+  ga.gate_wgs = (P.shared && P.G > 1 ? P.Hkv : P.H) * P.w128;
+  ga.rank_wgs = P.H * P.w1024;
   ga.head_dim = (int)P.D;
   ga.bf16_in = P.bf16_in;
   ga.causal = P.causal;
@@ -259,22 +348,44 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   return MOBA_OK;
 }
 
-AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, void* o) {
+AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, void* o, void* ws, bool dense) {
   AttnArgs aa{};
   aa.q = q;
   aa.k = k;
   aa.v = v;
   aa.o = o;
-  aa.bh = P.bh;
-  aa.seq_len = P.S;
+  aa.sq = seqs_of(P, ws);
+  aa.heads = P.H;
   aa.block_size = P.Bs;
-  aa.n_blocks = P.nb;
+  aa.diag_wgs = P.H * (diag_tile(P.Bs, dense) == 128 ? P.w128 : P.w64);
   aa.head_dim = (int)P.D;
   aa.bf16_in = P.bf16_in;
   aa.causal = P.causal;
   aa.k_eff = (int)P.k_eff;
   aa.group = (int)P.G;
   return aa;
+}
+
+PackArgs pack_args(const Plan& P, const int32_t* block_idx, void* ws) {
+  PackArgs pk{};
+  pk.sq = seqs_of(P, ws);
+  pk.heads = P.H;
+  pk.block_size = P.Bs;
+  pk.rows = P.H * P.T;
+  pk.q_blocks = P.H * P.nb_total;
+  pk.causal = P.causal;
+  pk.top_k = (int)P.top_k;
+  pk.k_eff = (int)P.k_eff;
+  pk.tile_m = kGatherTileM;
+  pk.block_idx = block_idx;
+  pk.count = at<int32_t>(ws, P.count);
+  pk.rank = at<int32_t>(ws, P.rank);
+  pk.offset = at<int32_t>(ws, P.offset);
+  pk.tile_start = at<int32_t>(ws, P.tile_start);
+  pk.qlist = at<int32_t>(ws, P.qlist);
+  pk.grid = gather_grid_for(P.max_tiles);
+  pk.tile_map = at<int32_t>(ws, P.tile_map);
+  return pk;
 }
 
 }  // namespace
@@ -297,28 +408,12 @@ int run_forward(const Plan& P, const void* q, const void* k, const void* v, void
                 void* workspace, hipStream_t s, float* lse = nullptr) {
   int st = run_select(P, q, k, block_idx, workspace, s, nullptr);
   if (st != MOBA_OK) return st;
-  AttnArgs aa = attn_args(P, q, k, v, o);
+  AttnArgs aa = attn_args(P, q, k, v, o, workspace, false);
   aa.lse_out = lse;
   aa.part_o = at<void>(workspace, P.part_o);
   aa.part_lse = at<float>(workspace, P.part_lse);
   if (P.pairs > 0) {
-    PackArgs pk{};
-    pk.bh = P.bh;
-    pk.seq_len = P.S;
-    pk.block_size = P.Bs;
-    pk.n_blocks = P.nb;
-    pk.causal = P.causal;
-    pk.top_k = (int)P.top_k;
-    pk.k_eff = (int)P.k_eff;
-    pk.tile_m = kGatherTileM;
-    pk.block_idx = block_idx;
-    pk.count = at<int32_t>(workspace, P.count);
-    pk.rank = at<int32_t>(workspace, P.rank);
-    pk.offset = at<int32_t>(workspace, P.offset);
-    pk.tile_start = at<int32_t>(workspace, P.tile_start);
-    pk.qlist = at<int32_t>(workspace, P.qlist);
-    pk.grid = gather_grid_for(P.max_tiles);
-    pk.tile_map = at<int32_t>(workspace, P.tile_map);
+    const PackArgs pk = pack_args(P, block_idx, workspace);
     MOBA_TRY(launch_pack(pk, s), "pack launch");
     aa.qlist = pk.qlist;
     aa.tile_map = pk.tile_map;
@@ -329,8 +424,9 @@ int run_forward(const Plan& P, const void* q, const void* k, const void* v, void
   return MOBA_OK;
 }
 
-// Sequence i of a varlen batch as a [1, heads, len_i, head_dim] problem.
-int varlen_plans(const moba_problem_t* p, const int64_t* cu, int64_t n, std::vector<Plan>* plans) {
+// A varlen batch: n sequences of the cu_seqlens lengths, one plan (and one
+// launch chain) for all of them.
+int varlen_plan(const moba_problem_t* p, const int64_t* cu, int64_t n, Plan* P) {
   if (!p) return fail(MOBA_ERR_NULL, "problem pointer is NULL");
   if (!cu) return fail(MOBA_ERR_NULL, "cu_seqlens is NULL");
   if (n < 1) return fail(MOBA_ERR_ARG, "n_seqs must be >= 1, got " + std::to_string(n));
@@ -340,22 +436,17 @@ int varlen_plans(const moba_problem_t* p, const int64_t* cu, int64_t n, std::vec
   if (p->seq_len != cu[n])
     return fail(MOBA_ERR_ARG, "seq_len must equal cu_seqlens[n_seqs] (" + std::to_string(cu[n]) + "), got " +
                                   std::to_string(p->seq_len));
-  plans->resize((size_t)n);
+  std::vector<int64_t> lens((size_t)n);
   for (int64_t i = 0; i < n; ++i) {
-    const int64_t len = cu[i + 1] - cu[i];
-    if (len < 1)
-      return fail(MOBA_ERR_SHAPE, "sequence " + std::to_string(i) + " has length " + std::to_string(len) +
+    lens[(size_t)i] = cu[i + 1] - cu[i];
+    if (lens[(size_t)i] < 1)
+      return fail(MOBA_ERR_SHAPE, "sequence " + std::to_string(i) + " has length " + std::to_string(lens[(size_t)i]) +
                                       " (cu_seqlens must increase)");
-    moba_problem_t one = *p;
-    one.batch = 1;
-    one.seq_len = len;
-    const int st = plan_problem(&one, &(*plans)[(size_t)i], true);
-    if (st != MOBA_OK) {
-      g_err = "sequence " + std::to_string(i) + ": " + g_err;
-      return st;
-    }
   }
-  return MOBA_OK;
+  int st = plan_common(p, P);
+  if (st != MOBA_OK) return st;
+  P->S = 0;
+  return plan_seqs(*P, lens.data(), n, true, "every sequence length");
 }
 }  // namespace
 
@@ -416,6 +507,8 @@ int plan_backward_problem(const moba_problem_t* p, Plan* P, BwdPlan* B) {
   const int st = plan_problem(p, P, true);
   if (st != MOBA_OK) return st;
   if (!P->bf16_in) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports bf16 inputs only (dtype MOBA_BF16)");
+  if (P->S % 64 != 0)
+    return fail(MOBA_ERR_UNSUPPORTED, "the backward needs seq_len to be a multiple of 64, got " + std::to_string(P->S));
   if (P->nb > 16384) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports at most 16384 blocks");
   *B = plan_backward(*P);
   return MOBA_OK;
@@ -494,23 +587,7 @@ int impl_backward(const moba_problem_t* p, const void* q, const void* k, const v
     ga.rank = at<int32_t>(workspace, P.rank);
     ga.group = (int)P.G;
     MOBA_TRY(launch_rank(ga, s, at<int32_t>(workspace, B.chunk_counts)), "rank launch");
-    PackArgs pk{};
-    pk.bh = P.bh;
-    pk.seq_len = P.S;
-    pk.block_size = P.Bs;
-    pk.n_blocks = P.nb;
-    pk.causal = P.causal;
-    pk.top_k = (int)P.top_k;
-    pk.k_eff = (int)P.k_eff;
-    pk.tile_m = kGatherTileM;
-    pk.block_idx = block_idx;
-    pk.count = count;
-    pk.rank = ga.rank;
-    pk.offset = at<int32_t>(workspace, P.offset);
-    pk.tile_start = at<int32_t>(workspace, P.tile_start);
-    pk.qlist = at<int32_t>(workspace, P.qlist);
-    pk.grid = gather_grid_for(P.max_tiles);
-    pk.tile_map = at<int32_t>(workspace, P.tile_map);
+    const PackArgs pk = pack_args(P, block_idx, workspace);
     MOBA_TRY(launch_pack(pk, s), "pack launch");
     ba.qlist = pk.qlist;
     ba.offset = pk.offset;
@@ -524,12 +601,10 @@ int impl_backward(const moba_problem_t* p, const void* q, const void* k, const v
 int impl_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
-  std::vector<Plan> plans;
-  const int st = varlen_plans(p, cu_seqlens, n_seqs, &plans);
+  Plan P;
+  const int st = varlen_plan(p, cu_seqlens, n_seqs, &P);
   if (st != MOBA_OK) return st;
-  size_t m = 0;
-  for (const Plan& P : plans) m = std::max(m, P.total);
-  *bytes = m;
+  *bytes = P.total;
   return MOBA_OK;
 }
 
@@ -537,33 +612,15 @@ int impl_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int6
                         const void* k, const void* v, void* o, int32_t* block_idx, void* workspace,
                         size_t workspace_bytes, void* stream) {
   g_err.clear();
-  std::vector<Plan> plans;
-  int st = varlen_plans(p, cu_seqlens, n_seqs, &plans);
+  Plan P;
+  int st = varlen_plan(p, cu_seqlens, n_seqs, &P);
   if (st != MOBA_OK) return st;
   st = check_tensors(q, k, v, o, block_idx);
   if (st != MOBA_OK) return st;
-  for (const Plan& P : plans) {
-    st = check_ws(P, workspace, workspace_bytes);
-    if (st != MOBA_OK) return st;
-  }
-  // Every sequence is validated before the first launch; they then run in
-  // order on the one stream, sharing the workspace.
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t esz = p->dtype == MOBA_BF16 ? 2 : 4;
-  // Bytes per token of one sequence: all query heads, all key/value heads.
-  const size_t row = (size_t)p->heads * (size_t)p->head_dim * esz;
-  const size_t kv_row = (size_t)plans[0].Hkv * (size_t)p->head_dim * esz;
-  for (int64_t i = 0; i < n_seqs; ++i) {
-    const size_t off = (size_t)cu_seqlens[i] * row, kv_off = (size_t)cu_seqlens[i] * kv_row;
-    st = run_forward(plans[(size_t)i], static_cast<const char*>(q) + off, static_cast<const char*>(k) + kv_off,
-                     static_cast<const char*>(v) + kv_off, static_cast<char*>(o) + off,
-                     block_idx + cu_seqlens[i] * p->heads * p->top_k, workspace, s);
-    if (st != MOBA_OK) {
-      g_err = "sequence " + std::to_string(i) + ": " + g_err;
-      return st;
-    }
-  }
-  return MOBA_OK;
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != MOBA_OK) return st;
+  // Every sequence is validated above; one launch chain covers them all.
+  return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream));
 }
 
 int impl_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
@@ -574,21 +631,18 @@ int impl_dense_forward(const moba_problem_t* p, const void* q, const void* k, co
   // whose only block is the whole sequence.
   moba_problem_t d = *p;
   if (force_causal) d.causal = 1;
-  if (d.seq_len >= 1) d.block_size = d.seq_len % 64 == 0 ? 64 : d.seq_len;
+  d.block_size = 64;
   if (d.top_k < 1) return fail(MOBA_ERR_ARG, "top_k must be >= 1, got " + std::to_string(p->top_k));
+  if (p->block_size < 1) return fail(MOBA_ERR_SHAPE, "block_size must be >= 1, got " + std::to_string(p->block_size));
   d.top_k = 1;
   Plan P;
   const int st = plan_problem(&d, &P, false);
-  if (st != MOBA_OK) {
-    if (st == MOBA_ERR_UNSUPPORTED && p->seq_len % 64 != 0)
-      return fail(MOBA_ERR_UNSUPPORTED, "seq_len must be a multiple of 64 for dense attention");
-    return st;
-  }
+  if (st != MOBA_OK) return st;
   if (!q) return fail(MOBA_ERR_NULL, "q is NULL");
   if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
   if (!v) return fail(MOBA_ERR_NULL, "v is NULL");
   if (!o) return fail(MOBA_ERR_NULL, "o is NULL");
-  AttnArgs aa = attn_args(P, q, k, v, o);
+  AttnArgs aa = attn_args(P, q, k, v, o, nullptr, true);
   MOBA_TRY(launch_dense(aa, static_cast<hipStream_t>(stream)), "dense launch");
   return MOBA_OK;
 }

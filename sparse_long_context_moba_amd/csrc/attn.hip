@@ -46,47 +46,57 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   MOBA_KERNEL_LDS(E)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
 
-  // This workgroup's tile: its (head, block) and list range (written by the
-  // packing step, which also spreads tiles over the XCDs).
+  // This workgroup's tile: its block, list range and sequence (written by
+  // the packing step, which also spreads tiles over the XCDs).
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const i32x4 tm = *reinterpret_cast<const i32x4*>(a.tile_map + 4 * (int64_t)blockIdx.x);
   if (tm.x < 0) return;
-  const int64_t blk = __builtin_amdgcn_readfirstlane(tm.x);  // uniform: keeps the K/V bases in SGPRs
-  const int64_t bh = blk / a.n_blocks, j = blk % a.n_blocks;
+  // Uniform values (readfirstlane) keep the K/V bases in SGPRs.
+  const int64_t blk = __builtin_amdgcn_readfirstlane(tm.x);  // the block among all query heads' blocks
+  const int64_t si = __builtin_amdgcn_readfirstlane(tm.w);
+  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t rb = blk - a.heads * sa.blk0;
+  const int64_t hq = rb / sa.nb, j = rb % sa.nb;
   const int64_t e0 = __builtin_amdgcn_readfirstlane(tm.y), e1 = __builtin_amdgcn_readfirstlane(tm.z);
   const int64_t e = e0 + 32 * w + col;
   const bool valid = e < e1;
   const bool wave_on = e0 + 32 * w < e1;
   const int slots = a.k_eff - 1;
-  int ev = 0, t = 0;
+  int ev = 0;
 
   E eng;
   eng.init();
   const T* q = reinterpret_cast<const T*>(a.q);
-  // Query rows: read after the first K/V loads are queued.
+  // Query rows: read after the first K/V loads are queued. A list entry is
+  // the query's global row * slots + slot, which also numbers its partial.
   auto load_q = [&]() {
     ev = a.qlist[valid ? e : e0];
-    t = ev / slots;
-    if (wave_on) eng.load_q(q + (bh * a.seq_len + t) * D, h);
+    if (wave_on) eng.load_q(q + (int64_t)(ev / slots) * D, h);
   };
   // Keys and values of the query head's key/value head (grouped-query attention).
-  const int64_t kvh = bh / a.group;
-  const T* kp = reinterpret_cast<const T*>(a.k) + (kvh * a.seq_len + j * a.block_size) * D;
-  const T* vp = reinterpret_cast<const T*>(a.v) + (kvh * a.seq_len + j * a.block_size) * D;
+  const int64_t kv_heads = a.heads / a.group, kvh = hq / a.group;
+  const int64_t kvrow = sa.tok0 * kv_heads + kvh * sa.len + j * a.block_size;
+  const T* kp = reinterpret_cast<const T*>(a.k) + kvrow * D;
+  const T* vp = reinterpret_cast<const T*>(a.v) + kvrow * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
-  // A short last block (seq_len not a multiple of block_size) has fewer subtiles.
-  const int nsub = (int)(min<int64_t>(a.block_size, a.seq_len - j * a.block_size) / kSub);
+  // The sequence's last block may be short, down to one token; its last
+  // subtile then holds fewer than 64 keys.
+  const int rows = (int)min<int64_t>(a.block_size, sa.len - j * a.block_size);
+  const int nsub = (rows + kSub - 1) / kSub;
+  const int last_rows = rows - kSub * (nsub - 1);
   if constexpr (E::kDMA) {
-    stream_k_ahead<E, NT>(eng, bufA, bufB, kp, vp, nsub, tid, lane, wave_on, sl2, load_q);
+    stream_k_ahead<E, NT>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, wave_on, sl2, load_q);
   } else {
-    stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, load_q, [&](const char* buf, int) {
-      if (wave_on) eng.template step<false>(buf, lane, 0, 0, sl2);
+    stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, last_rows, D, tid, load_q, [&](const char* buf, int sub) {
+      if (!wave_on) return;
+      if (sub == nsub - 1 && last_rows < kSub) eng.template step<true>(buf, lane, 0, last_rows - 1, sl2);
+      else eng.template step<false>(buf, lane, 0, 0, sl2);
     });
   }
   if (!wave_on) return;
   const float lt = pair_sum(eng.l);
   if (valid) {
-    const int64_t rec = bh * a.seq_len * slots + ev;
+    const int64_t rec = ev;
     T* dst = reinterpret_cast<T*>(a.part_o) + rec * D + h * (D / 2);
     const float inv = 1.f / lt;
 #pragma unroll
@@ -102,16 +112,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int NT = 64 * NW, M = 32 * NW;
   MOBA_KERNEL_LDS(E)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  // Heavier tiles (later in the sequence) first, heads interleaved.
-  const int64_t ntile = a.seq_len / M;
-  const int64_t tile = ntile - 1 - blockIdx.x / a.bh;
-  const int64_t bh = blockIdx.x % a.bh;
+  // Work item -> (sequence, query head, tile of M queries); within a
+  // sequence heavier tiles (later in it) come first, heads interleaved.
+  constexpr int COL = M == 128 ? kSeqW128 : kSeqW64;
+  static_assert(M == 128 || M == 64, "tiles of 64 or 128 queries");
+  const int64_t item = blockIdx.x;
+  const int64_t si = seq_find(a.sq, COL, a.heads, item, a.block_size);
+  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t ntile = (sa.len + M - 1) / M;
+  const int64_t r_item = item - a.heads * seq_prefix(a.sq, si, COL, a.block_size);
+  const int64_t tile = ntile - 1 - r_item / a.heads;
+  const int64_t hq = r_item % a.heads;
+  const int len = (int)sa.len;
+  const int64_t row0 = sa.tok0 * a.heads + hq * sa.len;  // row of token 0 of this head
   const int q0 = (int)(tile * M);
   const int c = (int)(q0 / a.block_size);
   const int kb = DENSE ? 0 : (int)(c * a.block_size);
-  const int kend = a.causal ? q0 + M : (DENSE ? (int)a.seq_len : (int)min<int64_t>(kb + a.block_size, a.seq_len));
+  // Keys end at the tile's last query (causal), else at the block's (or,
+  // dense, the sequence's) end; never past the sequence.
+  const int kend = a.causal ? min(q0 + M, len) : (DENSE ? len : (int)min<int64_t>(kb + a.block_size, len));
   const int qw0 = q0 + 32 * w;
   const int t = qw0 + col;
+  // Lanes past the sequence's end (its last tile may be partial) compute on
+  // its last query and store nothing.
+  const int tq = min(t, len - 1);
+  const bool wave_on = qw0 < len;
 
   E eng;
   eng.init();
@@ -119,17 +144,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Query rows, and for the own block the merge's seed: run once the first
   // K/V loads are queued, so that their loads overlap.
   auto start = [&]() {
-    eng.load_q(q + (bh * a.seq_len + t) * D, h);
+    eng.load_q(q + (row0 + tq) * D, h);
     if (DENSE) return;
     // Start the online softmax from the past-block partials: with
     // m = max lse_i and w_i = 2^(lse_i - m), the state (m, sum w_i,
     // sum w_i o_i) is the partials' union, and the own block's keys then
     // continue it, so the merge needs no pass after the loop. l is kept on
     // one lane of the pair, which sums it at the end.
-    const int n_elig = a.causal ? c : (int)a.n_blocks - 1;
+    const int n_elig = a.causal ? c : (int)sa.nb - 1;
     const int n = min(a.k_eff - 1, n_elig);
     const int slots = a.k_eff - 1;
-    const int64_t rec0 = (bh * a.seq_len + t) * (int64_t)slots;
+    const int64_t rec0 = (row0 + tq) * (int64_t)slots;
     if constexpr (sizeof(T) == 2) {
       if (n > 0 && n <= 2) {
         // One or two past blocks (top_k <= 3): every load of both slots is
@@ -190,35 +215,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       eng.l = h == 0 ? wsum : 0.f;
     }
   };
-  const int64_t kvh = bh / a.group;  // the query head's key/value head
-  const T* kp = reinterpret_cast<const T*>(a.k) + (kvh * a.seq_len + kb) * D;
-  const T* vp = reinterpret_cast<const T*>(a.v) + (kvh * a.seq_len + kb) * D;
+  const int64_t kvh = hq / a.group;  // the query head's key/value head
+  const int64_t kvrow = sa.tok0 * (a.heads / a.group) + kvh * sa.len + kb;
+  const T* kp = reinterpret_cast<const T*>(a.k) + kvrow * D;
+  const T* vp = reinterpret_cast<const T*>(a.v) + kvrow * D;
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
-  const int nsub = (kend - kb) / kSub;
+  const int nsub = (kend - kb + kSub - 1) / kSub;
+  const int last_rows = (kend - kb) - kSub * (nsub - 1);  // keys of the last subtile (1..64)
   // Subtiles entirely before the workgroup's first query need no mask; with
-  // causal attention the last M/64 subtiles hold the diagonal.
-  const int nfree = a.causal ? (q0 - kb) / kSub : nsub;
-  stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, D, tid, start, [&](const char* buf, int sub) {
+  // causal attention the last subtiles hold the diagonal (and any partial
+  // last subtile, whose padding keys lie after every valid query). Without
+  // it only a partial last subtile needs one: keys at or past kend.
+  const int nfree = a.causal ? (q0 - kb) / kSub : (last_rows < kSub ? nsub - 1 : nsub);
+  const int lim = a.causal ? t : kend - 1;  // the last key a lane may attend
+  stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, last_rows, D, tid, start, [&](const char* buf, int sub) {
+    if (!wave_on) return;
     if (sub < nfree) {
       eng.template step<false>(buf, lane, 0, 0, sl2);
     } else {
       const int key0 = kb + sub * kSub;
       // Skip a subtile whose keys all come after every query of this wave.
-      if (key0 <= qw0 + 31) eng.template step<true>(buf, lane, key0, t, sl2);
+      if (!a.causal || key0 <= qw0 + 31) eng.template step<true>(buf, lane, key0, lim, sl2);
     }
   });
+  if (!wave_on) return;
 
   // Dense, or own block continuing the partials' state: normalise once.
   const float lt = pair_sum(eng.l);
   const float inv = 1.f / lt;
   // The natural-log log-sum-exp of the query's scaled logits over every key
   // it attended (m and l are in the log2 domain), for a backward pass.
-  if (a.lse_out && h == 0) a.lse_out[bh * a.seq_len + t] = (eng.m + fast_log2(lt)) * 0.69314718f;
+  if (t >= len) return;
+  if (a.lse_out && h == 0) a.lse_out[row0 + t] = (eng.m + fast_log2(lt)) * 0.69314718f;
 #pragma unroll
   for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) eng.o[dt][r] *= inv;
-  T* orow = reinterpret_cast<T*>(a.o) + (bh * a.seq_len + t) * D;
+  T* orow = reinterpret_cast<T*>(a.o) + (row0 + t) * D;
 #pragma unroll
   for (int dt = 0; dt < E::DT; ++dt)
 #pragma unroll
@@ -252,8 +285,9 @@ hipError_t gather_t(const AttnArgs& a, hipStream_t s) {
 template <typename T, int D, bool DENSE>
 hipError_t diag_t(const AttnArgs& a, hipStream_t s) {
   using E = typename EngOf<T, D>::type;
-  // 128-query tiles when they stay inside one block (and one sequence), else 64.
-  const bool four = a.seq_len % 128 == 0 && (DENSE || a.block_size % 128 == 0);
+  // 128-query tiles when they stay inside one block, else 64 (diag_tile);
+  // a.diag_wgs counts the tiles of that size over all sequences and heads.
+  const bool four = diag_tile(a.block_size, DENSE) == 128;
   const char* name = DENSE ? "dense_attn" : "diag_merge";
   constexpr int lds = dyn_lds_bytes<E>();
   if (four) {
@@ -261,13 +295,13 @@ hipError_t diag_t(const AttnArgs& a, hipStream_t s) {
     hipError_t e = prep_lds(kern, lds);
     if (e != hipSuccess) return e;
     KernelTimer timer(s, name);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.bh * (a.seq_len / 128))), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.diag_wgs), dim3(256), lds, s, a);
   } else {
     auto kern = diag_attn_kernel<T, D, 2, DENSE>;
     hipError_t e = prep_lds(kern, lds);
     if (e != hipSuccess) return e;
     KernelTimer timer(s, name);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), lds, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.diag_wgs), dim3(128), lds, s, a);
   }
   return hipGetLastError();
 }

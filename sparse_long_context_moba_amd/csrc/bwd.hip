@@ -201,9 +201,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int64_t e = e0 + 32 * w + col;
   const bool valid = e < e1, wave_on = e0 + 32 * w < e1;
   const int slots = a.k_eff - 1;
-  const int ev = a.qlist[valid ? e : e0];
-  const int t = ev / slots;
-  const int64_t row = bh * a.seq_len + t;
+  const int ev = a.qlist[valid ? e : e0];  // the query's global row * slots + slot
+  const int64_t row = ev / slots;
   bf16x8 qf[KC], gf[KC];
   load_frags<D>(qf, reinterpret_cast<const bf16*>(a.q) + row * D, h);
   load_frags<D>(gf, reinterpret_cast<const bf16*>(a.dout) + row * D, h);
@@ -233,7 +232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     lds_dma_wait();
     __syncthreads();
   }
-  if (valid) store_row_f32<D>(a.dq_part + ((bh * a.seq_len * slots) + ev) * D, acc, h, 1.f / __builtin_sqrtf((float)D));
+  if (valid) store_row_f32<D>(a.dq_part + (int64_t)ev * D, acc, h, 1.f / __builtin_sqrtf((float)D));
 }
 
 // The own block: 32 * NW consecutive queries of one head.
@@ -350,10 +349,10 @@ __global__ __launch_bounds__(256) void list_meta_kernel(BwdArgs a) {
   const int slots = a.k_eff - 1;
   const int o0 = a.offset[lst], o1 = a.offset[lst + 1];
   for (int pos = o0 + (int)threadIdx.x; pos < o1; pos += 256) {
-    const int t = a.qlist[pos] / slots;
-    a.lt[pos] = t;
-    a.ll[pos] = a.lse2[bh * a.seq_len + t];
-    a.ld[pos] = a.delta[bh * a.seq_len + t];
+    const int64_t row = a.qlist[pos] / slots;  // global query row (bh * seq_len + t)
+    a.lt[pos] = (int32_t)(row - bh * a.seq_len);
+    a.ll[pos] = a.lse2[row];
+    a.ld[pos] = a.delta[row];
   }
 }
 

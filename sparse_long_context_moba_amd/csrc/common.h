@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace moba {
 
 typedef __bf16 bf16;
@@ -64,6 +66,37 @@ __device__ __forceinline__ bool routed_past_block(int j, int c, int64_t n_blocks
 // Past blocks a query in block c keeps: min(k_eff - 1, eligible blocks).
 __device__ __forceinline__ int past_cap(int c, int64_t n_blocks, bool causal, int k_eff) {
   return min(k_eff - 1, causal ? c : (int)n_blocks - 1);
+}
+
+// ------------------------------------------------------------ sequences
+// (Seqs and its columns are declared in launch.h.)
+// Column col of table row i (the sum over sequences before i).
+__device__ __forceinline__ int64_t seq_prefix(const Seqs& s, int64_t i, int col, int64_t block_size) {
+  return s.tab ? s.tab[i * kSeqCols + col] : i * seq_units(col, s.len, block_size);
+}
+// The sequence owning work item `item` when sequence i owns items
+// [per * P_i, per * P_{i+1}) of column col (per = heads, for one item per
+// head and unit). Uniform: a division; varlen: a binary search.
+__device__ __forceinline__ int64_t seq_find(const Seqs& s, int col, int64_t per, int64_t item, int64_t block_size) {
+  if (!s.tab) return item / (per * seq_units(col, s.len, block_size));
+  int64_t lo = 0, hi = s.n;  // invariant: per * P_lo <= item < per * P_hi
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (per * s.tab[mid * kSeqCols + col] <= item) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+struct SeqAt {
+  int64_t tok0, len, blk0, nb;
+};
+__device__ __forceinline__ SeqAt seq_at(const Seqs& s, int64_t i, int64_t block_size) {
+  SeqAt r;
+  r.tok0 = seq_prefix(s, i, kSeqTok, block_size);
+  r.len = s.tab ? s.tab[(i + 1) * kSeqCols + kSeqTok] - r.tok0 : s.len;
+  r.blk0 = seq_prefix(s, i, kSeqBlk, block_size);
+  r.nb = (r.len + block_size - 1) / block_size;
+  return r;
 }
 
 template <typename T>

@@ -185,6 +185,21 @@ struct EngBF16 {
       lo.v[ii] = (unsigned)(row * D + 8 * ((sl % CPR) ^ swzv(row))) * 2u;
     }
   }
+  // The same offsets for a subtile holding only nrows (< 64) rows, the last
+  // of a block or sequence of any length: rows at or past nrows read row
+  // nrows - 1 instead (keeping the swizzle of their own LDS row), so no load
+  // leaves the block; the scores of those rows are masked by the caller.
+  template <int NT>
+  static __device__ __forceinline__ void load_offsets_tail(LoadOffsets<NT>& lo, int tid, int nrows) {
+    constexpr int NW = NT / 64;
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int ii = 0; ii < kLoadsPerWave<NT>; ++ii) {
+      const int sl = (ii * NW + w) * 64 + lane, row = sl / CPR, rs = min(row, nrows - 1);
+      lo.k[ii] = (unsigned)(rs * D + 8 * ((sl % CPR) ^ swz(row))) * 2u;
+      lo.v[ii] = (unsigned)(rs * D + 8 * ((sl % CPR) ^ swzv(row))) * 2u;
+    }
+  }
   // The loads of one subtile from a wave-uniform base p.
   template <int NT, bool IS_V>
   static __device__ __forceinline__ void begin_uniform(const bf16* p, const LoadOffsets<NT>& lo, char* buf, int tid) {
@@ -470,14 +485,17 @@ struct EngF32 {
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) qf[kk] = qrow[2 * kk + h];
   }
-  // Load one K and one V subtile into registers.
+  // Load one K and one V subtile into registers; a subtile holding only
+  // rows (< 64) rows reads row rows - 1 for the others (their scores are
+  // masked by the caller).
   template <int NT>
-  static __device__ __forceinline__ void begin(Stage<NT>& st, const float* kp, const float* vp, char*, int tid) {
+  static __device__ __forceinline__ void begin(Stage<NT>& st, const float* kp, const float* vp, char*, int tid,
+                                               int rows) {
 #pragma unroll
     for (int i = 0; i < (CH + NT - 1) / NT; ++i) {
       const int id = tid + NT * i;
       if (CH % NT == 0 || id < CH) {
-        const int row = id / (D / 4), cc = id % (D / 4);
+        const int row = min(id / (D / 4), rows - 1), cc = id % (D / 4);
         st.k[i] = *reinterpret_cast<const u32x4*>(kp + (int64_t)row * D + 4 * cc);
         st.v[i] = *reinterpret_cast<const u32x4*>(vp + (int64_t)row * D + 4 * cc);
       }
@@ -560,27 +578,52 @@ struct EngOf<float, D> {
   using type = EngF32<D>;
 };
 
+// The direct loads of one K (IS_V false) or V subtile holding `rows` rows
+// (64, or fewer for the last subtile of a block or sequence).
+template <class E, int NT, bool IS_V>
+__device__ __forceinline__ void load_subtile(const typename E::T* p, const typename E::template LoadOffsets<NT>& lo,
+                                             char* buf, int tid, int rows) {
+  if (rows < kSub) {
+    typename E::template LoadOffsets<NT> lt;
+    E::template load_offsets_tail<NT>(lt, tid, rows);
+    E::template begin_uniform<NT, IS_V>(p, lt, buf, tid);
+  } else {
+    E::template begin_uniform<NT, IS_V>(p, lo, buf, tid);
+  }
+}
+
+// Scores of keys at or past nvalid in a 64-key subtile set to -inf (the
+// padding rows of a partial last subtile; key 32 * nt + crow(r, h)).
+__device__ __forceinline__ void mask_rows(f32x16 (&s)[2], int nvalid, int h) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * nt + crow(r, h) >= nvalid) s[nt][r] = kNegInf;
+}
+
 // Streams nsub consecutive 64-key subtiles of K and V through LDS and calls
-// compute(buf, sub) on each. Direct-load engines double-buffer (loads of
-// subtile sub+1 run under the compute of subtile sub; the two buffers are
-// distinct objects so the compiler need not order the loads against the
-// reads of the other buffer); register-staged engines prefetch into
-// registers and use one buffer.
+// compute(buf, sub) on each; the last subtile holds last_rows (1..64) rows
+// (the others are padding the caller masks). Direct-load engines
+// double-buffer (loads of subtile sub+1 run under the compute of subtile
+// sub; the two buffers are distinct objects so the compiler need not order
+// the loads against the reads of the other buffer); register-staged engines
+// prefetch into registers and use one buffer.
 // start() runs once the first subtile's loads are queued (work whose own
 // loads should overlap them: the query rows, the merge's partials).
 template <class E, int NT, class S, class F>
 __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const typename E::T* kp,
-                                                const typename E::T* vp, int nsub, int D, int tid, S&& start,
-                                                F&& compute) {
-  typename E::template Stage<NT> st;
+                                                const typename E::T* vp, int nsub, int last_rows, int D, int tid,
+                                                S&& start, F&& compute) {
+  auto rows_of = [&](int sub) { return sub == nsub - 1 ? last_rows : kSub; };
   if constexpr (E::kDMA) {
     // Direct loads from wave-uniform bases with per-lane offsets computed
     // once (no per-load address arithmetic).
     typename E::template LoadOffsets<NT> lo;
     E::template load_offsets<NT>(lo, tid);
     auto issue = [&](int sub, char* buf) {
-      E::template begin_uniform<NT, false>(kp + sub * (int64_t)kSub * D, lo, buf, tid);
-      E::template begin_uniform<NT, true>(vp + sub * (int64_t)kSub * D, lo, buf + E::TB, tid);
+      load_subtile<E, NT, false>(kp + sub * (int64_t)kSub * D, lo, buf, tid, rows_of(sub));
+      load_subtile<E, NT, true>(vp + sub * (int64_t)kSub * D, lo, buf + E::TB, tid, rows_of(sub));
     };
     issue(0, bufA);
     start();
@@ -600,35 +643,23 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
       if (m2) lds_dma_wait();
       __syncthreads();
     }
-    return;
-  }
-  E::template begin<NT>(st, kp, vp, bufA, tid);
-  start();
-  E::template land<NT>(st, bufA, tid);
-  // Also tell the compiler that every vector-memory load issued so far (the
-  // query fragments) has completed, so that it emits no vmcnt waits inside
-  // the loop, where the only outstanding loads are the next subtile's.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  const int64_t step_elems = (int64_t)kSub * D;
-  if constexpr (E::kDMA) {
-    for (int sub = 0; sub < nsub; sub += 2) {
-      const bool m1 = sub + 1 < nsub;
-      if (m1) E::template begin<NT>(st, kp + (sub + 1) * step_elems, vp + (sub + 1) * step_elems, bufB, tid);
-      compute(bufA, sub);
-      if (m1) E::template land<NT>(st, bufB, tid);
-      __syncthreads();
-      if (!m1) break;
-      const bool m2 = sub + 2 < nsub;
-      if (m2) E::template begin<NT>(st, kp + (sub + 2) * step_elems, vp + (sub + 2) * step_elems, bufA, tid);
-      compute(bufB, sub + 1);
-      if (m2) E::template land<NT>(st, bufA, tid);
-      __syncthreads();
-    }
   } else {
+    typename E::template Stage<NT> st;
+    E::template begin<NT>(st, kp, vp, bufA, tid, rows_of(0));
+    start();
+    E::template land<NT>(st, bufA, tid);
+    // Also tell the compiler that every vector-memory load issued so far
+    // (the query fragments) has completed, so that it emits no vmcnt waits
+    // inside the loop, where the only outstanding loads are the next
+    // subtile's.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    const int64_t step_elems = (int64_t)kSub * D;
     for (int sub = 0; sub < nsub; ++sub) {
       const bool more = sub + 1 < nsub;
-      if (more) E::template begin<NT>(st, kp + (sub + 1) * step_elems, vp + (sub + 1) * step_elems, bufA, tid);
+      if (more)
+        E::template begin<NT>(st, kp + (sub + 1) * step_elems, vp + (sub + 1) * step_elems, bufA, tid,
+                              rows_of(sub + 1));
       compute(bufA, sub);
       if (more) {
         __syncthreads();
@@ -639,7 +670,8 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
   }
 }
 
-// K-ahead stream for direct-load engines, unmasked subtiles only (gather):
+// K-ahead stream for direct-load engines (gather; no causal mask, only the
+// padding rows of a partial last subtile are masked):
 // each buffer holds a K subtile then a V subtile (TB bytes each). Step sub
 // loads K of sub+2 and V of sub+1, computes the scores of sub+1 while the
 // weights and P.V of sub run, and ends at the barrier that publishes the
@@ -649,14 +681,17 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
 // step before.
 template <class E, int NT, bool ON, class S>
 __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB, const typename E::T* kp,
-                                                 const typename E::T* vp, int nsub, int tid, int lane, float sl2,
-                                                 S&& start) {
+                                                 const typename E::T* vp, int nsub, int last_rows, int tid, int lane,
+                                                 float sl2, S&& start) {
   constexpr int64_t SE = (int64_t)kSub * E::kD;
+  const int h = lane >> 5;
+  const bool tail = last_rows < kSub;  // the last subtile is partial: clamped loads, masked scores
+  auto rows_of = [&](int sub) { return sub == nsub - 1 ? last_rows : kSub; };
   typename E::template LoadOffsets<NT> lo;
   E::template load_offsets<NT>(lo, tid);
-  E::template begin_uniform<NT, false>(kp, lo, bufA, tid);
-  E::template begin_uniform<NT, true>(vp, lo, bufA + E::TB, tid);
-  if (nsub > 1) E::template begin_uniform<NT, false>(kp + SE, lo, bufB, tid);
+  load_subtile<E, NT, false>(kp, lo, bufA, tid, rows_of(0));
+  load_subtile<E, NT, true>(vp, lo, bufA + E::TB, tid, rows_of(0));
+  if (nsub > 1) load_subtile<E, NT, false>(kp + SE, lo, bufB, tid, rows_of(1));
   start();  // e.g. the query rows, under the first K/V loads
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see stream_subtiles
   lds_dma_wait();
@@ -665,6 +700,7 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
   float ma = kNegInf, mb = kNegInf;
   if (ON) {
     eng.qk(bufA, lane, sa);
+    if (tail && nsub == 1) mask_rows(sa, last_rows, h);
     ma = E::rowmax(sa, sl2);
   }
   __syncthreads();
@@ -674,11 +710,15 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
   // wave's loads before the barrier that publishes them to the other waves.
   auto full = [&](int sub, char* bc, char* bn, f32x16(&sc)[2], f32x16(&sn)[2], float mc, float& mn) {
     const bool k2 = sub + 2 < nsub;
-    E::template begin_uniform<NT, true>(vp + (sub + 1) * SE, lo, bn + E::TB, tid);
-    if (k2) E::template begin_uniform<NT, false>(kp + (sub + 2) * SE, lo, bc, tid);
+    load_subtile<E, NT, true>(vp + (sub + 1) * SE, lo, bn + E::TB, tid, rows_of(sub + 1));
+    if (k2) load_subtile<E, NT, false>(kp + (sub + 2) * SE, lo, bc, tid, rows_of(sub + 2));
     if (ON) {
       eng.rescale(mc);
       eng.fused(bn, sn, sc, bc + E::TB, lane, sl2, mn);
+      if (tail && sub + 1 == nsub - 1) {
+        mask_rows(sn, last_rows, h);
+        mn = E::rowmax(sn, sl2);
+      }
     }
     lds_dma_wait();
     __syncthreads();
@@ -707,10 +747,10 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
 // take part in the loads and barriers only.
 template <class E, int NT, class S>
 __device__ __forceinline__ void stream_k_ahead(E& eng, char* bufA, char* bufB, const typename E::T* kp,
-                                               const typename E::T* vp, int nsub, int tid, int lane, bool on,
-                                               float sl2, S&& start) {
-  if (on) stream_k_ahead_t<E, NT, true>(eng, bufA, bufB, kp, vp, nsub, tid, lane, sl2, start);
-  else stream_k_ahead_t<E, NT, false>(eng, bufA, bufB, kp, vp, nsub, tid, lane, sl2, start);
+                                               const typename E::T* vp, int nsub, int last_rows, int tid, int lane,
+                                               bool on, float sl2, S&& start) {
+  if (on) stream_k_ahead_t<E, NT, true>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
+  else stream_k_ahead_t<E, NT, false>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
 }
 
 // LDS for one kernel: two static subtile buffers for direct-load engines,

@@ -208,9 +208,10 @@ struct GateOps<bf16, D> {
   static constexpr int CPR = D / 8;             // chunks per row
   static constexpr int CH = kTileB * CPR;       // chunks per tile of hi (or lo)
   static constexpr int NLD = 2 * CH / 256;
-  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t kvh, int j0, int tid) {
-    const int64_t head = kvh * a.n_blocks * D;
-    if (j0 + kTileB <= a.n_blocks) {
+  // kvb0: index of the head's first pooled key; nb: the head's blocks.
+  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t kvb0, int nb, int j0, int tid) {
+    const int64_t head = kvb0 * D;
+    if (j0 + kTileB <= nb) {
       // Whole tile: a uniform base and a fixed per-thread offset.
       const bf16* hi = a.kbar_hi + head + (int64_t)j0 * D;
       const bf16* lo = a.kbar_lo + head + (int64_t)j0 * D;
@@ -223,7 +224,7 @@ struct GateOps<bf16, D> {
 #pragma unroll
       for (int n = 0; n < NLD; ++n) {
         const int i = tid + 256 * n, id = i % CH;
-        const int j = min(j0 + id / CPR, (int)a.n_blocks - 1);
+        const int j = min(j0 + id / CPR, nb - 1);
         r[n] = *reinterpret_cast<const Chunk*>((i < CH ? a.kbar_hi : a.kbar_lo) + head + (int64_t)j * D + 8 * (id % CPR));
       }
     }
@@ -307,9 +308,9 @@ struct GateOps<float, D> {
   static constexpr int CPR = D / 2;
   static constexpr int CH = kTileB * CPR;
   static constexpr int NLD = CH / 256;
-  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t kvh, int j0, int tid) {
-    const float* head = a.kbar32 + kvh * a.n_blocks * D;
-    if (j0 + kTileB <= a.n_blocks) {
+  static __device__ void fetch(Chunk (&r)[NLD], const GateArgs& a, int64_t kvb0, int nb, int j0, int tid) {
+    const float* head = a.kbar32 + kvb0 * D;
+    if (j0 + kTileB <= nb) {
       const float* base = head + (int64_t)j0 * D;
 #pragma unroll
       for (int n = 0; n < NLD; ++n) {
@@ -320,7 +321,7 @@ struct GateOps<float, D> {
 #pragma unroll
       for (int n = 0; n < NLD; ++n) {
         const int id = tid + 256 * n;
-        const int j = min(j0 + id / CPR, (int)a.n_blocks - 1);
+        const int j = min(j0 + id / CPR, nb - 1);
         r[n] = *reinterpret_cast<const Chunk*>(head + (int64_t)j * D + 2 * (id % CPR));
       }
     }
@@ -481,8 +482,9 @@ constexpr int gate_waves() {
 
 // fp64 re-scoring of the wave's ambiguous queries (lanes with `amb` set,
 // lane half 0), one query at a time by the whole wave. A query's fp64
-// vector is the sum of its rows in the nq query heads from qh0 (one head
-// unless the gate is shared); the pooled keys are those of key head kvh.
+// vector is the sum of its rows in nq query heads (one head unless the gate
+// is shared): row qrow0 + tg + lane column of the first, the others
+// head_stride rows apart; the pooled keys are the key head's, from kvb0.
 // The queries share c
 // and the eligible set. Candidates are the query's tracked list, or every
 // eligible block when its rounding band reaches past the list (`tracked`
@@ -490,10 +492,11 @@ constexpr int gate_waves() {
 // coordinates and sum the slices in a fixed order (deterministic). The
 // query in lane column L gets the exact top-TT in sel.
 template <typename TQ, int D, int TT>
-__device__ void rescore_ambiguous(const GateArgs& a, int64_t qh0, int nq, int64_t kvh, int64_t tg, int c, int jend,
-                                  bool amb, bool tracked, const int (&lj)[TT], int (&sel)[TT], int lane, int col) {
+__device__ void rescore_ambiguous(const GateArgs& a, int64_t qrow0, int64_t head_stride, int nq, int64_t kvb0,
+                                  int64_t tg, int c, int jend, bool amb, bool tracked, const int (&lj)[TT], int (&sel)[TT],
+                                  int lane, int col) {
   uint64_t pend = __builtin_amdgcn_ballot_w64(amb);
-  const double* kb64 = a.kbar64 + kvh * a.n_blocks * (int64_t)D;
+  const double* kb64 = a.kbar64 + kvb0 * (int64_t)D;
   constexpr int SL = D / 8;    // 8-coordinate slices per candidate
   constexpr int G = 64 / SL;   // candidates per pass
   const int gi = lane / SL, sl = lane % SL;
@@ -503,12 +506,12 @@ __device__ void rescore_ambiguous(const GateArgs& a, int64_t qh0, int nq, int64_
     const bool trk = __builtin_amdgcn_readlane((int)tracked, ln);
     // This lane's slice of the ambiguous query's coordinates, summed over
     // the heads in fp64.
-    const TQ* qL = reinterpret_cast<const TQ*>(a.q) + (qh0 * a.seq_len + tg + ln) * D + 8 * sl;
+    const TQ* qL = reinterpret_cast<const TQ*>(a.q) + (qrow0 + tg + ln) * D + 8 * sl;
     double qd[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) qd[e] = (double)(float)qL[e];
     for (int g = 1; g < nq; ++g) {
-      const TQ* qg = qL + g * a.seq_len * D;
+      const TQ* qg = qL + g * head_stride * D;
 #pragma unroll
       for (int e = 0; e < 8; ++e) qd[e] += (double)(float)qg[e];
     }
@@ -618,23 +621,34 @@ gate_topk_kernel(GateArgs a) {
   extern __shared__ __align__(16) char smem[];
   char* tile = smem;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int64_t wg_per_head = (a.seq_len + WGQ - 1) / WGQ;
-  // Within a head, workgroups run latest queries first: they scan the most
-  // blocks (causal), so the short ones fill the tail of the launch.
-  // Per-head gate: grp is a query head and reads key head grp / group.
-  // Shared gate: grp is a key/value head and routes its group of query heads.
-  const int64_t grp = blockIdx.x / wg_per_head;
+  static_assert(WGQ == 128, "the sequence table counts gate workgroups of 128 queries");
+  // Work item -> (sequence, routing row, workgroup). Per-head gate: the row
+  // is a query head, reading key head row / group. Shared gate: the row is
+  // a key/value head and routes its group of query heads.
+  const int64_t rows = SHARED ? a.kv_heads : a.heads;
+  const int64_t item = blockIdx.x;
+  const int64_t si = seq_find(a.sq, kSeqW128, rows, item, a.block_size);
+  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t wg_per_head = (sa.len + WGQ - 1) / WGQ;
+  const int64_t r_item = item - rows * seq_prefix(a.sq, si, kSeqW128, a.block_size);
+  const int64_t grp = r_item / wg_per_head;
   const int64_t kvh = SHARED ? grp : grp / a.group;
   const int64_t qh0 = SHARED ? grp * a.group : grp;
   const int nq = SHARED ? a.group : 1;
-  const int64_t qb = (wg_per_head - 1 - blockIdx.x % wg_per_head) * WGQ;
+  // Within a head, workgroups run latest queries first: they scan the most
+  // blocks (causal), so the short ones fill the tail of the launch.
+  const int64_t qb = (wg_per_head - 1 - r_item % wg_per_head) * WGQ;
+  const int64_t len = sa.len;
+  const int64_t qrow0 = sa.tok0 * a.heads + qh0 * len;    // row of token 0 in query head qh0
+  const int64_t kvb0 = sa.blk0 * a.kv_heads + kvh * sa.nb;  // the key head's first pooled key
   // The wave's queries t0 .. t0 + WQ - 1 (group g, lane column col: query
-  // t0 + 32 g + col) lie in one block, as block_size is a multiple of 64 and
-  // seq_len a multiple of block_size.
+  // t0 + 32 g + col) lie in one block, as block_size is a multiple of 64;
+  // lanes past the sequence's end (qvalid false) compute on its last query
+  // and write nothing.
   const int64_t t0 = qb + WQ * w;
-  const bool wave_on = t0 < a.seq_len;  // workgroup-uniform control flow below
+  const bool wave_on = t0 < len;  // workgroup-uniform control flow below
   const int64_t tw = wave_on ? t0 : qb;
-  const int NB = (int)a.n_blocks;
+  const int NB = (int)sa.nb;
   const int c = (int)(tw / a.block_size);
   const int n_elig = a.causal ? c : NB - 1;
   const int m = min(a.k_eff - 1, n_elig);
@@ -647,9 +661,9 @@ gate_topk_kernel(GateArgs a) {
   for (int g = 0; g < QG; ++g) {
     qnorm[g] = 0.f;
     if (scoring) {
-      const TQ* qrow = reinterpret_cast<const TQ*>(a.q) + (qh0 * a.seq_len + tw + 32 * g + col) * D;
+      const TQ* qrow = reinterpret_cast<const TQ*>(a.q) + (qrow0 + min<int64_t>(tw + 32 * g + col, len - 1)) * D;
       if constexpr (SHARED) {
-        qnorm[g] = qf[g].template load_sum<TQ>(qrow, a.seq_len * D, nq, h) * 1.0001f;
+        qnorm[g] = qf[g].template load_sum<TQ>(qrow, len * D, nq, h) * 1.0001f;
       } else {
         qf[g].load(qrow, h);
         float qss = qf[g].sumsq();
@@ -661,7 +675,7 @@ gate_topk_kernel(GateArgs a) {
   // Largest norm among the wave's scanned blocks, for the rounding bound:
   // the first 64 norms load now, under the scan; any others after it.
   const int jend = a.causal ? c : NB;  // this wave's scan bound
-  const float* nrm = a.norm + kvh * NB;
+  const float* nrm = a.norm + kvb0;
   float kmax = (scoring && lane < jend) ? nrm[lane] : 0.f;
   double L[QG][TT];
   float S[QG][TT];
@@ -673,7 +687,7 @@ gate_topk_kernel(GateArgs a) {
       S[g][i] = kNegInf;
     }
   // Scan bound of the whole workgroup (its last valid query has the largest c).
-  const int64_t t_last = min<int64_t>(qb + WGQ, a.seq_len) - 1;
+  const int64_t t_last = min<int64_t>(qb + WGQ, len) - 1;
   const int wg_jend = a.causal ? (int)(t_last / a.block_size) : NB;
   // Tile pipeline. Tile i sits in LDS buffer i & 1. Step i stores tile i+1
   // (fetched into registers one step earlier) to the other buffer, passes
@@ -686,17 +700,17 @@ gate_topk_kernel(GateArgs a) {
   typename Ops::Chunk stg[Ops::NLD];
   f32x16 acc_a[QG], acc_b[QG];
   if (ntiles > 0) {
-    Ops::fetch(stg, a, kvh, 0, tid);
+    Ops::fetch(stg, a, kvb0, NB, 0, tid);
     Ops::put(tile, stg, tid);
   }
   __syncthreads();
-  if (ntiles > 1) Ops::fetch(stg, a, kvh, kTileB, tid);
+  if (ntiles > 1) Ops::fetch(stg, a, kvb0, NB, kTileB, tid);
   if (my_tiles > 0) Ops::template scores<QG>(tile, col, h, qf, acc_a);
   auto step = [&](int i, f32x16(&cur)[QG], f32x16(&nxt)[QG]) {
     char* next_buf = tile + ((i + 1) & 1) * Ops::TILE_BYTES;
     if (i + 1 < ntiles) Ops::put(next_buf, stg, tid);
     __syncthreads();
-    if (i + 2 < ntiles) Ops::fetch(stg, a, kvh, (i + 2) * kTileB, tid);
+    if (i + 2 < ntiles) Ops::fetch(stg, a, kvb0, NB, (i + 2) * kTileB, tid);
     const bool do_next = i + 1 < my_tiles, do_cur = i < my_tiles;
     const int jt = i * kTileB, tis = i % kSegTiles;
     const int jb = jt + 4 * h;
@@ -728,6 +742,7 @@ gate_topk_kernel(GateArgs a) {
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     const int64_t t = tw + 32 * g + col;
+    const bool qvalid = t < len;
     int sel[TT];
     if (scoring) {
       // Merge the two lane halves (keys are distinct, so both halves end
@@ -753,13 +768,13 @@ gate_topk_kernel(GateArgs a) {
       const float eps = gam * qnorm[g] * kmax + 1e-30f;
       const bool amb = !(ls[m - 1] - ls[m] > 2.f * eps);
       const bool tracked = n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps;
-      rescore_ambiguous<TQ, D, TT>(a, qh0, nq, kvh, tw + 32 * g, c, jend, amb && h == 0, tracked, lj, sel, lane,
-                                   col);
+      rescore_ambiguous<TQ, D, TT>(a, qrow0, len, nq, kvb0, tw + 32 * g, c, jend, amb && h == 0 && qvalid, tracked,
+                                   lj, sel, lane, col);
     }
-    if (h == 0)
+    if (h == 0 && qvalid)
       for (int hq = 0; hq < nq; ++hq)
-        write_row<TT>(a.block_idx + ((qh0 + hq) * a.seq_len + t) * a.top_k, sel, scoring, m, c,
-                      a.causal ? c + 1 : NB, a.top_k);
+        write_row<TT>(a.block_idx + (qrow0 + hq * len + t) * a.top_k, sel, scoring, m, c, a.causal ? c + 1 : NB,
+                      a.top_k);
   }
 }
 
@@ -771,22 +786,28 @@ gate_topk_kernel(GateArgs a) {
 __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
   extern __shared__ __align__(16) char smem[];
   int* bins = reinterpret_cast<int*>(smem);
-  const int NB = (int)a.n_blocks;
-  const bool lds_bins = NB <= kLdsBinsMax;
-  const int64_t wg_per_head = (a.seq_len + kRankQ - 1) / kRankQ;
-  const int64_t bh = blockIdx.x / wg_per_head;
-  const int64_t q0 = (blockIdx.x % wg_per_head) * kRankQ;
+  // Work item -> (sequence, query head, chunk of kRankQ queries).
+  const int64_t item = blockIdx.x;
+  const int64_t si = seq_find(a.sq, kSeqW1024, a.heads, item, a.block_size);
+  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t per_head = (sa.len + kRankQ - 1) / kRankQ;
+  const int64_t r_item = item - a.heads * seq_prefix(a.sq, si, kSeqW1024, a.block_size);
+  const int64_t hq = r_item / per_head;
+  const int64_t q0 = (r_item % per_head) * kRankQ;
+  const int NB = (int)sa.nb;
+  const bool lds_bins = a.max_nb <= kLdsBinsMax;  // LDS holds max_nb bins when this is true
+  const int64_t row0 = sa.tok0 * a.heads + hq * sa.len;  // row of token 0 of this head
   const int slots = a.k_eff - 1;
-  int32_t* cnt = a.count + bh * NB;
+  int32_t* cnt = a.count + sa.blk0 * a.heads + hq * NB;
   if (lds_bins)
     for (int i = threadIdx.x; i < NB; i += 256) bins[i] = 0;
   __syncthreads();
   for (int qq = threadIdx.x; qq < kRankQ; qq += 256) {
     const int64_t t = q0 + qq;
-    if (t >= a.seq_len) break;
+    if (t >= sa.len) break;
     const int c = (int)(t / a.block_size);
-    const int32_t* row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
-    int32_t* rk = a.rank + (bh * a.seq_len + t) * (int64_t)slots;
+    const int32_t* row = a.block_idx + (row0 + t) * a.top_k;
+    int32_t* rk = a.rank + (row0 + t) * (int64_t)slots;
     const int cap = past_cap(c, NB, a.causal, a.k_eff);
     int s = 0;
     for (int i = 0; i < a.top_k && s < cap; ++i) {
@@ -805,10 +826,10 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
   __syncthreads();
   for (int qq = threadIdx.x; qq < kRankQ; qq += 256) {
     const int64_t t = q0 + qq;
-    if (t >= a.seq_len) break;
+    if (t >= sa.len) break;
     const int c = (int)(t / a.block_size);
-    const int32_t* row = a.block_idx + (bh * a.seq_len + t) * a.top_k;
-    int32_t* rk = a.rank + (bh * a.seq_len + t) * (int64_t)slots;
+    const int32_t* row = a.block_idx + (row0 + t) * a.top_k;
+    int32_t* rk = a.rank + (row0 + t) * (int64_t)slots;
     const int cap = past_cap(c, NB, a.causal, a.k_eff);
     int s = 0;
     for (int i = 0; i < a.top_k && s < cap; ++i) {
@@ -822,10 +843,7 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
 
 template <typename T, typename TQ, int D, int TT, bool SHARED>
 static void gate_go(const GateArgs& a, hipStream_t s) {
-  constexpr int WGQ = 4 * 32 * gate_groups<T, D, TT>();  // queries per workgroup
-  const int64_t wg_per_head = (a.seq_len + WGQ - 1) / WGQ;
-  const int64_t rows = SHARED ? a.bh / a.group : a.bh;
-  const dim3 grid((unsigned)(rows * wg_per_head));
+  const dim3 grid((unsigned)a.gate_wgs);
   const int lds = 2 * GateOps<T, D>::TILE_BYTES;
   hipLaunchKernelGGL((gate_topk_kernel<T, TQ, D, TT, SHARED>), grid, dim3(256), lds, s, a);
 }
@@ -852,11 +870,11 @@ static hipError_t gate_launch_t(const GateArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.k_eff < 2) return e;
-  const int64_t rank_wgs = a.bh * ((a.seq_len + kRankQ - 1) / kRankQ);
-  const int rank_lds = a.n_blocks <= kLdsBinsMax ? (int)a.n_blocks * 4 : 0;
+  static_assert(kRankQ == 1024, "the sequence table counts rank workgroups of 1024 queries");
+  const int rank_lds = a.max_nb <= kLdsBinsMax ? (int)a.max_nb * 4 : 0;
   {
     KernelTimer timer(s, "rank");
-    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)rank_wgs), dim3(256), rank_lds, s, a);
+    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)a.rank_wgs), dim3(256), rank_lds, s, a);
   }
   return hipGetLastError();
 }

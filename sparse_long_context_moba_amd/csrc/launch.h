@@ -7,6 +7,33 @@ namespace moba {
 
 typedef __bf16 bf16;
 
+// The sequences one launch covers: a batch of equal-length sequences
+// (tab == nullptr: every sequence has `len` tokens) or a varlen batch whose
+// per-sequence prefix sums sit in a small device table. Tensors hold the
+// sequences back to back, sequence i as [heads, len_i, ...] from token
+// offset tok0_i, so a query head's row of token t is tok0_i * heads +
+// h * len_i + t, and per-block arrays number the blocks of sequence i from
+// blk0_i * heads + h * nb_i (nb_i = ceil(len_i / block_size)).
+// Table row i (0 <= i <= n) holds the sums over the sequences before i;
+// row n holds the totals.
+enum SeqCol { kSeqTok = 0, kSeqBlk = 1, kSeqW64 = 2, kSeqW128 = 3, kSeqW1024 = 4 };
+constexpr int kSeqCols = 8;
+struct Seqs {
+  const int64_t* tab;  // [(n + 1) * kSeqCols] or nullptr (uniform)
+  int64_t n;           // sequences
+  int64_t len;         // tokens per sequence when uniform
+};
+
+// Units of column col for one sequence of len tokens.
+__host__ __device__ __forceinline__ int64_t seq_units(int col, int64_t len, int64_t block_size) {
+  switch (col) {
+    case kSeqTok: return len;
+    case kSeqBlk: return (len + block_size - 1) / block_size;
+    case kSeqW64: return (len + 63) / 64;
+    case kSeqW128: return (len + 127) / 128;
+    default: return (len + 1023) / 1024;
+  }
+}
 // Past blocks one query may keep when top_k < n_blocks (register top-k limit).
 constexpr int kMaxSlotsHost = 16;
 
@@ -22,17 +49,19 @@ struct KernelTimer {
 
 struct PoolArgs {
   const void* k;
-  int64_t bh, seq_len, block_size;
+  Seqs sq;           // the sequences (k is [tokens of sequence i][kv_heads] head-major per sequence)
+  int64_t kv_heads, block_size;
+  int64_t kv_blocks;  // kv_heads * total blocks: the launch's work items
   int head_dim;
   bool bf16_in;
   int pooling;       // moba_pooling_t: mean, max, or mean + max per coordinate
-  double* kbar64;    // [bh * nb, D]
-  float* kbar32;     // [bh * nb, D]
-  bf16* kbar_hi;     // [bh * nb, D]
-  bf16* kbar_lo;     // [bh * nb, D]
-  float* norm;       // [bh * nb] L2 norm of each pooled key, rounded up
-  int32_t* count;    // [bh * group * nb] the gate's per-block query counts: the pool zeroes them
-  int group;         // query heads per key/value head (bh counts key/value heads here)
+  double* kbar64;    // [kv blocks, D]
+  float* kbar32;     // [kv blocks, D]
+  bf16* kbar_hi;     // [kv blocks, D]
+  bf16* kbar_lo;     // [kv blocks, D]
+  float* norm;       // [kv blocks] L2 norm of each pooled key, rounded up
+  int32_t* count;    // [query-head blocks] the gate's per-block query counts: the pool zeroes them
+  int group;         // query heads per key/value head
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 
@@ -42,34 +71,43 @@ struct GateArgs {
   const float* kbar32;
   const bf16* kbar_hi;
   const bf16* kbar_lo;
-  const float* norm;  // [bh * nb] L2 norm of each pooled key, rounded up
-  int64_t bh, seq_len, block_size, n_blocks;
+  const float* norm;   // [kv blocks] L2 norm of each pooled key, rounded up
+  Seqs sq;             // the sequences
+  int64_t heads, kv_heads, block_size;
+  int64_t max_nb;      // most blocks of any sequence (LDS bins of the rank kernel)
+  int64_t gate_wgs;    // workgroups of the gate: (kv_heads if shared else heads) * sum ceil(len / 128)
+  int64_t rank_wgs;    // workgroups of the rank kernel: heads * sum ceil(len / 1024)
   int head_dim;
   bool bf16_in;
   bool causal;
   int top_k;        // columns of block_idx
-  int k_eff;        // min(top_k, n_blocks)
-  int32_t* block_idx;  // [bh, S, top_k]
-  int32_t* count;      // [bh * nb], zeroed before the launch
-  int32_t* rank;       // [bh, S, k_eff - 1]: position of (t, slot) in its block's list
-  int group;           // query heads per key/value head: query head bh pools key head bh / group
+  int k_eff;        // min(top_k, n_blocks of the longest sequence) (see api.cpp)
+  int32_t* block_idx;  // [query rows, top_k]
+  int32_t* count;      // [query-head blocks], zeroed before the launch
+  int32_t* rank;       // [query rows, k_eff - 1]: position of (row, slot) in its block's list
+  int group;           // query heads per key/value head
   bool shared;         // the group routes once, on the sum of its heads' scores
+  // Uniform batch fields, read only by the backward's ordered ranks:
+  int64_t bh, seq_len, n_blocks;
 };
 hipError_t launch_gate(const GateArgs& a, hipStream_t s);
 
 struct PackArgs {
-  int64_t bh, seq_len, block_size, n_blocks;
+  Seqs sq;                    // the sequences
+  int64_t heads, block_size;
+  int64_t rows;               // query rows: heads * total tokens
+  int64_t q_blocks;           // query-head blocks: heads * total blocks
   bool causal;
   int top_k, k_eff;
   int tile_m;                 // queries per gather tile
-  const int32_t* block_idx;   // [bh, S, top_k]
-  const int32_t* count;       // [bh * nb]
-  const int32_t* rank;        // [bh, S, k_eff - 1]
-  int32_t* offset;            // [bh * nb + 1] exclusive scan of count
-  int32_t* tile_start;        // [bh * nb + 1] exclusive scan of ceil(count / tile_m)
-  int32_t* qlist;             // [pairs]: t * (k_eff - 1) + slot
+  const int32_t* block_idx;   // [rows, top_k]
+  const int32_t* count;       // [q_blocks]
+  const int32_t* rank;        // [rows, k_eff - 1]
+  int32_t* offset;            // [q_blocks + 1] exclusive scan of count
+  int32_t* tile_start;        // [q_blocks + 1] exclusive scan of ceil(count / tile_m)
+  int32_t* qlist;             // [pairs]: row * (k_eff - 1) + slot (row: global query row)
   int64_t grid;               // gather workgroups (a multiple of 8)
-  int32_t* tile_map;          // [grid][4]: per gather workgroup {block, e0, e1, 0}, block -1 if idle
+  int32_t* tile_map;          // [grid][4]: per gather workgroup {block, e0, e1, sequence}, block -1 if idle
 };
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 
@@ -78,7 +116,9 @@ struct AttnArgs {
   const void* k;
   const void* v;
   void* o;
-  int64_t bh, seq_len, block_size, n_blocks;
+  Seqs sq;                    // the sequences
+  int64_t heads, block_size;
+  int64_t diag_wgs;           // own-block (or dense) workgroups: heads * sum ceil(len / tile)
   int head_dim;
   bool bf16_in;
   bool causal;
@@ -87,11 +127,14 @@ struct AttnArgs {
   const int32_t* qlist;
   const int32_t* tile_map;    // see PackArgs
   int64_t gather_grid;        // gather workgroups
-  void* part_o;               // [bh, S, k_eff - 1, D] in the input dtype, lane-native order
-  float* part_lse;            // [bh, S, k_eff - 1], log2 domain
-  int group;                  // query heads per key/value head: k, v of query head bh are head bh / group
-  float* lse_out;             // optional [bh, S]: natural-log log-sum-exp per query (own-block kernel)
+  void* part_o;               // [query rows, k_eff - 1, D] in the input dtype, lane-native order
+  float* part_lse;            // [query rows, k_eff - 1], log2 domain
+  int group;                  // query heads per key/value head
+  float* lse_out;             // optional [query rows]: natural-log log-sum-exp per query (own-block kernel)
 };
+// Queries per own-block (and dense) tile: 128 where tiles of 128 stay in
+// one block (block_size a multiple of 128, or dense attention), else 64.
+inline int diag_tile(int64_t block_size, bool dense) { return (dense || block_size % 128 == 0) ? 128 : 64; }
 constexpr int kGatherTileM = 128;
 // Gather workgroups for a bound on the number of tiles (a multiple of the
 // 8 XCDs, see tile_map_kernel).

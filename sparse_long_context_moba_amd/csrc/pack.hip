@@ -10,7 +10,8 @@
 //                 tile starts) over all heads and blocks.
 //  pack_scatter — one thread per query: places each of its kept past blocks
 //                 into that block's list at offset + rank, where rank came
-//                 from the gate's atomic count. Entries are t*(k_eff-1)+slot.
+//                 from the gate's atomic count. Entries are
+//                 row*(k_eff-1)+slot, row being the query's global row.
 //                 The same launch writes the tile map: one thread per gather
 //                 workgroup, its tile, block and list range (see tile_map).
 #include "common.h"
@@ -58,13 +59,13 @@ __global__ __launch_bounds__(1024) void pack_scan_kernel(const int32_t* __restri
   }
 }
 
-// Gather workgroup w's tile and that tile's block and list range, so the
-// gather kernel starts with one load. Tiles are dealt to workgroups so that
-// each of the 8 XCDs (workgroups go round robin over them) gets one
+// Gather workgroup w's tile and that tile's block, list range and sequence,
+// so the gather kernel starts with one load. Tiles are dealt to workgroups
+// so that each of the 8 XCDs (workgroups go round robin over them) gets one
 // contiguous range of tiles, which keeps a block's K/V in one L2:
 // tile L = (w % 8) * chunk + w / 8.
 __device__ void tile_map(const PackArgs& a, int64_t w) {
-  const int64_t nblk = a.bh * a.n_blocks;
+  const int64_t nblk = a.q_blocks;
   const int64_t total = a.tile_start[nblk];
   const int64_t chunk = (total + 7) / 8;
   const int64_t li = w / 8, L = (w % 8) * chunk + li;
@@ -85,32 +86,37 @@ __device__ void tile_map(const PackArgs& a, int64_t w) {
   out[0] = (int32_t)lo;
   out[1] = e0;
   out[2] = e1;
-  out[3] = 0;
+  out[3] = (int32_t)seq_find(a.sq, kSeqBlk, a.heads, lo, a.block_size);
 }
 
+// One thread per query row (global: sequence, head, token): each kept past
+// block's list gets the entry row * (k_eff - 1) + slot at offset + rank.
 __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q < a.grid) tile_map(a, q);
-  if (q >= a.bh * a.seq_len) return;
-  const int64_t bh = q / a.seq_len, t = q % a.seq_len;
+  if (q >= a.rows) return;
+  const int64_t si = seq_find(a.sq, kSeqTok, a.heads, q, a.block_size);
+  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t r = q - a.heads * sa.tok0;
+  const int64_t h = r / sa.len, t = r % sa.len;
   const int c = (int)(t / a.block_size);
   const int slots = a.k_eff - 1;
   const int32_t* row = a.block_idx + q * a.top_k;
   const int32_t* rk = a.rank + q * slots;
-  const int cap = past_cap(c, a.n_blocks, a.causal, a.k_eff);
+  const int64_t blk0 = sa.blk0 * a.heads + h * sa.nb;  // this head's first block
+  const int cap = past_cap(c, sa.nb, a.causal, a.k_eff);
   int s = 0;
   for (int i = 0; i < a.top_k && s < cap; ++i) {
     const int j = row[i];
     if (j < 0) break;
-    if (!routed_past_block(j, c, a.n_blocks, a.causal)) continue;
-    const int64_t blk = bh * a.n_blocks + j;
-    a.qlist[a.offset[blk] + rk[s]] = (int32_t)(t * slots + s);
+    if (!routed_past_block(j, c, sa.nb, a.causal)) continue;
+    a.qlist[a.offset[blk0 + j] + rk[s]] = (int32_t)(q * slots + s);
     ++s;
   }
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
-  const int64_t n = a.bh * a.n_blocks;
+  const int64_t n = a.q_blocks;
   {
     KernelTimer t(s, "pack_scan");
     hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(1024), 0, s, a.count, n, a.tile_m, a.offset,
@@ -118,8 +124,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nq = a.bh * a.seq_len;
-  const int64_t nt = nq > a.grid ? nq : a.grid;  // threads: queries and tile-map entries
+  const int64_t nt = a.rows > a.grid ? a.rows : a.grid;  // threads: query rows and tile-map entries
   {
     KernelTimer t(s, "pack_scatter");
     hipLaunchKernelGGL(pack_scatter_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a);

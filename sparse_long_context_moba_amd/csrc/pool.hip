@@ -21,7 +21,9 @@
 
 namespace moba {
 
-// U rows per thread are loaded before they are accumulated (in row order).
+// U rows per thread are loaded before they are accumulated (in row order);
+// a block's last pass loads only the rows it holds (a block can hold any
+// number of tokens from 1 to block_size).
 // MODE selects the summary (moba_pooling_t): 0 mean, 1 max, 2 mean + max.
 // The max is exact in any order (fp32 holds every input value).
 template <typename T, int D, int U, int MODE>
@@ -35,12 +37,16 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ double sq[D];
   const int tid = threadIdx.x;
   const int rg = tid / TPR, cv = tid % TPR;
-  const int64_t blk = blockIdx.x;  // bh * n_blocks + j
-  const int64_t nb = (a.seq_len + a.block_size - 1) / a.block_size;
-  const int64_t bh = blk / nb, j = blk % nb;
-  // Rows of block j; a short last block holds the remaining tokens.
-  const int Bs = (int)min<int64_t>(a.block_size, a.seq_len - j * a.block_size);
-  const T* base = reinterpret_cast<const T*>(a.k) + (bh * a.seq_len + j * a.block_size) * D + cv * VEC;
+  // Work item: one block of one key/value head of one sequence.
+  const int64_t blk = blockIdx.x;  // the block's index in the pooled-key arrays
+  const int64_t si = seq_find(a.sq, kSeqBlk, a.kv_heads, blk, a.block_size);
+  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t r = blk - a.kv_heads * sa.blk0;
+  const int64_t hk = r / sa.nb, j = r % sa.nb;
+  // Rows of block j; the sequence's last block holds the remaining tokens.
+  const int Bs = (int)min<int64_t>(a.block_size, sa.len - j * a.block_size);
+  const T* base = reinterpret_cast<const T*>(a.k) + (sa.tok0 * a.kv_heads + hk * sa.len + j * a.block_size) * D +
+                  cv * VEC;
   double acc[VEC];
   float mx[VEC];
 #pragma unroll
@@ -52,25 +58,30 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     if (SUM) acc[e] += (double)x;
     if (MAX) mx[e] = fmaxf(mx[e], x);
   };
-  for (int r0 = rg; r0 < Bs; r0 += U * RG) {
-    u32x4 raw[U];
+  auto take_row = [&](const u32x4& raw) {
+    if constexpr (sizeof(T) == 2) {
+      const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + u * RG) * D);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if constexpr (sizeof(T) == 2) {
-        const unsigned w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          take(2 * e, __uint_as_float(w[e] << 16));
-          take(2 * e + 1, __uint_as_float(w[e] & 0xffff0000u));
-        }
-      } else {
-        take(0, __uint_as_float(raw[u].x));
-        take(1, __uint_as_float(raw[u].y));
-        take(2, __uint_as_float(raw[u].z));
-        take(3, __uint_as_float(raw[u].w));
+      for (int e = 0; e < 4; ++e) {
+        take(2 * e, __uint_as_float(w[e] << 16));
+        take(2 * e + 1, __uint_as_float(w[e] & 0xffff0000u));
       }
+    } else {
+      take(0, __uint_as_float(raw.x));
+      take(1, __uint_as_float(raw.y));
+      take(2, __uint_as_float(raw.z));
+      take(3, __uint_as_float(raw.w));
+    }
+  };
+  for (int r0 = rg; r0 < Bs; r0 += U * RG) {
+    if (r0 + (U - 1) * RG < Bs) {
+      u32x4 raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + u * RG) * D);
+#pragma unroll
+      for (int u = 0; u < U; ++u) take_row(raw[u]);
+    } else {
+      for (int u = 0; r0 + u * RG < Bs; ++u) take_row(*reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + u * RG) * D));
     }
   }
 #pragma unroll
@@ -108,26 +119,17 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     a.norm[blk] = nrm;
   }
   // Every query head that reads this key/value head keeps its own list.
-  for (int g = tid; g < a.group; g += 256) a.count[(bh * a.group + g) * nb + j] = 0;
+  const int64_t heads = a.kv_heads * a.group;
+  for (int g = tid; g < a.group; g += 256) a.count[sa.blk0 * heads + (hk * a.group + g) * sa.nb + j] = 0;
 }
 
 template <typename T, int D>
 static hipError_t pool_launch_t(const PoolArgs& a, hipStream_t s) {
-  constexpr int RG = 256 / (D / (16 / (int)sizeof(T)));
-  const int64_t nb = (a.seq_len + a.block_size - 1) / a.block_size;
-  const int64_t nblk = a.bh * nb;
-  const int64_t last = a.seq_len - (nb - 1) * a.block_size;  // rows of the last block
-  // block_size is a multiple of 64, so the rows per thread are a multiple of
-  // 64 / RG >= 2; use 4 loads in flight where they divide evenly.
-  const bool four = (a.block_size / RG) % 4 == 0 && (last / RG) % 4 == 0;
   KernelTimer t(s, "pool");
-  const dim3 grid((unsigned)nblk);
-  switch (a.pooling * 2 + (four ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((pool_kernel<T, D, 2, 0>), grid, dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((pool_kernel<T, D, 4, 0>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((pool_kernel<T, D, 2, 1>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((pool_kernel<T, D, 4, 1>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((pool_kernel<T, D, 2, 2>), grid, dim3(256), 0, s, a); break;
+  const dim3 grid((unsigned)a.kv_blocks);
+  switch (a.pooling) {
+    case 0: hipLaunchKernelGGL((pool_kernel<T, D, 4, 0>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((pool_kernel<T, D, 4, 1>), grid, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL((pool_kernel<T, D, 4, 2>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();

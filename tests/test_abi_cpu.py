@@ -88,7 +88,6 @@ FAKE = 0x1000  # never dereferenced: validation fails or stops before any launch
     (dict(seq_len=0), 2, "seq_len"),
     (dict(head_dim=0), 2, "head_dim"),
     (dict(block_size=0), 2, "block_size"),
-    (dict(seq_len=1000), 5, "multiple of 64"),
     (dict(top_k=0), 3, "top_k"),
     (dict(pooling=3), 3, "pooling"),
     (dict(pooling=-1), 3, "pooling"),
@@ -125,7 +124,7 @@ def test_null_pointers_and_workspace():
     assert _lib.moba_forward(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 6
     assert _lib.moba_forward(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == 6
     assert _lib.moba_forward(_p(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, need, None) == 6
-    assert _lib.moba_dense_forward(_p(seq_len=1000, block_size=1000), FAKE, FAKE, FAKE, FAKE, None) == 5
+    assert _lib.moba_dense_forward(_p(seq_len=1000, block_size=1000, head_dim=96), FAKE, FAKE, FAKE, FAKE, None) == 5
     assert _lib.moba_dense_forward(_p(), None, FAKE, FAKE, FAKE, None) == 1
     assert _lib.moba_debug_pool(_p(), FAKE, None, FAKE, need, None) == 1
     assert _lib.moba_debug_gate_topk(_p(), FAKE, FAKE, None, FAKE, need, None) == 1
@@ -165,14 +164,20 @@ def test_varlen_validation_and_workspace():
     p = _p(batch=3, seq_len=1792, block_size=128)
     st, need = _lib.moba_workspace_size_varlen(p, cu)
     assert st == 0, _lib.moba_last_error()
+    # one launch chain for the whole batch: its workspace holds every
+    # sequence's lists and partials at once (more than the largest alone)
     per = [_lib.moba_workspace_size(_p(batch=1, seq_len=b - a, block_size=128))[1] for a, b in zip(cu, cu[1:])]
-    assert need == max(per)
+    assert need > max(per)
+    # a one-sequence varlen batch needs the single problem's workspace plus its table
+    st1, one = _lib.moba_workspace_size_varlen(_p(batch=1, seq_len=1000, block_size=128), [0, 1000])
+    assert st1 == 0 and one >= _lib.moba_workspace_size(_p(batch=1, seq_len=1000, block_size=128))[1]
+    big = 1 << 27
     cases = [
         (dict(cu=None), 1, "cu_seqlens"),
         (dict(cu=[1, 576, 1600, 1792]), 3, "cu_seqlens[0]"),
         (dict(p=_p(batch=2, seq_len=1792, block_size=128)), 3, "batch"),
         (dict(p=_p(batch=3, seq_len=1700, block_size=128)), 3, "seq_len"),
-        (dict(cu=[0, 600, 1600, 1792], p=_p(batch=3, seq_len=1792, block_size=128)), 5, "sequence 0"),
+        (dict(cu=[0, 600, 600 + big, 700 + big], p=_p(batch=3, seq_len=700 + big, block_size=128)), 5, "2^27"),
         (dict(cu=[0, 576, 576, 1792]), 2, "sequence 1"),
     ]
     for kw, code, word in cases:
@@ -187,6 +192,20 @@ def test_varlen_validation_and_workspace():
     # too small a workspace is rejected before any launch
     assert _lib.moba_forward_varlen(p, cu, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 6
     assert _lib.moba_forward_varlen(p, cu, None, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+
+
+def test_any_sequence_length_is_accepted():
+    """Lengths need not be multiples of 64 (a partial last tile of queries
+    and keys is masked); block_size still must be. The backward keeps the
+    multiple-of-64 rule."""
+    from sparse_long_context_moba_amd import _lib
+    for S, Bs in ((1000, 128), (77, 64), (1, 64), (2049, 512), (33023, 512)):
+        st, n = _lib.moba_workspace_size(_p(seq_len=S, block_size=Bs))
+        assert st == 0 and n > 0, (S, Bs, _lib.moba_last_error())
+    st, _ = _lib.moba_backward_workspace_size(_p(seq_len=1000, block_size=128))
+    assert st == 5 and "multiple of 64" in _lib.moba_last_error()
+    st, _ = _lib.moba_workspace_size_varlen(_p(batch=3, seq_len=3126, block_size=64), [0, 1000, 1077, 3126])
+    assert st == 0, _lib.moba_last_error()
 
 
 def test_struct_layout_matches_header():

@@ -67,6 +67,16 @@ CASES = [
     ("f32-d64-bs128-short64-k4", 23, 1, 1, 576, 64, 128, 4, True, "f32"),
     ("bf16-d64-bs192-short128-noncausal", 24, 1, 2, 704, 64, 192, 2, False, "bf16"),
     ("bf16-d64-bs128-short64-topk-all", 25, 1, 1, 704, 64, 128, 9, True, "bf16"),
+    # any length: partial last tiles of queries and keys (not multiples of 64)
+    ("bf16-d128-bs128-len1000", 26, 1, 2, 1000, 128, 128, 3, True, "bf16"),
+    ("bf16-d64-bs64-len77", 27, 1, 2, 77, 64, 64, 3, True, "bf16"),
+    ("f32-d128-bs256-len2049-noncausal", 28, 1, 1, 2049, 128, 256, 3, False, "f32"),
+    ("bf16-d128-bs512-len2049-noncausal-1token-block", 29, 1, 2, 2049, 128, 512, 2, False, "bf16"),
+    ("bf16-d64-bs192-len1001-k4", 30, 1, 2, 1001, 64, 192, 4, True, "bf16"),
+    ("bf16-d128-len1", 31, 2, 1, 1, 128, 64, 3, True, "bf16"),
+    ("f32-d64-bs64-len130-topk-all", 32, 1, 1, 130, 64, 64, 9, True, "f32"),
+    ("bf16-d128-bs64-len1000-k17", 33, 1, 1, 1000, 128, 64, 17, True, "bf16"),
+    ("f32-d64-bs128-len333-noncausal", 34, 1, 2, 333, 64, 128, 2, False, "f32"),
 ]
 
 
@@ -90,6 +100,23 @@ def test_topk_at_least_blocks_equals_dense(dtype, causal):
         ref = orc.dense_attention(q[0, h], k[0, h], v[0, h], causal)
         assert np.abs(od[0, h] - ref).max() <= tol
         assert np.abs(o[0, h] - ref).max() <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("S", [1000, 77, 1])
+def test_dense_any_length(dtype, causal, S):
+    """The dense kernel on lengths that are not multiples of 64 (a partial
+    last tile of queries and keys), every row against the oracle."""
+    import sparse_long_context_moba_amd as moba
+    q, k, v = _inputs(40 + S, 1, 2, S, 128 if dtype == "bf16" else 64, 64, dtype)
+    say(f"[gpu] dense any length: S={S} causal={causal} {dtype}")
+    od = moba.dense(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), causal).float().cpu().numpy()
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for h in range(2):
+        ref = orc.dense_attention(q[0, h], k[0, h], v[0, h], causal)
+        err = np.abs(od[0, h] - ref).max()
+        assert err <= tol, f"h={h}: max|o - oracle| = {err:.3e}"
 
 
 def test_exact_ties_prefer_lower_block():
@@ -230,27 +257,49 @@ def test_errors_raise_and_leave_outputs():
 
 
 VARLEN_CASES = [
-    # label, seed, H, D, Bs, top_k, causal, dtype, lengths
-    ("bf16-d128-bs128-causal", 30, 2, 128, 128, 3, True, "bf16", [576, 1024, 192]),
-    ("f32-d64-bs256-noncausal", 31, 1, 64, 256, 2, False, "f32", [512, 64, 1344]),
+    # label, seed, H, Hkv, D, Bs, top_k, causal, dtype, lengths
+    ("bf16-d128-bs128-causal", 30, 2, 2, 128, 128, 3, True, "bf16", [576, 1024, 192]),
+    ("f32-d64-bs256-noncausal", 31, 1, 1, 64, 256, 2, False, "f32", [512, 64, 1344]),
+    # ragged lengths (not multiples of 64), mixed in one batch
+    ("bf16-d128-bs128-causal-ragged", 32, 2, 2, 128, 128, 3, True, "bf16", [1000, 77, 2049]),
+    ("bf16-d128-bs128-noncausal-ragged", 33, 2, 2, 128, 128, 3, False, "bf16", [1000, 77, 2049]),
+    ("f32-d64-bs64-noncausal-ragged", 34, 1, 1, 64, 64, 3, False, "f32", [77, 1000, 1, 2049]),
+    ("bf16-d64-bs192-causal-ragged-k4", 35, 2, 2, 64, 192, 4, True, "bf16", [1001, 64, 513]),
+    ("bf16-d128-bs64-causal-gqa2-ragged", 36, 4, 2, 128, 64, 3, True, "bf16", [300, 1, 129, 700]),
 ]
+
+
+def _varlen_inputs(seed, H, Hkv, n, D, Bs, dtype):
+    q, k, v = _inputs(seed, 1, H, n, D, Bs, dtype)
+    return q, k[:, :Hkv].copy(), v[:, :Hkv].copy()
 
 
 @pytest.mark.parametrize("case", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
 def test_varlen_batch(case):
-    """A varlen batch: every sequence routed and attended on its own (blocks
-    start at its first token), every row against the oracle for that
-    sequence alone, and bit-identical to one forward per sequence."""
+    """A varlen batch in one launch chain: every sequence routed and attended
+    on its own (blocks start at its first token), every row against the
+    oracle for that sequence alone, bit-identical to one forward per
+    sequence, and the same kernel launches as a single-sequence forward."""
     import sparse_long_context_moba_amd as moba
-    label, seed, H, D, Bs, top_k, causal, dtype, lengths = case
-    seqs = [_inputs(seed + i, 1, H, n, D, Bs, dtype) for i, n in enumerate(lengths)]
+    label, seed, H, Hkv, D, Bs, top_k, causal, dtype, lengths = case
+    G = H // Hkv
+    seqs = [_varlen_inputs(seed + i, H, Hkv, n, D, Bs, dtype) for i, n in enumerate(lengths)]
     dev = [[to_dev(x, dtype) for x in s] for s in seqs]
     qp, cu = moba.pack_varlen([d[0] for d in dev])
     kp, _ = moba.pack_varlen([d[1] for d in dev])
     vp, _ = moba.pack_varlen([d[2] for d in dev])
     say(f"[gpu] varlen {label}: lengths={lengths} cu={cu}")
-    o, idx = moba.forward_varlen(qp, kp, vp, cu, H, Bs, top_k, causal)
-    torch.cuda.synchronize()
+    with moba.timing() as tm:
+        o, idx = moba.forward_varlen(qp, kp, vp, cu, H, Bs, top_k, causal, kv_heads=Hkv)
+        torch.cuda.synchronize()
+    launches = {name: n for name, n, _ in tm.rows}
+    with moba.timing() as tm1:
+        moba.forward(dev[0][0], dev[0][1], dev[0][2], Bs, top_k, causal)
+        torch.cuda.synchronize()
+    launches1 = {name: n for name, n, _ in tm1.rows}
+    # one chain for the batch (a single sequence can skip the gather when it keeps no past block)
+    assert all(n == 1 for n in launches.values()), launches
+    assert set(launches1) <= set(launches), (launches, launches1)
     os_ = moba.unpack_varlen(o, cu, H)
     is_ = moba.unpack_varlen(idx, cu, H)
     for i, ((q, k, v), d) in enumerate(zip(seqs, dev)):
@@ -261,7 +310,7 @@ def test_varlen_batch(case):
         og = os_[i].float().cpu().numpy()
         ig = is_[i].cpu().numpy()
         for h in range(H):
-            res = orc.forward_head(q[0, h], k[0, h], v[0, h], Bs, top_k, causal)
-            check_rows(og[0, h], ig[0, h], res, np.arange(lengths[i]), q[0, h], k[0, h], v[0, h], Bs, top_k,
-                       causal, dtype, label=f"{label} seq={i} h={h}")
-    say(f"[gpu] varlen {label}: ok")
+            res = orc.forward_head(q[0, h], k[0, h // G], v[0, h // G], Bs, top_k, causal)
+            check_rows(og[0, h], ig[0, h], res, np.arange(lengths[i]), q[0, h], k[0, h // G], v[0, h // G], Bs,
+                       top_k, causal, dtype, label=f"{label} seq={i} h={h}")
+    say(f"[gpu] varlen {label}: ok, launches {launches}")
