@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Uniform values (readfirstlane) keep the K/V bases in SGPRs.
   const int64_t blk = __builtin_amdgcn_readfirstlane(tm.x);  // the block among all query heads' blocks
   const int64_t si = __builtin_amdgcn_readfirstlane(tm.w);
-  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const SeqAt sa = seq_at_u(a.sq, si, a.block_size);
   const int64_t rb = blk - a.heads * sa.blk0;
   const int64_t hq = rb / sa.nb, j = rb % sa.nb;
   const int64_t e0 = __builtin_amdgcn_readfirstlane(tm.y), e1 = __builtin_amdgcn_readfirstlane(tm.z);
@@ -117,10 +117,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int COL = M == 128 ? kSeqW128 : kSeqW64;
   static_assert(M == 128 || M == 64, "tiles of 64 or 128 queries");
   const int64_t item = blockIdx.x;
-  const int64_t si = seq_find(a.sq, COL, a.heads, item, a.block_size);
-  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t si = seq_find_u(a.sq, COL, a.heads, item, a.block_size);
+  const SeqAt sa = seq_at_u(a.sq, si, a.block_size);
   const int64_t ntile = (sa.len + M - 1) / M;
-  const int64_t r_item = item - a.heads * seq_prefix(a.sq, si, COL, a.block_size);
+  const int64_t r_item = item - a.heads * seq_prefix_u(a.sq, si, COL, a.block_size);
   const int64_t tile = ntile - 1 - r_item / a.heads;
   const int64_t hq = r_item % a.heads;
   const int len = (int)sa.len;

@@ -99,6 +99,27 @@ __device__ __forceinline__ SeqAt seq_at(const Seqs& s, int64_t i, int64_t block_
   return r;
 }
 
+// A value the whole wave holds alike, marked so for the compiler (a value
+// loaded from the sequence table is otherwise taken as per-lane, which
+// turns the branches that depend on it into masked ones and defeats the
+// instruction scheduling of the loops behind them).
+__device__ __forceinline__ int64_t wave_uniform(int64_t x) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+// seq_find and seq_at for a work item the whole workgroup shares.
+__device__ __forceinline__ int64_t seq_find_u(const Seqs& s, int col, int64_t per, int64_t item, int64_t block_size) {
+  return wave_uniform(seq_find(s, col, per, wave_uniform(item), block_size));
+}
+__device__ __forceinline__ SeqAt seq_at_u(const Seqs& s, int64_t i, int64_t block_size) {
+  const SeqAt r = seq_at(s, wave_uniform(i), block_size);
+  return SeqAt{wave_uniform(r.tok0), wave_uniform(r.len), wave_uniform(r.blk0), wave_uniform(r.nb)};
+}
+__device__ __forceinline__ int64_t seq_prefix_u(const Seqs& s, int64_t i, int col, int64_t block_size) {
+  return wave_uniform(seq_prefix(s, wave_uniform(i), col, block_size));
+}
+
 template <typename T>
 struct io;
 template <>

@@ -4,6 +4,8 @@
 // P.V steps and the subtile streams. Everything is in an anonymous
 // namespace: each translation unit that includes it gets its own copy.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -611,19 +613,26 @@ __device__ __forceinline__ void mask_rows(f32x16 (&s)[2], int nvalid, int h) {
 // prefetch into registers and use one buffer.
 // start() runs once the first subtile's loads are queued (work whose own
 // loads should overlap them: the query rows, the merge's partials).
-template <class E, int NT, class S, class F>
-__device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const typename E::T* kp,
-                                                const typename E::T* vp, int nsub, int last_rows, int D, int tid,
-                                                S&& start, F&& compute) {
-  auto rows_of = [&](int sub) { return sub == nsub - 1 ? last_rows : kSub; };
+template <class E, int NT, bool TAIL, class S, class F>
+__device__ __forceinline__ void stream_subtiles_t(char* bufA, char* bufB, const typename E::T* kp,
+                                                  const typename E::T* vp, int nsub, int last_rows, int D, int tid,
+                                                  S&& start, F&& compute) {
+  // Without a partial last subtile (TAIL false) every subtile holds 64 rows
+  // and the loop carries no tail logic.
+  auto rows_of = [&](int sub) { return (TAIL && sub == nsub - 1) ? last_rows : kSub; };
   if constexpr (E::kDMA) {
     // Direct loads from wave-uniform bases with per-lane offsets computed
     // once (no per-load address arithmetic).
     typename E::template LoadOffsets<NT> lo;
     E::template load_offsets<NT>(lo, tid);
     auto issue = [&](int sub, char* buf) {
-      load_subtile<E, NT, false>(kp + sub * (int64_t)kSub * D, lo, buf, tid, rows_of(sub));
-      load_subtile<E, NT, true>(vp + sub * (int64_t)kSub * D, lo, buf + E::TB, tid, rows_of(sub));
+      if (TAIL) {
+        load_subtile<E, NT, false>(kp + sub * (int64_t)kSub * D, lo, buf, tid, rows_of(sub));
+        load_subtile<E, NT, true>(vp + sub * (int64_t)kSub * D, lo, buf + E::TB, tid, rows_of(sub));
+      } else {
+        E::template begin_uniform<NT, false>(kp + sub * (int64_t)kSub * D, lo, buf, tid);
+        E::template begin_uniform<NT, true>(vp + sub * (int64_t)kSub * D, lo, buf + E::TB, tid);
+      }
     };
     issue(0, bufA);
     start();
@@ -670,6 +679,16 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
   }
 }
 
+// stream_subtiles_t, its tail handling compiled in only where the last
+// subtile is partial (last_rows < 64).
+template <class E, int NT, class S, class F>
+__device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const typename E::T* kp,
+                                                const typename E::T* vp, int nsub, int last_rows, int D, int tid,
+                                                S&& start, F&& compute) {
+  if (last_rows < kSub) stream_subtiles_t<E, NT, true>(bufA, bufB, kp, vp, nsub, last_rows, D, tid, start, compute);
+  else stream_subtiles_t<E, NT, false>(bufA, bufB, kp, vp, nsub, last_rows, D, tid, start, compute);
+}
+
 // K-ahead stream for direct-load engines (gather; no causal mask, only the
 // padding rows of a partial last subtile are masked):
 // each buffer holds a K subtile then a V subtile (TB bytes each). Step sub
@@ -679,19 +698,27 @@ __device__ __forceinline__ void stream_subtiles(char* bufA, char* bufB, const ty
 // K(sub+2) overwrites K(sub), read in the step before (or the prologue,
 // followed by its own barrier), V(sub+1) overwrites V(sub-1), read in the
 // step before.
-template <class E, int NT, bool ON, class S>
+template <class E, int NT, bool ON, bool TAIL, class S>
 __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB, const typename E::T* kp,
                                                  const typename E::T* vp, int nsub, int last_rows, int tid, int lane,
                                                  float sl2, S&& start) {
   constexpr int64_t SE = (int64_t)kSub * E::kD;
   const int h = lane >> 5;
-  const bool tail = last_rows < kSub;  // the last subtile is partial: clamped loads, masked scores
-  auto rows_of = [&](int sub) { return sub == nsub - 1 ? last_rows : kSub; };
+  constexpr bool tail = TAIL;  // the last subtile is partial: clamped loads, masked scores
+  auto rows_of = [&](int sub) { return (TAIL && sub == nsub - 1) ? last_rows : kSub; };
   typename E::template LoadOffsets<NT> lo;
   E::template load_offsets<NT>(lo, tid);
-  load_subtile<E, NT, false>(kp, lo, bufA, tid, rows_of(0));
-  load_subtile<E, NT, true>(vp, lo, bufA + E::TB, tid, rows_of(0));
-  if (nsub > 1) load_subtile<E, NT, false>(kp + SE, lo, bufB, tid, rows_of(1));
+  // Loads of subtile sub (K: IS_V false); only a TAIL stream can meet a partial one.
+  auto ld = [&](auto is_v, const typename E::T* p, int sub, char* buf) {
+    constexpr bool V = decltype(is_v)::value;
+    if (TAIL) load_subtile<E, NT, V>(p, lo, buf, tid, rows_of(sub));
+    else E::template begin_uniform<NT, V>(p, lo, buf, tid);
+  };
+  using KL = std::integral_constant<bool, false>;
+  using VL = std::integral_constant<bool, true>;
+  ld(KL{}, kp, 0, bufA);
+  ld(VL{}, vp, 0, bufA + E::TB);
+  if (nsub > 1) ld(KL{}, kp + SE, 1, bufB);
   start();  // e.g. the query rows, under the first K/V loads
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see stream_subtiles
   lds_dma_wait();
@@ -710,8 +737,8 @@ __device__ __forceinline__ void stream_k_ahead_t(E& eng, char* bufA, char* bufB,
   // wave's loads before the barrier that publishes them to the other waves.
   auto full = [&](int sub, char* bc, char* bn, f32x16(&sc)[2], f32x16(&sn)[2], float mc, float& mn) {
     const bool k2 = sub + 2 < nsub;
-    load_subtile<E, NT, true>(vp + (sub + 1) * SE, lo, bn + E::TB, tid, rows_of(sub + 1));
-    if (k2) load_subtile<E, NT, false>(kp + (sub + 2) * SE, lo, bc, tid, rows_of(sub + 2));
+    ld(VL{}, vp + (sub + 1) * SE, sub + 1, bn + E::TB);
+    if (k2) ld(KL{}, kp + (sub + 2) * SE, sub + 2, bc);
     if (ON) {
       eng.rescale(mc);
       eng.fused(bn, sn, sc, bc + E::TB, lane, sl2, mn);
@@ -749,8 +776,13 @@ template <class E, int NT, class S>
 __device__ __forceinline__ void stream_k_ahead(E& eng, char* bufA, char* bufB, const typename E::T* kp,
                                                const typename E::T* vp, int nsub, int last_rows, int tid, int lane,
                                                bool on, float sl2, S&& start) {
-  if (on) stream_k_ahead_t<E, NT, true>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
-  else stream_k_ahead_t<E, NT, false>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
+  if (last_rows < kSub) {
+    if (on) stream_k_ahead_t<E, NT, true, true>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
+    else stream_k_ahead_t<E, NT, false, true>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
+  } else {
+    if (on) stream_k_ahead_t<E, NT, true, false>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
+    else stream_k_ahead_t<E, NT, false, false>(eng, bufA, bufB, kp, vp, nsub, last_rows, tid, lane, sl2, start);
+  }
 }
 
 // LDS for one kernel: two static subtile buffers for direct-load engines,

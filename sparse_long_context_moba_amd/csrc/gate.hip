@@ -45,6 +45,8 @@
 // A second kernel (rank_kernel) then numbers each query inside the lists
 // of the past blocks it kept: an LDS histogram per 1024 queries plus one
 // global atomic per (workgroup, block), so hot blocks see few atomics.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -257,6 +259,43 @@ struct GateOps<bf16, D> {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(lo + 16 * kk);
 #pragma unroll
       for (int g = 0; g < QG; ++g) acc[g] = mfma_bf16(af, qf[g].f[kk], acc[g]);
+    }
+  }
+  // The steady state in issue order (waves issue in order, so the MFMA
+  // chain only overlaps the selection work if the two are interleaved in
+  // the instruction stream): scores of the next tile (nxt) from LDS with
+  // fragment reads AH ahead, and between consecutive MFMAs the fold of
+  // 16 / (2 KC) of the current tile's scores (cur) into the segment list S.
+  // Scheduling fences keep this order. One query group.
+  template <int TT>
+  static __device__ __forceinline__ void scores_fold(const char* lds, int col, int h, const GateOps& qf, f32x16& nxt,
+                                                     const f32x16& cur, float (&S)[TT], unsigned pos0) {
+    const bf16* hi = reinterpret_cast<const bf16*>(lds) + col * KR + 8 * h;
+    const bf16* lo = hi + kTileB * KR;
+    constexpr int NF = 2 * KC, AH = 4, EPF = 16 / NF;  // fragments, reads ahead, elements folded per fragment
+    static_assert(16 % NF == 0, "fold elements split evenly over the fragments");
+    auto frag = [&](int c) { return *reinterpret_cast<const bf16x8*>((c < KC ? hi : lo) + 16 * (c % KC)); };
+    bf16x8 f[AH];
+#pragma unroll
+    for (int c = 0; c < AH; ++c) f[c] = frag(c);
+    nxt = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NF; ++c) {
+      nxt = mfma_bf16(f[c % AH], qf.f[c % KC], nxt);
+      if (c + AH < NF) f[c % AH] = frag(c + AH);
+#pragma unroll
+      for (int u = 0; u < EPF; ++u) {
+        const int r = EPF * c + u;
+        const float sv = cur[r];
+        const float x = __uint_as_float((__float_as_uint(sv) & ~kSegMask) | (pos0 + r));
+        float n[TT];
+        n[0] = __builtin_fmaxf(S[0], x);
+#pragma unroll
+        for (int i = 1; i < TT; ++i) n[i] = __builtin_amdgcn_fmed3f(S[i - 1], S[i], x);
+#pragma unroll
+        for (int i = 0; i < TT; ++i) S[i] = n[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // Issue order for the steady state (waves issue in order, so the MFMA
@@ -627,10 +666,10 @@ gate_topk_kernel(GateArgs a) {
   // a key/value head and routes its group of query heads.
   const int64_t rows = SHARED ? a.kv_heads : a.heads;
   const int64_t item = blockIdx.x;
-  const int64_t si = seq_find(a.sq, kSeqW128, rows, item, a.block_size);
-  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t si = seq_find_u(a.sq, kSeqW128, rows, item, a.block_size);
+  const SeqAt sa = seq_at_u(a.sq, si, a.block_size);
   const int64_t wg_per_head = (sa.len + WGQ - 1) / WGQ;
-  const int64_t r_item = item - rows * seq_prefix(a.sq, si, kSeqW128, a.block_size);
+  const int64_t r_item = item - rows * seq_prefix_u(a.sq, si, kSeqW128, a.block_size);
   const int64_t grp = r_item / wg_per_head;
   const int64_t kvh = SHARED ? grp : grp / a.group;
   const int64_t qh0 = SHARED ? grp * a.group : grp;
@@ -716,9 +755,14 @@ gate_topk_kernel(GateArgs a) {
     const int jb = jt + 4 * h;
     const bool full = jt + kTileB <= jend && (a.causal || c < jt || c >= jt + kTileB);
     if (do_cur && do_next && full) {  // the steady state: one basic block
-      Ops::template scores<QG>(next_buf, col, h, qf, nxt);
-      absorb<QG, TT, false>(S, cur, tis, jb, jend, c);
-      Ops::template interleave<QG, TT>();
+      if constexpr (std::is_same<Ops, GateOps<bf16, D>>::value && QG == 1) {
+        // the MFMAs of tile i + 1 and the fold of tile i, in a fixed order
+        Ops::template scores_fold<TT>(next_buf, col, h, qf[0], nxt[0], cur[0], S[0], (unsigned)tis << 4);
+      } else {
+        Ops::template scores<QG>(next_buf, col, h, qf, nxt);
+        absorb<QG, TT, false>(S, cur, tis, jb, jend, c);
+        Ops::template interleave<QG, TT>();
+      }
     } else if (do_cur && full) {
       absorb<QG, TT, false>(S, cur, tis, jb, jend, c);
     } else {
@@ -788,10 +832,10 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
   int* bins = reinterpret_cast<int*>(smem);
   // Work item -> (sequence, query head, chunk of kRankQ queries).
   const int64_t item = blockIdx.x;
-  const int64_t si = seq_find(a.sq, kSeqW1024, a.heads, item, a.block_size);
-  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t si = seq_find_u(a.sq, kSeqW1024, a.heads, item, a.block_size);
+  const SeqAt sa = seq_at_u(a.sq, si, a.block_size);
   const int64_t per_head = (sa.len + kRankQ - 1) / kRankQ;
-  const int64_t r_item = item - a.heads * seq_prefix(a.sq, si, kSeqW1024, a.block_size);
+  const int64_t r_item = item - a.heads * seq_prefix_u(a.sq, si, kSeqW1024, a.block_size);
   const int64_t hq = r_item / per_head;
   const int64_t q0 = (r_item % per_head) * kRankQ;
   const int NB = (int)sa.nb;

@@ -39,8 +39,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   const int rg = tid / TPR, cv = tid % TPR;
   // Work item: one block of one key/value head of one sequence.
   const int64_t blk = blockIdx.x;  // the block's index in the pooled-key arrays
-  const int64_t si = seq_find(a.sq, kSeqBlk, a.kv_heads, blk, a.block_size);
-  const SeqAt sa = seq_at(a.sq, si, a.block_size);
+  const int64_t si = seq_find_u(a.sq, kSeqBlk, a.kv_heads, blk, a.block_size);
+  const SeqAt sa = seq_at_u(a.sq, si, a.block_size);
   const int64_t r = blk - a.kv_heads * sa.blk0;
   const int64_t hk = r / sa.nb, j = r % sa.nb;
   // Rows of block j; the sequence's last block holds the remaining tokens.
@@ -73,17 +73,15 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
       take(3, __uint_as_float(raw.w));
     }
   };
-  for (int r0 = rg; r0 < Bs; r0 += U * RG) {
-    if (r0 + (U - 1) * RG < Bs) {
-      u32x4 raw[U];
+  int r0 = rg;
+  for (; r0 + (U - 1) * RG < Bs; r0 += U * RG) {
+    u32x4 raw[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) raw[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + u * RG) * D);
+    for (int u = 0; u < U; ++u) raw[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + u * RG) * D);
 #pragma unroll
-      for (int u = 0; u < U; ++u) take_row(raw[u]);
-    } else {
-      for (int u = 0; r0 + u * RG < Bs; ++u) take_row(*reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + u * RG) * D));
-    }
+    for (int u = 0; u < U; ++u) take_row(raw[u]);
   }
+  for (; r0 < Bs; r0 += RG) take_row(*reinterpret_cast<const u32x4*>(base + (int64_t)r0 * D));  // the block's last rows
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     if (SUM) red[rg][cv * VEC + e] = acc[e];
