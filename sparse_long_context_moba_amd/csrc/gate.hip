@@ -711,11 +711,7 @@ gate_topk_kernel(GateArgs a) {
       }
     }
   }
-  // Largest norm among the wave's scanned blocks, for the rounding bound:
-  // the first 64 norms load now, under the scan; any others after it.
   const int jend = a.causal ? c : NB;  // this wave's scan bound
-  const float* nrm = a.norm + kvb0;
-  float kmax = (scoring && lane < jend) ? nrm[lane] : 0.f;
   double L[QG][TT];
   float S[QG][TT];
 #pragma unroll
@@ -728,6 +724,29 @@ gate_topk_kernel(GateArgs a) {
   // Scan bound of the whole workgroup (its last valid query has the largest c).
   const int64_t t_last = min<int64_t>(qb + WGQ, len) - 1;
   const int wg_jend = a.causal ? (int)(t_last / a.block_size) : NB;
+  // Largest pooled-key norm among the blocks the workgroup scans (each wave
+  // scans a prefix of them, so it bounds every wave's norms), for the
+  // rounding bound. All threads request their share of the norms at once,
+  // 2048 per round trip, next to the first tile's loads; the result is
+  // published by the pipeline's first barrier.
+  __shared__ float wg_kmax[4];
+  {
+    const float* nrm = a.norm + kvb0;
+    float kpart = 0.f;
+    for (int j0 = 0; j0 < wg_jend; j0 += 256 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + 256 * u + tid;
+        v[u] = j < wg_jend ? nrm[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kpart = fmaxf(kpart, v[u]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kpart = fmaxf(kpart, __shfl_xor(kpart, off));
+    if (lane == 0) wg_kmax[w] = kpart;
+  }
   // Tile pipeline. Tile i sits in LDS buffer i & 1. Step i stores tile i+1
   // (fetched into registers one step earlier) to the other buffer, passes
   // the workgroup barrier, fetches tile i+2, issues the MFMAs of tile i+1
@@ -778,11 +797,7 @@ gate_topk_kernel(GateArgs a) {
   }
   if (!wave_on) return;
 
-  if (scoring) {
-    for (int j = lane + 64; j < jend; j += 64) kmax = fmaxf(kmax, nrm[j]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off));
-  }
+  const float kmax = fmaxf(fmaxf(wg_kmax[0], wg_kmax[1]), fmaxf(wg_kmax[2], wg_kmax[3]));
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     const int64_t t = tw + 32 * g + col;
