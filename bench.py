@@ -9,7 +9,10 @@ seeded synthetic Q/K/V already resident in HBM. Prints one JSON line:
 throughput in tokens/s, effective TFLOP/s of the algorithmic work, the
 roofline of the dominant kernel (HIP-event durations of its launches inside
 the timed region), the speedup over the library's dense causal kernel, and
-the CPU fp64 oracle timed on a bounded sample of the same workload.
+the CPU fp64 oracle timed on a bounded sample of the same workload. The
+line's `long_context` list repeats the GPU measurements (not the CPU
+baseline) at 128K and 1M tokens, the other lengths the metric is quoted
+at, on inputs drawn on the device with the same distribution.
 """
 from __future__ import annotations
 
@@ -128,6 +131,109 @@ def upload(w, torch, workers=None):
         v[b, hk].copy_(cast(torch.from_numpy(vh)))
     torch.cuda.synchronize()
     return q, k, v
+
+
+def upload_device(w, torch, seed):
+    """q, v ~ N(0,1) and k = N(0,1) + a per-(b, kv head, block) N(0, 0.5^2)
+    bias shared by the block's tokens: the recipe's distribution, drawn on
+    the device by torch's seeded generator (used where generating the
+    seeded host streams would take minutes: the long-context sub-results)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B, S, D, Bs, nb = w.batch, w.seq_len, w.head_dim, w.block_size, w.n_blocks
+    q = torch.randn(B, w.heads, S, D, device="cuda", generator=g).to(dt)
+    k = torch.empty(B, w.kvh, S, D, dtype=dt, device="cuda")
+    for hk in range(w.kvh):  # one key/value head at a time bounds the fp32 temporaries
+        kk = torch.randn(B, nb * Bs, D, device="cuda", generator=g).view(B, nb, Bs, D)
+        kk += 0.5 * torch.randn(B, nb, 1, D, device="cuda", generator=g)
+        k[:, hk] = kk.view(B, nb * Bs, D)[:, :S].to(dt)
+        del kk
+    v = torch.randn(B, w.kvh, S, D, device="cuda", generator=g).to(dt)
+    torch.cuda.synchronize()
+    return q, k, v
+
+
+def time_forward(w, q, k, v, moba, torch, steps, warmup):
+    """ms per forward and per-kernel average ms (HIP events on the stream)."""
+    p = moba.problem(q, w.block_size, w.top_k, w.causal, w.pooling, w.kvh, w.gate_shared)
+    ws = torch.empty(moba.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    idx = torch.empty((w.batch, w.heads, w.seq_len, w.top_k), dtype=torch.int32, device="cuda")
+
+    def step():
+        moba.forward(q, k, v, w.block_size, w.top_k, w.causal, out=o, idx=idx, workspace=ws, pooling=w.pooling,
+                     gate_shared=w.gate_shared)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    with moba.timing() as tm:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    del ws, o, idx
+    return 1e3 * elapsed / steps, {n: {"launches": c, "avg_ms": tot / c, "total_ms": tot} for n, c, tot in tm.rows}
+
+
+def roofline_of(w, wm, kern, peak):
+    """Roofline entry of the kernel with the largest time (algorithmic work
+    per launch over its average launch duration)."""
+    units = kernel_units(w, wm)
+    dom = max((n for n in kern if n in units), key=lambda n: kern[n]["total_ms"])
+    bound, work, unit = units[dom]
+    avg_s = kern[dom]["avg_ms"] * 1e-3
+    if bound == "hbm":
+        achieved, rpeak, runit = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, rpeak, runit = work / avg_s / 1e12, peak, "TFLOP/s"
+    return {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": rpeak, "unit": runit,
+            "frac": round(achieved / rpeak, 4), "traffic": measured_traffic(dom, w.name),
+            "work_per_launch": work, "work_unit": unit, "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
+
+
+def long_context_result(name, args, moba, torch):
+    """One sub-result of the long-context workloads the metric is quoted at
+    (128K and 1M tokens): the same measurements as the main line, on
+    device-drawn inputs of the recipe's distribution."""
+    w = synth.WORKLOADS[name]
+    wm = work_model(w)
+    t0 = time.time()
+    q, k, v = upload_device(w, torch, 1000 + w.seed)
+    log(f"{name}: inputs drawn on the device in {time.time() - t0:.1f}s")
+    ms, kern = time_forward(w, q, k, v, moba, torch, args.long_steps, 1)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    flops = wm["gate_flops"] + wm["past_flops"] + wm["own_flops"]
+    ag_ms = sum(kern[n]["avg_ms"] for n in ("gate_topk", "gather_attn", "diag_merge") if n in kern)
+    res = {
+        "workload": name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "block_size": w.block_size,
+        "top_k": w.top_k, "steps": args.long_steps, "ms_per_step": round(ms, 3),
+        "tokens_per_s": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+        "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "pct_peak": round(100 * flops / (ms * 1e-3) / 1e12 / peak, 2),
+        "attn_gate_kernels_pct_peak": round(100 * flops / (ag_ms * 1e-3) / 1e12 / peak, 2),
+        "kernels_ms": {n: round(x["avg_ms"], 4) for n, x in kern.items()},
+        "roofline": roofline_of(w, wm, kern, peak),
+        "data": "synthetic, drawn on the device (torch seeded generator; the recipe's distribution)",
+    }
+    log(f"{name}: {ms:.3f} ms per forward, " + ", ".join(f"{n} {x['avg_ms']:.3f}ms" for n, x in kern.items()))
+    if args.dense_steps > 0:
+        od = torch.empty_like(q)
+        moba.dense(q, k, v, w.causal, out=od)  # one untimed run first
+        torch.cuda.synchronize()
+        td = time.perf_counter()
+        moba.dense(q, k, v, w.causal, out=od)
+        torch.cuda.synchronize()
+        dense_ms = 1e3 * (time.perf_counter() - td)
+        res["dense_causal"] = {"ms": round(dense_ms, 3), "speedup": round(dense_ms / ms, 2),
+                               "tflops": round(wm["dense_flops"] / (dense_ms * 1e-3) / 1e12, 1), "timed_runs": 1}
+        log(f"{name}: dense causal {dense_ms:.1f} ms, speedup {dense_ms / ms:.1f}x")
+        del od
+    del q, k, v
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_model():
@@ -271,6 +377,14 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the MoBA backward (dq, dk, dv for a fixed block choice) instead of the forward "
                          "and print its own JSON line (bf16 workloads)")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw the workload's inputs on the device (the recipe's distribution, torch's seeded "
+                         "generator) instead of the seeded host streams: for profiling the long workloads, whose "
+                         "host streams take minutes to generate")
+    ap.add_argument("--long", default="long_128k,long_1m",
+                    help="comma-separated long-context workloads measured as sub-results of the main line "
+                         "('' = none)")
+    ap.add_argument("--long-steps", type=int, default=3, help="timed forwards per long-context sub-result")
     ap.add_argument("--gen-workers", type=int, default=None,
                     help="processes generating the inputs (default: one per core, up to 16; use 1 under a profiler)")
     args = ap.parse_args()
@@ -288,7 +402,7 @@ def main():
     log(f"workload {w.name}: B={w.batch} H={w.heads} S={w.seq_len} D={w.head_dim} "
         f"block={w.block_size} top_k={w.top_k} {w.dtype}; generating inputs")
     t0 = time.time()
-    q, k, v = upload(w, torch, args.gen_workers)
+    q, k, v = upload_device(w, torch, 1000 + w.seed) if args.device_inputs else upload(w, torch, args.gen_workers)
     log(f"inputs resident in HBM after {time.time() - t0:.1f}s")
     p = moba.problem(q, w.block_size, w.top_k, w.causal, w.pooling, w.kvh, w.gate_shared)
     ws = torch.empty(moba.workspace_bytes(p), dtype=torch.uint8, device="cuda")
@@ -368,6 +482,14 @@ def main():
         cpu = cpu_baseline(w, args.cpu_rows)
         log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
 
+    long_results = []
+    names = [n for n in args.long.split(",") if n and n != w.name]
+    if names:
+        del q, k, v, o, idx, ws
+        torch.cuda.empty_cache()
+        for name in names:
+            long_results.append(long_context_result(name, args, moba, torch))
+
     tokens = w.batch * w.seq_len
     line = {
         "metric": METRIC,
@@ -396,6 +518,7 @@ def main():
         "dense_causal": dense,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "long_context": long_results,
     }
     print(json.dumps(line), flush=True)
 
