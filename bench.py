@@ -12,7 +12,8 @@ the timed region), the speedup over the library's dense causal kernel, and
 the CPU fp64 oracle timed on a bounded sample of the same workload. The
 line's `long_context` list repeats the GPU measurements (not the CPU
 baseline) at 128K and 1M tokens, the other lengths the metric is quoted
-at, on inputs drawn on the device with the same distribution.
+at, on inputs drawn on the device with the same distribution; its
+`backward` entry times moba_backward on the main workload's inputs.
 """
 from __future__ import annotations
 
@@ -281,15 +282,12 @@ def cpu_baseline(w, n_rows):
     }
 
 
-def backward_bench(args, w, wm, q, k, v, moba, torch):
-    """One step = one moba_backward over the workload (the forward's o,
+def measure_backward(w, wm, q, k, v, moba, torch, steps, warmup):
+    """Timed moba_backward passes over the workload (the forward's o,
     block_idx and log-sum-exp resident in HBM, a seeded upstream gradient).
     Algorithmic work: 10*D flops per (query, attended key), the five
     D-length products of a softmax-attention backward (scores, dP, dQ, dK,
     dV); the kernels recompute the scores once more per pass."""
-    if w.dtype != "bf16":
-        print("the backward is built for bf16 workloads only", file=sys.stderr)
-        sys.exit(2)
     o, idx, lse = moba.forward(q, k, v, w.block_size, w.top_k, w.causal, pooling=w.pooling,
                                gate_shared=w.gate_shared, return_lse=True)
     g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
@@ -299,21 +297,20 @@ def backward_bench(args, w, wm, q, k, v, moba, torch):
     def bstep():
         moba.backward(q, k, v, o, dout, idx, lse, w.block_size, w.top_k, w.causal)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         bstep()
     torch.cuda.synchronize()
-    log(f"backward warmup {args.warmup} done; timing {args.steps} steps")
     with moba.timing() as tm:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             bstep()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-    ms = 1e3 * elapsed / args.steps
+    del o, idx, lse, dout
+    ms = 1e3 * elapsed / steps
     kern = {n: {"launches": c, "avg_ms": tot / c} for n, c, tot in tm.rows}
-    log("kernels: " + ", ".join(f"{n} {x['avg_ms']:.3f}ms" for n, x in kern.items()))
-    D, bh = w.head_dim, w.batch * w.heads
+    D = w.head_dim
     past_keys = wm["past_flops"] // (4 * D)
     own_keys = wm["own_flops"] // (4 * D)
     flops = 10 * D * (past_keys + own_keys)
@@ -323,15 +320,9 @@ def backward_bench(args, w, wm, q, k, v, moba, torch):
              "bwd_dv": 4 * D * (past_keys + own_keys), "bwd_dk": 6 * D * (past_keys + own_keys)}
     dom = max((n for n in kern if n in units), key=lambda n: kern[n]["avg_ms"])
     ach = units[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
-    line = {
-        "metric": "MoBA bwd tokens/sec + effective TFLOP/s (% bf16 MFMA peak)",
-        "value": round(w.batch * w.seq_len / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-        "data": "synthetic (the forward's recipe; upstream gradient ~ N(0,1))",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kvh, "seq_len": w.seq_len,
-                   "head_dim": D, "block_size": w.block_size, "top_k": w.top_k, "causal": w.causal,
-                   "parallelism": "single GPU"},
+    return {
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(w.batch * w.seq_len / (ms * 1e-3), 1),
         "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "pct_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {n: round(x["avg_ms"], 4) for n, x in kern.items()},
@@ -339,7 +330,30 @@ def backward_bench(args, w, wm, q, k, v, moba, torch):
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "work_per_launch": units[dom], "work_unit": "flop",
                      "avg_launch_ms": round(kern[dom]["avg_ms"], 4)},
-        "cpu_baseline": None,
+    }
+
+
+def backward_bench(args, w, wm, q, k, v, moba, torch):
+    """--backward: one step = one moba_backward over the workload; its own
+    JSON line (see measure_backward)."""
+    if w.dtype != "bf16":
+        print("the backward is built for bf16 workloads only", file=sys.stderr)
+        sys.exit(2)
+    log(f"backward: warmup {args.warmup}, timing {args.steps} steps")
+    r = measure_backward(w, wm, q, k, v, moba, torch, args.steps, args.warmup)
+    log("kernels: " + ", ".join(f"{n} {x:.3f}ms" for n, x in r["kernels_ms"].items()))
+    D = w.head_dim
+    line = {
+        "metric": "MoBA bwd tokens/sec + effective TFLOP/s (% bf16 MFMA peak)",
+        "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (the forward's recipe; upstream gradient ~ N(0,1))",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kvh, "seq_len": w.seq_len,
+                   "head_dim": D, "block_size": w.block_size, "top_k": w.top_k, "causal": w.causal,
+                   "parallelism": "single GPU"},
+        "effective_tflops": r["effective_tflops"], "pct_peak": r["pct_peak"], "kernels_ms": r["kernels_ms"],
+        "roofline": r["roofline"], "cpu_baseline": None,
     }
     if args.cpu_rows > 0:
         from oracle import sampled
@@ -385,6 +399,8 @@ def main():
                     help="comma-separated long-context workloads measured as sub-results of the main line "
                          "('' = none)")
     ap.add_argument("--long-steps", type=int, default=3, help="timed forwards per long-context sub-result")
+    ap.add_argument("--backward-steps", type=int, default=5,
+                    help="timed moba_backward passes reported as the line's backward sub-result (0 = skip)")
     ap.add_argument("--gen-workers", type=int, default=None,
                     help="processes generating the inputs (default: one per core, up to 16; use 1 under a profiler)")
     args = ap.parse_args()
@@ -482,6 +498,12 @@ def main():
         cpu = cpu_baseline(w, args.cpu_rows)
         log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
 
+    backward = None
+    if args.backward_steps > 0 and w.dtype == "bf16" and w.seq_len % 64 == 0:
+        log(f"backward: timing {args.backward_steps} passes")
+        backward = measure_backward(w, wm, q, k, v, moba, torch, args.backward_steps, 2)
+        log(f"backward: {backward['ms_per_step']} ms ({backward['pct_peak']} % of peak)")
+
     long_results = []
     names = [n for n in args.long.split(",") if n and n != w.name]
     if names:
@@ -518,6 +540,7 @@ def main():
         "dense_causal": dense,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "backward": backward,
         "long_context": long_results,
     }
     print(json.dumps(line), flush=True)
