@@ -519,6 +519,62 @@ constexpr int gate_waves() {
   return (sizeof(T) == 2 && TT <= 6 && !SHARED) ? 3 : 2;
 }
 
+// Exact top-TT over every eligible block of one query, by the whole wave:
+// the query's fp64 vector (D values) is in this wave's LDS slice qs; lane l
+// scores blocks l, l + 64, ... as fp64 dot products summed over the
+// coordinates in order, and keeps its own top-TT by (score desc, index
+// asc). TT rounds of a wave-wide arg-max over the lists' heads (the lane
+// holding the winner drops it) then give the overall top-TT in order, the
+// same in every lane. One load round trip serves 64 blocks.
+template <int D, int TT>
+__device__ void rescan_all(const double* kb64, const double* qs, int c, int jend, int lane, int (&top)[TT]) {
+  double es[TT];
+  int ej[TT];
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    es[i] = -__builtin_huge_val();
+    ej[i] = kNoBlock;
+  }
+  for (int j0 = 0; j0 < jend; j0 += 64) {
+    const int j = j0 + lane;
+    const bool on = j < jend && j != c;
+    const double* kr = kb64 + (int64_t)(on ? j : 0) * D;
+    double p = 0.0;
+#pragma unroll 4
+    for (int d = 0; d < D; d += 2) {
+      const double2 kv = *reinterpret_cast<const double2*>(kr + d);
+      const double2 qv = *reinterpret_cast<const double2*>(qs + d);
+      p = __builtin_fma(qv.x, kv.x, p);
+      p = __builtin_fma(qv.y, kv.y, p);
+    }
+    if (on && better64(p, j, es[TT - 1], ej[TT - 1])) insert_full64(es, ej, p, j);
+  }
+#pragma unroll
+  for (int r = 0; r < TT; ++r) {
+    double bs = es[0];
+    int bj = ej[0];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const double os = __shfl_xor(bs, off);
+      const int oj = __shfl_xor(bj, off);
+      if (better64(os, oj, bs, bj)) {
+        bs = os;
+        bj = oj;
+      }
+    }
+    top[r] = bj;
+    if (bj != kNoBlock && ej[0] == bj) {  // this lane held the winner
+#pragma unroll
+      for (int i = 0; i + 1 < TT; ++i) {
+        es[i] = es[i + 1];
+        ej[i] = ej[i + 1];
+      }
+      es[TT - 1] = -__builtin_huge_val();
+      ej[TT - 1] = kNoBlock;
+    }
+  }
+}
+
 // fp64 re-scoring of the wave's ambiguous queries (lanes with `amb` set,
 // lane half 0), one query at a time by the whole wave. A query's fp64
 // vector is the sum of its rows in nq query heads (one head unless the gate
@@ -527,13 +583,15 @@ constexpr int gate_waves() {
 // The queries share c
 // and the eligible set. Candidates are the query's tracked list, or every
 // eligible block when its rounding band reaches past the list (`tracked`
-// false). 64 lanes split each candidate's dot product into D/8 slices of 8
-// coordinates and sum the slices in a fixed order (deterministic). The
-// query in lane column L gets the exact top-TT in sel.
+// false). For the tracked list, 64 lanes split each candidate's dot product
+// into D/8 slices of 8 coordinates and sum the slices in a fixed order
+// (deterministic); every eligible block goes through rescan_all, with the
+// query in the wave's LDS slice qs (D doubles). The query in lane column L
+// gets the exact top-TT in sel.
 template <typename TQ, int D, int TT>
 __device__ void rescore_ambiguous(const GateArgs& a, int64_t qrow0, int64_t head_stride, int nq, int64_t kvb0,
                                   int64_t tg, int c, int jend, bool amb, bool tracked, const int (&lj)[TT], int (&sel)[TT],
-                                  int lane, int col) {
+                                  int lane, int col, double* qs) {
   uint64_t pend = __builtin_amdgcn_ballot_w64(amb);
   const double* kb64 = a.kbar64 + kvb0 * (int64_t)D;
   constexpr int SL = D / 8;    // 8-coordinate slices per candidate
@@ -543,6 +601,23 @@ __device__ void rescore_ambiguous(const GateArgs& a, int64_t qrow0, int64_t head
     const int ln = __builtin_ctzll(pend);
     pend &= pend - 1;
     const bool trk = __builtin_amdgcn_readlane((int)tracked, ln);
+    if (!trk) {
+      // The query (summed over its heads in fp64) into the wave's LDS slice,
+      // then every eligible block.
+      const TQ* qA = reinterpret_cast<const TQ*>(a.q) + (qrow0 + tg + ln) * D;
+      for (int d = lane; d < D; d += 64) {
+        double x = (double)(float)qA[d];
+        for (int g = 1; g < nq; ++g) x += (double)(float)qA[g * head_stride * D + d];
+        qs[d] = x;
+      }
+      int top[TT];
+      rescan_all<D, TT>(kb64, qs, c, jend, lane, top);
+      if (col == ln) {
+#pragma unroll
+        for (int i = 0; i < TT; ++i) sel[i] = top[i];
+      }
+      continue;
+    }
     // This lane's slice of the ambiguous query's coordinates, summed over
     // the heads in fp64.
     const TQ* qL = reinterpret_cast<const TQ*>(a.q) + (qrow0 + tg + ln) * D + 8 * sl;
@@ -564,17 +639,12 @@ __device__ void rescore_ambiguous(const GateArgs& a, int64_t qrow0, int64_t head
       es[i] = -__builtin_huge_val();
       ej[i] = kNoBlock;
     }
-    const int ncand = trk ? TT : jend;
-    for (int base = 0; base < ncand; base += G) {
+    for (int base = 0; base < TT; base += G) {
       const int ci = base + gi;
       int j = kNoBlock;
-      if (trk) {
 #pragma unroll
-        for (int i = 0; i < TT; ++i)
-          if (ci == i) j = cj[i];
-      } else if (ci < jend && ci != c) {
-        j = ci;
-      }
+      for (int i = 0; i < TT; ++i)
+        if (ci == i) j = cj[i];
       double p = 0.0;
       if (j != kNoBlock) {
         const double* kr = kb64 + (int64_t)j * D + 8 * sl;
@@ -828,7 +898,7 @@ gate_topk_kernel(GateArgs a) {
       const bool amb = !(ls[m - 1] - ls[m] > 2.f * eps);
       const bool tracked = n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps;
       rescore_ambiguous<TQ, D, TT>(a, qrow0, len, nq, kvb0, tw + 32 * g, c, jend, amb && h == 0 && qvalid, tracked,
-                                   lj, sel, lane, col);
+                                   lj, sel, lane, col, reinterpret_cast<double*>(tile) + w * D);
     }
     if (h == 0 && qvalid)
       for (int hq = 0; hq < nq; ++hq)
