@@ -45,6 +45,36 @@ __device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32);
 __device__ __forceinline__ int shfl_xor32(int x) { return __shfl_xor(x, 32); }
 __device__ __forceinline__ double shfl_xor32(double x) { return __shfl_xor(x, 32); }
 
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16*l, lds_base being wave-uniform.
+// Issued from inline assembly so that the compiler does not make unrelated
+// LDS reads wait for it (the builtin form is followed by a full vmcnt wait
+// wherever an LDS read of the same array comes later, which would serialise
+// the K-ahead stream); the caller waits explicitly (lds_dma_wait) before
+// the barrier that publishes the data. The instruction takes its LDS
+// address from M0: it is passed as an input operand bound to M0, so the
+// compiler itself writes M0 before the instruction and knows its value.
+// The instruction has no register outputs (the data goes to LDS), so no
+// output register can be reused while the load is in flight.
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+}
+// The same with a wave-uniform base address (SGPR pair) and a 32-bit
+// per-lane byte offset, so no per-load 64-bit address arithmetic.
+__device__ __forceinline__ void lds_dma16_s(const void* base, unsigned off, unsigned lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N vector memory operations of this wave are in
+// flight (they complete in issue order), leaving the newest N running.
+template <int N>
+__device__ __forceinline__ void lds_dma_wait_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 __device__ __forceinline__ float bf16_to_f32(unsigned short u) {
   return __uint_as_float(((unsigned)u) << 16);
 }

@@ -239,6 +239,34 @@ struct GateOps<bf16, D> {
       *reinterpret_cast<Chunk*>(hi + which * kTileB * KR + (id / CPR) * KR + 8 * (id % CPR)) = r[n];
     }
   }
+  // Direct HBM -> LDS staging instead of fetch/put. A tile is a run of
+  // 16-byte slots: rows of RC slots (hi rows, then lo rows), each row's last
+  // slot padding, which repeats the row's first chunk. One wave-wide load
+  // fills 64 consecutive slots, so the four waves share NDMA_ALL loads; a
+  // wave with fewer repeats the last one (same data to the same slots).
+  static constexpr bool kDma = true;
+  static constexpr int RC = KR / 8;
+  static constexpr int SLOTS = 2 * kTileB * RC;
+  static constexpr int NDMA_ALL = SLOTS / 64;
+  static_assert(SLOTS % 64 == 0 && KR % 8 == 0, "whole wave-wide loads per tile");
+  static constexpr int NDMA = (NDMA_ALL + 3) / 4;  // loads per wave per tile
+  static __device__ int dma_ins(int w, int n) { return min(w + 4 * n, NDMA_ALL - 1); }
+  // Byte offsets of this lane's slots from the tile's first hi row; lo rows
+  // lie lo_off bytes further; rows at or past `rows` repeat the last one.
+  static __device__ void dma_offsets(unsigned (&off)[NDMA], int w, int lane, unsigned lo_off, int rows) {
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const int sl = 64 * dma_ins(w, n) + lane;
+      const int row = sl / RC;
+      const int ch = sl % RC < D / 8 ? sl % RC : 0;
+      const int r = min(row % kTileB, rows - 1);
+      off[n] = (row < kTileB ? 0u : lo_off) + (unsigned)r * (D * 2) + 16u * ch;
+    }
+  }
+  static __device__ void dma(const bf16* tile_hi, const unsigned (&off)[NDMA], unsigned lds, int w) {
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) lds_dma16_s(tile_hi, off[n], lds + 1024u * dma_ins(w, n));
+  }
   static constexpr int QG_MAX = 2;  // 32-query groups per wave
   // Scores of every group against the tile: each pooled-key fragment is read
   // from LDS once and feeds one MFMA per group (independent chains).
@@ -365,6 +393,12 @@ struct GateOps<float, D> {
       }
     }
   }
+  // Register staging (8-byte chunks at an odd row stride cannot be
+  // loaded straight into LDS 16 bytes at a time).
+  static constexpr bool kDma = false;
+  static constexpr int NDMA = 1;
+  static __device__ void dma_offsets(unsigned (&)[NDMA], int, int, unsigned, int) {}
+  static __device__ void dma(const bf16*, const unsigned (&)[NDMA], unsigned, int) {}
   static __device__ void put(char* lds, const Chunk (&r)[NLD], int tid) {
     float* kt = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -729,7 +763,8 @@ gate_topk_kernel(GateArgs a) {
   constexpr int WGQ = 4 * WQ;       // queries per workgroup
   extern __shared__ __align__(16) char smem[];
   char* tile = smem;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave (uniform)
   static_assert(WGQ == 128, "the sequence table counts gate workgroups of 128 queries");
   // Work item -> (sequence, routing row, workgroup). Per-head gate: the row
   // is a query head, reading key head row / group. Shared gate: the row is
@@ -817,28 +852,65 @@ gate_topk_kernel(GateArgs a) {
     for (int off = 32; off > 0; off >>= 1) kpart = fmaxf(kpart, __shfl_xor(kpart, off));
     if (lane == 0) wg_kmax[w] = kpart;
   }
-  // Tile pipeline. Tile i sits in LDS buffer i & 1. Step i stores tile i+1
-  // (fetched into registers one step earlier) to the other buffer, passes
-  // the workgroup barrier, fetches tile i+2, issues the MFMAs of tile i+1
-  // and, while they run, folds the scores of tile i (issued one step
-  // earlier) into the key lists. Only the ordering of independent work
-  // changes; every tile is scored and folded exactly once.
+  // Tile pipeline. Step i passes a workgroup barrier behind which tile i+1
+  // is in LDS, issues the MFMAs of tile i+1 and, while they run, folds the
+  // scores of tile i (issued one step earlier) into the key lists. Only the
+  // ordering of independent work changes; every tile is scored and folded
+  // exactly once.
+  //  * bf16 ops load tiles straight into LDS (three buffers, tile t in
+  //    buffer t % 3): step i waits for its own loads of tile i+1 (issued
+  //    two steps earlier, leaving tile i+2's in flight), passes the barrier
+  //    (all waves' loads of tile i+1 landed; every wave is done reading
+  //    tile i, which its MFMAs read in step i-1) and then loads tile i+3
+  //    into tile i's buffer.
+  //  * fp32 ops stage through registers (two buffers, tile t in buffer
+  //    t & 1): step i stores tile i+1 (fetched one step earlier), passes the
+  //    barrier and fetches tile i+2.
+  constexpr bool DMA = Ops::kDma;
+  constexpr int NBUF = DMA ? 3 : 2;
+  auto buf = [&](int t) { return tile + (t % NBUF) * Ops::TILE_BYTES; };
   const int ntiles = (wg_jend + kTileB - 1) / kTileB;  // workgroup-uniform
   const int my_tiles = scoring ? (jend + kTileB - 1) / kTileB : 0;
   typename Ops::Chunk stg[Ops::NLD];
+  unsigned doff[Ops::NDMA];
+  const unsigned lo_off = (unsigned)(reinterpret_cast<const char*>(a.kbar_lo) - reinterpret_cast<const char*>(a.kbar_hi));
+  auto issue = [&](int t) {  // loads of tile t (bf16 ops)
+    const bf16* base = a.kbar_hi + (kvb0 + (int64_t)t * kTileB) * D;
+    const int rows = NB - t * kTileB;  // the head's blocks from the tile's first
+    if (rows >= kTileB) {
+      Ops::dma(base, doff, lds_addr(buf(t)), w);
+    } else {
+      unsigned po[Ops::NDMA];
+      Ops::dma_offsets(po, w, lane, lo_off, rows);
+      Ops::dma(base, po, lds_addr(buf(t)), w);
+    }
+  };
   f32x16 acc_a[QG], acc_b[QG];
-  if (ntiles > 0) {
+  if constexpr (DMA) {
+    Ops::dma_offsets(doff, w, lane, lo_off, kTileB);
+    for (int t = 0; t < min(ntiles, 3); ++t) issue(t);
+    if (ntiles >= 3) lds_dma_wait_n<2 * Ops::NDMA>();
+    else if (ntiles == 2) lds_dma_wait_n<Ops::NDMA>();
+    else lds_dma_wait();
+  } else if (ntiles > 0) {
     Ops::fetch(stg, a, kvb0, NB, 0, tid);
     Ops::put(tile, stg, tid);
   }
   __syncthreads();
-  if (ntiles > 1) Ops::fetch(stg, a, kvb0, NB, kTileB, tid);
+  if (!DMA && ntiles > 1) Ops::fetch(stg, a, kvb0, NB, kTileB, tid);
   if (my_tiles > 0) Ops::template scores<QG>(tile, col, h, qf, acc_a);
   auto step = [&](int i, f32x16(&cur)[QG], f32x16(&nxt)[QG]) {
-    char* next_buf = tile + ((i + 1) & 1) * Ops::TILE_BYTES;
-    if (i + 1 < ntiles) Ops::put(next_buf, stg, tid);
-    __syncthreads();
-    if (i + 2 < ntiles) Ops::fetch(stg, a, kvb0, NB, (i + 2) * kTileB, tid);
+    char* next_buf = buf(i + 1);
+    if constexpr (DMA) {
+      if (i + 2 < ntiles) lds_dma_wait_n<Ops::NDMA>();
+      else lds_dma_wait();
+      __syncthreads();
+      if (i + 3 < ntiles) issue(i + 3);
+    } else {
+      if (i + 1 < ntiles) Ops::put(next_buf, stg, tid);
+      __syncthreads();
+      if (i + 2 < ntiles) Ops::fetch(stg, a, kvb0, NB, (i + 2) * kTileB, tid);
+    }
     const bool do_next = i + 1 < my_tiles, do_cur = i < my_tiles;
     const int jt = i * kTileB, tis = i % kSegTiles;
     const int jb = jt + 4 * h;
@@ -973,7 +1045,8 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
 template <typename T, typename TQ, int D, int TT, bool SHARED>
 static void gate_go(const GateArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.gate_wgs);
-  const int lds = 2 * GateOps<T, D>::TILE_BYTES;
+  using Ops = typename pick_type<SHARED, GateOpsSplitQ<D>, GateOps<T, D>>::type;
+  const int lds = (Ops::kDma ? 3 : 2) * Ops::TILE_BYTES;
   hipLaunchKernelGGL((gate_topk_kernel<T, TQ, D, TT, SHARED>), grid, dim3(256), lds, s, a);
 }
 
