@@ -835,6 +835,7 @@ gate_topk_kernel(GateArgs a) {
   // 2048 per round trip, next to the first tile's loads; the result is
   // published by the pipeline's first barrier.
   __shared__ float wg_kmax[4];
+  __shared__ int wg_full[4];
   {
     const float* nrm = a.norm + kvb0;
     float kpart = 0.f;
@@ -850,7 +851,12 @@ gate_topk_kernel(GateArgs a) {
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kpart = fmaxf(kpart, __shfl_xor(kpart, off));
-    if (lane == 0) wg_kmax[w] = kpart;
+    if (lane == 0) {
+      wg_kmax[w] = kpart;
+      // Leading tiles of this wave's scan that hold no own block and no
+      // block past its bound (none if it does not score).
+      wg_full[w] = !scoring ? 0 : a.causal ? jend / kTileB : min(jend, c) / kTileB;
+    }
   }
   // Tile pipeline. Step i passes a workgroup barrier behind which tile i+1
   // is in LDS, issues the MFMAs of tile i+1 and, while they run, folds the
@@ -933,7 +939,41 @@ gate_topk_kernel(GateArgs a) {
     if (do_cur && (tis == kSegTiles - 1 || i + 1 == my_tiles))
       flush_segment<QG, TT>(S, L, (i - tis) * kTileB, h);
   };
-  for (int i = 0; i < ntiles; i += 2) {
+  int i0 = 0;
+  if constexpr (DMA) {
+    // Steady stretch: a segment of kSegTiles steps at a time with no
+    // per-step conditions, while every wave of the workgroup has the
+    // segment's tiles and the next one full, and the tiles the segment
+    // loads exist (the counts are workgroup-uniform, so every wave takes
+    // the same barriers). The general step takes the rest.
+    const int n_full = min(min(wg_full[0], wg_full[1]), min(wg_full[2], wg_full[3]));
+    auto steady = [&](int i, int k, f32x16(&cur)[QG], f32x16(&nxt)[QG]) {
+      lds_dma_wait_n<Ops::NDMA>();
+      __syncthreads();
+      Ops::dma(a.kbar_hi + (kvb0 + (int64_t)(i + 3) * kTileB) * D, doff, lds_addr(buf(i + 3)), w);
+      char* next_buf = buf(i + 1);
+      if constexpr (std::is_same<Ops, GateOps<bf16, D>>::value && QG == 1) {
+        Ops::template scores_fold<TT>(next_buf, col, h, qf[0], nxt[0], cur[0], S[0], (unsigned)k << 4);
+      } else {
+        Ops::template scores<QG>(next_buf, col, h, qf, nxt);
+        absorb<QG, TT, false>(S, cur, k, i * kTileB + 4 * h, jend, c);
+        Ops::template interleave<QG, TT>();
+      }
+    };
+    static_assert(kSegTiles == 8, "the steady stretch is unrolled over one segment");
+    for (; i0 + kSegTiles + 1 <= n_full && i0 + kSegTiles + 2 < ntiles; i0 += kSegTiles) {
+      steady(i0, 0, acc_a, acc_b);
+      steady(i0 + 1, 1, acc_b, acc_a);
+      steady(i0 + 2, 2, acc_a, acc_b);
+      steady(i0 + 3, 3, acc_b, acc_a);
+      steady(i0 + 4, 4, acc_a, acc_b);
+      steady(i0 + 5, 5, acc_b, acc_a);
+      steady(i0 + 6, 6, acc_a, acc_b);
+      steady(i0 + 7, 7, acc_b, acc_a);
+      flush_segment<QG, TT>(S, L, i0 * kTileB, h);
+    }
+  }
+  for (int i = i0; i < ntiles; i += 2) {
     step(i, acc_a, acc_b);
     if (i + 1 < ntiles) step(i + 1, acc_b, acc_a);
   }
