@@ -940,7 +940,9 @@ gate_topk_kernel(GateArgs a) {
       flush_segment<QG, TT>(S, L, (i - tis) * kTileB, h);
   };
   int i0 = 0;
-  if constexpr (DMA) {
+  // (Only where it pays for its code size: the per-head bf16 gate with a
+  // short list, i.e. top_k up to 5.)
+  if constexpr (DMA && std::is_same<Ops, GateOps<bf16, D>>::value && QG == 1 && TT <= 6) {
     // Steady stretch: a segment of kSegTiles steps at a time with no
     // per-step conditions, while every wave of the workgroup has the
     // segment's tiles and the next one full, and the tiles the segment
@@ -951,14 +953,7 @@ gate_topk_kernel(GateArgs a) {
       lds_dma_wait_n<Ops::NDMA>();
       __syncthreads();
       Ops::dma(a.kbar_hi + (kvb0 + (int64_t)(i + 3) * kTileB) * D, doff, lds_addr(buf(i + 3)), w);
-      char* next_buf = buf(i + 1);
-      if constexpr (std::is_same<Ops, GateOps<bf16, D>>::value && QG == 1) {
-        Ops::template scores_fold<TT>(next_buf, col, h, qf[0], nxt[0], cur[0], S[0], (unsigned)k << 4);
-      } else {
-        Ops::template scores<QG>(next_buf, col, h, qf, nxt);
-        absorb<QG, TT, false>(S, cur, k, i * kTileB + 4 * h, jend, c);
-        Ops::template interleave<QG, TT>();
-      }
+      Ops::template scores_fold<TT>(buf(i + 1), col, h, qf[0], nxt[0], cur[0], S[0], (unsigned)k << 4);
     };
     static_assert(kSegTiles == 8, "the steady stretch is unrolled over one segment");
     for (; i0 + kSegTiles + 1 <= n_full && i0 + kSegTiles + 2 < ntiles; i0 += kSegTiles) {
