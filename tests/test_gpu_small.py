@@ -136,6 +136,46 @@ def test_exact_ties_prefer_lower_block():
     assert not (idx[6 * Bs:, 0] == 5).any()
 
 
+def _band_inputs(H, S, D, Bs):
+    """Every block copies one key pattern; block j adds j + 1 bf16 ulps to
+    one key of coordinate d_h, and every query has exactly +1 (head 0) or
+    -1 (head 1) there. The block means then differ by about 1e-4, strictly
+    ordered by j: inside the fast scores' rounding band, far above fp64
+    rounding."""
+    import synth
+    nb = S // Bs
+    rng = np.random.default_rng(77)
+    q = synth.round_to_bf16(rng.standard_normal((1, H, S, D)).astype(np.float32))
+    pat = synth.round_to_bf16(rng.standard_normal((H, Bs, D)).astype(np.float32))
+    k = np.repeat(pat[None, :, None], nb, axis=2).reshape(1, H, S, D).copy()
+    for h in range(H):
+        d = 5 + 17 * h
+        q[0, h, :, d] = 1.0 if h % 2 == 0 else -1.0
+        for j in range(nb):
+            x = np.float32(k[0, h, j * Bs, d])
+            u = np.frombuffer(x.tobytes(), np.uint32)[0] + np.uint32(0x10000 * (j + 1))
+            k[0, h, j * Bs, d] = np.frombuffer(np.uint32(u).tobytes(), np.float32)[0]
+    v = synth.round_to_bf16(rng.standard_normal((1, H, S, D)).astype(np.float32))
+    return q, k, v
+
+
+@pytest.mark.parametrize("top_k,causal", [(3, True), (5, False)])
+def test_full_rescan_when_every_block_is_in_the_band(top_k, causal):
+    """With the inputs of _band_inputs every query's rounding band reaches
+    past its tracked list, so the gate re-scores all its eligible blocks in
+    fp64 (one block per lane, the whole wave). The choice must be the
+    oracle's, row for row."""
+    import sparse_long_context_moba_amd as moba
+    H, S, D, Bs = 2, 4096, 128, 64
+    q, k, v = _band_inputs(H, S, D, Bs)
+    idx = moba.select(to_dev(q, "bf16"), to_dev(k, "bf16"), Bs, top_k, causal)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for h in range(H):
+        res = orc.forward_head(q[0, h], k[0, h], v[0, h], Bs, top_k, causal)
+        np.testing.assert_array_equal(idx[0, h], res["idx"], err_msg=f"head {h}")
+
+
 def test_deterministic_bitwise():
     import sparse_long_context_moba_amd as moba
     q, k, v = _inputs(13, 1, 2, 2048, 128, 128, "bf16")
