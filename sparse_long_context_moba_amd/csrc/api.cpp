@@ -70,7 +70,7 @@ struct Plan {
   int pooling;         // moba_pooling_t
   // the sequences
   bool uniform;
-  int64_t n_seq, T, nb_total, max_nb, w64, w128, w1024;  // totals over the sequences
+  int64_t n_seq, T, nb_total, max_nb, w128, w1024;  // totals over the sequences
   std::vector<int64_t> tab;  // varlen: the sequence table (rows of kSeqCols prefix sums)
   int64_t pairs;       // (query, kept past block) pairs over all heads
   int64_t max_tiles;   // upper bound on gather tiles
@@ -138,14 +138,13 @@ int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const c
   P.uniform = lens == nullptr;
   P.n_seq = n;
   auto len_of = [&](int64_t i) { return lens ? lens[i] : P.S; };
-  P.T = P.nb_total = P.max_nb = P.w64 = P.w128 = P.w1024 = 0;
+  P.T = P.nb_total = P.max_nb = P.w128 = P.w1024 = 0;
   if (!P.uniform) P.tab.assign((size_t)(n + 1) * kSeqCols, 0);
   for (int64_t i = 0; i <= n; ++i) {
     if (!P.uniform) {
       int64_t* row = &P.tab[(size_t)i * kSeqCols];
       row[kSeqTok] = P.T;
       row[kSeqBlk] = P.nb_total;
-      row[kSeqW64] = P.w64;
       row[kSeqW128] = P.w128;
       row[kSeqW1024] = P.w1024;
     }
@@ -157,7 +156,6 @@ int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const c
     P.T += L;
     P.nb_total += nbi;
     P.max_nb = std::max(P.max_nb, nbi);
-    P.w64 += seq_units(kSeqW64, L, P.Bs);
     P.w128 += seq_units(kSeqW128, L, P.Bs);
     P.w1024 += seq_units(kSeqW1024, L, P.Bs);
     if (P.uniform) break;  // every sequence alike: scale below
@@ -166,7 +164,6 @@ int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const c
     P.T *= n;
     P.nb = P.nb_total;
     P.nb_total *= n;
-    P.w64 *= n;
     P.w128 *= n;
     P.w1024 *= n;
   }
@@ -348,7 +345,7 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   return MOBA_OK;
 }
 
-AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, void* o, void* ws, bool dense) {
+AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, void* o, void* ws) {
   AttnArgs aa{};
   aa.q = q;
   aa.k = k;
@@ -357,7 +354,7 @@ AttnArgs attn_args(const Plan& P, const void* q, const void* k, const void* v, v
   aa.sq = seqs_of(P, ws);
   aa.heads = P.H;
   aa.block_size = P.Bs;
-  aa.diag_wgs = P.H * (diag_tile(P.Bs, dense) == 128 ? P.w128 : P.w64);
+  aa.diag_wgs = P.H * P.w128;
   aa.head_dim = (int)P.D;
   aa.bf16_in = P.bf16_in;
   aa.causal = P.causal;
@@ -408,7 +405,7 @@ int run_forward(const Plan& P, const void* q, const void* k, const void* v, void
                 void* workspace, hipStream_t s, float* lse = nullptr) {
   int st = run_select(P, q, k, block_idx, workspace, s, nullptr);
   if (st != MOBA_OK) return st;
-  AttnArgs aa = attn_args(P, q, k, v, o, workspace, false);
+  AttnArgs aa = attn_args(P, q, k, v, o, workspace);
   aa.lse_out = lse;
   aa.part_o = at<void>(workspace, P.part_o);
   aa.part_lse = at<float>(workspace, P.part_lse);
@@ -642,7 +639,7 @@ int impl_dense_forward(const moba_problem_t* p, const void* q, const void* k, co
   if (!k) return fail(MOBA_ERR_NULL, "k is NULL");
   if (!v) return fail(MOBA_ERR_NULL, "v is NULL");
   if (!o) return fail(MOBA_ERR_NULL, "o is NULL");
-  AttnArgs aa = attn_args(P, q, k, v, o, nullptr, true);
+  AttnArgs aa = attn_args(P, q, k, v, o, nullptr);
   MOBA_TRY(launch_dense(aa, static_cast<hipStream_t>(stream)), "dense launch");
   return MOBA_OK;
 }

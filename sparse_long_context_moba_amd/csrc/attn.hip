@@ -10,10 +10,12 @@
 //                 streams that block's K/V through LDS in 64-key subtiles and
 //                 writes, per (query, slot), the normalised partial output
 //                 and its log2-sum-exp.
-//  diag_merge   — the own block. A workgroup takes 32*NW consecutive queries
-//                 of one block, starts each query's online softmax from its
+//  diag_merge   — the own block. A workgroup takes 128 consecutive queries
+//                 (32 per wave; a wave's queries share one block, which is a
+//                 multiple of 64 long, while a workgroup's may span two or
+//                 more blocks), starts each query's online softmax from its
 //                 past partials (the log-sum-exp merge, done first), attends
-//                 the block's keys up to the query (causal) and writes o in
+//                 its block's keys up to the query (causal) and writes o in
 //                 the input dtype.
 //  dense_attn   — plain full attention (causal or not) with the same engine,
 //                 the baseline MoBA is measured against.
@@ -114,8 +116,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   // Work item -> (sequence, query head, tile of M queries); within a
   // sequence heavier tiles (later in it) come first, heads interleaved.
-  constexpr int COL = M == 128 ? kSeqW128 : kSeqW64;
-  static_assert(M == 128 || M == 64, "tiles of 64 or 128 queries");
+  constexpr int COL = kSeqW128;
+  static_assert(M == 128, "tiles of 128 queries");
   const int64_t item = blockIdx.x;
   const int64_t si = seq_find_u(a.sq, COL, a.heads, item, a.block_size);
   const SeqAt sa = seq_at_u(a.sq, si, a.block_size);
@@ -126,17 +128,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int len = (int)sa.len;
   const int64_t row0 = sa.tok0 * a.heads + hq * sa.len;  // row of token 0 of this head
   const int q0 = (int)(tile * M);
-  const int c = (int)(q0 / a.block_size);
-  const int kb = DENSE ? 0 : (int)(c * a.block_size);
-  // Keys end at the tile's last query (causal), else at the block's (or,
-  // dense, the sequence's) end; never past the sequence.
-  const int kend = a.causal ? min(q0 + M, len) : (DENSE ? len : (int)min<int64_t>(kb + a.block_size, len));
   const int qw0 = q0 + 32 * w;
   const int t = qw0 + col;
   // Lanes past the sequence's end (its last tile may be partial) compute on
   // its last query and store nothing.
   const int tq = min(t, len - 1);
   const bool wave_on = qw0 < len;
+  // This wave's block c and its keys [kbw, kew); the tile's key stream runs
+  // from the block of its first query to its last query (causal), else to
+  // the end of that query's block (or, dense, of the sequence); never past
+  // the sequence. Subtiles of another wave's block are skipped.
+  const int bs = (int)a.block_size;
+  const int c = min(qw0, len - 1) / bs;
+  const int kbw = DENSE ? 0 : c * bs;
+  const int kew = DENSE ? len : min(kbw + bs, len);
+  const int qlast = min(q0 + M, len) - 1;
+  const int kb = DENSE ? 0 : (q0 / bs) * bs;
+  const int kend = a.causal ? qlast + 1 : (DENSE ? len : min((qlast / bs + 1) * bs, len));
 
   E eng;
   eng.init();
@@ -222,21 +230,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const float sl2 = kLog2e / __builtin_sqrtf((float)D);
   const int nsub = (kend - kb + kSub - 1) / kSub;
   const int last_rows = (kend - kb) - kSub * (nsub - 1);  // keys of the last subtile (1..64)
-  // Subtiles entirely before the workgroup's first query need no mask; with
-  // causal attention the last subtiles hold the diagonal (and any partial
-  // last subtile, whose padding keys lie after every valid query). Without
-  // it only a partial last subtile needs one: keys at or past kend.
-  const int nfree = a.causal ? (q0 - kb) / kSub : (last_rows < kSub ? nsub - 1 : nsub);
-  const int lim = a.causal ? t : kend - 1;  // the last key a lane may attend
+  // block_size and kb are multiples of 64, so a subtile lies wholly inside
+  // or outside the wave's block. Causal: a subtile ending at or before the
+  // wave's first query needs no mask (its keys come before every query of
+  // the wave and before the sequence's end), one starting after its last
+  // query is skipped, the rest are masked at the lane's query. Otherwise
+  // only a partial last subtile of the block is masked, at kew - 1.
+  const int lim = a.causal ? t : kew - 1;  // the last key a lane may attend
   stream_subtiles<E, NT>(bufA, bufB, kp, vp, nsub, last_rows, D, tid, start, [&](const char* buf, int sub) {
     if (!wave_on) return;
-    if (sub < nfree) {
-      eng.template step<false>(buf, lane, 0, 0, sl2);
-    } else {
-      const int key0 = kb + sub * kSub;
-      // Skip a subtile whose keys all come after every query of this wave.
-      if (!a.causal || key0 <= qw0 + 31) eng.template step<true>(buf, lane, key0, lim, sl2);
-    }
+    const int key0 = kb + sub * kSub;
+    if (key0 < kbw || key0 >= kew || (a.causal && key0 > qw0 + 31)) return;
+    if (key0 + kSub <= (a.causal ? qw0 : kew)) eng.template step<false>(buf, lane, 0, 0, sl2);
+    else eng.template step<true>(buf, lane, key0, lim, sl2);
   });
   if (!wave_on) return;
 
@@ -285,24 +291,14 @@ hipError_t gather_t(const AttnArgs& a, hipStream_t s) {
 template <typename T, int D, bool DENSE>
 hipError_t diag_t(const AttnArgs& a, hipStream_t s) {
   using E = typename EngOf<T, D>::type;
-  // 128-query tiles when they stay inside one block, else 64 (diag_tile);
-  // a.diag_wgs counts the tiles of that size over all sequences and heads.
-  const bool four = diag_tile(a.block_size, DENSE) == 128;
+  // 128-query tiles; a.diag_wgs counts them over all sequences and heads.
   const char* name = DENSE ? "dense_attn" : "diag_merge";
   constexpr int lds = dyn_lds_bytes<E>();
-  if (four) {
-    auto kern = diag_attn_kernel<T, D, 4, DENSE>;
-    hipError_t e = prep_lds(kern, lds);
-    if (e != hipSuccess) return e;
-    KernelTimer timer(s, name);
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.diag_wgs), dim3(256), lds, s, a);
-  } else {
-    auto kern = diag_attn_kernel<T, D, 2, DENSE>;
-    hipError_t e = prep_lds(kern, lds);
-    if (e != hipSuccess) return e;
-    KernelTimer timer(s, name);
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.diag_wgs), dim3(128), lds, s, a);
-  }
+  auto kern = diag_attn_kernel<T, D, 4, DENSE>;
+  hipError_t e = prep_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  KernelTimer timer(s, name);
+  hipLaunchKernelGGL(kern, dim3((unsigned)a.diag_wgs), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 }  // namespace

@@ -22,9 +22,10 @@ namespace moba {
 //                path (the same K copy read through the LDS transpose
 //                load); subtiles double-buffered; one fp32 partial per
 //                (query, slot);
-//  dq_own      — the own block, 128 (or 64) queries per workgroup, causal
-//                mask, double-buffered; it then adds the slots' partials in
-//                slot order and writes dq (no atomics);
+//  dq_own      — the own block, 128 queries per workgroup (each wave on
+//                its own block's keys), causal mask, double-buffered; it
+//                then adds the slots' partials in slot order and writes dq
+//                (no atomics);
 //  dkv, dk     — key-major: a workgroup holds 128 (or 64) keys of one block
 //                (32 per wave, as the B operand the way the forward holds
 //                queries) and streams 64-row subtiles of the queries that
@@ -32,9 +33,9 @@ namespace moba {
 //                queries (gathered rows), for every query head of the
 //                key/value head; blocks in order, heaviest first. dkv
 //                (software-pipelined over two buffer sets) accumulates
-//                dV^T += dO^T P, dk (single-buffered) dK^T += Q^T dS, both
-//                on the P.V path; one pass for both would not fit the
-//                register file.
+//                dV^T += dO^T P for 128 keys, dk (single-buffered)
+//                dK^T += Q^T dS, and dV for 64 keys, both on the P.V path;
+//                one pass for both would not fit the register file.
 namespace {
 
 // C[row][lane column] for 64 LDS rows (K-swizzled layout) against the B
@@ -235,22 +236,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   if (valid) store_row_f32<D>(a.dq_part + (int64_t)ev * D, acc, h, 1.f / __builtin_sqrtf((float)D));
 }
 
-// The own block: 32 * NW consecutive queries of one head.
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
+// The own block: 128 consecutive queries of one head, 32 per wave. A
+// wave's queries share one block (block_size and seq_len are multiples of
+// 64); the workgroup's may span blocks, and each wave takes only its own
+// block's subtiles of the workgroup's key stream. The last tile may hold
+// only 64 queries (waves 2 and 3 then compute nothing and store nothing).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
   using E = EngBF16<D>;
-  constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, M = 32 * NW;
+  constexpr int NT = 256, KC = D / 16, DT = D / 32, M = 128;
   // Double-buffered (64 KB): registers already limit a compute unit to two
   // of these workgroups (four waves each), which the LDS still holds.
   __shared__ __align__(16) char bk0[E::TB], bv0[E::TB], bk1[E::TB], bv1[E::TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int64_t ntile = a.seq_len / M;
+  const int64_t ntile = (a.seq_len + M - 1) / M;
   const int64_t bh = blockIdx.x / ntile;
   const int q0 = (int)((blockIdx.x % ntile) * M);
-  const int c = (int)(q0 / a.block_size);
-  const int kb = (int)(c * a.block_size);
-  const int kend = a.causal ? q0 + M : (int)min<int64_t>(kb + a.block_size, a.seq_len);
-  const int t = q0 + 32 * w + col;
+  const int len = (int)a.seq_len, bs = (int)a.block_size;
+  const int qw0 = q0 + 32 * w;
+  const bool wave_on = qw0 < len;
+  // This wave's block c and its keys [kbw, kew); the stream runs from the
+  // block of the tile's first query to its last query (causal), else to
+  // the end of that query's block.
+  const int c = min(qw0, len - 1) / bs;
+  const int kbw = c * bs, kew = min(kbw + bs, len);
+  const int qlast = min(q0 + M, len) - 1;
+  const int kb = (q0 / bs) * bs;
+  const int kend = a.causal ? qlast + 1 : min((qlast / bs + 1) * bs, len);
+  const int t = wave_on ? qw0 + col : len - 1;
   const int64_t row = bh * a.seq_len + t;
   bf16x8 qf[KC], gf[KC];
   load_frags<D>(qf, reinterpret_cast<const bf16*>(a.q) + row * D, h);
@@ -280,14 +293,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const char* bk = odd ? bk1 : bk0;
     const char* bv = odd ? bv1 : bv0;
     const int key0 = kb + sub * kSub;
-    if (a.causal && key0 + kSub > q0 + 32 * w) {
-      if (key0 <= q0 + 32 * w + 31) dq_step<D, true>(bk, bv, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
-    } else {
-      dq_step<D, false>(bk, bv, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+    if (wave_on && key0 >= kbw && key0 < kew) {
+      if (a.causal && key0 + kSub > qw0) {
+        if (key0 <= qw0 + 31) dq_step<D, true>(bk, bv, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
+      } else {
+        dq_step<D, false>(bk, bv, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+      }
     }
     lds_dma_wait();
     __syncthreads();
   }
+  if (!wave_on) return;
   // dq = own-block part + the past slots' partials (written by dq_past, an
   // earlier launch) in slot order, rounded once to bf16.
   const float scale = 1.f / __builtin_sqrtf((float)D);
@@ -529,8 +545,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   store_row_bf16<D>(dst, acc, h, PASS == 0 ? 1.f : 1.f / __builtin_sqrtf((float)D));
 }
 
-// dK (launched with PASS = 1; PASS = 0 would give dV) for 32 * NW keys of
-// one block of one key/value head, single-buffered: each 64-row query
+// dK (PASS = 1), or dV for 64 keys (PASS = 0), for 32 * NW keys of one
+// block of one key/value head, single-buffered: each 64-row query
 // subtile is staged (row numbers, log-sum-exps and deltas, for listed rows
 // from list_meta_kernel's contiguous arrays, then the rows of Q and dO,
 // K-swizzled) and then computed; dK^T += Q^T dS reads Q transposed from
@@ -664,11 +680,7 @@ hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
   }
   {
     KernelTimer t(s, "bwd_dq_own");
-    // 128 queries per workgroup where tiles of 128 stay inside one block.
-    if (a.seq_len % 128 == 0 && a.block_size % 128 == 0)
-      hipLaunchKernelGGL((dq_own_kernel<D, 4>), dim3((unsigned)(a.bh * (a.seq_len / 128))), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((dq_own_kernel<D, 2>), dim3((unsigned)(a.bh * (a.seq_len / 64))), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(dq_own_kernel<D>, dim3((unsigned)(a.bh * ((a.seq_len + 127) / 128))), dim3(256), 0, s, a);
   }
   // 128 keys per workgroup where every block length is a multiple of 128,
   // else 64.
@@ -676,9 +688,11 @@ hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
   const bool wide = a.block_size % 128 == 0 && last % 128 == 0;
   const int64_t kv_wgs = (a.bh / a.group) * a.n_blocks * (a.block_size / (wide ? 128 : 64));
   {
+    // 64 keys: the single-buffered kernel (32 KB of LDS) keeps two waves per
+    // SIMD, which the pipelined one (64 KB for two waves) would not.
     KernelTimer t(s, "bwd_dv");
     if (wide) hipLaunchKernelGGL((dkv_kernel<D, 0, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dkv_kernel<D, 0, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((dk_kernel<D, 0, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
   }
   {
     KernelTimer t(s, "bwd_dk");

@@ -16,7 +16,7 @@ typedef __bf16 bf16;
 // blk0_i * heads + h * nb_i (nb_i = ceil(len_i / block_size)).
 // Table row i (0 <= i <= n) holds the sums over the sequences before i;
 // row n holds the totals.
-enum SeqCol { kSeqTok = 0, kSeqBlk = 1, kSeqW64 = 2, kSeqW128 = 3, kSeqW1024 = 4 };
+enum SeqCol { kSeqTok = 0, kSeqBlk = 1, kSeqW128 = 2, kSeqW1024 = 3 };
 constexpr int kSeqCols = 8;
 struct Seqs {
   const int64_t* tab;  // [(n + 1) * kSeqCols] or nullptr (uniform)
@@ -29,7 +29,6 @@ __host__ __device__ __forceinline__ int64_t seq_units(int col, int64_t len, int6
   switch (col) {
     case kSeqTok: return len;
     case kSeqBlk: return (len + block_size - 1) / block_size;
-    case kSeqW64: return (len + 63) / 64;
     case kSeqW128: return (len + 127) / 128;
     default: return (len + 1023) / 1024;
   }
@@ -118,7 +117,7 @@ struct AttnArgs {
   void* o;
   Seqs sq;                    // the sequences
   int64_t heads, block_size;
-  int64_t diag_wgs;           // own-block (or dense) workgroups: heads * sum ceil(len / tile)
+  int64_t diag_wgs;           // own-block (or dense) workgroups: heads * sum ceil(len / 128)
   int head_dim;
   bool bf16_in;
   bool causal;
@@ -132,9 +131,6 @@ struct AttnArgs {
   int group;                  // query heads per key/value head
   float* lse_out;             // optional [query rows]: natural-log log-sum-exp per query (own-block kernel)
 };
-// Queries per own-block (and dense) tile: 128 where tiles of 128 stay in
-// one block (block_size a multiple of 128, or dense attention), else 64.
-inline int diag_tile(int64_t block_size, bool dense) { return (dense || block_size % 128 == 0) ? 128 : 64; }
 constexpr int kGatherTileM = 128;
 // Gather workgroups for a bound on the number of tiles (a multiple of the
 // 8 XCDs, see tile_map_kernel).
