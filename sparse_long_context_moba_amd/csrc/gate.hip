@@ -1001,9 +1001,14 @@ gate_topk_kernel(GateArgs a) {
       // A shared gate's fp32 query sum adds at most (nq - 1) roundings of
       // 2^-24 per coordinate, covered by nq * 2^-22 against sum_h ||q_h||.
       const float gam = Ops::gamma() + (SHARED ? (float)nq * 2.3841858e-07f : 0.f);
+      // Fast scores are bounded by ||q|| max ||kbar||; where that bound
+      // leaves fp32 they may be infinite or NaN, which the lists drop, so
+      // such a query is re-scanned in full (decided on the norms alone: the
+      // build assumes no NaNs in comparisons).
+      const bool beyond = qnorm[g] > 3.0e38f || kmax > 3.0e38f || qnorm[g] * kmax > 3.0e38f;
       const float eps = gam * qnorm[g] * kmax + 1e-30f;
-      const bool amb = !(ls[m - 1] - ls[m] > 2.f * eps);
-      const bool tracked = n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps;
+      const bool amb = beyond || !(ls[m - 1] - ls[m] > 2.f * eps);
+      const bool tracked = !beyond && (n_elig <= TT || ls[TT - 1] < ls[m - 1] - 2.f * eps);
       rescore_ambiguous<TQ, D, TT>(a, qrow0, len, nq, kvb0, tw + 32 * g, c, jend, amb && h == 0 && qvalid, tracked,
                                    lj, sel, lane, col, reinterpret_cast<double*>(tile) + w * D);
     }

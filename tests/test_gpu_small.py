@@ -176,6 +176,36 @@ def test_full_rescan_when_every_block_is_in_the_band(top_k, causal):
         np.testing.assert_array_equal(idx[0, h], res["idx"], err_msg=f"head {h}")
 
 
+@pytest.mark.parametrize("case", ["query-norm-overflows", "scores-overflow", "key-norm-huge", "query-tiny"])
+def test_gate_with_extreme_magnitudes(case):
+    """The gate's fast scores and rounding bound are fp32. A query whose
+    norm overflows fp32, or a query and pooled key whose norms multiply
+    past it (fast scores that may be infinite or NaN), is re-scanned in
+    full in fp64; a huge pooled key or a tiny query only widens the band.
+    The routing must be the oracle's, row for row."""
+    import sparse_long_context_moba_amd as moba
+    H, S, D, Bs = 2, 2048, 128, 128
+    q, k, v = _inputs(41, 1, H, S, D, Bs, "bf16")
+    if case == "query-norm-overflows":
+        q[0, 0, 1000:1100, 3] = 2.0 ** 120  # exact in bf16; its square is not finite in fp32
+        q[0, 1, 1500:1600, 90] = -(2.0 ** 120)
+    elif case == "scores-overflow":
+        q[0, :, 700:900, 11] = 2.0 ** 100
+        k[0, :, 2 * Bs:3 * Bs, 11] = 2.0 ** 100  # q . kbar near 2^200 for those queries
+    elif case == "key-norm-huge":
+        k[0, 0, 3 * Bs:4 * Bs, 7] = 2.0 ** 120
+        k[0, 1, 9 * Bs:10 * Bs, 11] = -(2.0 ** 120)
+    else:
+        q = _round(q * np.float32(2.0 ** -100), "bf16")
+    say(f"[gpu] extreme magnitudes: {case}")
+    idx = moba.select(to_dev(q, "bf16"), to_dev(k, "bf16"), Bs, 3, True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for h in range(H):
+        res = orc.forward_head(q[0, h], k[0, h], v[0, h], Bs, 3, True)
+        np.testing.assert_array_equal(idx[0, h], res["idx"], err_msg=f"{case} head {h}")
+
+
 def test_deterministic_bitwise():
     import sparse_long_context_moba_amd as moba
     q, k, v = _inputs(13, 1, 2, 2048, 128, 128, "bf16")
