@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 6
+#define MOBA_ABI_VERSION 7
 
 typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype_t;
 
@@ -247,6 +247,37 @@ moba_status_t moba_workspace_size_varlen(const moba_problem_t* p, const int64_t*
 moba_status_t moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
                         const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* moba_forward_varlen plus each query's natural-log log-sum-exp (as
+ * moba_forward_lse), for moba_backward_varlen.
+ *   lse — device float32, sequence i as [heads, len_i] from element
+ *         cu_seqlens[i] * heads; must not be NULL.
+ * Everything else as moba_forward_varlen (same workspace size). */
+moba_status_t moba_forward_varlen_lse(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                            const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* MoBA backward of a varlen batch: each sequence's dq, dk, dv exactly as
+ * moba_backward computes them for that sequence alone (sequences never
+ * interact: the cu_seqlens packing of [R] §3.3). Sequence i is the uniform
+ * problem of batch 1 and seq_len len_i at its offset; the sequences run one
+ * after another on the stream, each a launch chain of its own, reusing the
+ * workspace.
+ *   cu_seqlens, p — as moba_forward_varlen; bf16 inputs, every length a
+ *           multiple of 64 (MOBA_ERR_UNSUPPORTED names the first sequence
+ *           that is not);
+ *   q, k, v, o, dout, dq — the sequences back to back as q in
+ *           moba_forward_varlen; dk, dv as k and v there;
+ *   block_idx, lse — from moba_forward_varlen_lse on the same batch;
+ *   workspace — at least moba_backward_workspace_size_varlen bytes (the
+ *           largest one sequence needs), 256-byte aligned.
+ * Every sequence is validated before anything is launched. */
+moba_status_t moba_backward_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens,
+                                        int64_t n_seqs, size_t* bytes);
+moba_status_t moba_backward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                         const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const int32_t* block_idx, const float* lse, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Full causal softmax attention on the same layout, the method MoBA
  * approximates: with top_k covering every block MoBA becomes exactly this,

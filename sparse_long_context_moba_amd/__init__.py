@@ -22,8 +22,8 @@ from ._lib import (MOBA_BF16, MOBA_F32, moba_abi_version, moba_dense_causal_forw
                    moba_forward, moba_forward_lse, moba_last_error, moba_debug_pool, moba_problem_t,
                    moba_debug_gate_topk, moba_status_str,
                    moba_timing_enable, moba_timing_read, moba_workspace_size,
-                   moba_forward_varlen, moba_workspace_size_varlen, moba_backward,
-                   moba_backward_workspace_size)
+                   moba_forward_varlen, moba_forward_varlen_lse, moba_workspace_size_varlen, moba_backward,
+                   moba_backward_workspace_size, moba_backward_varlen, moba_backward_workspace_size_varlen)
 
 __all__ = ["MobaError", "forward", "dense", "pool", "select", "problem", "workspace_bytes",
            "timing", "moba_abi_version", "moba_forward", "moba_dense_causal_forward", "moba_dense_forward",
@@ -188,7 +188,7 @@ def backward(q, k, v, o, dout, idx, lse, block_size: int, top_k: int, causal: bo
 
 
 def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int, causal: bool = True,
-                   pooling: str = "mean", kv_heads: int = 0, gate_shared: bool = False):
+                   pooling: str = "mean", kv_heads: int = 0, gate_shared: bool = False, return_lse: bool = False):
     """MoBA over a varlen batch: sequences of different lengths (any length
     >= 1) back to back, run as one launch chain.
 
@@ -196,7 +196,8 @@ def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int,
     rows from row cu_seqlens[i] * heads (see pack_varlen); k, v likewise
     with kv_heads (0 = heads). cu_seqlens: host ints, cu_seqlens[0] = 0.
     Returns (o like q, block_idx int32 [sum_i heads * len_i, top_k] in the
-    same order)."""
+    same order), and with return_lse also lse float32 [sum_i heads * len_i]
+    (each query's natural-log log-sum-exp, for backward_varlen)."""
     if q.dim() != 2:
         raise ValueError(f"q must be [tokens * heads, head_dim], got shape {tuple(q.shape)}")
     hkv = int(kv_heads) or int(heads)
@@ -222,9 +223,50 @@ def forward_varlen(q, k, v, cu_seqlens, heads: int, block_size: int, top_k: int,
     o = torch.empty_like(q)
     bi = torch.empty((q.shape[0], int(top_k)), dtype=torch.int32, device=q.device)
     with torch.cuda.device(q.device):
+        if return_lse:
+            lse = torch.empty(q.shape[0], dtype=torch.float32, device=q.device)
+            _check(moba_forward_varlen_lse(p, cu, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                           bi.data_ptr(), lse.data_ptr(), ws.data_ptr(), n, _stream(q.device)),
+                   "moba_forward_varlen_lse")
+            return o, bi, lse
         _check(moba_forward_varlen(p, cu, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), bi.data_ptr(),
                                    ws.data_ptr(), n, _stream(q.device)), "moba_forward_varlen")
     return o, bi
+
+
+def backward_varlen(q, k, v, o, dout, idx, lse, cu_seqlens, heads: int, block_size: int, top_k: int,
+                    causal: bool = True, kv_heads: int = 0, gate_shared: bool = False):
+    """MoBA backward (bf16) of a varlen batch laid out as forward_varlen's:
+    (dq like q, dk like k, dv like v), each sequence's gradients as
+    backward computes them for that sequence alone; idx and lse from
+    forward_varlen(..., return_lse=True) on the same batch."""
+    if q.dim() != 2:
+        raise ValueError(f"q must be [tokens * heads, head_dim], got shape {tuple(q.shape)}")
+    for t in (q, k, v, o, dout):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 2 or t.shape[1] != q.shape[1] \
+                or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o and dout must be contiguous 2-D tensors on one GPU, of one head_dim and dtype")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {q.dtype}")
+    hkv = int(kv_heads) or int(heads)
+    if o.shape != q.shape or dout.shape != q.shape or k.shape != v.shape or k.shape[0] * heads != q.shape[0] * hkv:
+        raise ValueError("o and dout must be shaped like q, and k, v must hold kv_heads rows per token of q")
+    cu = [int(x) for x in cu_seqlens]
+    if q.shape[0] != cu[-1] * heads:
+        raise ValueError(f"q has {q.shape[0]} rows, cu_seqlens and heads give {cu[-1] * heads}")
+    p = moba_problem_t(len(cu) - 1, int(heads), cu[-1], q.shape[1], int(block_size), int(top_k),
+                       1 if causal else 0, _DTYPES[q.dtype], 0, 0, int(kv_heads), 1 if gate_shared else 0, 0)
+    st, n = moba_backward_workspace_size_varlen(p, cu)  # validates every sequence through the library first
+    _check(st, "moba_backward_workspace_size_varlen")
+    check_buffer(idx, "idx", (q.shape[0], int(top_k)), torch.int32, q.device)
+    check_buffer(lse, "lse", (q.shape[0],), torch.float32, q.device)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        _check(moba_backward_varlen(p, cu, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                    idx.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    ws.data_ptr(), n, _stream(q.device)), "moba_backward_varlen")
+    return dq, dk, dv
 
 
 def pack_varlen(seqs):

@@ -21,8 +21,9 @@ STATUS_NAMES = {0: "MOBA_OK", 1: "MOBA_ERR_NULL", 2: "MOBA_ERR_SHAPE", 3: "MOBA_
 EXPORTED = ["moba_abi_version", "moba_status_str", "moba_last_error", "moba_workspace_size",
             "moba_forward", "moba_forward_noalloc", "moba_forward_lse", "moba_dense_causal_forward", "moba_dense_forward",
             "moba_debug_pool", "moba_debug_gate_topk",
-            "moba_workspace_size_varlen", "moba_forward_varlen",
+            "moba_workspace_size_varlen", "moba_forward_varlen", "moba_forward_varlen_lse",
             "moba_backward_workspace_size", "moba_backward",
+            "moba_backward_workspace_size_varlen", "moba_backward_varlen",
             "moba_timing_enable", "moba_timing_read"]
 
 
@@ -61,8 +62,14 @@ def _load():
                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moba_forward_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, vp, vp, vp, vp, i32p, vp,
                                  sz, vp], ctypes.c_int),
+        "moba_forward_varlen_lse": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, vp, vp, vp, vp, i32p, vp,
+                                     vp, sz, vp], ctypes.c_int),
         "moba_backward_workspace_size": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moba_backward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "moba_backward_workspace_size_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                                 ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+        "moba_backward_varlen": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "moba_timing_enable": ([ctypes.c_int], ctypes.c_int),
         "moba_timing_read": ([ctypes.POINTER(moba_kernel_time_t), ctypes.c_int,
                               ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
@@ -145,6 +152,31 @@ def moba_forward_varlen(problem, cu_seqlens, q, k, v, o, block_idx, workspace, w
     return lib().moba_forward_varlen(ctypes.byref(problem) if problem is not None else None, arr,
                                      n if n_seqs is None else n_seqs, q, k, v, o, block_idx, workspace,
                                      workspace_bytes, stream)
+
+
+def moba_forward_varlen_lse(problem, cu_seqlens, q, k, v, o, block_idx, lse, workspace, workspace_bytes, stream,
+                            n_seqs=None) -> int:
+    arr, n = _cu(cu_seqlens)
+    return lib().moba_forward_varlen_lse(ctypes.byref(problem) if problem is not None else None, arr,
+                                         n if n_seqs is None else n_seqs, q, k, v, o, block_idx, lse, workspace,
+                                         workspace_bytes, stream)
+
+
+def moba_backward_workspace_size_varlen(problem, cu_seqlens, n_seqs=None):
+    """-> (status, bytes); n_seqs defaults to len(cu_seqlens) - 1."""
+    arr, n = _cu(cu_seqlens)
+    out = ctypes.c_size_t(0)
+    st = lib().moba_backward_workspace_size_varlen(ctypes.byref(problem) if problem is not None else None, arr,
+                                                   n if n_seqs is None else n_seqs, ctypes.byref(out))
+    return st, out.value
+
+
+def moba_backward_varlen(problem, cu_seqlens, q, k, v, o, dout, block_idx, lse, dq, dk, dv, workspace,
+                         workspace_bytes, stream, n_seqs=None) -> int:
+    arr, n = _cu(cu_seqlens)
+    return lib().moba_backward_varlen(ctypes.byref(problem) if problem is not None else None, arr,
+                                      n if n_seqs is None else n_seqs, q, k, v, o, dout, block_idx, lse, dq, dk,
+                                      dv, workspace, workspace_bytes, stream)
 
 
 def moba_dense_causal_forward(problem, q, k, v, o, stream) -> int:

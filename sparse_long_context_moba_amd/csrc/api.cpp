@@ -522,25 +522,25 @@ int impl_backward_workspace_size(const moba_problem_t* p, size_t* bytes) {
   return MOBA_OK;
 }
 
-int impl_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
-                  const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk, void* dv,
-                  void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  Plan P;
-  BwdPlan B;
-  int st = plan_backward_problem(p, &P, &B);
-  if (st != MOBA_OK) return st;
-  const void* ins[] = {q, k, v, o, dout, block_idx, lse, dq, dk, dv};
+// The backward's pointers and workspace, checked once every problem is valid.
+int check_backward_buffers(const void* const (&ins)[10], size_t need, const void* workspace,
+                           size_t workspace_bytes) {
   const char* names[] = {"q", "k", "v", "o", "dout", "block_idx", "lse", "dq", "dk", "dv"};
   for (int i = 0; i < 10; ++i)
     if (!ins[i]) return fail(MOBA_ERR_NULL, std::string(names[i]) + " is NULL");
-  if (workspace_bytes < B.total)
+  if (workspace_bytes < need)
     return fail(MOBA_ERR_WORKSPACE, "workspace_bytes " + std::to_string(workspace_bytes) + " < required " +
-                                        std::to_string(B.total));
+                                        std::to_string(need));
   if (!workspace) return fail(MOBA_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return fail(MOBA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOBA_OK;
+}
+
+// The whole backward of one validated (uniform) problem, queued on s.
+int run_backward(const Plan& P, const BwdPlan& B, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, hipStream_t s) {
   BwdArgs ba{};
   ba.q = q;
   ba.k = k;
@@ -595,6 +595,79 @@ int impl_backward(const moba_problem_t* p, const void* q, const void* k, const v
   return MOBA_OK;
 }
 
+int impl_backward(const moba_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const int32_t* block_idx, const float* lse, void* dq, void* dk, void* dv,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan P;
+  BwdPlan B;
+  int st = plan_backward_problem(p, &P, &B);
+  if (st != MOBA_OK) return st;
+  st = check_backward_buffers({q, k, v, o, dout, block_idx, lse, dq, dk, dv}, B.total, workspace, workspace_bytes);
+  if (st != MOBA_OK) return st;
+  return run_backward(P, B, q, k, v, o, dout, block_idx, lse, dq, dk, dv, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+// A varlen batch's backward: every sequence planned as its own uniform
+// problem (batch 1, seq_len len_i); the workspace is the largest of theirs.
+int plan_backward_varlen(const moba_problem_t* p, const int64_t* cu, int64_t n, std::vector<Plan>* Ps,
+                         std::vector<BwdPlan>* Bs, size_t* need) {
+  Plan V;
+  int st = varlen_plan(p, cu, n, &V);  // lengths, batch and seq_len against cu_seqlens
+  if (st != MOBA_OK) return st;
+  Ps->assign((size_t)n, Plan{});
+  Bs->assign((size_t)n, BwdPlan{});
+  *need = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    moba_problem_t one = *p;
+    one.batch = 1;
+    one.seq_len = cu[i + 1] - cu[i];
+    st = plan_backward_problem(&one, &(*Ps)[(size_t)i], &(*Bs)[(size_t)i]);
+    if (st != MOBA_OK) return fail(st, "sequence " + std::to_string(i) + ": " + g_err);
+    *need = std::max(*need, (*Bs)[(size_t)i].total);
+  }
+  return MOBA_OK;
+}
+
+int impl_backward_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                                        size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
+  std::vector<Plan> Ps;
+  std::vector<BwdPlan> Bs;
+  return plan_backward_varlen(p, cu_seqlens, n_seqs, &Ps, &Bs, bytes);
+}
+
+int impl_backward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, const void* q,
+                         const void* k, const void* v, const void* o, const void* dout, const int32_t* block_idx,
+                         const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_err.clear();
+  std::vector<Plan> Ps;
+  std::vector<BwdPlan> Bs;
+  size_t need = 0;
+  int st = plan_backward_varlen(p, cu_seqlens, n_seqs, &Ps, &Bs, &need);
+  if (st != MOBA_OK) return st;
+  st = check_backward_buffers({q, k, v, o, dout, block_idx, lse, dq, dk, dv}, need, workspace, workspace_bytes);
+  if (st != MOBA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // Sequence i is a uniform [1, heads, len_i, D] problem from token
+  // cu_seqlens[i]; the sequences run one after another on the stream and
+  // reuse the workspace (bf16 inputs: 2 bytes per element).
+  const int64_t H = p->heads, Hkv = Ps[0].Hkv, D = p->head_dim, K = p->top_k;
+  for (int64_t i = 0; i < n_seqs; ++i) {
+    const int64_t t0 = cu_seqlens[i];
+    auto qo = [&](const void* x) { return static_cast<const char*>(x) + t0 * H * D * 2; };
+    auto kv = [&](const void* x) { return static_cast<const char*>(x) + t0 * Hkv * D * 2; };
+    st = run_backward(Ps[(size_t)i], Bs[(size_t)i], qo(q), kv(k), kv(v), qo(o), qo(dout), block_idx + t0 * H * K,
+                      lse + t0 * H, const_cast<char*>(qo(dq)), const_cast<char*>(kv(dk)),
+                      const_cast<char*>(kv(dv)), workspace, s);
+    if (st != MOBA_OK) return st;
+  }
+  return MOBA_OK;
+}
+
 int impl_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(MOBA_ERR_NULL, "bytes pointer is NULL");
@@ -607,17 +680,18 @@ int impl_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlen
 
 int impl_forward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs, const void* q,
                         const void* k, const void* v, void* o, int32_t* block_idx, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, float* lse = nullptr, bool want_lse = false) {
   g_err.clear();
   Plan P;
   int st = varlen_plan(p, cu_seqlens, n_seqs, &P);
   if (st != MOBA_OK) return st;
   st = check_tensors(q, k, v, o, block_idx);
   if (st != MOBA_OK) return st;
+  if (want_lse && !lse) return fail(MOBA_ERR_NULL, "lse is NULL");
   st = check_ws(P, workspace, workspace_bytes);
   if (st != MOBA_OK) return st;
   // Every sequence is validated above; one launch chain covers them all.
-  return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream));
+  return run_forward(P, q, k, v, o, block_idx, workspace, static_cast<hipStream_t>(stream), lse);
 }
 
 int impl_dense_forward(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
@@ -816,6 +890,26 @@ moba_status_t moba_forward_varlen(const moba_problem_t* p, const int64_t* cu_seq
                                   const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return st_(impl_forward_varlen(p, cu_seqlens, n_seqs, q, k, v, o, block_idx, workspace, workspace_bytes, stream));
+}
+
+moba_status_t moba_forward_varlen_lse(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                                      const void* q, const void* k, const void* v, void* o, int32_t* block_idx,
+                                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return st_(impl_forward_varlen(p, cu_seqlens, n_seqs, q, k, v, o, block_idx, workspace, workspace_bytes, stream,
+                                 lse, true));
+}
+
+moba_status_t moba_backward_workspace_size_varlen(const moba_problem_t* p, const int64_t* cu_seqlens,
+                                                  int64_t n_seqs, size_t* bytes) {
+  return st_(impl_backward_workspace_size_varlen(p, cu_seqlens, n_seqs, bytes));
+}
+
+moba_status_t moba_backward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int64_t n_seqs,
+                                   const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const int32_t* block_idx, const float* lse, void* dq, void* dk, void* dv,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return st_(impl_backward_varlen(p, cu_seqlens, n_seqs, q, k, v, o, dout, block_idx, lse, dq, dk, dv, workspace,
+                                  workspace_bytes, stream));
 }
 
 moba_status_t moba_dense_causal_forward(const moba_problem_t* p, const void* q, const void* k, const void* v,

@@ -66,7 +66,7 @@ def test_boundary_entry_points_validate_through_ctypes():
 
 def test_abi_version_and_status_strings():
     from sparse_long_context_moba_amd import _lib
-    assert _lib.moba_abi_version() == 6
+    assert _lib.moba_abi_version() == 7
     for code in range(8):
         assert _lib.moba_status_str(code)
     assert _lib.moba_status_str(99) == "unknown status"
@@ -233,6 +233,37 @@ def test_grouped_query_heads_workspace():
     up = lambda x: (x + 255) // 256 * 256
     saved = sum(up(8 * nb * D * e) - up(2 * nb * D * e) for e in (8, 4, 2, 2)) + up(8 * nb * 4) - up(2 * nb * 4)
     assert mha - gqa == saved
+
+
+def test_varlen_backward_validation():
+    """moba_backward_varlen plans every sequence as its own uniform backward
+    (bf16, length a multiple of 64) before anything is launched: an error
+    names the sequence; the workspace is the largest sequence's."""
+    from sparse_long_context_moba_amd import _lib
+    cu = [0, 576, 1600, 1792]
+    p = _p(batch=3, seq_len=1792, block_size=128)
+    st, need = _lib.moba_backward_workspace_size_varlen(p, cu)
+    assert st == 0, _lib.moba_last_error()
+    per = [_lib.moba_backward_workspace_size(_p(batch=1, seq_len=b - a, block_size=128))[1]
+           for a, b in zip(cu, cu[1:])]
+    assert need == max(per)
+    # a length that is not a multiple of 64 names its sequence
+    st, _ = _lib.moba_backward_workspace_size_varlen(_p(batch=3, seq_len=1790, block_size=128), [0, 576, 1598, 1790])
+    assert st == 5 and "sequence 1" in _lib.moba_last_error()
+    # fp32 inputs, batch and seq_len disagreeing with cu_seqlens
+    assert _lib.moba_backward_workspace_size_varlen(_p(batch=3, seq_len=1792, block_size=128, dtype=0), cu)[0] == 5
+    assert _lib.moba_backward_workspace_size_varlen(_p(batch=2, seq_len=1792, block_size=128), cu)[0] == 3
+    args = [FAKE] * 10
+    assert _lib.moba_backward_varlen(p, cu, *args, FAKE, need - 1, None) == 6
+    for i, name in enumerate(["q", "k", "v", "o", "dout", "block_idx", "lse", "dq", "dk", "dv"]):
+        a2 = list(args)
+        a2[i] = None
+        assert _lib.moba_backward_varlen(p, cu, *a2, FAKE, need, None) == 1 and name in _lib.moba_last_error()
+    # the forward with log-sum-exp checks lse like the other outputs
+    st, fneed = _lib.moba_workspace_size_varlen(p, cu)
+    assert st == 0
+    assert _lib.moba_forward_varlen_lse(p, cu, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, fneed, None) == 1
+    assert "lse" in _lib.moba_last_error()
 
 
 def test_backward_and_lse_validation():

@@ -60,9 +60,18 @@ def test_backward_parity(case):
     torch.cuda.synchronize()
     for x, y in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16)), "backward is not run-to-run bit-identical"
+    _check_against_oracle(label, q, k, v, do, idx, lse, dq, dk, dv, Bs, causal)
+
+
+def _check_against_oracle(label, q, k, v, do, idx, lse, dq, dk, dv, Bs, causal):
+    """Every dq row and lse value per query head, and dk, dv per key/value
+    head (the oracle's per-head gradients summed over the heads that read
+    it), against backward_head with the GPU's block choice."""
     idx = idx.cpu().numpy()
     lse = lse.cpu().numpy()
     dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    B, H, S, D = q.shape
+    Hkv = k.shape[1]
     G = H // Hkv
     worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0, "lse": 0.0}
     for b in range(B):
@@ -85,6 +94,53 @@ def test_backward_parity(case):
                 assert e <= REL * np.abs(ref).max(), f"{label} b={b} kv={hk}: {name} error {e:.3e} (scale {np.abs(ref).max():.3e})"
                 worst[name] = max(worst[name], e / np.abs(ref).max())
     say(f"[gpu] backward {label}: ok, max error / scale: " + ", ".join(f"{n}={v:.2e}" for n, v in worst.items()))
+
+
+VARLEN_CASES = [
+    # label, seed, H, Hkv, D, Bs, top_k, causal, shared, lengths (multiples of 64)
+    ("d128-bs128-causal", 80, 2, 2, 128, 128, 3, True, False, [576, 1024, 192]),
+    ("d64-bs64-noncausal-gqa2-shared", 81, 4, 2, 64, 64, 3, False, True, [128, 704, 64]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
+def test_backward_varlen(case):
+    """The backward of a varlen batch (forward_varlen with its log-sum-exp,
+    then backward_varlen): every sequence's lse, dq, dk and dv bit-identical
+    to those of that sequence run alone, and the first sequence's against
+    the oracle."""
+    import sparse_long_context_moba_amd as moba
+    label, seed, H, Hkv, D, Bs, top_k, causal, shared, lengths = case
+    seqs = [_inputs(seed + i, 1, H, Hkv, n, D, Bs) for i, n in enumerate(lengths)]
+    dev = [[to_dev(x, "bf16") for x in s] for s in seqs]
+    qp, cu = moba.pack_varlen([d[0] for d in dev])
+    kp, _ = moba.pack_varlen([d[1] for d in dev])
+    vp, _ = moba.pack_varlen([d[2] for d in dev])
+    dop, _ = moba.pack_varlen([d[3] for d in dev])
+    say(f"[gpu] backward varlen {label}: lengths={lengths} cu={cu}")
+    o, idx, lse = moba.forward_varlen(qp, kp, vp, cu, H, Bs, top_k, causal, kv_heads=Hkv, gate_shared=shared,
+                                      return_lse=True)
+    dq, dk, dv = moba.backward_varlen(qp, kp, vp, o, dop, idx, lse, cu, H, Bs, top_k, causal, kv_heads=Hkv,
+                                      gate_shared=shared)
+    torch.cuda.synchronize()
+    parts = {"dq": moba.unpack_varlen(dq, cu, H), "dk": moba.unpack_varlen(dk, cu, Hkv),
+             "dv": moba.unpack_varlen(dv, cu, Hkv)}
+    idxs = moba.unpack_varlen(idx, cu, H)
+    for i, d in enumerate(dev):
+        n = lengths[i]
+        lse_i = lse[cu[i] * H:cu[i + 1] * H].view(1, H, n)
+        o1, i1, l1 = moba.forward(d[0], d[1], d[2], Bs, top_k, causal, gate_shared=shared, return_lse=True)
+        assert torch.equal(idxs[i], i1), f"sequence {i}: block choice differs from the sequence alone"
+        assert torch.equal(lse_i.view(torch.int32), l1.view(torch.int32)), f"sequence {i}: lse differs"
+        g1 = moba.backward(d[0], d[1], d[2], o1, d[3], i1, l1, Bs, top_k, causal)
+        torch.cuda.synchronize()
+        for name, ref in zip(("dq", "dk", "dv"), g1):
+            got = parts[name][i].contiguous()
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"sequence {i}: {name} differs"
+        if i == 0:
+            q, k, v, do = seqs[0]
+            _check_against_oracle(f"{label} seq=0", q, k, v, do, i1, l1, g1[0], g1[1], g1[2], Bs, causal)
+    say(f"[gpu] backward varlen {label}: ok")
 
 
 def _check_sampled(w):
