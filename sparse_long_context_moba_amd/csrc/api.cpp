@@ -259,7 +259,7 @@ BwdPlan plan_backward(const Plan& P) {
   const size_t rows = (size_t)(P.bh * P.S);
   B.delta = take(rows * 4);
   B.lse2 = take(rows * 4);
-  B.dq_part = take(rows * (size_t)P.slots * (size_t)P.D * 4);
+  B.dq_part = take(rows * (size_t)P.slots * (size_t)P.D * 2);
   B.chunk_counts = take((size_t)P.bh * (size_t)((P.S + rank_chunk(P.S) - 1) / rank_chunk(P.S)) * (size_t)P.nb * 4);
   B.lt = take((size_t)P.pairs * 4);
   B.ll = take((size_t)P.pairs * 4);
@@ -563,7 +563,7 @@ int run_backward(const Plan& P, const BwdPlan& B, const void* q, const void* k, 
   ba.top_k = (int)P.top_k;
   ba.delta = at<float>(workspace, B.delta);
   ba.lse2 = at<float>(workspace, B.lse2);
-  ba.dq_part = at<float>(workspace, B.dq_part);
+  ba.dq_part = at<bf16>(workspace, B.dq_part);
   ba.lt = at<int32_t>(workspace, B.lt);
   ba.ll = at<float>(workspace, B.ll);
   ba.ld = at<float>(workspace, B.ld);

@@ -20,8 +20,8 @@ namespace moba {
 //                tiles): per 64-key subtile S^T = K Q^T and dP^T = V dO^T on
 //                the forward's score path, then dQ^T += K^T dS^T on its P.V
 //                path (the same K copy read through the LDS transpose
-//                load); subtiles double-buffered; one fp32 partial per
-//                (query, slot);
+//                load); subtiles double-buffered; one partial per
+//                (query, slot), in bf16 like the forward's output partials;
 //  dq_own      — the own block, 128 queries per workgroup (each wave on
 //                its own block's keys), causal mask, double-buffered; it
 //                then adds the slots' partials in slot order and writes dq
@@ -95,17 +95,7 @@ __device__ __forceinline__ void load_frags(bf16x8 (&f)[D / 16], const bf16* row,
 }
 
 // acc (C layout of mm_trans: lane column = row of dst, element r = coordinate
-// 32 dt + crow(r, h)) times scale, to a row of dst in fp32 or bf16.
-template <int D>
-__device__ __forceinline__ void store_row_f32(float* dst, const f32x16 (&acc)[D / 32], int h, float scale) {
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-      *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * rg + 4 * h) =
-          f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
-                acc[dt][4 * rg + 3] * scale};
-}
+// 32 dt + crow(r, h)) times scale, to a bf16 row of dst.
 template <int D>
 __device__ __forceinline__ void store_row_bf16(bf16* dst, const f32x16 (&acc)[D / 32], int h, float scale) {
 #pragma unroll
@@ -233,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     lds_dma_wait();
     __syncthreads();
   }
-  if (valid) store_row_f32<D>(a.dq_part + (int64_t)ev * D, acc, h, 1.f / __builtin_sqrtf((float)D));
+  if (valid) store_row_bf16<D>(a.dq_part + (int64_t)ev * D, acc, h, 1.f / __builtin_sqrtf((float)D));
 }
 
 // The own block: 128 consecutive queries of one head, 32 per wave. A
@@ -304,8 +294,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     __syncthreads();
   }
   if (!wave_on) return;
-  // dq = own-block part + the past slots' partials (written by dq_past, an
-  // earlier launch) in slot order, rounded once to bf16.
+  // dq = own-block part + the past slots' bf16 partials (written by
+  // dq_past, an earlier launch), added in fp32 in slot order and rounded
+  // to bf16.
   const float scale = 1.f / __builtin_sqrtf((float)D);
   // The row's past blocks, counted as the list-building kernels count them
   // (the same validity test and cap), so exactly the partials dq_past wrote.
@@ -321,7 +312,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
   }
   bf16* dst = reinterpret_cast<bf16*>(a.dq) + row * D;
-  const float* p0 = a.dq_part + (row * slots) * D;
+  const bf16* p0 = a.dq_part + (row * slots) * D;
+  auto ld4 = [](const bf16* p) {
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+  };
   if (n <= 2) {
     // One or two past blocks (top_k <= 3): every partial is requested
     // before any is added (one memory round trip); slot order kept (the
@@ -330,8 +325,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int i = 0; i < DT * 4; ++i) {
       const int d = 32 * (i / 4) + 8 * (i % 4) + 4 * h;
-      if (n > 0) y0[i] = *reinterpret_cast<const f32x4*>(p0 + d);
-      if (n > 1) y1[i] = *reinterpret_cast<const f32x4*>(p0 + D + d);
+      if (n > 0) y0[i] = ld4(p0 + d);
+      if (n > 1) y1[i] = ld4(p0 + D + d);
     }
 #pragma unroll
     for (int i = 0; i < DT * 4; ++i) {
@@ -351,7 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       const int d = 32 * dt + 8 * rg + 4 * h;
       f32x4 x = f32x4{acc[dt][4 * rg] * scale, acc[dt][4 * rg + 1] * scale, acc[dt][4 * rg + 2] * scale,
                       acc[dt][4 * rg + 3] * scale};
-      for (int sl = 0; sl < n; ++sl) x += *reinterpret_cast<const f32x4*>(p0 + sl * D + d);
+      for (int sl = 0; sl < n; ++sl) x += ld4(p0 + sl * D + d);
       E::put4(dst + d, x[0], x[1], x[2], x[3]);
     }
 }

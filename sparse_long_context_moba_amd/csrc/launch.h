@@ -163,7 +163,7 @@ struct BwdArgs {
   int64_t gather_grid;
   float* delta;                // [bh, S] do . o
   float* lse2;                 // [bh, S] log-sum-exp in the log2 domain
-  float* dq_part;              // [bh, S, k_eff - 1, D] past-block dq partials
+  bf16* dq_part;               // [bh, S, k_eff - 1, D] past-block dq partials (bf16, as the forward's)
   int32_t* lt;                 // [pairs] per list position: the query row
   float* ll;                   // [pairs] its log-sum-exp (log2 domain)
   float* ld;                   // [pairs] its delta
