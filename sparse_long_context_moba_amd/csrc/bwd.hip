@@ -61,30 +61,50 @@ __device__ __forceinline__ void mm_rows(const char* buf, int lane, const bf16x8 
 // T in LDS read transposed, V-swizzled (VSW; conflict-free) or K-swizzled
 // (two-way bank conflicts on these reads, but the same copy serves mm_rows),
 // x in the C layout of mm_rows (rounded to bf16): the forward's P.V step.
-template <int D, bool VSW = true>
+template <int D, bool VSW = true, bool FENCE = true>
 __device__ __forceinline__ void mm_trans(const char* buf, int lane, const f32x16 (&x)[2], f32x16 (&acc)[D / 32]) {
   using E = EngBF16<D>;
+  constexpr int DT = D / 32, NP = 4 * DT, VA = 2;  // MFMAs, fragments read ahead
   const int h = lane >> 5, j = lane & 15, half = (lane >> 4) & 1;
   bf16x8 pb[2][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) pb[nt][r >> 3][r & 7] = to_bf16(x[nt][r]);
+  // MFMA c: row chunk c / DT (16 rows), d-tile c % DT. With FENCE the
+  // fragments are read VA MFMAs ahead and a scheduling fence after each
+  // MFMA keeps the reads from all being hoisted to the front (which would
+  // hold every fragment in registers at once); without it the compiler
+  // orders them (the dK pass, at the register limit, spills less so).
+  auto frag = [&](int c) {
+    const int i = c / DT, dt = c % DT, nt = i >> 1, g = i & 1;
+    const int d = 32 * dt + 16 * half + 4 * (j & 3);
+    const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
+    const int s0 = VSW ? E::swzv(r0) : E::swz(r0), s1 = VSW ? E::swzv(r1) : E::swz(r1);
+    const char* a0 = buf + r0 * E::ROWB + 16 * ((d >> 3) ^ s0) + 2 * (d & 7);
+    const char* a1 = buf + r1 * E::ROWB + 16 * ((d >> 3) ^ s1) + 2 * (d & 7);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  if constexpr (FENCE) {
+    bf16x8 vq[NP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < VA; ++c) vq[c] = frag(c);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int nt = i >> 1, g = i & 1;
-      const int d = 32 * dt + 16 * half + 4 * (j & 3);
-      const int r0 = 32 * nt + 16 * g + 4 * h + (j >> 2), r1 = r0 + 8;
-      const int s0 = VSW ? E::swzv(r0) : E::swz(r0), s1 = VSW ? E::swzv(r1) : E::swz(r1);
-      const char* a0 = buf + r0 * E::ROWB + 16 * ((d >> 3) ^ s0) + 2 * (d & 7);
-      const char* a1 = buf + r1 * E::ROWB + 16 * ((d >> 3) ^ s1) + 2 * (d & 7);
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[dt] = mfma_bf16(vf, pb[nt][g], acc[dt]);
+    for (int c = 0; c < NP; ++c) {
+      if (c + VA < NP) vq[c + VA] = frag(c + VA);
+      const int i = c / DT;
+      acc[c % DT] = mfma_bf16(vq[c], pb[i >> 1][i & 1], acc[c % DT]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      const int i = c / DT;
+      acc[c % DT] = mfma_bf16(frag(c), pb[i >> 1][i & 1], acc[c % DT]);
+    }
+  }
 }
 
 // A row's D/16 B fragments for this lane half (like EngBF16::load_q).
@@ -634,7 +654,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       }
     if constexpr (PASS == 0) mm_trans<D>(bx, lane, s, acc);
-    else mm_trans<D, false>(bq, lane, s, acc);
+    else mm_trans<D, false, false>(bq, lane, s, acc);
     __syncthreads();
   };
   for (int g = 0; g < a.group; ++g) {
