@@ -658,11 +658,12 @@ int impl_backward_varlen(const moba_problem_t* p, const int64_t* cu_seqlens, int
   const int64_t H = p->heads, Hkv = Ps[0].Hkv, D = p->head_dim, K = p->top_k;
   for (int64_t i = 0; i < n_seqs; ++i) {
     const int64_t t0 = cu_seqlens[i];
-    auto qo = [&](const void* x) { return static_cast<const char*>(x) + t0 * H * D * 2; };
-    auto kv = [&](const void* x) { return static_cast<const char*>(x) + t0 * Hkv * D * 2; };
-    st = run_backward(Ps[(size_t)i], Bs[(size_t)i], qo(q), kv(k), kv(v), qo(o), qo(dout), block_idx + t0 * H * K,
-                      lse + t0 * H, const_cast<char*>(qo(dq)), const_cast<char*>(kv(dk)),
-                      const_cast<char*>(kv(dv)), workspace, s);
+    const size_t qoff = (size_t)(t0 * H * D * 2), kvoff = (size_t)(t0 * Hkv * D * 2);
+    auto in = [](const void* x, size_t off) { return static_cast<const char*>(x) + off; };
+    auto out = [](void* x, size_t off) { return static_cast<char*>(x) + off; };
+    st = run_backward(Ps[(size_t)i], Bs[(size_t)i], in(q, qoff), in(k, kvoff), in(v, kvoff), in(o, qoff),
+                      in(dout, qoff), block_idx + t0 * H * K, lse + t0 * H, out(dq, qoff), out(dk, kvoff),
+                      out(dv, kvoff), workspace, s);
     if (st != MOBA_OK) return st;
   }
   return MOBA_OK;
