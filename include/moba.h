@@ -185,8 +185,8 @@ moba_status_t moba_forward_lse(const moba_problem_t* p, const void* q, const voi
                      void* o, int32_t* block_idx, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
-/* MoBA backward (bf16 inputs and seq_len a multiple of 64 only;
- * MOBA_ERR_UNSUPPORTED otherwise): the
+/* MoBA backward (bf16 inputs only; MOBA_ERR_UNSUPPORTED otherwise; any
+ * seq_len, as the forward): the
  * gradients of o with respect to q, k and v for the upstream gradient dout,
  * with the forward's block choice held fixed. The routing is a top-k over
  * block scores, constant between ties, and the gate's scores do not weight
@@ -263,9 +263,8 @@ moba_status_t moba_forward_varlen_lse(const moba_problem_t* p, const int64_t* cu
  * problem of batch 1 and seq_len len_i at its offset; the sequences run one
  * after another on the stream, each a launch chain of its own, reusing the
  * workspace.
- *   cu_seqlens, p — as moba_forward_varlen; bf16 inputs, every length a
- *           multiple of 64 (MOBA_ERR_UNSUPPORTED names the first sequence
- *           that is not);
+ *   cu_seqlens, p — as moba_forward_varlen; bf16 inputs (an error names
+ *           the first sequence the backward rejects);
  *   q, k, v, o, dout, dq — the sequences back to back as q in
  *           moba_forward_varlen; dk, dv as k and v there;
  *   block_idx, lse — from moba_forward_varlen_lse on the same batch;

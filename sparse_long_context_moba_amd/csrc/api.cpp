@@ -504,8 +504,6 @@ int plan_backward_problem(const moba_problem_t* p, Plan* P, BwdPlan* B) {
   const int st = plan_problem(p, P, true);
   if (st != MOBA_OK) return st;
   if (!P->bf16_in) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports bf16 inputs only (dtype MOBA_BF16)");
-  if (P->S % 64 != 0)
-    return fail(MOBA_ERR_UNSUPPORTED, "the backward needs seq_len to be a multiple of 64, got " + std::to_string(P->S));
   if (P->nb > 16384) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports at most 16384 blocks");
   *B = plan_backward(*P);
   return MOBA_OK;

@@ -197,7 +197,9 @@ __device__ __forceinline__ void dq_step(const char* bk, const char* bv, int lane
 }
 
 // Past blocks: one gather tile (a block and up to 128 listed queries).
-template <int D>
+// TAIL: the sequence length is not a multiple of 64, so a block's last
+// subtile may be partial.
+template <int D, bool TAIL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_past_kernel(BwdArgs a) {
   using E = EngBF16<D>;
   constexpr int NT = 256, KC = D / 16, DT = D / 32;
@@ -222,24 +224,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int64_t kvh = bh / a.group;
   const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + j * a.block_size) * D;
   const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + j * a.block_size) * D;
-  const int nsub = (int)(min<int64_t>(a.block_size, a.seq_len - j * a.block_size) / kSub);
+  // The block's keys (the sequence's last block may be short, its last
+  // subtile partial: rows past its end are loaded as copies and masked).
+  const int nkeys = (int)min<int64_t>(a.block_size, a.seq_len - j * a.block_size);
+  const int nsub = (nkeys + kSub - 1) / kSub;
+  const int last_rows = nkeys - kSub * (nsub - 1);
+  auto rows_of = [&](int sub) { return TAIL && sub == nsub - 1 ? last_rows : kSub; };
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   // Double-buffered: the loads of subtile sub + 1 run under the compute of
   // sub (buffer sub & 1); each step ends waiting for them, then the barrier.
-  E::template begin_one<NT, false>(kp, bk0, tid);
-  E::template begin_one<NT, false>(vp, bv0, tid);
+  E::template begin_one<NT, false>(kp, bk0, tid, rows_of(0));
+  E::template begin_one<NT, false>(vp, bv0, tid, rows_of(0));
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
   lds_dma_wait();
   __syncthreads();
   for (int sub = 0; sub < nsub; ++sub) {
     const bool odd = sub & 1;
     if (sub + 1 < nsub) {
-      E::template begin_one<NT, false>(kp + (int64_t)(sub + 1) * kSub * D, odd ? bk0 : bk1, tid);
-      E::template begin_one<NT, false>(vp + (int64_t)(sub + 1) * kSub * D, odd ? bv0 : bv1, tid);
+      E::template begin_one<NT, false>(kp + (int64_t)(sub + 1) * kSub * D, odd ? bk0 : bk1, tid, rows_of(sub + 1));
+      E::template begin_one<NT, false>(vp + (int64_t)(sub + 1) * kSub * D, odd ? bv0 : bv1, tid, rows_of(sub + 1));
     }
-    if (wave_on) dq_step<D, false>(odd ? bk1 : bk0, odd ? bv1 : bv0, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+    // With TAIL one masked step serves every subtile (keys past the
+    // subtile's rows get no weight; a full subtile masks nothing): a second,
+    // unmasked copy of the step would push the kernel past the register
+    // file.
+    if (wave_on) {
+      if constexpr (TAIL)
+        dq_step<D, true>(odd ? bk1 : bk0, odd ? bv1 : bv0, lane, qf, gf, lse2, delta, sl2, 0, rows_of(sub) - 1, acc);
+      else
+        dq_step<D, false>(odd ? bk1 : bk0, odd ? bv1 : bv0, lane, qf, gf, lse2, delta, sl2, 0, 0, acc);
+    }
     lds_dma_wait();
     __syncthreads();
   }
@@ -247,11 +263,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 }
 
 // The own block: 128 consecutive queries of one head, 32 per wave. A
-// wave's queries share one block (block_size and seq_len are multiples of
-// 64); the workgroup's may span blocks, and each wave takes only its own
-// block's subtiles of the workgroup's key stream. The last tile may hold
-// only 64 queries (waves 2 and 3 then compute nothing and store nothing).
-template <int D>
+// wave's queries share one block (block_size is a multiple of 64); the
+// workgroup's may span blocks, and each wave takes only its own block's
+// subtiles of the workgroup's key stream. The sequence's last tile may be
+// partial: waves past its end compute nothing, lanes past it compute on
+// its last query and store nothing, and its last key subtile may be
+// partial (rows past the end are loaded as copies and masked; TAIL: the
+// length is not a multiple of 64).
+template <int D, bool TAIL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_own_kernel(BwdArgs a) {
   using E = EngBF16<D>;
   constexpr int NT = 256, KC = D / 16, DT = D / 32, M = 128;
@@ -273,7 +292,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int qlast = min(q0 + M, len) - 1;
   const int kb = (q0 / bs) * bs;
   const int kend = a.causal ? qlast + 1 : min((qlast / bs + 1) * bs, len);
-  const int t = wave_on ? qw0 + col : len - 1;
+  const bool lane_on = TAIL ? qw0 + col < len : wave_on;
+  const int t = lane_on ? qw0 + col : len - 1;
   const int64_t row = bh * a.seq_len + t;
   bf16x8 qf[KC], gf[KC];
   load_frags<D>(qf, reinterpret_cast<const bf16*>(a.q) + row * D, h);
@@ -283,12 +303,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int64_t kvh = bh / a.group;
   const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + kb) * D;
   const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + kb) * D;
-  const int nsub = (kend - kb) / kSub;
+  const int nsub = (kend - kb + kSub - 1) / kSub;
+  const int last_rows = (kend - kb) - kSub * (nsub - 1);
+  auto rows_of = [&](int sub) { return TAIL && sub == nsub - 1 ? last_rows : kSub; };
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  E::template begin_one<NT, false>(kp, bk0, tid);
-  E::template begin_one<NT, false>(vp, bv0, tid);
+  E::template begin_one<NT, false>(kp, bk0, tid, rows_of(0));
+  E::template begin_one<NT, false>(vp, bv0, tid, rows_of(0));
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), also for the query rows
   lds_dma_wait();
   __syncthreads();
@@ -297,13 +319,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // (last read in step sub - 1, before its barrier).
     const bool odd = sub & 1;
     if (sub + 1 < nsub) {
-      E::template begin_one<NT, false>(kp + (int64_t)(sub + 1) * kSub * D, odd ? bk0 : bk1, tid);
-      E::template begin_one<NT, false>(vp + (int64_t)(sub + 1) * kSub * D, odd ? bv0 : bv1, tid);
+      E::template begin_one<NT, false>(kp + (int64_t)(sub + 1) * kSub * D, odd ? bk0 : bk1, tid, rows_of(sub + 1));
+      E::template begin_one<NT, false>(vp + (int64_t)(sub + 1) * kSub * D, odd ? bv0 : bv1, tid, rows_of(sub + 1));
     }
     const char* bk = odd ? bk1 : bk0;
     const char* bv = odd ? bv1 : bv0;
     const int key0 = kb + sub * kSub;
-    if (wave_on && key0 >= kbw && key0 < kew) {
+    // Causal: masked at the lane's query on the diagonal (which also masks
+    // keys past the sequence's end), skipped past the wave's last query.
+    // Otherwise only a partial last subtile of the block is masked, at
+    // kew - 1. With TAIL one masked step serves every subtile (a second,
+    // unmasked copy of the step would push the kernel past the register
+    // file).
+    if constexpr (TAIL) {
+      if (wave_on && key0 >= kbw && key0 < kew && !(a.causal && key0 > qw0 + 31)) {
+        const bool need = key0 + kSub > (a.causal ? qw0 : kew);
+        const int lim = need ? (a.causal ? t : kew - 1) : key0 + kSub - 1;
+        dq_step<D, true>(bk, bv, lane, qf, gf, lse2, delta, sl2, key0, lim, acc);
+      }
+    } else if (wave_on && key0 >= kbw && key0 < kew) {
       if (a.causal && key0 + kSub > qw0) {
         if (key0 <= qw0 + 31) dq_step<D, true>(bk, bv, lane, qf, gf, lse2, delta, sl2, key0, t, acc);
       } else {
@@ -313,7 +347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     lds_dma_wait();
     __syncthreads();
   }
-  if (!wave_on) return;
+  if (!lane_on) return;
   // dq = own-block part + the past slots' bf16 partials (written by
   // dq_past, an earlier launch), added in fp32 in slot order and rounded
   // to bf16.
@@ -413,9 +447,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int64_t j = blockIdx.x / (nchunk * nkv);
   const int64_t k0 = j * a.block_size + kc * KEYS;
   if (k0 >= a.seq_len) return;  // past the end of a short last block
-  const int u = (int)k0 + 32 * w + col;  // this lane's key
-  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + u) * D;
-  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + u) * D;
+  // This lane's key; lanes past the sequence's end compute on its last
+  // key and store nothing.
+  const int u = (int)k0 + 32 * w + col;
+  const int uc = min(u, (int)a.seq_len - 1);
+  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + uc) * D;
+  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + uc) * D;
   bf16x8 kf[KC], vf[PASS == 1 ? KC : 1];
   load_frags<D>(kf, krow, h);
   if constexpr (PASS == 1) load_frags<D>(vf, vrow, h);
@@ -556,6 +593,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     cur = nxt;
     nxt = nn;
   }
+  if (u >= a.seq_len) return;
   bf16* dst = reinterpret_cast<bf16*>(PASS == 0 ? a.dv : a.dk) + (kvh * a.seq_len + u) * D;
   store_row_bf16<D>(dst, acc, h, PASS == 0 ? 1.f : 1.f / __builtin_sqrtf((float)D));
 }
@@ -587,9 +625,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int64_t j = blockIdx.x / (nchunk * nkv);
   const int64_t k0 = j * a.block_size + kc * KEYS;
   if (k0 >= a.seq_len) return;  // past the end of a short last block
-  const int u = (int)k0 + 32 * w + col;  // this lane's key
-  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + u) * D;
-  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + u) * D;
+  // This lane's key; lanes past the sequence's end compute on its last
+  // key and store nothing.
+  const int u = (int)k0 + 32 * w + col;
+  const int uc = min(u, (int)a.seq_len - 1);
+  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + uc) * D;
+  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + uc) * D;
   bf16x8 kf[KC], vf[PASS == 1 ? KC : 1];
   load_frags<D>(kf, krow, h);
   if constexpr (PASS == 1) load_frags<D>(vf, vrow, h);
@@ -672,6 +713,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int i0 = 0; i0 < cnt; i0 += 64) subtile(bh, min(64, cnt - i0), false, o0 + i0);
     }
   }
+  if (u >= a.seq_len) return;
   bf16* dst = reinterpret_cast<bf16*>(PASS == 0 ? a.dv : a.dk) + (kvh * a.seq_len + u) * D;
   store_row_bf16<D>(dst, acc, h, PASS == 0 ? 1.f : 1.f / __builtin_sqrtf((float)D));
 }
@@ -679,6 +721,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 template <int D>
 hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = a.bh * a.seq_len;
+  const bool tail = a.seq_len % kSub != 0;  // partial last query tiles and key subtiles
   {
     KernelTimer t(s, "bwd_prep");
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
@@ -691,11 +734,14 @@ hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
   }
   if (a.k_eff > 1 && a.gather_grid > 0) {
     KernelTimer t(s, "bwd_dq_past");
-    hipLaunchKernelGGL(dq_past_kernel<D>, dim3((unsigned)a.gather_grid), dim3(256), 0, s, a);
+    if (tail) hipLaunchKernelGGL((dq_past_kernel<D, true>), dim3((unsigned)a.gather_grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dq_past_kernel<D, false>), dim3((unsigned)a.gather_grid), dim3(256), 0, s, a);
   }
   {
     KernelTimer t(s, "bwd_dq_own");
-    hipLaunchKernelGGL(dq_own_kernel<D>, dim3((unsigned)(a.bh * ((a.seq_len + 127) / 128))), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)(a.bh * ((a.seq_len + 127) / 128)));
+    if (tail) hipLaunchKernelGGL((dq_own_kernel<D, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dq_own_kernel<D, false>), grid, dim3(256), 0, s, a);
   }
   // 128 keys per workgroup where every block length is a multiple of 128,
   // else 64.

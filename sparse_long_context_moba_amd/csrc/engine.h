@@ -188,9 +188,11 @@ struct EngBF16 {
     for (int ii = 0; ii < kLoadsPerWave<NT>; ++ii)
       lds_dma16_s(p, IS_V ? lo.v[ii] : lo.k[ii], base + (ii * NW + w) * 1024);
   }
-  // The same loads for K or V alone, into a buffer of TB bytes.
+  // The same loads for K or V alone, into a buffer of TB bytes, from the
+  // wave-uniform base p with 32-bit lane offsets; rows at or past nrows (a
+  // partial last subtile) repeat row nrows - 1.
   template <int NT, bool IS_V>
-  static __device__ __forceinline__ void begin_one(const bf16* p, char* buf, int tid) {
+  static __device__ __forceinline__ void begin_one(const bf16* p, char* buf, int tid, int nrows = kSub) {
     constexpr int NW = NT / 64, INSTS = SLOTS / 64;
     static_assert(INSTS % NW == 0, "subtile slots must split evenly over the waves");
     const int lane = tid & 63;
@@ -202,7 +204,7 @@ struct EngBF16 {
       const int sl = i * 64 + lane;
       const int row = sl / CPR;
       const int x = (sl % CPR) ^ (IS_V ? swzv(row) : swz(row));
-      lds_dma16(p + row * D + 8 * x, base + i * 1024);
+      lds_dma16_s(p, (unsigned)(min(row, nrows - 1) * D + 8 * x) * 2u, base + i * 1024);
     }
   }
 

@@ -196,14 +196,15 @@ def test_varlen_validation_and_workspace():
 
 def test_any_sequence_length_is_accepted():
     """Lengths need not be multiples of 64 (a partial last tile of queries
-    and keys is masked); block_size still must be. The backward keeps the
-    multiple-of-64 rule."""
+    and keys is masked), for the forward and the backward; block_size
+    still must be."""
     from sparse_long_context_moba_amd import _lib
     for S, Bs in ((1000, 128), (77, 64), (1, 64), (2049, 512), (33023, 512)):
         st, n = _lib.moba_workspace_size(_p(seq_len=S, block_size=Bs))
         assert st == 0 and n > 0, (S, Bs, _lib.moba_last_error())
-    st, _ = _lib.moba_backward_workspace_size(_p(seq_len=1000, block_size=128))
-    assert st == 5 and "multiple of 64" in _lib.moba_last_error()
+    for S, Bs in ((1000, 128), (77, 64), (1, 64)):
+        st, n = _lib.moba_backward_workspace_size(_p(seq_len=S, block_size=Bs))
+        assert st == 0 and n > 0, (S, Bs, _lib.moba_last_error())
     st, _ = _lib.moba_workspace_size_varlen(_p(batch=3, seq_len=3126, block_size=64), [0, 1000, 1077, 3126])
     assert st == 0, _lib.moba_last_error()
 
@@ -237,8 +238,8 @@ def test_grouped_query_heads_workspace():
 
 def test_varlen_backward_validation():
     """moba_backward_varlen plans every sequence as its own uniform backward
-    (bf16, length a multiple of 64) before anything is launched: an error
-    names the sequence; the workspace is the largest sequence's."""
+    (bf16, any length) before anything is launched: an error names the
+    sequence; the workspace is the largest sequence's."""
     from sparse_long_context_moba_amd import _lib
     cu = [0, 576, 1600, 1792]
     p = _p(batch=3, seq_len=1792, block_size=128)
@@ -247,8 +248,12 @@ def test_varlen_backward_validation():
     per = [_lib.moba_backward_workspace_size(_p(batch=1, seq_len=b - a, block_size=128))[1]
            for a, b in zip(cu, cu[1:])]
     assert need == max(per)
-    # a length that is not a multiple of 64 names its sequence
+    # ragged lengths are accepted; a sequence beyond the backward's block
+    # limit (16384 blocks) is named
     st, _ = _lib.moba_backward_workspace_size_varlen(_p(batch=3, seq_len=1790, block_size=128), [0, 576, 1598, 1790])
+    assert st == 0, _lib.moba_last_error()
+    big = [0, 576, 576 + 64 * 16385]
+    st, _ = _lib.moba_backward_workspace_size_varlen(_p(batch=2, seq_len=big[-1], block_size=64), big)
     assert st == 5 and "sequence 1" in _lib.moba_last_error()
     # fp32 inputs, batch and seq_len disagreeing with cu_seqlens
     assert _lib.moba_backward_workspace_size_varlen(_p(batch=3, seq_len=1792, block_size=128, dtype=0), cu)[0] == 5

@@ -44,6 +44,11 @@ CASES = [
     ("d64-topk-all", 74, 1, 1, 1, 512, 64, 64, 9, True, False),
     ("d128-gqa2-shared", 75, 1, 4, 2, 1024, 128, 128, 3, True, True),
     ("d128-gqa4-per-head-b2", 76, 2, 4, 1, 512, 128, 128, 2, True, False),
+    # any length: partial last query tiles and key subtiles
+    ("d128-bs128-len1000", 77, 1, 2, 2, 1000, 128, 128, 3, True, False),
+    ("d64-bs64-len77-noncausal", 78, 1, 2, 2, 77, 64, 64, 3, False, False),
+    ("d128-bs256-len1000-noncausal", 79, 1, 2, 2, 1000, 128, 256, 3, False, False),
+    ("d128-gqa2-shared-len513-b2", 84, 2, 4, 2, 513, 128, 64, 4, True, True),
 ]
 
 
@@ -97,9 +102,10 @@ def _check_against_oracle(label, q, k, v, do, idx, lse, dq, dk, dv, Bs, causal):
 
 
 VARLEN_CASES = [
-    # label, seed, H, Hkv, D, Bs, top_k, causal, shared, lengths (multiples of 64)
+    # label, seed, H, Hkv, D, Bs, top_k, causal, shared, lengths
     ("d128-bs128-causal", 80, 2, 2, 128, 128, 3, True, False, [576, 1024, 192]),
     ("d64-bs64-noncausal-gqa2-shared", 81, 4, 2, 64, 64, 3, False, True, [128, 704, 64]),
+    ("d128-bs128-causal-ragged", 82, 2, 2, 128, 128, 3, True, False, [1000, 77, 513]),
 ]
 
 
