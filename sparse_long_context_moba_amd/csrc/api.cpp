@@ -70,7 +70,7 @@ struct Plan {
   int pooling;         // moba_pooling_t
   // the sequences
   bool uniform;
-  int64_t n_seq, T, nb_total, max_nb, w128, w1024;  // totals over the sequences
+  int64_t n_seq, T, nb_total, max_nb, w128, w256, w1024;  // totals over the sequences
   std::vector<int64_t> tab;  // varlen: the sequence table (rows of kSeqCols prefix sums)
   int64_t pairs;       // (query, kept past block) pairs over all heads
   int64_t max_tiles;   // upper bound on gather tiles
@@ -138,7 +138,7 @@ int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const c
   P.uniform = lens == nullptr;
   P.n_seq = n;
   auto len_of = [&](int64_t i) { return lens ? lens[i] : P.S; };
-  P.T = P.nb_total = P.max_nb = P.w128 = P.w1024 = 0;
+  P.T = P.nb_total = P.max_nb = P.w128 = P.w256 = P.w1024 = 0;
   if (!P.uniform) P.tab.assign((size_t)(n + 1) * kSeqCols, 0);
   for (int64_t i = 0; i <= n; ++i) {
     if (!P.uniform) {
@@ -146,6 +146,7 @@ int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const c
       row[kSeqTok] = P.T;
       row[kSeqBlk] = P.nb_total;
       row[kSeqW128] = P.w128;
+      row[kSeqW256] = P.w256;
       row[kSeqW1024] = P.w1024;
     }
     if (i == n) break;
@@ -157,6 +158,7 @@ int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const c
     P.nb_total += nbi;
     P.max_nb = std::max(P.max_nb, nbi);
     P.w128 += seq_units(kSeqW128, L, P.Bs);
+    P.w256 += seq_units(kSeqW256, L, P.Bs);
     P.w1024 += seq_units(kSeqW1024, L, P.Bs);
     if (P.uniform) break;  // every sequence alike: scale below
   }
@@ -165,6 +167,7 @@ int plan_seqs(Plan& P, const int64_t* lens, int64_t n, bool need_select, const c
     P.nb = P.nb_total;
     P.nb_total *= n;
     P.w128 *= n;
+    P.w256 *= n;
     P.w1024 *= n;
   }
   // k_eff - 1 past-block slots per query row: a sequence with fewer blocks
@@ -330,6 +333,7 @@ int run_select(const Plan& P, const void* q, const void* k, int32_t* block_idx, 
   ga.block_size = P.Bs;
   ga.max_nb = P.max_nb;
   ga.gate_wgs = (P.shared && P.G > 1 ? P.Hkv : P.H) * P.w128;
+  ga.gate_wgs256 = P.H * P.w256;
   ga.rank_wgs = P.H * P.w1024;
   ga.head_dim = (int)P.D;
   ga.bf16_in = P.bf16_in;

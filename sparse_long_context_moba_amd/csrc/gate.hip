@@ -11,7 +11,8 @@
 //    scores, equal scores resolved towards the lower block index.
 //
 // Mapping on gfx950: a workgroup owns 128 consecutive queries of one head,
-// a wave 32 of them (they share c because block_size is a multiple of 64).
+// a wave 32 of them; for long sequences 256 and 64, two 32-query groups per
+// wave (a wave's queries share c because block_size is a multiple of 64).
 // Tiles of 32 pooled keys are staged in LDS once per workgroup, double
 // buffered, one barrier per tile. Scores come from bf16 MFMA 32x32x16 with
 // the pooled keys as the A operand (rows = blocks) and the queries as the
@@ -267,7 +268,6 @@ struct GateOps<bf16, D> {
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) lds_dma16_s(tile_hi, off[n], lds + 1024u * dma_ins(w, n));
   }
-  static constexpr int QG_MAX = 2;  // 32-query groups per wave
   // Scores of every group against the tile: each pooled-key fragment is read
   // from LDS once and feeds one MFMA per group (independent chains).
   template <int QG>
@@ -290,14 +290,16 @@ struct GateOps<bf16, D> {
     }
   }
   // The steady state in issue order (waves issue in order, so the MFMA
-  // chain only overlaps the selection work if the two are interleaved in
+  // chains only overlap the selection work if the two are interleaved in
   // the instruction stream): scores of the next tile (nxt) from LDS with
-  // fragment reads AH ahead, and between consecutive MFMAs the fold of
-  // 16 / (2 KC) of the current tile's scores (cur) into the segment list S.
-  // Scheduling fences keep this order. One query group.
-  template <int TT>
-  static __device__ __forceinline__ void scores_fold(const char* lds, int col, int h, const GateOps& qf, f32x16& nxt,
-                                                     const f32x16& cur, float (&S)[TT], unsigned pos0) {
+  // fragment reads AH ahead, each fragment feeding one MFMA per query
+  // group, and between consecutive fragments the fold of 16 / (2 KC) of
+  // each group's current scores (cur) into its segment list S. Scheduling
+  // fences keep this order.
+  template <int QG, int TT>
+  static __device__ __forceinline__ void scores_fold(const char* lds, int col, int h, const GateOps (&qf)[QG],
+                                                     f32x16 (&nxt)[QG], const f32x16 (&cur)[QG], float (&S)[QG][TT],
+                                                     unsigned pos0) {
     const bf16* hi = reinterpret_cast<const bf16*>(lds) + col * KR + 8 * h;
     const bf16* lo = hi + kTileB * KR;
     constexpr int NF = 2 * KC, AH = 4, EPF = 16 / NF;  // fragments, reads ahead, elements folded per fragment
@@ -306,23 +308,27 @@ struct GateOps<bf16, D> {
     bf16x8 f[AH];
 #pragma unroll
     for (int c = 0; c < AH; ++c) f[c] = frag(c);
-    nxt = f32x16{};
+#pragma unroll
+    for (int g = 0; g < QG; ++g) nxt[g] = f32x16{};
 #pragma unroll
     for (int c = 0; c < NF; ++c) {
-      nxt = mfma_bf16(f[c % AH], qf.f[c % KC], nxt);
+#pragma unroll
+      for (int g = 0; g < QG; ++g) nxt[g] = mfma_bf16(f[c % AH], qf[g].f[c % KC], nxt[g]);
       if (c + AH < NF) f[c % AH] = frag(c + AH);
 #pragma unroll
-      for (int u = 0; u < EPF; ++u) {
-        const int r = EPF * c + u;
-        const float sv = cur[r];
-        const float x = __uint_as_float((__float_as_uint(sv) & ~kSegMask) | (pos0 + r));
-        float n[TT];
-        n[0] = __builtin_fmaxf(S[0], x);
+      for (int g = 0; g < QG; ++g)
 #pragma unroll
-        for (int i = 1; i < TT; ++i) n[i] = __builtin_amdgcn_fmed3f(S[i - 1], S[i], x);
+        for (int u = 0; u < EPF; ++u) {
+          const int r = EPF * c + u;
+          const float sv = cur[g][r];
+          const float x = __uint_as_float((__float_as_uint(sv) & ~kSegMask) | (pos0 + r));
+          float n[TT];
+          n[0] = __builtin_fmaxf(S[g][0], x);
 #pragma unroll
-        for (int i = 0; i < TT; ++i) S[i] = n[i];
-      }
+          for (int i = 1; i < TT; ++i) n[i] = __builtin_amdgcn_fmed3f(S[g][i - 1], S[g][i], x);
+#pragma unroll
+          for (int i = 0; i < TT; ++i) S[g][i] = n[i];
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -538,20 +544,21 @@ struct pick_type<false, A, B> {
   using type = B;
 };
 
-// 32-query groups per wave. A second group would give independent MFMA and
-// selection chains and halve the LDS fragment reads, but with the pipelined
-// accumulators it does not fit the register file without spills; one group
-// at three waves per SIMD does.
-template <typename T, int D, int TT>
-__host__ __device__ constexpr int gate_groups() {
-  return 1;
-}
+// 32-query groups per wave (QG). With one group every pooled-key fragment
+// read from LDS feeds a single MFMA; two groups halve the reads per MFMA
+// and give each wave two independent chains, at two waves per SIMD
+// (256-query workgroups) instead of three. Two groups are taken for long
+// sequences of the per-head bf16 gate with short lists; with few tiles per
+// workgroup, short sequences run faster with more, smaller workgroups.
 // Waves per SIMD the register budget is set for (a shared gate holds two
 // query fragments).
-template <typename T, int D, int TT, bool SHARED = false>
+template <typename T, int D, int TT, bool SHARED, int QG>
 constexpr int gate_waves() {
-  return (sizeof(T) == 2 && TT <= 6 && !SHARED) ? 3 : 2;
+  return (sizeof(T) == 2 && TT <= 6 && !SHARED && QG == 1) ? 3 : 2;
 }
+// Sequences of at least this many blocks take the two-group gate (measured:
+// 4 % faster at 2048 blocks, even at 512, 2 % slower at 256).
+constexpr int kTwoGroupMinBlocks = 512;
 
 // Exact top-TT over every eligible block of one query, by the whole wave:
 // the query's fp64 vector (D values) is in this wave's LDS slice qs; lane l
@@ -752,29 +759,30 @@ __device__ void write_row(int32_t* row, const int (&sel)[TT], bool scoring, int 
 // query type. SHARED: one workgroup row of queries per key/value head, the
 // scores being those of the group's summed query (bf16 MFMA on its hi/lo
 // split, T = bf16).
-template <typename T, typename TQ, int D, int TT, bool SHARED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT, SHARED>()))) void
+template <typename T, typename TQ, int D, int TT, bool SHARED, int QG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT, SHARED, QG>()))) void
 gate_topk_kernel(GateArgs a) {
   using Ops = typename pick_type<SHARED, GateOpsSplitQ<D>, GateOps<T, D>>::type;
   static_assert(!SHARED || sizeof(T) == 2, "a shared gate scores on the bf16 pair");
   static_assert(SHARED || sizeof(T) == sizeof(TQ), "a per-head gate scores in the query's own type");
-  constexpr int QG = gate_groups<T, D, TT>();
+  static_assert(QG == 1 || (std::is_same<Ops, GateOps<bf16, D>>::value && TT <= 6), "two groups: per-head bf16, short lists");
   constexpr int WQ = 32 * QG;       // queries per wave
   constexpr int WGQ = 4 * WQ;       // queries per workgroup
+  constexpr int COL = WGQ == 128 ? kSeqW128 : kSeqW256;
   extern __shared__ __align__(16) char smem[];
   char* tile = smem;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave (uniform)
-  static_assert(WGQ == 128, "the sequence table counts gate workgroups of 128 queries");
+  static_assert(WGQ == 128 || WGQ == 256, "the sequence table counts gate workgroups of 128 or 256 queries");
   // Work item -> (sequence, routing row, workgroup). Per-head gate: the row
   // is a query head, reading key head row / group. Shared gate: the row is
   // a key/value head and routes its group of query heads.
   const int64_t rows = SHARED ? a.kv_heads : a.heads;
   const int64_t item = blockIdx.x;
-  const int64_t si = seq_find_u(a.sq, kSeqW128, rows, item, a.block_size);
+  const int64_t si = seq_find_u(a.sq, COL, rows, item, a.block_size);
   const SeqAt sa = seq_at_u(a.sq, si, a.block_size);
   const int64_t wg_per_head = (sa.len + WGQ - 1) / WGQ;
-  const int64_t r_item = item - rows * seq_prefix_u(a.sq, si, kSeqW128, a.block_size);
+  const int64_t r_item = item - rows * seq_prefix_u(a.sq, si, COL, a.block_size);
   const int64_t grp = r_item / wg_per_head;
   const int64_t kvh = SHARED ? grp : grp / a.group;
   const int64_t qh0 = SHARED ? grp * a.group : grp;
@@ -922,9 +930,9 @@ gate_topk_kernel(GateArgs a) {
     const int jb = jt + 4 * h;
     const bool full = jt + kTileB <= jend && (a.causal || c < jt || c >= jt + kTileB);
     if (do_cur && do_next && full) {  // the steady state: one basic block
-      if constexpr (std::is_same<Ops, GateOps<bf16, D>>::value && QG == 1) {
+      if constexpr (std::is_same<Ops, GateOps<bf16, D>>::value) {
         // the MFMAs of tile i + 1 and the fold of tile i, in a fixed order
-        Ops::template scores_fold<TT>(next_buf, col, h, qf[0], nxt[0], cur[0], S[0], (unsigned)tis << 4);
+        Ops::template scores_fold<QG, TT>(next_buf, col, h, qf, nxt, cur, S, (unsigned)tis << 4);
       } else {
         Ops::template scores<QG>(next_buf, col, h, qf, nxt);
         absorb<QG, TT, false>(S, cur, tis, jb, jend, c);
@@ -942,7 +950,7 @@ gate_topk_kernel(GateArgs a) {
   int i0 = 0;
   // (Only where it pays for its code size: the per-head bf16 gate with a
   // short list, i.e. top_k up to 5.)
-  if constexpr (DMA && std::is_same<Ops, GateOps<bf16, D>>::value && QG == 1 && TT <= 6) {
+  if constexpr (DMA && std::is_same<Ops, GateOps<bf16, D>>::value && TT <= 6) {
     // Steady stretch: a segment of kSegTiles steps at a time with no
     // per-step conditions, while every wave of the workgroup has the
     // segment's tiles and the next one full, and the tiles the segment
@@ -953,7 +961,7 @@ gate_topk_kernel(GateArgs a) {
       lds_dma_wait_n<Ops::NDMA>();
       __syncthreads();
       Ops::dma(a.kbar_hi + (kvb0 + (int64_t)(i + 3) * kTileB) * D, doff, lds_addr(buf(i + 3)), w);
-      Ops::template scores_fold<TT>(buf(i + 1), col, h, qf[0], nxt[0], cur[0], S[0], (unsigned)k << 4);
+      Ops::template scores_fold<QG, TT>(buf(i + 1), col, h, qf, nxt, cur, S, (unsigned)k << 4);
     };
     static_assert(kSegTiles == 8, "the steady stretch is unrolled over one segment");
     for (; i0 + kSegTiles + 1 <= n_full && i0 + kSegTiles + 2 < ntiles; i0 += kSegTiles) {
@@ -1082,12 +1090,12 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
   }
 }
 
-template <typename T, typename TQ, int D, int TT, bool SHARED>
+template <typename T, typename TQ, int D, int TT, bool SHARED, int QG = 1>
 static void gate_go(const GateArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.gate_wgs);
+  const dim3 grid((unsigned)(QG == 2 ? a.gate_wgs256 : a.gate_wgs));
   using Ops = typename pick_type<SHARED, GateOpsSplitQ<D>, GateOps<T, D>>::type;
   const int lds = (Ops::kDma ? 3 : 2) * Ops::TILE_BYTES;
-  hipLaunchKernelGGL((gate_topk_kernel<T, TQ, D, TT, SHARED>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gate_topk_kernel<T, TQ, D, TT, SHARED, QG>), grid, dim3(256), lds, s, a);
 }
 
 template <typename T, typename TQ, int D, bool SHARED>
@@ -1095,6 +1103,13 @@ static void gate_pick(const GateArgs& a, hipStream_t s) {
   // The list tracks m + 2 or more blocks so that a rounding band at the
   // cut usually ends inside it.
   const int m = a.k_eff - 1;
+  if constexpr (sizeof(T) == 2 && !SHARED) {
+    if (a.max_nb >= kTwoGroupMinBlocks && m <= 4) {
+      if (m <= 2) gate_go<T, TQ, D, 4, SHARED, 2>(a, s);
+      else gate_go<T, TQ, D, 6, SHARED, 2>(a, s);
+      return;
+    }
+  }
   if (m <= 2) gate_go<T, TQ, D, 4, SHARED>(a, s);
   else if (m <= 4) gate_go<T, TQ, D, 6, SHARED>(a, s);
   else if (m <= 8) gate_go<T, TQ, D, 10, SHARED>(a, s);

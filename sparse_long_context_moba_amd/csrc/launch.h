@@ -16,7 +16,7 @@ typedef __bf16 bf16;
 // blk0_i * heads + h * nb_i (nb_i = ceil(len_i / block_size)).
 // Table row i (0 <= i <= n) holds the sums over the sequences before i;
 // row n holds the totals.
-enum SeqCol { kSeqTok = 0, kSeqBlk = 1, kSeqW128 = 2, kSeqW1024 = 3 };
+enum SeqCol { kSeqTok = 0, kSeqBlk = 1, kSeqW128 = 2, kSeqW1024 = 3, kSeqW256 = 4 };
 constexpr int kSeqCols = 8;
 struct Seqs {
   const int64_t* tab;  // [(n + 1) * kSeqCols] or nullptr (uniform)
@@ -30,6 +30,7 @@ __host__ __device__ __forceinline__ int64_t seq_units(int col, int64_t len, int6
     case kSeqTok: return len;
     case kSeqBlk: return (len + block_size - 1) / block_size;
     case kSeqW128: return (len + 127) / 128;
+    case kSeqW256: return (len + 255) / 256;
     default: return (len + 1023) / 1024;
   }
 }
@@ -75,6 +76,7 @@ struct GateArgs {
   int64_t heads, kv_heads, block_size;
   int64_t max_nb;      // most blocks of any sequence (LDS bins of the rank kernel)
   int64_t gate_wgs;    // workgroups of the gate: (kv_heads if shared else heads) * sum ceil(len / 128)
+  int64_t gate_wgs256; // the same for 256-query workgroups: heads * sum ceil(len / 256)
   int64_t rank_wgs;    // workgroups of the rank kernel: heads * sum ceil(len / 1024)
   int head_dim;
   bool bf16_in;

@@ -119,13 +119,23 @@ def test_dense_any_length(dtype, causal, S):
         assert err <= tol, f"h={h}: max|o - oracle| = {err:.3e}"
 
 
-def test_exact_ties_prefer_lower_block():
+# Sequences of 512 blocks or more take the gate's long-sequence form (two
+# 32-query groups per wave); the gate tests below run both forms.
+LONG = (32768, 64)
+
+
+@pytest.mark.parametrize("S,Bs", [(1024, 128), LONG])
+def test_exact_ties_prefer_lower_block(S, Bs):
     """Blocks 2 and 5 are identical, so their gate scores tie exactly for
     every query; the lower index must win wherever the tie decides, on the
-    GPU exactly as in the oracle."""
+    GPU exactly as in the oracle. (With 512 blocks, block 2 is made the
+    best block of most queries, so that the tie decides their choice.)"""
     import sparse_long_context_moba_amd as moba
-    B, H, S, D, Bs = 1, 1, 1024, 128, 128
+    B, H, D = 1, 1, 128
     q, k, v = _inputs(12, B, H, S, D, Bs, "bf16", bias=0.3)
+    if S // Bs >= 512:
+        q[0, 0, :, 0] = _round(q[0, 0, :, 0] + 3.0, "bf16")
+        k[0, 0, 2 * Bs:3 * Bs, 0] = _round(k[0, 0, 2 * Bs:3 * Bs, 0] + 2.0, "bf16")
     k[0, 0, 5 * Bs:6 * Bs] = k[0, 0, 2 * Bs:3 * Bs]
     _, idx = moba.forward(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), Bs, 2, True)
     idx = idx.cpu().numpy()[0, 0]
@@ -159,14 +169,15 @@ def _band_inputs(H, S, D, Bs):
     return q, k, v
 
 
+@pytest.mark.parametrize("S", [4096, LONG[0]])
 @pytest.mark.parametrize("top_k,causal", [(3, True), (5, False)])
-def test_full_rescan_when_every_block_is_in_the_band(top_k, causal):
+def test_full_rescan_when_every_block_is_in_the_band(top_k, causal, S):
     """With the inputs of _band_inputs every query's rounding band reaches
     past its tracked list, so the gate re-scores all its eligible blocks in
     fp64 (one block per lane, the whole wave). The choice must be the
     oracle's, row for row."""
     import sparse_long_context_moba_amd as moba
-    H, S, D, Bs = 2, 4096, 128, 64
+    H, D, Bs = 2, 128, 64
     q, k, v = _band_inputs(H, S, D, Bs)
     idx = moba.select(to_dev(q, "bf16"), to_dev(k, "bf16"), Bs, top_k, causal)
     torch.cuda.synchronize()
@@ -176,15 +187,16 @@ def test_full_rescan_when_every_block_is_in_the_band(top_k, causal):
         np.testing.assert_array_equal(idx[0, h], res["idx"], err_msg=f"head {h}")
 
 
+@pytest.mark.parametrize("S,Bs", [(2048, 128), LONG])
 @pytest.mark.parametrize("case", ["query-norm-overflows", "scores-overflow", "key-norm-huge", "query-tiny"])
-def test_gate_with_extreme_magnitudes(case):
+def test_gate_with_extreme_magnitudes(case, S, Bs):
     """The gate's fast scores and rounding bound are fp32. A query whose
     norm overflows fp32, or a query and pooled key whose norms multiply
     past it (fast scores that may be infinite or NaN), is re-scanned in
     full in fp64; a huge pooled key or a tiny query only widens the band.
     The routing must be the oracle's, row for row."""
     import sparse_long_context_moba_amd as moba
-    H, S, D, Bs = 2, 2048, 128, 128
+    H, D = 2, 128
     q, k, v = _inputs(41, 1, H, S, D, Bs, "bf16")
     if case == "query-norm-overflows":
         q[0, 0, 1000:1100, 3] = 2.0 ** 120  # exact in bf16; its square is not finite in fp32
@@ -197,7 +209,7 @@ def test_gate_with_extreme_magnitudes(case):
         k[0, 1, 9 * Bs:10 * Bs, 11] = -(2.0 ** 120)
     else:
         q = _round(q * np.float32(2.0 ** -100), "bf16")
-    say(f"[gpu] extreme magnitudes: {case}")
+    say(f"[gpu] extreme magnitudes: {case} S={S} Bs={Bs}")
     idx = moba.select(to_dev(q, "bf16"), to_dev(k, "bf16"), Bs, 3, True)
     torch.cuda.synchronize()
     idx = idx.cpu().numpy()
@@ -281,11 +293,11 @@ def _grouped_keys(seed, S, D, Bs, groups, jitter, dtype):
     return _round(q, dtype), _round(k, dtype)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("top_k", [2, 3, 5, 9, 17])
-def test_select_crowded_scores(dtype, top_k):
+@pytest.mark.parametrize("dtype,top_k,S", [(d, k, 16384) for d in ("bf16", "f32") for k in (2, 3, 5, 9, 17)]
+                         + [("bf16", 3, LONG[0]), ("bf16", 5, LONG[0])])
+def test_select_crowded_scores(dtype, top_k, S):
     import sparse_long_context_moba_amd as moba
-    S, D, Bs = 16384, 128, 64
+    D, Bs = 128, 64
     q, k = _grouped_keys(20 + top_k, S, D, Bs, 7, 4e-3, dtype)
     say(f"[gpu] crowded select {dtype} top_k={top_k} S={S} Bs={Bs}")
     idx = moba.select(to_dev(q, dtype), to_dev(k, dtype), Bs, top_k).cpu().numpy()[0, 0]
