@@ -40,9 +40,19 @@
 
 namespace moba {
 
+// Waves per SIMD the register budget is set for: two, except fp32 inputs
+// at head_dim 128, whose query fragment (64 registers) and staged K/V
+// subtile (64) beside the output accumulators (64) do not fit in 256
+// registers; they run at one wave per SIMD with the whole register file.
+template <typename T, int D>
+constexpr int attn_waves() {
+  return sizeof(T) == 4 && D == 128 ? 1 : 2;
+}
+
 // ------------------------------------------------------- past-block gather
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gather_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(attn_waves<T, D>()))) void
+gather_attn_kernel(AttnArgs a) {
   using E = typename EngOf<T, D>::type;
   constexpr int NT = 64 * NW;
   MOBA_KERNEL_LDS(E)
@@ -109,7 +119,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // --------------------------------------------- own block + merge (and dense)
 template <typename T, int D, int NW, bool DENSE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void diag_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(attn_waves<T, D>()))) void
+diag_attn_kernel(AttnArgs a) {
   using E = typename EngOf<T, D>::type;
   constexpr int NT = 64 * NW, M = 32 * NW;
   MOBA_KERNEL_LDS(E)
