@@ -77,6 +77,8 @@ CASES = [
     ("f32-d64-bs64-len130-topk-all", 32, 1, 1, 130, 64, 64, 9, True, "f32"),
     ("bf16-d128-bs64-len1000-k17", 33, 1, 1, 1000, 128, 64, 17, True, "bf16"),
     ("f32-d64-bs128-len333-noncausal", 34, 1, 2, 333, 64, 128, 2, False, "f32"),
+    # 512 blocks: the gate's two-group form, head_dim 64, lists of 6
+    ("bf16-d64-bs64-k5-512-blocks", 35, 1, 1, 32768, 64, 64, 5, True, "bf16"),
 ]
 
 
@@ -342,6 +344,10 @@ VARLEN_CASES = [
     # label, seed, H, Hkv, D, Bs, top_k, causal, dtype, lengths
     ("bf16-d128-bs128-causal", 30, 2, 2, 128, 128, 3, True, "bf16", [576, 1024, 192]),
     ("f32-d64-bs256-noncausal", 31, 1, 1, 64, 256, 2, False, "f32", [512, 64, 1344]),
+    # a 514-block sequence: every sequence takes the gate's two-group form
+    # (256-query workgroups counted by the table's 256-row column), with
+    # two query heads per key/value head routing on their own
+    ("bf16-d64-bs64-gqa2-long", 36, 2, 1, 64, 64, 3, True, "bf16", [32768 + 77, 1000, 77]),
     # ragged lengths (not multiples of 64), mixed in one batch
     ("bf16-d128-bs128-causal-ragged", 32, 2, 2, 128, 128, 3, True, "bf16", [1000, 77, 2049]),
     ("bf16-d128-bs128-noncausal-ragged", 33, 2, 2, 128, 128, 3, False, "bf16", [1000, 77, 2049]),
