@@ -13,8 +13,8 @@
 // Mapping on gfx950: a workgroup owns 128 consecutive queries of one head,
 // a wave 32 of them; for long sequences 256 and 64, two 32-query groups per
 // wave (a wave's queries share c because block_size is a multiple of 64).
-// Tiles of 32 pooled keys are staged in LDS once per workgroup, double
-// buffered, one barrier per tile. Scores come from bf16 MFMA 32x32x16 with
+// Tiles of 32 pooled keys are staged in LDS once per workgroup (two or
+// three buffers), one barrier per tile. Scores come from bf16 MFMA 32x32x16 with
 // the pooled keys as the A operand (rows = blocks) and the queries as the
 // B operand (columns = queries), so lane l holds 16 block scores of query
 // l%32. The pooled keys enter as a bf16 hi/lo pair (two MFMA passes, fp32
@@ -544,21 +544,25 @@ struct pick_type<false, A, B> {
   using type = B;
 };
 
-// 32-query groups per wave (QG). With one group every pooled-key fragment
-// read from LDS feeds a single MFMA; two groups halve the reads per MFMA
-// and give each wave two independent chains, at two waves per SIMD
-// (256-query workgroups) instead of three. Two groups are taken for long
-// sequences of the per-head bf16 gate with short lists; with few tiles per
-// workgroup, short sequences run faster with more, smaller workgroups.
-// Waves per SIMD the register budget is set for (a shared gate holds two
-// query fragments).
-template <typename T, int D, int TT, bool SHARED, int QG>
+// Shapes of the per-head bf16 gate with short lists (top_k <= 5), by the
+// longest sequence's block count (same-box A/Bs, identical routing):
+//  * up to kShortMaxBlocks: one 32-query group per wave, two tile buffers
+//    (35 KB of LDS at head_dim 128) and four waves per SIMD, so four
+//    workgroups per compute unit; their short scans are bound by load
+//    latency (against three buffers at three waves: -9 % at 64 blocks,
+//    -13 % at 128, -6 % at 256 and 384; -3 % at 512 against two groups);
+//  * above it: two 32-query groups per wave (QG), 256-query workgroups at
+//    two waves per SIMD with three buffers and the branch-free stretch.
+//    Every pooled-key fragment read from LDS feeds two MFMAs, half the LDS
+//    reads per MFMA (-4 % at 2048 blocks against the one-group three-buffer
+//    form; the short form is 2 % slower at 1024 blocks and 5 % at 2048).
+// Other gates (shared, fp32, longer lists) take one group, three buffers
+// (two for fp32) and two waves per SIMD.
+template <typename T, int D, int TT, bool SHARED, int QG, int NBUF>
 constexpr int gate_waves() {
-  return (sizeof(T) == 2 && TT <= 6 && !SHARED && QG == 1) ? 3 : 2;
+  return (sizeof(T) == 2 && TT <= 6 && !SHARED && QG == 1 && NBUF == 2) ? 4 : 2;
 }
-// Sequences of at least this many blocks take the two-group gate (measured:
-// 4 % faster at 2048 blocks, even at 512, 2 % slower at 256).
-constexpr int kTwoGroupMinBlocks = 512;
+constexpr int kShortMaxBlocks = 512;
 
 // Exact top-TT over every eligible block of one query, by the whole wave:
 // the query's fp64 vector (D values) is in this wave's LDS slice qs; lane l
@@ -759,8 +763,8 @@ __device__ void write_row(int32_t* row, const int (&sel)[TT], bool scoring, int 
 // query type. SHARED: one workgroup row of queries per key/value head, the
 // scores being those of the group's summed query (bf16 MFMA on its hi/lo
 // split, T = bf16).
-template <typename T, typename TQ, int D, int TT, bool SHARED, int QG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT, SHARED, QG>()))) void
+template <typename T, typename TQ, int D, int TT, bool SHARED, int QG, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gate_waves<T, D, TT, SHARED, QG, NBUF>()))) void
 gate_topk_kernel(GateArgs a) {
   using Ops = typename pick_type<SHARED, GateOpsSplitQ<D>, GateOps<T, D>>::type;
   static_assert(!SHARED || sizeof(T) == 2, "a shared gate scores on the bf16 pair");
@@ -871,17 +875,18 @@ gate_topk_kernel(GateArgs a) {
   // scores of tile i (issued one step earlier) into the key lists. Only the
   // ordering of independent work changes; every tile is scored and folded
   // exactly once.
-  //  * bf16 ops load tiles straight into LDS (three buffers, tile t in
-  //    buffer t % 3): step i waits for its own loads of tile i+1 (issued
-  //    two steps earlier, leaving tile i+2's in flight), passes the barrier
-  //    (all waves' loads of tile i+1 landed; every wave is done reading
-  //    tile i, which its MFMAs read in step i-1) and then loads tile i+3
-  //    into tile i's buffer.
+  //  * bf16 ops load tiles straight into LDS (NBUF buffers, tile t in
+  //    buffer t % NBUF): step i waits for its own loads of tile i+1 (with
+  //    three buffers issued two steps earlier, leaving tile i+2's in
+  //    flight; with two, one step earlier), passes the barrier (all waves'
+  //    loads of tile i+1 landed; every wave is done reading tile i, which
+  //    its MFMAs read in step i-1) and then loads tile i+NBUF into tile
+  //    i's buffer.
   //  * fp32 ops stage through registers (two buffers, tile t in buffer
   //    t & 1): step i stores tile i+1 (fetched one step earlier), passes the
   //    barrier and fetches tile i+2.
   constexpr bool DMA = Ops::kDma;
-  constexpr int NBUF = DMA ? 3 : 2;
+  static_assert(NBUF == 2 || (DMA && NBUF == 3), "tile buffers: two, or three for direct loads");
   auto buf = [&](int t) { return tile + (t % NBUF) * Ops::TILE_BYTES; };
   const int ntiles = (wg_jend + kTileB - 1) / kTileB;  // workgroup-uniform
   const int my_tiles = scoring ? (jend + kTileB - 1) / kTileB : 0;
@@ -902,9 +907,9 @@ gate_topk_kernel(GateArgs a) {
   f32x16 acc_a[QG], acc_b[QG];
   if constexpr (DMA) {
     Ops::dma_offsets(doff, w, lane, lo_off, kTileB);
-    for (int t = 0; t < min(ntiles, 3); ++t) issue(t);
-    if (ntiles >= 3) lds_dma_wait_n<2 * Ops::NDMA>();
-    else if (ntiles == 2) lds_dma_wait_n<Ops::NDMA>();
+    for (int t = 0; t < min(ntiles, NBUF); ++t) issue(t);
+    if (NBUF == 3 && ntiles >= 3) lds_dma_wait_n<2 * Ops::NDMA>();
+    else if (ntiles >= 2) lds_dma_wait_n<Ops::NDMA>();
     else lds_dma_wait();
   } else if (ntiles > 0) {
     Ops::fetch(stg, a, kvb0, NB, 0, tid);
@@ -916,10 +921,10 @@ gate_topk_kernel(GateArgs a) {
   auto step = [&](int i, f32x16(&cur)[QG], f32x16(&nxt)[QG]) {
     char* next_buf = buf(i + 1);
     if constexpr (DMA) {
-      if (i + 2 < ntiles) lds_dma_wait_n<Ops::NDMA>();
+      if (NBUF == 3 && i + 2 < ntiles) lds_dma_wait_n<Ops::NDMA>();
       else lds_dma_wait();
       __syncthreads();
-      if (i + 3 < ntiles) issue(i + 3);
+      if (i + NBUF < ntiles) issue(i + NBUF);
     } else {
       if (i + 1 < ntiles) Ops::put(next_buf, stg, tid);
       __syncthreads();
@@ -950,7 +955,7 @@ gate_topk_kernel(GateArgs a) {
   int i0 = 0;
   // (Only where it pays for its code size: the per-head bf16 gate with a
   // short list, i.e. top_k up to 5.)
-  if constexpr (DMA && std::is_same<Ops, GateOps<bf16, D>>::value && TT <= 6) {
+  if constexpr (DMA && NBUF == 3 && std::is_same<Ops, GateOps<bf16, D>>::value && TT <= 6) {
     // Steady stretch: a segment of kSegTiles steps at a time with no
     // per-step conditions, while every wave of the workgroup has the
     // segment's tiles and the next one full, and the tiles the segment
@@ -1090,12 +1095,13 @@ __global__ __launch_bounds__(256) void rank_kernel(GateArgs a) {
   }
 }
 
-template <typename T, typename TQ, int D, int TT, bool SHARED, int QG = 1>
+template <typename T, typename TQ, int D, int TT, bool SHARED, int QG = 1, int NBUF = 3>
 static void gate_go(const GateArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(QG == 2 ? a.gate_wgs256 : a.gate_wgs));
   using Ops = typename pick_type<SHARED, GateOpsSplitQ<D>, GateOps<T, D>>::type;
-  const int lds = (Ops::kDma ? 3 : 2) * Ops::TILE_BYTES;
-  hipLaunchKernelGGL((gate_topk_kernel<T, TQ, D, TT, SHARED, QG>), grid, dim3(256), lds, s, a);
+  constexpr int NB = Ops::kDma ? NBUF : 2;
+  const int lds = NB * Ops::TILE_BYTES;
+  hipLaunchKernelGGL((gate_topk_kernel<T, TQ, D, TT, SHARED, QG, NB>), grid, dim3(256), lds, s, a);
 }
 
 template <typename T, typename TQ, int D, bool SHARED>
@@ -1104,15 +1110,28 @@ static void gate_pick(const GateArgs& a, hipStream_t s) {
   // cut usually ends inside it.
   const int m = a.k_eff - 1;
   if constexpr (sizeof(T) == 2 && !SHARED) {
-    if (a.max_nb >= kTwoGroupMinBlocks && m <= 4) {
-      if (m <= 2) gate_go<T, TQ, D, 4, SHARED, 2>(a, s);
-      else gate_go<T, TQ, D, 6, SHARED, 2>(a, s);
+    if (m <= 4) {  // the per-head bf16 gate with short lists (see gate_waves)
+      const bool two_groups = a.max_nb > kShortMaxBlocks;
+      if (m <= 2) {
+        if (two_groups) gate_go<T, TQ, D, 4, SHARED, 2>(a, s);
+        else gate_go<T, TQ, D, 4, SHARED, 1, 2>(a, s);
+      } else {
+        if (two_groups) gate_go<T, TQ, D, 6, SHARED, 2>(a, s);
+        else gate_go<T, TQ, D, 6, SHARED, 1, 2>(a, s);
+      }
+      return;
+    }
+  } else {
+    if (m <= 2) {
+      gate_go<T, TQ, D, 4, SHARED>(a, s);
+      return;
+    }
+    if (m <= 4) {
+      gate_go<T, TQ, D, 6, SHARED>(a, s);
       return;
     }
   }
-  if (m <= 2) gate_go<T, TQ, D, 4, SHARED>(a, s);
-  else if (m <= 4) gate_go<T, TQ, D, 6, SHARED>(a, s);
-  else if (m <= 8) gate_go<T, TQ, D, 10, SHARED>(a, s);
+  if (m <= 8) gate_go<T, TQ, D, 10, SHARED>(a, s);
   else gate_go<T, TQ, D, kMaxSlots + 2, SHARED>(a, s);
 }
 

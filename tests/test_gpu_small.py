@@ -77,8 +77,8 @@ CASES = [
     ("f32-d64-bs64-len130-topk-all", 32, 1, 1, 130, 64, 64, 9, True, "f32"),
     ("bf16-d128-bs64-len1000-k17", 33, 1, 1, 1000, 128, 64, 17, True, "bf16"),
     ("f32-d64-bs128-len333-noncausal", 34, 1, 2, 333, 64, 128, 2, False, "f32"),
-    # 512 blocks: the gate's two-group form, head_dim 64, lists of 6
-    ("bf16-d64-bs64-k5-512-blocks", 35, 1, 1, 32768, 64, 64, 5, True, "bf16"),
+    # 520 blocks: the gate's two-group form, head_dim 64, lists of 6
+    ("bf16-d64-bs64-k5-520-blocks", 35, 1, 1, 33280, 64, 64, 5, True, "bf16"),
 ]
 
 
@@ -121,16 +121,17 @@ def test_dense_any_length(dtype, causal, S):
         assert err <= tol, f"h={h}: max|o - oracle| = {err:.3e}"
 
 
-# Sequences of 512 blocks or more take the gate's long-sequence form (two
-# 32-query groups per wave); the gate tests below run both forms.
-LONG = (32768, 64)
+# Sequences of more than 512 blocks take the gate's long-sequence form (two
+# 32-query groups per wave), shorter ones its short form (two tile buffers,
+# four waves per SIMD); the gate tests below run both.
+LONG = (33280, 64)
 
 
 @pytest.mark.parametrize("S,Bs", [(1024, 128), LONG])
 def test_exact_ties_prefer_lower_block(S, Bs):
     """Blocks 2 and 5 are identical, so their gate scores tie exactly for
     every query; the lower index must win wherever the tie decides, on the
-    GPU exactly as in the oracle. (With 512 blocks, block 2 is made the
+    GPU exactly as in the oracle. (With 520 blocks, block 2 is made the
     best block of most queries, so that the tie decides their choice.)"""
     import sparse_long_context_moba_amd as moba
     B, H, D = 1, 1, 128
