@@ -26,16 +26,15 @@ namespace moba {
 //                its own block's keys), causal mask, double-buffered; it
 //                then adds the slots' partials in slot order and writes dq
 //                (no atomics);
-//  dkv, dk     — key-major: a workgroup holds 128 (or 64) keys of one block
+//  dk (x2)     — key-major: a workgroup holds 128 (or 64) keys of one block
 //                (32 per wave, as the B operand the way the forward holds
 //                queries) and streams 64-row subtiles of the queries that
 //                attend them: the block's own queries, then its listed
 //                queries (gathered rows), for every query head of the
-//                key/value head; blocks in order, heaviest first. dkv
-//                (software-pipelined over two buffer sets) accumulates
-//                dV^T += dO^T P for 128 keys, dk (single-buffered)
-//                dK^T += Q^T dS, and dV for 64 keys, both on the P.V path;
-//                one pass for both would not fit the register file.
+//                key/value head; blocks in order, heaviest first. One pass
+//                accumulates dV^T += dO^T P, the other dK^T += Q^T dS, both
+//                on the P.V path; one pass for both would not fit the
+//                register file.
 namespace {
 
 // C[row][lane column] for 64 LDS rows (K-swizzled layout) against the B
@@ -421,195 +420,19 @@ __global__ __launch_bounds__(256) void list_meta_kernel(BwdArgs a) {
   }
 }
 
-// dV (PASS 0; dK is dk_kernel) for 32 * NW keys of one block of one
-// key/value head. The 64-row query subtiles that attend those keys (for
-// every query head of the group: the block's own queries at or after the
-// keys, then its listed queries) are numbered 0 .. N-1 and software
-// pipelined over two LDS buffer sets: while subtile i is computed from one
-// set, the rows of i + 1 load into the other, and wave 0 holds the row
-// numbers, log-sum-exps and deltas of i + 2 in registers. Q and dO are
-// staged once each (K-swizzled); the dK and dV products read them
-// transposed from the same copy.
+// dV (PASS = 0) or dK (PASS = 1) for 32 * NW keys of one block of one
+// key/value head, single-buffered: each 64-row query subtile is staged
+// (row numbers, log-sum-exps and deltas, for listed rows from
+// list_meta_kernel's contiguous arrays, then the rows of Q and dO) and
+// then computed; dV^T += dO^T P reads dO transposed from a V-swizzled copy,
+// dK^T += Q^T dS reads Q transposed from its one K-swizzled copy. The dV
+// pass (168 registers) runs at three waves per SIMD, three workgroups of
+// 32 KB of LDS per compute unit, which hides the row gathers' latency
+// better than two waves of a two-buffer pipeline; the dK pass holds K and V
+// fragments besides its accumulators and runs at two.
 template <int D, int PASS, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dkv_kernel(BwdArgs a) {
-  using E = EngBF16<D>;
-  constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, KEYS = 32 * NW;
-  __shared__ __align__(16) char bq[2][E::TB], bx[2][E::TB];
-  __shared__ int rows[2][64];
-  __shared__ float lse2s[2][64], deltas[2][64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  // Blocks in order, all heads of a block together: early blocks are in
-  // the most lists (causal routing), so the longest workgroups start first.
-  const int64_t nchunk = a.block_size / KEYS;
-  const int64_t nkv = a.bh / a.group;
-  const int64_t kc = blockIdx.x % nchunk;
-  const int64_t kvh = (blockIdx.x / nchunk) % nkv;
-  const int64_t j = blockIdx.x / (nchunk * nkv);
-  const int64_t k0 = j * a.block_size + kc * KEYS;
-  if (k0 >= a.seq_len) return;  // past the end of a short last block
-  // This lane's key; lanes past the sequence's end compute on its last
-  // key and store nothing.
-  const int u = (int)k0 + 32 * w + col;
-  const int uc = min(u, (int)a.seq_len - 1);
-  const bf16* krow = reinterpret_cast<const bf16*>(a.k) + (kvh * a.seq_len + uc) * D;
-  const bf16* vrow = reinterpret_cast<const bf16*>(a.v) + (kvh * a.seq_len + uc) * D;
-  bf16x8 kf[KC], vf[PASS == 1 ? KC : 1];
-  load_frags<D>(kf, krow, h);
-  if constexpr (PASS == 1) load_frags<D>(vf, vrow, h);
-  const float sl2 = kLog2e / __builtin_sqrtf((float)D);
-  const int slots = a.k_eff - 1;
-  const int64_t jend = min<int64_t>((j + 1) * a.block_size, a.seq_len);
-  const int64_t qs = a.causal ? k0 : j * a.block_size;  // first own query that sees the keys
-  const int n_own = (int)((jend - qs + 63) / 64);
-  // Subtile i: (query head, own or listed, first row or list position, rows).
-  struct Sub {
-    int64_t bh;
-    int64_t first;
-    int n;
-    bool own;
-  };
-  auto sub_at = [&](int i) {
-    Sub d{};
-    for (int g = 0; g < a.group; ++g) {
-      const int64_t bh = kvh * a.group + g;
-      if (i < n_own) {
-        d.bh = bh;
-        d.own = true;
-        d.first = qs + 64 * (int64_t)i;
-        d.n = (int)min<int64_t>(64, jend - d.first);
-        return d;
-      }
-      i -= n_own;
-      int64_t o0 = 0, cnt = 0;
-      if (slots > 0) {
-        o0 = a.offset[bh * a.n_blocks + j];
-        cnt = a.offset[bh * a.n_blocks + j + 1] - o0;
-      }
-      const int n_list = (int)((cnt + 63) / 64);
-      if (i < n_list) {
-        d.bh = bh;
-        d.own = false;
-        d.first = o0 + 64 * (int64_t)i;
-        d.n = (int)min<int64_t>(64, cnt - 64 * (int64_t)i);
-        return d;
-      }
-      i -= n_list;
-    }
-    return d;
-  };
-  int total = 0;
-  for (int g = 0; g < a.group; ++g) {
-    const int64_t bh = kvh * a.group + g;
-    int64_t cnt = 0;
-    if (slots > 0) cnt = a.offset[bh * a.n_blocks + j + 1] - a.offset[bh * a.n_blocks + j];
-    total += n_own + (int)((cnt + 63) / 64);
-  }
-  // Wave 0's registers: row number, log-sum-exp and delta of its lane's row
-  // of a subtile (a padding row repeats the first row with weight 0).
-  int mt = 0;
-  float ml = 0.f, md = 0.f;
-  auto meta_load = [&](const Sub& d) {
-    const bool ok = lane < d.n;
-    const int64_t i = d.first + (ok ? lane : 0);
-    if (d.own) {
-      mt = (int)i;
-      ml = a.lse2[d.bh * a.seq_len + i];
-      md = a.delta[d.bh * a.seq_len + i];
-    } else {
-      mt = a.lt[i];
-      ml = a.ll[i];
-      md = a.ld[i];
-    }
-    if (!ok) {
-      ml = __builtin_inff();
-      md = 0.f;
-    }
-  };
-  auto meta_store = [&](int x) {
-    rows[x][lane] = mt;
-    lse2s[x][lane] = ml;
-    deltas[x][lane] = md;
-  };
-  auto rows_in = [&](const Sub& d, int x) {
-    const bf16* qb = reinterpret_cast<const bf16*>(a.q) + d.bh * a.seq_len * D;
-    const bf16* gb = reinterpret_cast<const bf16*>(a.dout) + d.bh * a.seq_len * D;
-    load_rows<D, NT, false>(qb, rows[x], bq[x], tid);
-    load_rows<D, NT, false>(gb, rows[x], bx[x], tid);
-  };
-  f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  auto compute = [&](const Sub& d, int x) {
-    const bool mask = d.own && a.causal;
-    f32x16 s[2];
-    mm_rows<D>(bq[x], lane, kf, s);
-    f32x16 dp[2];
-    if constexpr (PASS == 1) mm_rows<D>(bx[x], lane, vf, dp);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int r0 = 32 * nt + 8 * rg + 4 * h;  // rows of elements 4 rg .. 4 rg + 3
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[x][r0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&deltas[x][r0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rg + e;
-          float p = fast_exp2(__builtin_fmaf(s[nt][r], sl2, -l4[e]));
-          if (mask && u > rows[x][r0 + e]) p = 0.f;
-          if constexpr (PASS == 0) s[nt][r] = p;
-          else s[nt][r] = p * (dp[nt][r] - d4[e]);
-        }
-      }
-    // dV^T += dO^T P or dK^T += Q^T dS, read transposed from the K-swizzled copy.
-    mm_trans<D, false>(PASS == 0 ? bx[x] : bq[x], lane, s, acc);
-  };
-  // Prologue: metadata of 0 stored, rows of 0 loading, metadata of 1 in
-  // wave 0's registers.
-  Sub cur = sub_at(0);
-  if (w == 0) {
-    meta_load(cur);
-    meta_store(0);
-  }
-  __syncthreads();
-  rows_in(cur, 0);
-  Sub nxt = total > 1 ? sub_at(1) : Sub{};
-  if (w == 0 && total > 1) meta_load(nxt);
-  for (int i = 0; i < total; ++i) {
-    const int x = i & 1;
-    // Wave 0 publishes the metadata of i + 1, requested during step i - 1
-    // (set x ^ 1 was last read by step i - 1, before its closing barrier).
-    if (w == 0 && i + 1 < total) meta_store(x ^ 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows of i, loaded during step i - 1
-    lds_dma_wait();
-    __syncthreads();
-    // Under the compute of i: the rows of i + 1 and the metadata of i + 2.
-    Sub nn{};
-    if (i + 2 < total) nn = sub_at(i + 2);
-    if (i + 1 < total) rows_in(nxt, x ^ 1);
-    if (w == 0 && i + 2 < total) meta_load(nn);
-    compute(cur, x);
-    __syncthreads();  // set x is free for step i + 1's metadata and rows
-    cur = nxt;
-    nxt = nn;
-  }
-  if (u >= a.seq_len) return;
-  bf16* dst = reinterpret_cast<bf16*>(PASS == 0 ? a.dv : a.dk) + (kvh * a.seq_len + u) * D;
-  store_row_bf16<D>(dst, acc, h, PASS == 0 ? 1.f : 1.f / __builtin_sqrtf((float)D));
-}
-
-// dK (PASS = 1), or dV for 64 keys (PASS = 0), for 32 * NW keys of one
-// block of one key/value head, single-buffered: each 64-row query
-// subtile is staged (row numbers, log-sum-exps and deltas, for listed rows
-// from list_meta_kernel's contiguous arrays, then the rows of Q and dO,
-// K-swizzled) and then computed; dK^T += Q^T dS reads Q transposed from
-// its one copy. For dK this beats the pipelined dkv_kernel, which spills
-// registers in this pass (same-box A/B at headline_32k: 1.75-1.79 against
-// 1.94 ms; for dV the pipelined kernel wins, 1.47 against 1.49-1.54 ms),
-// and it beats this kernel with double-buffered metadata (12-24 registers
-// spilled: 2.16-2.33 against 1.67-1.69 ms).
-template <int D, int PASS, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void dk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PASS == 0 ? 3 : 2))) void
+dk_kernel(BwdArgs a) {
   using E = EngBF16<D>;
   constexpr int NT = 64 * NW, KC = D / 16, DT = D / 32, KEYS = 32 * NW;
   __shared__ __align__(16) char bq[E::TB], bx[E::TB];
@@ -748,17 +571,17 @@ hipError_t backward_t(const BwdArgs& a, hipStream_t s) {
   const int64_t last = a.seq_len - (a.n_blocks - 1) * a.block_size;
   const bool wide = a.block_size % 128 == 0 && last % 128 == 0;
   const int64_t kv_wgs = (a.bh / a.group) * a.n_blocks * (a.block_size / (wide ? 128 : 64));
-  {
-    // 64 keys: the single-buffered kernel (32 KB of LDS) keeps two waves per
-    // SIMD, which the pipelined one (64 KB for two waves) would not.
-    KernelTimer t(s, "bwd_dv");
-    if (wide) hipLaunchKernelGGL((dkv_kernel<D, 0, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dk_kernel<D, 0, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
-  }
+  // dK before dV: in that order both passes ran faster in a same-box A/B
+  // (4.56 against 4.62 ms per backward at headline_32k).
   {
     KernelTimer t(s, "bwd_dk");
     if (wide) hipLaunchKernelGGL((dk_kernel<D, 1, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((dk_kernel<D, 1, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
+  }
+  {
+    KernelTimer t(s, "bwd_dv");
+    if (wide) hipLaunchKernelGGL((dk_kernel<D, 0, 4>), dim3((unsigned)kv_wgs), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dk_kernel<D, 0, 2>), dim3((unsigned)kv_wgs), dim3(128), 0, s, a);
   }
   return hipGetLastError();
 }
