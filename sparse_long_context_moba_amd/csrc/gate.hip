@@ -556,11 +556,15 @@ struct pick_type<false, A, B> {
 //    Every pooled-key fragment read from LDS feeds two MFMAs, half the LDS
 //    reads per MFMA (-4 % at 2048 blocks against the one-group three-buffer
 //    form; the short form is 2 % slower at 1024 blocks and 5 % at 2048).
-// Other gates (shared, fp32, longer lists) take one group, three buffers
-// (two for fp32) and two waves per SIMD.
+// The shared gate (two query fragments, hi and lo of the group's summed
+// query) takes the short form at three waves per SIMD at every length
+// (against three buffers at two waves: -15 % at 64 blocks with top_k 3,
+// -11 % with top_k 5, -18 % at 256 blocks, -16 % at 512, -17 % at 1024,
+// -19 % at 2048); fp32 gates and longer lists take one group and two waves
+// (two buffers for fp32, three else).
 template <typename T, int D, int TT, bool SHARED, int QG, int NBUF>
 constexpr int gate_waves() {
-  return (sizeof(T) == 2 && TT <= 6 && !SHARED && QG == 1 && NBUF == 2) ? 4 : 2;
+  return (sizeof(T) == 2 && TT <= 6 && QG == 1 && NBUF == 2) ? (SHARED ? 3 : 4) : 2;
 }
 constexpr int kShortMaxBlocks = 512;
 
@@ -1119,6 +1123,20 @@ static void gate_pick(const GateArgs& a, hipStream_t s) {
         if (two_groups) gate_go<T, TQ, D, 6, SHARED, 2>(a, s);
         else gate_go<T, TQ, D, 6, SHARED, 1, 2>(a, s);
       }
+      return;
+    }
+  } else if constexpr (SHARED) {
+    if (m <= 4) {
+      if (m <= 2) gate_go<T, TQ, D, 4, SHARED, 1, 2>(a, s);
+      else gate_go<T, TQ, D, 6, SHARED, 1, 2>(a, s);
+      return;
+    }
+    if (m <= 2) {
+      gate_go<T, TQ, D, 4, SHARED>(a, s);
+      return;
+    }
+    if (m <= 4) {
+      gate_go<T, TQ, D, 6, SHARED>(a, s);
       return;
     }
   } else {

@@ -58,6 +58,10 @@ CASES = [
     ("bf16-d64-g2-shared-k5", 41, 2, 4, 2, 1536, 64, 64, 5, True, "bf16", True),
     ("f32-d64-g2-shared-noncausal", 42, 1, 4, 2, 512, 64, 128, 2, False, "f32", True),
     ("f32-d128-g2-per-head", 43, 1, 2, 1, 768, 128, 128, 4, True, "f32", False),
+    # 520 blocks: the long forms of both gates (two query groups per wave
+    # per head; the shared gate's two-buffer form)
+    ("bf16-d128-g2-shared-520-blocks", 48, 1, 2, 1, 33280, 128, 64, 3, True, "bf16", True),
+    ("bf16-d128-g2-per-head-520-blocks", 49, 1, 2, 1, 33280, 128, 64, 5, True, "bf16", False),
     ("bf16-d128-g8-shared-k17", 44, 1, 8, 1, 2048, 128, 64, 17, True, "bf16", True),
     ("bf16-d128-g2-shared-short-block", 45, 1, 4, 2, 1216, 128, 256, 3, True, "bf16", True),
     ("bf16-d128-g4-shared-topk-all", 46, 1, 4, 1, 512, 128, 64, 9, True, "bf16", True),
